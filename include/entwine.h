@@ -1,0 +1,237 @@
+/*
+ * entwine.h -- C ABI of a tile-overlapped GEMM-ReduceScatter for AMD Instinct
+ * MI355X (gfx950), taken at one GPU's share of the work.
+ *
+ * Method: "Entwine: Coordinating Tiled Computation and Fine-Grained
+ * Communication across GPUs" (paperpeel.com/paper/2609.11562).
+ *
+ * The operation (Sec. 2.1, GEMM-ReduceScatter Execution; Sec. 3.1): P ranks
+ * each hold a slice of the reduction dimension; rank r computes the partial
+ * product C_r = X_r * W_r (M x N) and the ReduceScatter hands rank d the row
+ * partition [d*M/P, (d+1)*M/P) of sum_r C_r.  This library runs rank
+ * `rank`'s side on one GPU: a bf16 MFMA GEMM produces C_rank tile by tile in a
+ * selectable order (Sec. 3.1, "Interleaved production", Equation (1)) and
+ * publishes one ready flag per output tile after the tile's stores (Sec. 4.2);
+ * a concurrent persistent reduction kernel whose grid is capped by the
+ * communication budget (Sec. 3.2) waits on each tile's flags and reduces the
+ * local contribution with the P-1 peer contributions in rank order (Sec. 4.2,
+ * ReduceTile).  The peers' contributions are caller-provided device buffers:
+ * on one GPU they stand in for the data that peers would publish.
+ *
+ * Conventions for every entry point:
+ *   - Return value: an entwine_status.  Errors never abort the process and
+ *     never throw.  When an error is detected before launch nothing is
+ *     enqueued; entwine_last_error_message() gives a thread-local detail.
+ *   - Calls that take a stream are asynchronous: they enqueue device work on
+ *     `stream` (a hipStream_t passed as void*, NULL = the null stream) and
+ *     return.  Device-side failures (the reduction watchdog) are reported by
+ *     entwine_device_status().
+ *   - The caller owns every buffer it passes; buffers must stay valid until
+ *     the work enqueued on `stream` has completed.  The library owns its
+ *     workspace (per device, grown on demand, reused across calls, released
+ *     by entwine_release()).
+ *   - Calls are serialized on the library's workspace: each call's kernels
+ *     start after the previous call's kernels on the same device finished.
+ *     Host threads may call concurrently; a mutex guards the workspace.
+ *   - Element types: bf16 is IEEE binary32 truncated to its upper 16 bits
+ *     (stored as uint16), rounding is to nearest even.
+ */
+#ifndef ENTWINE_H
+#define ENTWINE_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum entwine_status {
+  ENTWINE_OK = 0,
+  ENTWINE_ERR_INVALID_ARGUMENT = 1, /* shape, rank, pointer, alignment, alias or enum out of range */
+  ENTWINE_ERR_UNSUPPORTED = 2,      /* well-formed but not built: P > 8, K_local % 64 != 0, sizes
+                                       beyond 32-bit element indexing, unsupported tile shape */
+  ENTWINE_ERR_OUT_OF_MEMORY = 3,    /* workspace growth failed */
+  ENTWINE_ERR_HIP = 4,              /* a HIP runtime call failed (detail in the message) */
+  ENTWINE_ERR_TIMEOUT = 5           /* a reduction workgroup gave up waiting on a tile flag */
+} entwine_status;
+
+/* Production orders of the GEMM's output blocks (Sec. 2.2 "Insight 1",
+ * Sec. 3.1 "Interleaved production" and Equation (1), Sec. 5.3.1).
+ * Blocks inside a partition are always numbered N-major (column index
+ * fastest); the orders differ in how the P partitions are visited. */
+enum {
+  ENTWINE_ORDER_AUTO = -1,           /* from the tuning table, else INTERLEAVED */
+  ENTWINE_ORDER_ROW_MAJOR = 0,       /* partitions 0..P-1, one contiguous run each */
+  ENTWINE_ORDER_PARTITION_MAJOR = 1, /* contiguous runs starting after `rank`, the local run last */
+  ENTWINE_ORDER_INTERLEAVED = 2,     /* logical block p -> partition p mod P, block p / P */
+  ENTWINE_ORDER_COL_MAJOR = 3        /* M-major raster over the global block grid */
+};
+
+/* comm_budget: the reduction kernel's grid size x (Sec. 3.2 "Communication
+ * budget"), capped at the number Q of tiles in the rank's partition and
+ * required to stay below the device's CU count (Sec. 4.3).
+ * ENTWINE_BUDGET_SEQUENTIAL runs the GEMM to completion and then the
+ * reduction over all tiles, with no overlap (the non-overlapped baseline). */
+#define ENTWINE_BUDGET_AUTO (-1)
+#define ENTWINE_BUDGET_SEQUENTIAL 0
+
+enum { ENTWINE_BF16 = 0, ENTWINE_F32 = 1 };
+
+/* How the readiness of a peer's contribution is modelled on one GPU.
+ * PRESEEDED: the peer buffers hold finished contributions; only the local
+ * tile flag is awaited.  SYMMETRIC: peer r's contribution to tile t counts as
+ * ready once this GPU's GEMM has finished the block at the logical position
+ * where rank r would produce tile t, i.e. all ranks are assumed to progress
+ * alike (Sec. 3.1: every rank runs the same traversal). */
+enum { ENTWINE_PEERS_PRESEEDED = 0, ENTWINE_PEERS_SYMMETRIC = 1 };
+
+/* Layout of W (K_local x N). */
+enum {
+  ENTWINE_W_NK = 0, /* [N][K_local] row-major: K contiguous (a linear layer's weight) */
+  ENTWINE_W_KN = 1  /* [K_local][N] row-major: N contiguous (reserved; not built yet) */
+};
+
+/* Release granularity (Sec. 5.3.2): tiles released together. */
+#define ENTWINE_RELEASE_TILE 1       /* each tile on its own flag (the method) */
+#define ENTWINE_RELEASE_PARTITION 0  /* a tile waits for the last tile of its partition */
+#define ENTWINE_RELEASE_OUTPUT (-1)  /* a tile waits for the last block of the whole GEMM */
+
+/*
+ * entwine_gemm_rs -- rank `rank`'s share of C = sum_r X_r * W_r followed by
+ * ReduceScatter (Sec. 2.1, 3.1), with tile-level overlap.
+ *
+ *   X              device, bf16 [M][K_local] row-major: this rank's slice of
+ *                  the activations.  16-byte aligned.
+ *   W              device, bf16 [N][K_local] row-major (K contiguous): this
+ *                  rank's slice of the weight, element (k, n) at W[n*K_local+k].
+ *                  16-byte aligned.
+ *   peer_partials  HOST array of P device pointers.  peer_partials[r] (r !=
+ *                  rank) is bf16 [M/P][N] row-major: peer r's contribution to
+ *                  partition `rank`.  peer_partials[rank] is ignored (may be
+ *                  NULL).  May be NULL when P == 1.  16-byte aligned.
+ *   out            device, bf16 [M/P][N] row-major: rows [rank*M/P,
+ *                  (rank+1)*M/P) of sum_r C_r.  Fully overwritten, never read;
+ *                  must not overlap any input.  16-byte aligned.
+ *   M, N, K_local  M % P == 0, N % 8 == 0, K_local % 64 == 0, all > 0;
+ *                  M*K_local, N*K_local and M*N below 2^31.
+ *   P, rank        1 <= P <= 8, 0 <= rank < P.
+ *   tile_order     ENTWINE_ORDER_* (AUTO = tuning table, else INTERLEAVED).
+ *   comm_budget    x >= 1 overlapped (clamped to Q), 0 sequential, -1 AUTO.
+ *                  x must be below the device's CU count.
+ *   stream         hipStream_t (as void*) the work is ordered on.
+ * Defaults: 128x128 reduction tiles, GEMM blocks from the tuning table or a
+ * shape heuristic, 256 reducer threads, PRESEEDED peers, per-tile release.
+ * Numerics: fp32 accumulation; the local own-partition partial is kept in
+ * fp32, the reduction adds peers in ascending rank order in fp32 and rounds
+ * once to bf16.  For a fixed GEMM block shape the output bits do not depend
+ * on tile_order, comm_budget, reducer threads or peer readiness mode.
+ */
+int entwine_gemm_rs(const void* X, const void* W, const void* const* peer_partials, void* out,
+                    int64_t M, int64_t N, int64_t K_local, int P, int rank,
+                    int tile_order, int comm_budget, void* stream);
+
+/* Extended configuration.  Zero-initialise with entwine_config_init(). */
+typedef struct entwine_config {
+  int32_t struct_size;     /* sizeof(entwine_config) */
+  int32_t block_m;         /* GEMM block rows BM: 0 = auto, else 128 or 256 */
+  int32_t block_n;         /* GEMM block cols BN: 0 = auto, else 128 or 256 */
+  int32_t tile_m;          /* reduction tile rows TM: 0 = 128, else 64 or 128; BM % TM == 0 */
+  int32_t tile_n;          /* reduction tile cols TN: 0 = 128, else 64 or 128; BN % TN == 0 */
+  int32_t reducer_threads; /* b: 0 = 256, else 128, 256 or 512 (Sec. 4.3) */
+  int32_t w_layout;        /* ENTWINE_W_NK */
+  int32_t peer_dtype;      /* ENTWINE_BF16 or ENTWINE_F32: peers and outgoing contributions */
+  int32_t out_dtype;       /* ENTWINE_BF16 or ENTWINE_F32 */
+  int32_t peer_ready;      /* ENTWINE_PEERS_PRESEEDED or ENTWINE_PEERS_SYMMETRIC */
+  int32_t release_group;   /* ENTWINE_RELEASE_* or g > 1 tiles per release group */
+  int32_t seq_reduce_slabs;/* sequential mode: row slabs per tile for the reduction grid; 0 = auto */
+  uint32_t poll_timeout_ms;/* reduction watchdog; 0 = 2000 ms */
+  int32_t withhold_tile;   /* failure injection for tests: 0 = off; t+1 makes tile t's local
+                              wait watch a flag that no GEMM of the call sets, so that tile's
+                              reduction workgroup times out (ENTWINE_ERR_TIMEOUT) */
+  int32_t reserved[7];
+} entwine_config;
+
+void entwine_config_init(entwine_config* cfg);
+
+/* As entwine_gemm_rs with an explicit configuration (cfg may be NULL). */
+int entwine_gemm_rs_ex(const void* X, const void* W, const void* const* peer_partials, void* out,
+                       int64_t M, int64_t N, int64_t K_local, int P, int rank,
+                       int tile_order, int comm_budget, void* stream,
+                       const entwine_config* cfg);
+
+/* ------------------------------------------------------------------------
+ * Schedule queries (host only, no GPU needed).  They return the tables that
+ * the kernels receive, for inspection and testing.
+ * ---------------------------------------------------------------------- */
+
+/* Block and tile counts for a shape (Sec. 3.1: Q = tiles in one partition).
+ * Any output pointer may be NULL. */
+int entwine_plan_shape(int64_t M, int64_t N, int P, int block_m, int block_n, int tile_m,
+                       int tile_n, int64_t* num_blocks, int64_t* blocks_per_partition,
+                       int64_t* tiles_per_partition);
+
+/* The production order (Equation (1) for INTERLEAVED): for logical position
+ * p in [0, num_blocks), blocks[4p..4p+3] = (partition d, block row br within
+ * the partition, block col bc, number of the block's first tile within
+ * partition d).  `capacity` = number of int32 elements available. */
+int entwine_plan_blocks(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                        int block_n, int tile_m, int tile_n, int32_t* blocks, int64_t capacity);
+
+/* Tile t of a partition (numbered in N-major producer order, Sec. 3.1
+ * "Matching task order") sits at tile row tiles[2t], tile col tiles[2t+1]. */
+int entwine_plan_tiles(int64_t M, int64_t N, int P, int block_m, int block_n, int tile_m,
+                       int tile_n, int32_t* tiles, int64_t capacity);
+
+/* waits[t*P + r] = index into the flag array F[P][Q] (flattened d*Q + t')
+ * that stands for source rank r's contribution to tile t of partition
+ * `rank`, or -1 when that contribution needs no wait (PRESEEDED peers). */
+int entwine_plan_waits(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                       int block_n, int tile_m, int tile_n, int peer_ready, int release_group,
+                       int32_t* waits, int64_t capacity);
+
+/* Consumer j's task sequence j, j+x, j+2x, ... < Q (Sec. 3.1 "Matching task
+ * order") with x = min(comm_budget, Q).  Writes at most `capacity` entries
+ * and stores the sequence length in *count. */
+int entwine_plan_tasks(int64_t Q, int comm_budget, int consumer, int32_t* tasks,
+                       int64_t capacity, int64_t* count);
+
+/* ------------------------------------------------------------------------
+ * Status, diagnostics and lifetime.
+ * ---------------------------------------------------------------------- */
+
+/* Synchronizes `stream`, then returns and clears the sticky device error of
+ * the current device (ENTWINE_ERR_TIMEOUT if a reduction workgroup's
+ * watchdog fired since the last query, else ENTWINE_OK). */
+int entwine_device_status(void* stream);
+
+const char* entwine_status_string(int status);
+const char* entwine_last_error_message(void);
+
+/* Device pointers of the current device's workspace (for tests): the fp32
+ * own-partition partial [M/P][N] and the outgoing contributions [M][N]
+ * (peer dtype) written by the last call.  Any pointer may be NULL. */
+int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* bytes);
+
+/* Per-kernel timing with HIP events recorded on the stream each kernel is
+ * launched on.  entwine_timing(1) starts recording every call; reading
+ * synchronizes the recorded events and returns the summed kernel durations
+ * (ms) and the number of calls since the last read. */
+int entwine_timing(int enable);
+int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls);
+
+/* Load an offline tuning table (text; one entry per line:
+ * "M N K_local P tile_order comm_budget block_m block_n reducer_threads").
+ * Entries are consulted by the AUTO settings. */
+int entwine_load_tuning(const char* path);
+
+/* Frees the current device's workspace; the next call re-creates it. */
+int entwine_release(void);
+
+/* Number of compute units of the current device (0 when no device). */
+int entwine_device_cus(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ENTWINE_H */

@@ -1,0 +1,92 @@
+"""Helpers for GPU tests: upload seeded inputs, call the library, read back."""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+import tile_overlapped_gemm_amd as tog
+import workloads as wl
+from libentwine import ensure_built
+
+_hip = None
+
+
+def hip():
+    global _hip
+    if _hip is None:
+        # the HIP runtime already loaded by torch (and used by the library)
+        torch.cuda.init()
+        _hip = ctypes.CDLL("libamdhip64.so.7")
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+        _hip.hipMemcpy.restype = ctypes.c_int
+    return _hip
+
+
+def device():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    ensure_built()
+    return torch.device("cuda:0")
+
+
+def up(a: np.ndarray, dev):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def down(t: torch.Tensor) -> np.ndarray:
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
+def as_f64(a: np.ndarray) -> np.ndarray:
+    return (wl.bf16_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
+
+
+class Case:
+    """Device copies of one workload's inputs plus an output buffer."""
+
+    def __init__(self, w: wl.Workload, X, W, peers, dev):
+        self.w = w
+        self.X, self.W, self.peers = X, W, peers
+        self.Xd, self.Wd = up(X, dev), up(W, dev)
+        self.pd = [None if p is None else up(p, dev) for p in peers]
+        self.out_dtype = torch.float32 if w.fp32_io else torch.bfloat16
+        self.dev = dev
+
+    def base_cfg(self, **kw):
+        d = dict(tile_m=self.w.tile, tile_n=self.w.tile)
+        if self.w.fp32_io:
+            d.update(peer_dtype=tog.F32, out_dtype=tog.F32)
+        d.update(kw)
+        return tog.config(**d)
+
+    def run(self, order=tog.ORDER_INTERLEAVED, budget=4, check_status=True, **kw):
+        out = torch.full((self.w.rows, self.w.N), float("nan"), dtype=self.out_dtype, device=self.dev)
+        tog.gemm_rs(self.Xd, self.Wd, self.pd, out, self.w.P, self.w.rank, order, budget,
+                    cfg=self.base_cfg(**kw))
+        if check_status:
+            st = tog.entwine_device_status(torch.cuda.current_stream().cuda_stream)
+            assert st == tog.ENTWINE_OK, f"device status {st}"
+        return out
+
+
+def read_workspace(rows: int, N: int, M: int, outgoing_f32: bool):
+    """(own fp32 [rows][N], outgoing [M][N]) as written by the last call."""
+    own_p, out_p, _ = tog.entwine_workspace()
+    own = np.empty((rows, N), dtype=np.float32)
+    assert hip().hipMemcpy(own.ctypes.data, own_p, own.nbytes, 2) == 0
+    og = np.empty((M, N), dtype=np.float32 if outgoing_f32 else np.uint16)
+    assert hip().hipMemcpy(og.ctypes.data, out_p, og.nbytes, 2) == 0
+    return own, og
+
+
+def err_ratio(got: np.ndarray, ref: np.ndarray) -> float:
+    """max |got - ref| / (1e-2 * max(1, |ref|)); <= 1 passes the parity bar."""
+    g = as_f64(got)
+    assert np.isfinite(g).all(), "non-finite output (an element was never written?)"
+    return float((np.abs(g - ref) / (1e-2 * np.maximum(1.0, np.abs(ref)))).max())

@@ -1,0 +1,48 @@
+"""Every workload at full size, in the launch configuration the benchmark
+times (the tuning table's AUTO choices): sampled rows against the CPU
+oracle, and bit-identity with the sequential (non-overlapped) schedule over
+the whole output."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import tile_overlapped_gemm_amd as tog
+import workloads as wl
+from gpu_util import Case, device, down, err_ratio
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+
+def sample_rows(R):
+    """First, middle and last rows of the partition (the last tile row is the
+    ragged one when R is not a multiple of the tile)."""
+    rows = sorted({0, 1, 2, R // 2, R // 2 + 1, R - 3, R - 2, R - 1})
+    return [r for r in rows if 0 <= r < R]
+
+
+@pytest.mark.parametrize("w", wl.WORKLOADS, ids=lambda w: w.name)
+def test_full_size_sampled_parity(w):
+    dev = device()
+    tog.entwine_load_tuning(os.path.join(os.path.dirname(tog.__file__), "tuning.txt"))
+    print(f"workload {w.name}: generating inputs", flush=True)
+    X, W = wl.operands(w)
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    print(f"workload {w.name}: overlapped run (AUTO)", flush=True)
+    out = case.run(tog.ORDER_AUTO, tog.BUDGET_AUTO)
+    print(f"workload {w.name}: sequential run", flush=True)
+    seq = case.run(tog.ORDER_AUTO, tog.BUDGET_SEQUENTIAL)
+    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
+                       seq.view(torch.int16) if seq.dtype == torch.bfloat16 else seq)
+    got = down(out)
+    worst = 0.0
+    for r in sample_rows(w.rows):
+        ref = orc.gemm_rs(X, W, peers, w.P, w.rank, row_begin=r, row_end=r + 1)
+        worst = max(worst, err_ratio(got[r:r + 1], ref))
+    print(f"workload {w.name}: max err/tol over sampled rows {worst:.3f}", flush=True)
+    assert worst <= 1.0
+    del case
+    torch.cuda.empty_cache()

@@ -1,0 +1,194 @@
+"""Parity of the HIP path with the CPU oracle on multi-tile and ragged shapes.
+
+Bar: |out - ref| <= 1e-2 * max(1, |ref|) element by element against the fp64
+oracle; bit-identical output across production orders, budgets (sequential
+included), reducer thread counts, peer-readiness modes and release groups;
+bit-exact on integer inputs; bit-exact reduction given the device's own fp32
+partial.
+"""
+import numpy as np
+import pytest
+import torch
+
+import tile_overlapped_gemm_amd as tog
+import workloads as wl
+from gpu_util import Case, as_f64, device, down, err_ratio, read_workspace
+from oracle import oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+ORDERS = [tog.ORDER_ROW_MAJOR, tog.ORDER_PARTITION_MAJOR, tog.ORDER_INTERLEAVED, tog.ORDER_COL_MAJOR]
+SMALL = [
+    wl.custom("multi", 1024, 768, 512, 4, rank=1, index=300),        # 256-row partitions
+    wl.custom("ragged", 1000, 1536, 512, 8, rank=5, index=301),      # 125-row partitions
+    wl.custom("odd_n", 512, 1160, 256, 2, rank=1, index=302),        # N = 9*128 + 8
+    wl.BY_NAME["tiny"],                                              # fp32 peers/out, 64x64 tiles
+]
+BLOCKS = [(128, 128), (128, 256), (256, 128)]
+
+
+@pytest.fixture(scope="module")
+def dev():
+    return device()
+
+
+_cases = {}
+
+
+def case_for(w, dev):
+    if w.name not in _cases:
+        X, W = wl.operands(w)
+        peers = wl.peer_partials(w)
+        ref = orc.gemm_rs(X, W, peers, w.P, w.rank)
+        _cases[w.name] = (Case(w, X, W, peers, dev), ref)
+    return _cases[w.name]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_parity_and_schedule_invariance(dev, w):
+    case, ref = case_for(w, dev)
+    _, _, q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
+    first = None
+    runs = 0
+    for bm, bn in BLOCKS:
+        for order in ORDERS:
+            for budget in (0, 1, 3, min(q, 64)):
+                print(f"case {w.name} block {bm}x{bn} order {order} budget {budget}", flush=True)
+                out = down(case.run(order, budget, block_m=bm, block_n=bn))
+                runs += 1
+                if first is None:
+                    first = out
+                    r = err_ratio(out, ref)
+                    assert r <= 1.0, f"max err/tol {r:.3f}"
+                else:
+                    np.testing.assert_array_equal(out, first)
+    assert runs == len(BLOCKS) * len(ORDERS) * 4
+
+
+@pytest.mark.parametrize("w", SMALL[:2], ids=lambda w: w.name)
+def test_reducer_variants_bit_identical(dev, w):
+    case, ref = case_for(w, dev)
+    base = down(case.run(tog.ORDER_INTERLEAVED, 4))
+    for threads in (128, 256, 512):
+        for mode in (tog.PEERS_PRESEEDED, tog.PEERS_SYMMETRIC):
+            for order in (tog.ORDER_INTERLEAVED, tog.ORDER_PARTITION_MAJOR):
+                for group in (tog.RELEASE_TILE, 3, tog.RELEASE_PARTITION, tog.RELEASE_OUTPUT):
+                    print(f"case {w.name} b={threads} mode={mode} order={order} g={group}", flush=True)
+                    out = down(case.run(order, 5, reducer_threads=threads, peer_ready=mode,
+                                        release_group=group))
+                    np.testing.assert_array_equal(out, base)
+    for slabs in (1, 2, 8):
+        out = down(case.run(tog.ORDER_INTERLEAVED, 0, seq_reduce_slabs=slabs))
+        np.testing.assert_array_equal(out, base)
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_reduction_bit_exact_given_own_partial(dev, w):
+    """The reduction's closed form: acc = own fp32, + peers in rank order in
+    fp32, one round to the output type (oracle.reduce_f32 on the device's own
+    partial, read back from the workspace)."""
+    case, ref = case_for(w, dev)
+    out = down(case.run(tog.ORDER_INTERLEAVED, 3))
+    own, outgoing = read_workspace(w.rows, w.N, w.M, w.fp32_io)
+    want = orc.reduce_f32(own, case.peers, w.P, w.rank, orc.F32 if w.fp32_io else orc.BF16)
+    np.testing.assert_array_equal(out, want)
+    # the own partial itself is the GEMM of the partition's rows in fp32
+    C = orc.partial_gemm(case.X, case.W)
+    R = w.rows
+    own_ref = C[w.rank * R:(w.rank + 1) * R]
+    gamma = w.K * 2.0 ** -23
+    absxw = orc.partial_gemm(case.X & 0x7FFF, case.W & 0x7FFF)  # sum |x||w| (sign bits cleared)
+    bound = 2 * gamma * absxw[w.rank * R:(w.rank + 1) * R] + 1e-30
+    assert (np.abs(own - own_ref) <= bound).all()
+    # outgoing contributions (every other partition) in the peer dtype
+    og = as_f64(outgoing)
+    rows = np.ones(w.M, dtype=bool)
+    rows[w.rank * R:(w.rank + 1) * R] = False
+    rel = 2.0 ** -23 if w.fp32_io else 2.0 ** -8
+    bound = rel * np.abs(C[rows]) + 2 * gamma * absxw[rows] + 1e-30
+    assert (np.abs(og[rows] - C[rows]) <= bound).all()
+
+
+@pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)
+def test_exact_integer_inputs_bit_exact(dev, w):
+    """Integer inputs keep every intermediate exact: the device output must
+    equal the oracle's value exactly, for every order and budget."""
+    X, W, peers = wl.exact_operands(w)
+    case = Case(w, X, W, peers, dev)
+    ref = orc.gemm_rs(X, W, peers, w.P, w.rank)
+    assert (np.abs(ref) < 256).all() and (ref == np.round(ref)).all()
+    for order in ORDERS:
+        for budget in (0, 2):
+            out = down(case.run(order, budget))
+            np.testing.assert_array_equal(as_f64(out), ref)
+
+
+def test_special_cases(dev):
+    """P = 1 is a plain GEMM; W = 0 leaves the sum of the peers; X = I passes W's rows."""
+    w = wl.custom("p1", 256, 512, 128, 1, index=303)
+    X, W = wl.operands(w)
+    case = Case(w, X, W, [None], dev)
+    out = down(case.run(tog.ORDER_INTERLEAVED, 2))
+    assert err_ratio(out, orc.partial_gemm(X, W)) <= 1.0
+    w = wl.custom("w0", 512, 256, 128, 4, rank=3, index=304)
+    X, W = wl.operands(w)
+    W[:] = 0
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    out = down(case.run(tog.ORDER_ROW_MAJOR, 3))
+    zero = np.zeros((w.rows, w.N), dtype=np.float32)
+    np.testing.assert_array_equal(out, orc.reduce_f32(zero, peers, w.P, w.rank))
+    w = wl.custom("eye", 256, 384, 256, 2, rank=1, index=305)
+    X = wl.bf16_bits(np.eye(256, dtype=np.float32))
+    _, W = wl.operands(w)
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    out = down(case.run(tog.ORDER_COL_MAJOR, 1))
+    own = wl.bf16_to_f32(W.T[128:256]).copy()  # rows of W (as K x N) of partition 1
+    np.testing.assert_array_equal(out, orc.reduce_f32(own, peers, w.P, w.rank))
+
+
+def test_repeated_calls_and_release(dev):
+    w = SMALL[1]
+    case, ref = case_for(w, dev)
+    a = down(case.run(tog.ORDER_INTERLEAVED, 7))
+    for _ in range(5):
+        np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 7)), a)
+    tog.entwine_release()
+    np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 7)), a)
+
+
+def test_watchdog_reports_timeout_then_recovers(dev):
+    """A tile whose flag never arrives (forced from the host) makes its
+    reduction workgroup give up after the poll timeout; the device status
+    reports ENTWINE_ERR_TIMEOUT once, and the next call is correct."""
+    w = SMALL[0]
+    case, ref = case_for(w, dev)
+    good = down(case.run(tog.ORDER_INTERLEAVED, 4))
+    case.run(tog.ORDER_INTERLEAVED, 4, check_status=False, withhold_tile=3, poll_timeout_ms=20)
+    st = tog.entwine_device_status(torch.cuda.current_stream().cuda_stream)
+    assert st == tog.ENTWINE_ERR_TIMEOUT
+    assert tog.entwine_device_status(torch.cuda.current_stream().cuda_stream) == tog.ENTWINE_OK
+    np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 4)), good)
+
+
+def test_timing_api(dev):
+    w = SMALL[0]
+    case, _ = case_for(w, dev)
+    tog.entwine_timing_read()
+    tog.entwine_timing(True)
+    for b in (0, 4):
+        case.run(tog.ORDER_INTERLEAVED, b)
+    tog.entwine_timing(False)
+    g, r, n = tog.entwine_timing_read()
+    assert n == 2 and g > 0 and r > 0
+
+
+def test_budget_at_cu_count_rejected(dev):
+    w = SMALL[0]
+    case, _ = case_for(w, dev)
+    cus = tog.entwine_device_cus()
+    assert cus > 0
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, cus)
+    assert e.value.status == tog.ENTWINE_ERR_INVALID_ARGUMENT

@@ -1,0 +1,154 @@
+"""Production orders, tile numbering, task and wait tables (host only)."""
+import itertools
+import json
+import os
+
+import pytest
+
+import tile_overlapped_gemm_amd as tog
+from libentwine import ensure_built
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+ORDERS = [tog.ORDER_ROW_MAJOR, tog.ORDER_PARTITION_MAJOR, tog.ORDER_INTERLEAVED, tog.ORDER_COL_MAJOR]
+# (M, N, P, bm, bn, tm, tn): multi-block, ragged partitions (125 rows), N
+# not a multiple of the block, wide and tall blocks.
+SHAPES = [
+    (512, 768, 4, 128, 256, 128, 128),
+    (1000, 1536, 8, 128, 128, 128, 128),
+    (1000, 1408, 8, 256, 256, 128, 128),
+    (256, 256, 4, 128, 128, 64, 64),
+    (2048, 640, 2, 256, 128, 128, 64),
+    (96, 136, 3, 128, 128, 64, 128),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def lib():
+    return ensure_built()
+
+
+def test_figure4b_worked_example():
+    with open(os.path.join(GOLDEN, "fig4b_interleaved_schedule.json")) as f:
+        fx = json.load(f)
+    s = fx["shape"]
+    P = s["P"]
+    M = P * s["rows_per_partition"]
+    geo = (s["block_m"], s["block_n"], s["tile_m"], s["tile_n"])
+    nb, bd, q = tog.entwine_plan_shape(M, s["N"], P, *geo)
+    assert (bd, q) == (3, 6)
+    tiles_of_block = {}
+    for t, (tr, tc) in enumerate(tog.entwine_plan_tiles(M, s["N"], P, *geo)):
+        tiles_of_block.setdefault((tr, tc // 2), []).append(t)
+    for rank in range(P):  # the same on every rank
+        blocks = tog.entwine_plan_blocks(M, s["N"], P, rank, tog.ORDER_INTERLEAVED, *geo)
+        for p, want in fx["visits"]:
+            d, br, bc, first = blocks[p]
+            assert d == fx["partition"]
+            assert tiles_of_block[(br, bc)] == want
+            assert first == want[0]
+    for j, want in fx["consumers"].items():
+        assert tog.entwine_plan_tasks(q, fx["budget"], int(j)) == want
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+@pytest.mark.parametrize("order", ORDERS)
+def test_every_block_produced_once(shape, order):
+    M, N, P, bm, bn, tm, tn = shape
+    nb, bd, q = tog.entwine_plan_shape(*shape)
+    R = M // P
+    assert bd == -(-R // bm) * -(-N // bn) and nb == P * bd
+    for rank in range(P):
+        blocks = tog.entwine_plan_blocks(M, N, P, rank, order, bm, bn, tm, tn)
+        seen = {(d, br, bc) for d, br, bc, _ in blocks}
+        assert len(seen) == nb
+        assert seen == {(d, br, bc) for d in range(P) for br in range(-(-R // bm))
+                        for bc in range(-(-N // bn))}
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_order_definitions(shape):
+    M, N, P, bm, bn, tm, tn = shape
+    nb, bd, q = tog.entwine_plan_shape(*shape)
+    cb = -(-N // bn)
+    rb = -(-(M // P) // bm)
+    for rank in range(P):
+        inter = tog.entwine_plan_blocks(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn)
+        assert [b[0] for b in inter] == [p % P for p in range(nb)]
+        # block i within partition is N-major: (i // cb, i % cb), i = p // P
+        assert [(b[1], b[2]) for b in inter] == [((p // P) // cb, (p // P) % cb) for p in range(nb)]
+        row = tog.entwine_plan_blocks(M, N, P, rank, tog.ORDER_ROW_MAJOR, bm, bn, tm, tn)
+        assert [b[0] for b in row] == [p // bd for p in range(nb)]
+        part = tog.entwine_plan_blocks(M, N, P, rank, tog.ORDER_PARTITION_MAJOR, bm, bn, tm, tn)
+        runs = [part[k * bd][0] for k in range(P)]
+        assert runs == [(rank + 1 + k) % P for k in range(P)] and runs[-1] == rank
+        for k in range(P):
+            assert {b[0] for b in part[k * bd:(k + 1) * bd]} == {runs[k]}
+        col = tog.entwine_plan_blocks(M, N, P, rank, tog.ORDER_COL_MAJOR, bm, bn, tm, tn)
+        assert [b[2] for b in col] == sorted(b[2] for b in col)
+        assert [(b[0] * rb + b[1]) for b in col[:P * rb]] == list(range(P * rb))
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_tile_numbering(shape):
+    M, N, P, bm, bn, tm, tn = shape
+    nb, bd, q = tog.entwine_plan_shape(*shape)
+    R = M // P
+    tiles = tog.entwine_plan_tiles(*shape)
+    rt, ct = -(-R // tm), -(-N // tn)
+    assert q == rt * ct and sorted(tiles) == sorted(itertools.product(range(rt), range(ct)))
+    # numbered block by block in N-major block order, row-major inside a block
+    keys = [((tr * tm // bm) * -(-N // bn) + tc * tn // bn, tr, tc) for tr, tc in tiles]
+    assert keys == sorted(keys)
+    # a block's first-tile field points at its first tile
+    blocks = tog.entwine_plan_blocks(M, N, P, 0, tog.ORDER_ROW_MAJOR, bm, bn, tm, tn)
+    for d, br, bc, first in blocks:
+        assert tiles[first] == (br * bm // tm, bc * bn // tn)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_wait_tables(shape):
+    M, N, P, bm, bn, tm, tn = shape
+    nb, bd, q = tog.entwine_plan_shape(*shape)
+    for rank in range(P):
+        for order in ORDERS:
+            pre = tog.entwine_plan_waits(M, N, P, rank, order, bm, bn, tm, tn, tog.PEERS_PRESEEDED)
+            assert pre == [[rank * q + t if r == rank else -1 for r in range(P)] for t in range(q)]
+        for order in (tog.ORDER_INTERLEAVED, tog.ORDER_ROW_MAJOR, tog.ORDER_COL_MAJOR):
+            sym = tog.entwine_plan_waits(M, N, P, rank, order, bm, bn, tm, tn, tog.PEERS_SYMMETRIC)
+            assert sym == [[rank * q + t] * P for t in range(q)]
+        # Partition-major: peer r reaches partition `rank` after (rank-r-1) mod P runs;
+        # this GPU is then in partition (rank+1+k) mod P = (2*rank - r) mod P.
+        sym = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_PARTITION_MAJOR, bm, bn, tm, tn,
+                                     tog.PEERS_SYMMETRIC)
+        assert sym == [[((2 * rank - r) % P) * q + t for r in range(P)] for t in range(q)]
+
+
+def test_release_groups():
+    M, N, P, bm, bn, tm, tn = 512, 768, 4, 128, 256, 128, 128
+    nb, bd, q = tog.entwine_plan_shape(M, N, P, bm, bn, tm, tn)
+    rank = 2
+    blocks = tog.entwine_plan_blocks(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn)
+    part = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn,
+                                  tog.PEERS_PRESEEDED, tog.RELEASE_PARTITION)
+    last = max(p for p in range(nb) if blocks[p][0] == rank)
+    # any flag of the closing block will do: a block publishes all of its
+    # tiles' flags together, after all of its stores
+    closing = {rank * q + blocks[last][3], rank * q + blocks[last][3] + 1}
+    assert {w[rank] for w in part} <= closing
+    out = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn,
+                                 tog.PEERS_PRESEEDED, tog.RELEASE_OUTPUT)
+    d, _, _, first = blocks[nb - 1]
+    assert {w[rank] for w in out} <= {d * q + first, d * q + first + 1}
+    g2 = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn,
+                                tog.PEERS_PRESEEDED, 4)
+    # groups {0..3} and {4,5}: closed by the blocks holding tiles {2,3} and {4,5}
+    assert [w[rank] - rank * q for w in g2] == [2, 2, 2, 3, 4, 5]
+
+
+@pytest.mark.parametrize("q,x", [(6, 2), (128, 32), (96, 1), (5, 9), (1, 1)])
+def test_tasks_partition_the_tiles(q, x):
+    seqs = [tog.entwine_plan_tasks(q, x, j) for j in range(x + 2)]
+    flat = sorted(t for s in seqs for t in s)
+    assert flat == list(range(q))
+    for j, s in enumerate(seqs):
+        assert s == list(range(j, q, min(x, q))) if j < min(x, q) else s == []

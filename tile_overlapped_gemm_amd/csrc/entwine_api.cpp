@@ -1,0 +1,672 @@
+// entwine_api.cpp -- the C ABI: validation, workspace, plans, launch.
+//
+// Method: "Entwine: Coordinating Tiled Computation and Fine-Grained
+// Communication across GPUs" (paperpeel.com/paper/2609.11562).
+//  * Sec. 4.1: partial outputs and flags live in buffers allocated once and
+//    reused across invocations; flags are reset before each invocation; the
+//    GEMM and the reduction kernel are launched on independent streams after a
+//    common start event.
+//  * Sec. 3.2 / 4.3: the reduction kernel's grid is the communication budget x,
+//    capped by the partition's tile count and kept below the CU count.
+//
+// MI355X choices.  Flags hold the call's epoch instead of being cleared: a
+// flag is ready when it equals the current epoch, which is equivalent to
+// "reset, then set" without a clearing pass per call.  Both internal streams
+// run at the default priority; the fork/join uses HIP events.  Sequential
+// mode (budget 0) runs the same two kernels one after the other on one
+// stream.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cinttypes>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "entwine.h"
+#include "kernels.h"
+#include "plan.h"
+
+using namespace entwine;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return status;
+}
+
+#define HIP_TRY(expr)                                                                    \
+  do {                                                                                   \
+    hipError_t e_ = (expr);                                                              \
+    if (e_ != hipSuccess)                                                                \
+      return fail(ENTWINE_ERR_HIP, "%s failed: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+struct DevicePlan {
+  Plan plan;
+  int32_t* d_blocks = nullptr;
+  int32_t* d_tiles = nullptr;
+  int32_t* d_waits = nullptr;
+};
+
+using PlanKey = std::tuple<int64_t, int64_t, int, int, int, int, int, int, int, int, int>;
+
+struct TimingPair {
+  hipEvent_t g0, g1, r0, r1;
+};
+
+struct Workspace {
+  int device = -1;
+  int cus = 0;
+  int wall_khz = 100000;
+  hipStream_t s_gemm = nullptr, s_red = nullptr;
+  hipEvent_t ev_fork = nullptr, ev_gemm = nullptr, ev_red = nullptr;
+  bool have_prev = false;
+  float* own = nullptr;
+  size_t own_bytes = 0;
+  void* outgoing = nullptr;
+  size_t outgoing_bytes = 0;
+  uint32_t* flags = nullptr;
+  size_t flag_count = 0;
+  int32_t* error = nullptr;
+  uint32_t epoch = 0;
+  std::map<PlanKey, std::unique_ptr<DevicePlan>> plans;
+  std::vector<TimingPair> timing_live;
+  std::vector<TimingPair> timing_free;
+};
+
+struct TuneEntry {
+  int order, budget, bm, bn, threads;
+};
+
+std::mutex g_mu;
+std::map<int, std::unique_ptr<Workspace>> g_ws;
+std::map<std::tuple<int64_t, int64_t, int64_t, int>, TuneEntry> g_tuning;
+bool g_timing = false;
+
+void free_plan(DevicePlan* p) {
+  if (p->d_blocks) (void)hipFree(p->d_blocks);
+  if (p->d_tiles) (void)hipFree(p->d_tiles);
+  if (p->d_waits) (void)hipFree(p->d_waits);
+  p->d_blocks = p->d_tiles = p->d_waits = nullptr;
+}
+
+void destroy_workspace(Workspace* w) {
+  int prev = -1;
+  (void)hipGetDevice(&prev);
+  (void)hipSetDevice(w->device);
+  if (w->s_gemm) (void)hipStreamSynchronize(w->s_gemm);
+  if (w->s_red) (void)hipStreamSynchronize(w->s_red);
+  for (auto& kv : w->plans) free_plan(kv.second.get());
+  w->plans.clear();
+  for (auto* v : {&w->timing_live, &w->timing_free})
+    for (auto& t : *v) {
+      (void)hipEventDestroy(t.g0);
+      (void)hipEventDestroy(t.g1);
+      (void)hipEventDestroy(t.r0);
+      (void)hipEventDestroy(t.r1);
+    }
+  if (w->own) (void)hipFree(w->own);
+  if (w->outgoing) (void)hipFree(w->outgoing);
+  if (w->flags) (void)hipFree(w->flags);
+  if (w->error) (void)hipFree(w->error);
+  if (w->ev_fork) (void)hipEventDestroy(w->ev_fork);
+  if (w->ev_gemm) (void)hipEventDestroy(w->ev_gemm);
+  if (w->ev_red) (void)hipEventDestroy(w->ev_red);
+  if (w->s_gemm) (void)hipStreamDestroy(w->s_gemm);
+  if (w->s_red) (void)hipStreamDestroy(w->s_red);
+  if (prev >= 0) (void)hipSetDevice(prev);
+}
+
+int get_workspace(Workspace** out) {
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it != g_ws.end()) {
+    *out = it->second.get();
+    return ENTWINE_OK;
+  }
+  auto w = std::make_unique<Workspace>();
+  w->device = dev;
+  HIP_TRY(hipDeviceGetAttribute(&w->cus, hipDeviceAttributeMultiprocessorCount, dev));
+  int khz = 0;
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
+    w->wall_khz = khz;
+  HIP_TRY(hipStreamCreateWithFlags(&w->s_gemm, hipStreamNonBlocking));
+  HIP_TRY(hipStreamCreateWithFlags(&w->s_red, hipStreamNonBlocking));
+  HIP_TRY(hipEventCreateWithFlags(&w->ev_fork, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&w->ev_gemm, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&w->ev_red, hipEventDisableTiming));
+  HIP_TRY(hipMalloc(&w->error, sizeof(int32_t)));
+  HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
+  *out = w.get();
+  g_ws[dev] = std::move(w);
+  return ENTWINE_OK;
+}
+
+// Grow a device buffer; growth waits for all of this workspace's work.
+int ensure(Workspace* w, void** buf, size_t* have, size_t need, bool zero) {
+  if (*have >= need && *buf) return ENTWINE_OK;
+  HIP_TRY(hipStreamSynchronize(w->s_gemm));
+  HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (*buf) {
+    HIP_TRY(hipFree(*buf));
+    *buf = nullptr;
+    *have = 0;
+  }
+  hipError_t e = hipMalloc(buf, need);
+  if (e != hipSuccess) {
+    *buf = nullptr;
+    return fail(ENTWINE_ERR_OUT_OF_MEMORY, "workspace allocation of %zu bytes failed: %s",
+                need, hipGetErrorString(e));
+  }
+  if (zero) HIP_TRY(hipMemset(*buf, 0, need));
+  *have = need;
+  return ENTWINE_OK;
+}
+
+int get_plan(Workspace* w, const Geometry& g, int rank, int order, int peer_ready,
+             int release_group, DevicePlan** out) {
+  PlanKey key{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, order, peer_ready, release_group};
+  auto it = w->plans.find(key);
+  if (it != w->plans.end()) {
+    *out = it->second.get();
+    return ENTWINE_OK;
+  }
+  auto dp = std::make_unique<DevicePlan>();
+  int rc = build_plan(g, rank, order, peer_ready, release_group, &dp->plan);
+  if (rc != ENTWINE_OK) return fail(rc, "schedule construction failed");
+  const Plan& p = dp->plan;
+  auto upload = [&](const std::vector<int32_t>& v, int32_t** d) -> int {
+    HIP_TRY(hipMalloc(d, v.size() * sizeof(int32_t)));
+    HIP_TRY(hipMemcpy(*d, v.data(), v.size() * sizeof(int32_t), hipMemcpyHostToDevice));
+    return ENTWINE_OK;
+  };
+  if ((rc = upload(p.blocks, &dp->d_blocks)) != ENTWINE_OK ||
+      (rc = upload(p.tiles, &dp->d_tiles)) != ENTWINE_OK ||
+      (rc = upload(p.waits, &dp->d_waits)) != ENTWINE_OK) {
+    free_plan(dp.get());
+    return rc;
+  }
+  *out = dp.get();
+  w->plans[key] = std::move(dp);
+  return ENTWINE_OK;
+}
+
+int take_timing_pair(Workspace* w, TimingPair* tp) {
+  if (!w->timing_free.empty()) {
+    *tp = w->timing_free.back();
+    w->timing_free.pop_back();
+    return ENTWINE_OK;
+  }
+  HIP_TRY(hipEventCreate(&tp->g0));
+  HIP_TRY(hipEventCreate(&tp->g1));
+  HIP_TRY(hipEventCreate(&tp->r0));
+  HIP_TRY(hipEventCreate(&tp->r1));
+  return ENTWINE_OK;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool overlaps(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
+  if (M <= 0 || N <= 0 || K <= 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "M, N, K_local must be positive (got %" PRId64
+                ", %" PRId64 ", %" PRId64 ")", M, N, K);
+  if (P < 1) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "P must be >= 1 (got %d)", P);
+  if (P > kMaxRanks) return fail(ENTWINE_ERR_UNSUPPORTED, "P = %d > %d is not built", P, kMaxRanks);
+  if (rank < 0 || rank >= P)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "rank %d outside [0, %d)", rank, P);
+  if (M % P != 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "M = %" PRId64 " is not divisible by P = %d", M, P);
+  if (N % 8 != 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "N = %" PRId64 " must be a multiple of 8", N);
+  if (K % 64 != 0)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "K_local = %" PRId64 " must be a multiple of 64", K);
+  const int64_t lim = (int64_t)1 << 31;
+  if (M * K >= lim || N * K >= lim || M * N >= lim)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "operands beyond 2^31 elements are not built");
+  return ENTWINE_OK;
+}
+
+struct Resolved {
+  int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
+      slabs, withhold_tile;
+  uint32_t timeout_ms;
+};
+
+int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, int tile_order,
+            int comm_budget, Resolved* r) {
+  entwine_config c;
+  entwine_config_init(&c);
+  if (cfg) {
+    if (cfg->struct_size < (int32_t)offsetof(entwine_config, reserved))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "entwine_config.struct_size too small");
+    std::memcpy(&c, cfg, std::min<size_t>(sizeof c, (size_t)cfg->struct_size));
+  }
+  if (tile_order < ENTWINE_ORDER_AUTO || tile_order > ENTWINE_ORDER_COL_MAJOR)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tile_order %d out of range", tile_order);
+  if (comm_budget < ENTWINE_BUDGET_AUTO)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "comm_budget %d out of range", comm_budget);
+  if (c.w_layout != ENTWINE_W_NK)
+    return fail(c.w_layout == ENTWINE_W_KN ? ENTWINE_ERR_UNSUPPORTED : ENTWINE_ERR_INVALID_ARGUMENT,
+                "w_layout %d is not built (only ENTWINE_W_NK)", c.w_layout);
+  if ((c.peer_dtype != ENTWINE_BF16 && c.peer_dtype != ENTWINE_F32) ||
+      (c.out_dtype != ENTWINE_BF16 && c.out_dtype != ENTWINE_F32))
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_dtype/out_dtype must be BF16 or F32");
+  if (c.peer_ready != ENTWINE_PEERS_PRESEEDED && c.peer_ready != ENTWINE_PEERS_SYMMETRIC)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_ready %d out of range", c.peer_ready);
+  if (c.release_group < ENTWINE_RELEASE_OUTPUT)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "release_group %d out of range", c.release_group);
+  if (c.reducer_threads != 0 && c.reducer_threads != 128 && c.reducer_threads != 256 &&
+      c.reducer_threads != 512)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "reducer_threads must be 128, 256 or 512");
+
+  const TuneEntry* te = nullptr;
+  auto it = g_tuning.find(std::make_tuple(M, N, K, P));
+  if (it != g_tuning.end()) te = &it->second;
+  const int64_t R = M / P;
+  r->bm = c.block_m ? c.block_m : (te ? te->bm : (R % 256 == 0 ? 256 : 128));
+  r->bn = c.block_n ? c.block_n : (te ? te->bn : (N % 256 == 0 ? 256 : 128));
+  r->tm = c.tile_m ? c.tile_m : 128;
+  r->tn = c.tile_n ? c.tile_n : 128;
+  r->threads = c.reducer_threads ? c.reducer_threads : (te ? te->threads : 256);
+  r->order = tile_order != ENTWINE_ORDER_AUTO ? tile_order
+                                              : (te ? te->order : ENTWINE_ORDER_INTERLEAVED);
+  r->budget = comm_budget != ENTWINE_BUDGET_AUTO ? comm_budget : (te ? te->budget : 32);
+  r->peer_f32 = c.peer_dtype == ENTWINE_F32;
+  r->out_f32 = c.out_dtype == ENTWINE_F32;
+  r->peer_ready = c.peer_ready;
+  r->release_group = c.release_group;
+  r->slabs = c.seq_reduce_slabs;
+  r->timeout_ms = c.poll_timeout_ms ? c.poll_timeout_ms : 2000;
+  r->withhold_tile = c.withhold_tile - 1;
+  if (r->slabs < 0 || (r->slabs > 0 && r->tm % r->slabs != 0))
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "seq_reduce_slabs must divide tile_m");
+  return ENTWINE_OK;
+}
+
+int run(const void* X, const void* W, const void* const* peers, void* out, int64_t M, int64_t N,
+        int64_t K, int P, int rank, int tile_order, int comm_budget, void* stream_,
+        const entwine_config* cfg) {
+  int rc = check_shape(M, N, K, P, rank);
+  if (rc) return rc;
+  Resolved rs;
+  if ((rc = resolve(cfg, M, N, K, P, tile_order, comm_budget, &rs))) return rc;
+  Geometry g;
+  if ((rc = make_geometry(M, N, P, rs.bm, rs.bn, rs.tm, rs.tn, &g)))
+    return fail(rc, "unsupported tile geometry (block %dx%d, tile %dx%d)", rs.bm, rs.bn, rs.tm,
+                rs.tn);
+
+  // Pointers: presence, alignment, no aliasing of the output.
+  if (!X || !W || !out) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "X, W and out must be non-NULL");
+  if (!aligned16(X) || !aligned16(W) || !aligned16(out))
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "X, W and out must be 16-byte aligned");
+  if (P > 1 && !peers) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_partials is NULL");
+  const size_t peer_sz = rs.peer_f32 ? 4 : 2, out_sz = rs.out_f32 ? 4 : 2;
+  const size_t out_bytes = (size_t)g.R * N * out_sz;
+  if (overlaps(out, out_bytes, X, (size_t)M * K * 2) || overlaps(out, out_bytes, W, (size_t)N * K * 2))
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "out overlaps X or W");
+  for (int r = 0; r < P; ++r) {
+    if (r == rank) continue;
+    if (!peers[r]) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_partials[%d] is NULL", r);
+    if (!aligned16(peers[r]))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_partials[%d] is not 16-byte aligned", r);
+    if (overlaps(out, out_bytes, peers[r], (size_t)g.R * N * peer_sz))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "out overlaps peer_partials[%d]", r);
+  }
+
+  std::lock_guard<std::mutex> lock(g_mu);
+  Workspace* w = nullptr;
+  if ((rc = get_workspace(&w))) return rc;
+  if (rs.budget >= w->cus)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT,
+                "comm_budget %d must stay below the device's %d compute units", rs.budget, w->cus);
+  const int x = (int)std::min<int64_t>(rs.budget, g.Q);
+
+  if ((rc = ensure(w, (void**)&w->own, &w->own_bytes, (size_t)g.R * N * 4, false))) return rc;
+  if ((rc = ensure(w, &w->outgoing, &w->outgoing_bytes, (size_t)M * N * peer_sz, false))) return rc;
+  size_t flag_bytes = w->flag_count * 4;
+  // One slot past the P x Q flags is never written by any GEMM (failure injection).
+  if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, ((size_t)g.P * g.Q + 1) * 4, true))) return rc;
+  w->flag_count = flag_bytes / 4;
+
+  DevicePlan* dp = nullptr;
+  if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, &dp))) return rc;
+
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  // Epochs skip 0 (the value of freshly cleared flags).  On wrap-around the
+  // flags are cleared once so that no flag left from 2^32 calls ago matches.
+  bool clear_flags = false;
+  if (++w->epoch == 0) {
+    w->epoch = 1;
+    clear_flags = true;
+  }
+
+  TimingPair tp{};
+  if (g_timing && (rc = take_timing_pair(w, &tp))) return rc;
+
+  GemmArgs ga{};
+  ga.X = static_cast<const uint16_t*>(X);
+  ga.W = static_cast<const uint16_t*>(W);
+  ga.own = w->own;
+  ga.outgoing = w->outgoing;
+  ga.flags = w->flags;
+  ga.blocks = dp->d_blocks;
+  ga.M = (int32_t)M;
+  ga.N = (int32_t)N;
+  ga.K = (int32_t)K;
+  ga.R = (int32_t)g.R;
+  ga.rank = rank;
+  ga.Q = (int32_t)g.Q;
+  ga.Rt = (int32_t)g.Rt;
+  ga.Ct = (int32_t)g.Ct;
+  ga.tm = g.tm;
+  ga.tn = g.tn;
+  ga.outgoing_f32 = rs.peer_f32;
+  ga.epoch = w->epoch;
+
+  ReduceArgs ra{};
+  ra.own = w->own;
+  for (int r = 0; r < P; ++r) ra.peers[r] = r == rank ? nullptr : peers[r];
+  ra.out = out;
+  ra.flags = w->flags;
+  ra.waits = dp->d_waits;
+  ra.tiles = dp->d_tiles;
+  ra.error = w->error;
+  ra.R = (int32_t)g.R;
+  ra.N = (int32_t)N;
+  ra.P = P;
+  ra.rank = rank;
+  ra.Q = (int32_t)g.Q;
+  ra.tm = g.tm;
+  ra.tn = g.tn;
+  ra.epoch = w->epoch;
+  ra.timeout_ticks = (uint64_t)rs.timeout_ms * (uint64_t)w->wall_khz;
+  ra.withhold_tile = rs.withhold_tile;
+  ra.never_flag = (int32_t)(g.P * g.Q);
+
+  // Fork: both internal streams start after the caller's prior work and after
+  // this workspace's previous call.
+  HIP_TRY(hipEventRecord(w->ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_fork, 0));
+  HIP_TRY(hipStreamWaitEvent(w->s_red, w->ev_fork, 0));
+  if (w->have_prev) HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_red, 0));
+  if (clear_flags) HIP_TRY(hipMemsetAsync(w->flags, 0, w->flag_count * 4, w->s_gemm));
+
+  const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
+  hipStream_t s_red = sequential ? w->s_gemm : w->s_red;
+  if (sequential) {
+    ra.slabs = rs.slabs ? rs.slabs : std::max(1, std::min(g.tm, (int)((4 * w->cus + g.Q - 1) / g.Q)));
+    while (g.tm % ra.slabs) --ra.slabs;
+  } else {
+    ra.slabs = 1;
+  }
+  ra.ntasks = (int32_t)(g.Q * ra.slabs);
+  const int grid = sequential ? ra.ntasks : x;
+
+  if (g_timing) HIP_TRY(hipEventRecord(tp.g0, w->s_gemm));
+  hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, w->s_gemm);
+  if (e != hipSuccess) return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  if (g_timing) HIP_TRY(hipEventRecord(tp.g1, w->s_gemm));
+  HIP_TRY(hipEventRecord(w->ev_gemm, w->s_gemm));
+  if (g_timing) HIP_TRY(hipEventRecord(tp.r0, s_red));
+  e = launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, grid, s_red);
+  if (e != hipSuccess)
+    return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
+  if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));
+  HIP_TRY(hipEventRecord(w->ev_red, s_red));
+  w->have_prev = true;
+  // Join: the caller's stream continues after both kernels.
+  HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
+  HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+  if (g_timing) w->timing_live.push_back(tp);
+  return ENTWINE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+void entwine_config_init(entwine_config* cfg) {
+  if (!cfg) return;
+  std::memset(cfg, 0, sizeof *cfg);
+  cfg->struct_size = (int32_t)sizeof *cfg;
+  cfg->w_layout = ENTWINE_W_NK;
+  cfg->peer_dtype = ENTWINE_BF16;
+  cfg->out_dtype = ENTWINE_BF16;
+  cfg->peer_ready = ENTWINE_PEERS_PRESEEDED;
+  cfg->release_group = ENTWINE_RELEASE_TILE;
+}
+
+int entwine_gemm_rs(const void* X, const void* W, const void* const* peer_partials, void* out,
+                    int64_t M, int64_t N, int64_t K_local, int P, int rank, int tile_order,
+                    int comm_budget, void* stream) {
+  return run(X, W, peer_partials, out, M, N, K_local, P, rank, tile_order, comm_budget, stream,
+             nullptr);
+}
+
+int entwine_gemm_rs_ex(const void* X, const void* W, const void* const* peer_partials, void* out,
+                       int64_t M, int64_t N, int64_t K_local, int P, int rank, int tile_order,
+                       int comm_budget, void* stream, const entwine_config* cfg) {
+  return run(X, W, peer_partials, out, M, N, K_local, P, rank, tile_order, comm_budget, stream,
+             cfg);
+}
+
+int entwine_plan_shape(int64_t M, int64_t N, int P, int block_m, int block_n, int tile_m,
+                       int tile_n, int64_t* num_blocks, int64_t* blocks_per_partition,
+                       int64_t* tiles_per_partition) {
+  Geometry g;
+  int rc = make_geometry(M, N, P, block_m, block_n, tile_m, tile_n, &g);
+  if (rc) return fail(rc, "invalid geometry");
+  if (num_blocks) *num_blocks = g.NB;
+  if (blocks_per_partition) *blocks_per_partition = g.Bd;
+  if (tiles_per_partition) *tiles_per_partition = g.Q;
+  return ENTWINE_OK;
+}
+
+static int plan_for(int64_t M, int64_t N, int P, int rank, int order, int bm, int bn, int tm,
+                    int tn, int peer_ready, int release_group, Plan* p) {
+  Geometry g;
+  int rc = make_geometry(M, N, P, bm, bn, tm, tn, &g);
+  if (rc) return fail(rc, "invalid geometry");
+  if (order == ENTWINE_ORDER_AUTO) order = ENTWINE_ORDER_INTERLEAVED;
+  rc = build_plan(g, rank, order, peer_ready, release_group, p);
+  if (rc) return fail(rc, "invalid schedule arguments");
+  return ENTWINE_OK;
+}
+
+int entwine_plan_blocks(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                        int block_n, int tile_m, int tile_n, int32_t* blocks, int64_t capacity) {
+  Plan p;
+  int rc = plan_for(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
+                    ENTWINE_PEERS_PRESEEDED, ENTWINE_RELEASE_TILE, &p);
+  if (rc) return rc;
+  if (!blocks || capacity < (int64_t)p.blocks.size())
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "blocks needs %zu entries", p.blocks.size());
+  std::copy(p.blocks.begin(), p.blocks.end(), blocks);
+  return ENTWINE_OK;
+}
+
+int entwine_plan_tiles(int64_t M, int64_t N, int P, int block_m, int block_n, int tile_m,
+                       int tile_n, int32_t* tiles, int64_t capacity) {
+  Plan p;
+  int rc = plan_for(M, N, P, 0, ENTWINE_ORDER_INTERLEAVED, block_m, block_n, tile_m, tile_n,
+                    ENTWINE_PEERS_PRESEEDED, ENTWINE_RELEASE_TILE, &p);
+  if (rc) return rc;
+  if (!tiles || capacity < (int64_t)p.tiles.size())
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tiles needs %zu entries", p.tiles.size());
+  std::copy(p.tiles.begin(), p.tiles.end(), tiles);
+  return ENTWINE_OK;
+}
+
+int entwine_plan_waits(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                       int block_n, int tile_m, int tile_n, int peer_ready, int release_group,
+                       int32_t* waits, int64_t capacity) {
+  Plan p;
+  int rc = plan_for(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n, peer_ready,
+                    release_group, &p);
+  if (rc) return rc;
+  if (!waits || capacity < (int64_t)p.waits.size())
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "waits needs %zu entries", p.waits.size());
+  std::copy(p.waits.begin(), p.waits.end(), waits);
+  return ENTWINE_OK;
+}
+
+int entwine_plan_tasks(int64_t Q, int comm_budget, int consumer, int32_t* tasks, int64_t capacity,
+                       int64_t* count) {
+  if (Q < 0 || comm_budget < 1 || consumer < 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "need Q >= 0, comm_budget >= 1, consumer >= 0");
+  const int64_t x = std::min<int64_t>(comm_budget, Q);
+  int64_t n = 0;
+  if (consumer < x)
+    for (int64_t t = consumer; t < Q; t += x) {
+      if (tasks && n < capacity) tasks[n] = (int32_t)t;
+      ++n;
+    }
+  if (count) *count = n;
+  if (n > capacity) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tasks needs %" PRId64 " entries", n);
+  return ENTWINE_OK;
+}
+
+int entwine_device_status(void* stream) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  Workspace* w = nullptr;
+  int rc = get_workspace(&w);
+  if (rc) return rc;
+  HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
+  HIP_TRY(hipStreamSynchronize(w->s_gemm));
+  HIP_TRY(hipStreamSynchronize(w->s_red));
+  int32_t err = 0;
+  HIP_TRY(hipMemcpy(&err, w->error, sizeof err, hipMemcpyDeviceToHost));
+  if (err != 0) {
+    HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
+    return fail(err, "a reduction workgroup timed out waiting for a tile flag");
+  }
+  return ENTWINE_OK;
+}
+
+const char* entwine_status_string(int status) {
+  switch (status) {
+    case ENTWINE_OK: return "ENTWINE_OK";
+    case ENTWINE_ERR_INVALID_ARGUMENT: return "ENTWINE_ERR_INVALID_ARGUMENT";
+    case ENTWINE_ERR_UNSUPPORTED: return "ENTWINE_ERR_UNSUPPORTED";
+    case ENTWINE_ERR_OUT_OF_MEMORY: return "ENTWINE_ERR_OUT_OF_MEMORY";
+    case ENTWINE_ERR_HIP: return "ENTWINE_ERR_HIP";
+    case ENTWINE_ERR_TIMEOUT: return "ENTWINE_ERR_TIMEOUT";
+    default: return "ENTWINE_ERR_UNKNOWN";
+  }
+}
+
+const char* entwine_last_error_message(void) { return g_last_error.c_str(); }
+
+int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* bytes) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end()) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no workspace on this device yet");
+  Workspace* w = it->second.get();
+  HIP_TRY(hipStreamSynchronize(w->s_gemm));
+  HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (own_partial) *own_partial = w->own;
+  if (outgoing) *outgoing = w->outgoing;
+  if (bytes) *bytes = (int64_t)(w->own_bytes + w->outgoing_bytes + w->flag_count * 4);
+  return ENTWINE_OK;
+}
+
+int entwine_timing(int enable) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_timing = enable != 0;
+  return ENTWINE_OK;
+}
+
+int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  double gs = 0, rsum = 0;
+  int64_t n = 0;
+  for (auto& kv : g_ws) {
+    Workspace* w = kv.second.get();
+    for (auto& t : w->timing_live) {
+      HIP_TRY(hipEventSynchronize(t.g1));
+      HIP_TRY(hipEventSynchronize(t.r1));
+      float a = 0, b = 0;
+      HIP_TRY(hipEventElapsedTime(&a, t.g0, t.g1));
+      HIP_TRY(hipEventElapsedTime(&b, t.r0, t.r1));
+      gs += a;
+      rsum += b;
+      ++n;
+      w->timing_free.push_back(t);
+    }
+    w->timing_live.clear();
+  }
+  if (gemm_ms) *gemm_ms = gs;
+  if (reduce_ms) *reduce_ms = rsum;
+  if (calls) *calls = n;
+  return ENTWINE_OK;
+}
+
+int entwine_load_tuning(const char* path) {
+  if (!path) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "path is NULL");
+  FILE* f = std::fopen(path, "r");
+  if (!f) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "cannot open %s", path);
+  std::map<std::tuple<int64_t, int64_t, int64_t, int>, TuneEntry> table;
+  char line[512];
+  int lineno = 0;
+  while (std::fgets(line, sizeof line, f)) {
+    ++lineno;
+    if (line[0] == '#' || line[0] == '\n') continue;
+    long long M, N, K;
+    int P, order, budget, bm, bn, threads;
+    if (std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d", &M, &N, &K, &P, &order, &budget,
+                    &bm, &bn, &threads) != 9) {
+      std::fclose(f);
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "%s:%d: expected 9 integers", path, lineno);
+    }
+    table[std::make_tuple((int64_t)M, (int64_t)N, (int64_t)K, P)] =
+        TuneEntry{order, budget, bm, bn, threads};
+  }
+  std::fclose(f);
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_tuning = std::move(table);
+  return ENTWINE_OK;
+}
+
+int entwine_release(void) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end()) return ENTWINE_OK;
+  destroy_workspace(it->second.get());
+  g_ws.erase(it);
+  return ENTWINE_OK;
+}
+
+int entwine_device_cus(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return cus;
+}
+
+}  // extern "C"

@@ -1,0 +1,60 @@
+// kernels.h -- argument blocks and launchers of the two device kernels.
+//
+// gemm_publish: the producer (Sec. 4.2, Producer): one workgroup per logical
+//   block position, bf16 MFMA main loop, stores, then one release flag per
+//   covered reduction tile.
+// tile_reduce: the consumer (Sec. 4.2, Consumer / ReduceTile): x persistent
+//   workgroups walking tasks j, j+x, ...; acquire-wait on the tile's flags,
+//   then local + peers (rank order) in fp32, one store per output element.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace entwine {
+
+constexpr int kMaxRanks = 8;
+
+struct GemmArgs {
+  const uint16_t* X;        // bf16 [M][K]
+  const uint16_t* W;        // bf16 [N][K]
+  float* own;               // fp32 [R][N]: partial of partition `rank`
+  void* outgoing;           // peer dtype [M][N]: partials for other partitions
+  uint32_t* flags;          // [P][Q] tile flags
+  const int32_t* blocks;    // [NB][4]: d, br, bc, first tile
+  int32_t M, N, K, R;       // R = M / P
+  int32_t rank, Q;
+  int32_t Rt, Ct;           // tile rows / cols per partition
+  int32_t tm, tn;           // reduction tile
+  int32_t outgoing_f32;     // outgoing partials in fp32 (else bf16)
+  uint32_t epoch;
+};
+
+struct ReduceArgs {
+  const float* own;                 // fp32 [R][N]
+  const void* peers[kMaxRanks];     // peer dtype [R][N]; [rank] unused
+  void* out;                        // out dtype [R][N]
+  const uint32_t* flags;            // [P][Q]
+  const int32_t* waits;             // [Q][P] flag index or -1
+  const int32_t* tiles;             // [Q][2] tile row, tile col
+  int32_t* error;                   // sticky device error word
+  int32_t R, N, P, rank, Q;
+  int32_t tm, tn;
+  int32_t slabs;                    // row slabs per tile (task = tile x slab)
+  int32_t ntasks;                   // Q * slabs
+  uint32_t epoch;
+  uint64_t timeout_ticks;           // watchdog, in wall-clock ticks
+  int32_t withhold_tile;            // -1, or a tile whose local wait watches `never_flag`
+  int32_t never_flag;               // a flag slot that no GEMM of this call writes
+};
+
+// GEMM block shapes built: (bm, bn) in {128, 256}^2.
+hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
+                               hipStream_t stream);
+
+// peer / out dtype: 0 = bf16, 1 = fp32.  threads in {128, 256, 512}.
+hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
+                              int grid, hipStream_t stream);
+
+}  // namespace entwine
