@@ -143,12 +143,17 @@ typedef struct entwine_config {
   int32_t out_dtype;       /* ENTWINE_BF16 or ENTWINE_F32 */
   int32_t peer_ready;      /* ENTWINE_PEERS_PRESEEDED or ENTWINE_PEERS_SYMMETRIC */
   int32_t release_group;   /* ENTWINE_RELEASE_* or g > 1 tiles per release group */
-  int32_t seq_reduce_slabs;/* sequential mode: row slabs per tile for the reduction grid; 0 = auto */
+  int32_t task_slabs;      /* overlapped schedule: row slabs per reduction task, dividing
+                              tile_m (0 = 1: one task per tile, Sec. 3.1) */
   uint32_t poll_timeout_ms;/* reduction watchdog; 0 = 2000 ms */
   int32_t withhold_tile;   /* failure injection for tests: 0 = off; t+1 makes tile t's local
                               wait watch a flag that no GEMM of the call sets, so that tile's
                               reduction workgroup times out (ENTWINE_ERR_TIMEOUT) */
-  int32_t reserved[7];
+  int32_t gemm_variant;    /* GEMM main-loop variant for the block shape: 0 = default */
+  int32_t publish_all;     /* 0: agent-scope release only for tiles a kernel on this device
+                              reads (the rank's partition), progress flags for the rest;
+                              1: release every tile (the cost of publishing to peers) */
+  int32_t reserved[5];
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);
@@ -182,9 +187,12 @@ int entwine_plan_blocks(int64_t M, int64_t N, int P, int rank, int tile_order, i
 int entwine_plan_tiles(int64_t M, int64_t N, int P, int block_m, int block_n, int tile_m,
                        int tile_n, int32_t* tiles, int64_t capacity);
 
-/* waits[t*P + r] = index into the flag array F[P][Q] (flattened d*Q + t')
- * that stands for source rank r's contribution to tile t of partition
- * `rank`, or -1 when that contribution needs no wait (PRESEEDED peers). */
+/* waits[t*(P+1) + r], r < P: index into the flag array F[P][Q] (flattened
+ * d*Q + t') of the flag that stands for source rank r's contribution to tile
+ * t of partition `rank`, or -1 when that contribution needs no wait
+ * (PRESEEDED peers).  The local slot r = rank is always the tile's own flag.
+ * waits[t*(P+1) + P]: the flag that releases t's release group (Sec. 5.3.2),
+ * or -1 with per-tile release. */
 int entwine_plan_waits(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
                        int block_n, int tile_m, int tile_n, int peer_ready, int release_group,
                        int32_t* waits, int64_t capacity);

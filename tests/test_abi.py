@@ -94,7 +94,8 @@ def test_validation_before_any_device_call(lib, kw, status):
     ("peer_dtype", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("peer_ready", 2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("release_group", -2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
-    ("seq_reduce_slabs", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("task_slabs", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("publish_all", 2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("struct_size", 4, tog.ENTWINE_ERR_INVALID_ARGUMENT),
 ])
 def test_config_validation(lib, field, value, status):

@@ -78,8 +78,14 @@ def test_reducer_variants_bit_identical(dev, w):
                                         release_group=group))
                     np.testing.assert_array_equal(out, base)
     for slabs in (1, 2, 8):
-        out = down(case.run(tog.ORDER_INTERLEAVED, 0, seq_reduce_slabs=slabs))
+        for budget in (1, 5, 64):
+            out = down(case.run(tog.ORDER_INTERLEAVED, budget, task_slabs=slabs))
+            np.testing.assert_array_equal(out, base)
+    for publish_all in (0, 1):
+        out = down(case.run(tog.ORDER_COL_MAJOR, 3, publish_all=publish_all))
         np.testing.assert_array_equal(out, base)
+    out = down(case.run(tog.ORDER_INTERLEAVED, 0))
+    np.testing.assert_array_equal(out, base)
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)

@@ -112,15 +112,15 @@ def test_wait_tables(shape):
     for rank in range(P):
         for order in ORDERS:
             pre = tog.entwine_plan_waits(M, N, P, rank, order, bm, bn, tm, tn, tog.PEERS_PRESEEDED)
-            assert pre == [[rank * q + t if r == rank else -1 for r in range(P)] for t in range(q)]
+            assert pre == [[rank * q + t if r == rank else -1 for r in range(P)] + [-1] for t in range(q)]
         for order in (tog.ORDER_INTERLEAVED, tog.ORDER_ROW_MAJOR, tog.ORDER_COL_MAJOR):
             sym = tog.entwine_plan_waits(M, N, P, rank, order, bm, bn, tm, tn, tog.PEERS_SYMMETRIC)
-            assert sym == [[rank * q + t] * P for t in range(q)]
+            assert sym == [[rank * q + t] * P + [-1] for t in range(q)]
         # Partition-major: peer r reaches partition `rank` after (rank-r-1) mod P runs;
         # this GPU is then in partition (rank+1+k) mod P = (2*rank - r) mod P.
         sym = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_PARTITION_MAJOR, bm, bn, tm, tn,
                                      tog.PEERS_SYMMETRIC)
-        assert sym == [[((2 * rank - r) % P) * q + t for r in range(P)] for t in range(q)]
+        assert sym == [[((2 * rank - r) % P) * q + t for r in range(P)] + [-1] for t in range(q)]
 
 
 def test_release_groups():
@@ -134,15 +134,16 @@ def test_release_groups():
     # any flag of the closing block will do: a block publishes all of its
     # tiles' flags together, after all of its stores
     closing = {rank * q + blocks[last][3], rank * q + blocks[last][3] + 1}
-    assert {w[rank] for w in part} <= closing
+    assert {w[P] for w in part} <= closing
+    assert [w[rank] for w in part] == [rank * q + t for t in range(q)]
     out = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn,
                                  tog.PEERS_PRESEEDED, tog.RELEASE_OUTPUT)
     d, _, _, first = blocks[nb - 1]
-    assert {w[rank] for w in out} <= {d * q + first, d * q + first + 1}
+    assert {w[P] for w in out} <= {d * q + first, d * q + first + 1}
     g2 = tog.entwine_plan_waits(M, N, P, rank, tog.ORDER_INTERLEAVED, bm, bn, tm, tn,
                                 tog.PEERS_PRESEEDED, 4)
     # groups {0..3} and {4,5}: closed by the blocks holding tiles {2,3} and {4,5}
-    assert [w[rank] - rank * q for w in g2] == [2, 2, 2, 3, 4, 5]
+    assert [w[P] - rank * q for w in g2] == [2, 2, 2, 3, 4, 5]
 
 
 @pytest.mark.parametrize("q,x", [(6, 2), (128, 32), (96, 1), (5, 9), (1, 1)])

@@ -60,10 +60,12 @@ class entwine_config(ctypes.Structure):
         ("out_dtype", ctypes.c_int32),
         ("peer_ready", ctypes.c_int32),
         ("release_group", ctypes.c_int32),
-        ("seq_reduce_slabs", ctypes.c_int32),
+        ("task_slabs", ctypes.c_int32),
         ("poll_timeout_ms", ctypes.c_uint32),
         ("withhold_tile", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 7),
+        ("gemm_variant", ctypes.c_int32),
+        ("publish_all", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 5),
     ]
 
 
@@ -218,10 +220,11 @@ def entwine_plan_tiles(M, N, P, block_m, block_n, tile_m, tile_n):
 def entwine_plan_waits(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
                        peer_ready=PEERS_PRESEEDED, release_group=RELEASE_TILE):
     _, _, q = entwine_plan_shape(M, N, P, block_m, block_n, tile_m, tile_n)
-    buf = _i32_array(q * P)
+    S = P + 1
+    buf = _i32_array(q * S)
     _check(load().entwine_plan_waits(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
-                                     peer_ready, release_group, buf, q * P))
-    return [list(buf[t * P:(t + 1) * P]) for t in range(q)]
+                                     peer_ready, release_group, buf, q * S))
+    return [list(buf[t * S:(t + 1) * S]) for t in range(q)]
 
 
 def entwine_plan_tasks(Q, comm_budget, consumer):

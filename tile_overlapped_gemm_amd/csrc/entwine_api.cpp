@@ -249,7 +249,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile;
+      slabs, withhold_tile, variant, publish_all;
   uint32_t timeout_ms;
 };
 
@@ -296,11 +296,15 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->out_f32 = c.out_dtype == ENTWINE_F32;
   r->peer_ready = c.peer_ready;
   r->release_group = c.release_group;
-  r->slabs = c.seq_reduce_slabs;
+  r->slabs = c.task_slabs;
+  r->publish_all = c.publish_all;
   r->timeout_ms = c.poll_timeout_ms ? c.poll_timeout_ms : 2000;
   r->withhold_tile = c.withhold_tile - 1;
+  r->variant = c.gemm_variant;
   if (r->slabs < 0 || (r->slabs > 0 && r->tm % r->slabs != 0))
-    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "seq_reduce_slabs must divide tile_m");
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
+  if (c.publish_all != 0 && c.publish_all != 1)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "publish_all must be 0 or 1");
   return ENTWINE_OK;
 }
 
@@ -382,6 +386,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ga.tm = g.tm;
   ga.tn = g.tn;
   ga.outgoing_f32 = rs.peer_f32;
+  ga.variant = rs.variant;
   ga.epoch = w->epoch;
 
   ReduceArgs ra{};
@@ -397,6 +402,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ra.P = P;
   ra.rank = rank;
   ra.Q = (int32_t)g.Q;
+  ra.wait_slots = dp->plan.wait_slots;
   ra.tm = g.tm;
   ra.tn = g.tn;
   ra.epoch = w->epoch;
@@ -412,16 +418,27 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   if (w->have_prev) HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_red, 0));
   if (clear_flags) HIP_TRY(hipMemsetAsync(w->flags, 0, w->flag_count * 4, w->s_gemm));
 
+  // Sequential schedule (budget 0): the GEMM publishes nothing and the
+  // reduction streams the whole partition after the GEMM kernel has ended.
+  // Overlapped schedule: the GEMM releases its tiles and x persistent
+  // reduction workgroups consume them as they become ready.
   const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
   hipStream_t s_red = sequential ? w->s_gemm : w->s_red;
+  int grid;
   if (sequential) {
-    ra.slabs = rs.slabs ? rs.slabs : std::max(1, std::min(g.tm, (int)((4 * w->cus + g.Q - 1) / g.Q)));
-    while (g.tm % ra.slabs) --ra.slabs;
-  } else {
+    ga.publish = 0;
     ra.slabs = 1;
+    ra.ntasks = 0;
+    const int64_t chunks = g.R * N / 8;
+    const int64_t per_wg = (int64_t)rs.threads * 2;
+    grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + per_wg - 1) / per_wg,
+                                                        (int64_t)8 * w->cus));
+  } else {
+    ga.publish = rs.publish_all ? 2 : 1;
+    ra.slabs = rs.slabs ? rs.slabs : 1;
+    ra.ntasks = (int32_t)(g.Q * ra.slabs);
+    grid = (int)std::min<int64_t>(rs.budget, ra.ntasks);
   }
-  ra.ntasks = (int32_t)(g.Q * ra.slabs);
-  const int grid = sequential ? ra.ntasks : x;
 
   if (g_timing) HIP_TRY(hipEventRecord(tp.g0, w->s_gemm));
   hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, w->s_gemm);
@@ -429,7 +446,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   if (g_timing) HIP_TRY(hipEventRecord(tp.g1, w->s_gemm));
   HIP_TRY(hipEventRecord(w->ev_gemm, w->s_gemm));
   if (g_timing) HIP_TRY(hipEventRecord(tp.r0, s_red));
-  e = launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, grid, s_red);
+  e = launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, sequential, grid, s_red);
   if (e != hipSuccess)
     return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
   if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));

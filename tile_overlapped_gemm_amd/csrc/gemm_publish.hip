@@ -14,22 +14,29 @@
 // MI355X (gfx950) design.
 //  * 256 threads = 4 waves of 64 in a 2 x 2 arrangement; a wave owns a
 //    (BM/2) x (BN/2) sub-block computed with v_mfma_f32_32x32x16_bf16 into
-//    fp32 accumulators.
-//  * K advances in stages of 64 (128 bytes per row).  Each stage of X rows and
-//    W rows (W is [N][K], K contiguous, so both operands are K-major) moves
-//    from global memory straight into LDS with global_load_lds_dwordx4: one
-//    wave instruction fills 1 KiB = 8 rows of 128 bytes.  Two stages are
-//    double-buffered so the next stage's loads overlap the current MFMAs.
+//    fp32 accumulators.  The MFMA's first operand is the W fragment and the
+//    second the X fragment, so each lane ends up holding runs of 4
+//    consecutive output columns (16-byte fp32 / 8-byte bf16 stores).
+//  * K advances in stages of 64 (128 bytes per row).  X and W are both
+//    K-contiguous, so each stage is a BM x 128 B and a BN x 128 B slab.  Slabs
+//    move from global memory straight into LDS with buffer_load_dwordx4 ...
+//    lds: one wave instruction fills 1 KiB = 8 rows.  The buffer descriptors
+//    bound the block's rows, so rows past the partition's (or N's) end read as
+//    zeros without any clamping.  Two LDS stages: the loads of stage k+1 are
+//    in flight while stage k is multiplied.
 //  * LDS rows are XOR-swizzled in 16-byte chunks (chunk c of row r is stored
-//    at c ^ swz(r)), so the 32 rows that one MFMA operand read touches spread
-//    over all banks.  The swizzle is realised by choosing each lane's global
-//    source address, since the LDS destination of lane l is fixed at 16*l.
-//  * Rows past the partition's end (or N's end) are clamped on load and
-//    masked on store, so edge blocks never read out of bounds.
-//  * Publication: every wave issues an agent-scope release fence after its
-//    own stores (the gfx950 workgroup barrier does not wait for other waves'
-//    stores), the workgroup synchronizes, then one lane per covered tile
-//    release-stores the call's epoch into the tile's flag.
+//    at c ^ swz(r)), so the 32 rows one fragment read touches spread over all
+//    banks.  The swizzle is realised through each lane's global source
+//    address, since the LDS destination of lane l is fixed at 16*l.
+//  * Fragments are double-buffered in registers across the four 16-deep K
+//    steps of a stage and across the stage boundary: the workgroup barrier
+//    that hands over the next stage sits before the last K step's MFMAs, which
+//    cover the barrier and the next stage's first fragment reads.
+//  * Epilogue: accumulators leave through LDS in 32-row strips so that the
+//    global stores write whole cache lines.
+//  * Publication: the workgroup synchronizes after its stores, then thread 0
+//    issues one agent-scope release fence and stores the call's epoch into the
+//    flag of every tile the block covers.
 #include "kernels.h"
 
 namespace entwine {
@@ -37,62 +44,103 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
-
-constexpr int kBK = 64;          // K per stage
-constexpr int kRowBytes = 128;   // kBK bf16
-constexpr int kThreads = 256;
-
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-__device__ __forceinline__ int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+constexpr int kThreads = 256;
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-template <int BM, int BN>
-struct Tile {
-  static constexpr int kWM = BM / 2, kWN = BN / 2;  // wave sub-block
+// Block BM x BN, K stage BK (32 or 64), NS LDS stages.
+template <int BM, int BN, int BK, int NS>
+struct Shape {
+  static constexpr int kRow = BK * 2;                 // bytes per slab row
+  static constexpr int kRowsPerLoad = 1024 / kRow;    // rows per 1 KiB wave load
+  static constexpr int kLanesPerRow = kRow / 16;
+  static constexpr int kKS = BK / 16;                 // MFMA K steps per stage
+  static constexpr int kWM = BM / 2, kWN = BN / 2;    // wave sub-block
   static constexpr int kMT = kWM / 32, kNT = kWN / 32;
-  static constexpr int kStageA = BM * kRowBytes, kStageB = BN * kRowBytes;
-  static constexpr int kStage = kStageA + kStageB;
-  static constexpr int kLds = 2 * kStage;
-  static constexpr int kOctA = BM / 8 / 4, kOctB = BN / 8 / 4;  // octets per wave
+  static constexpr int kA = BM * kRow, kB = BN * kRow;  // stage slabs
+  static constexpr int kStage = kA + kB;
+  static constexpr int kLds = NS * kStage;
+  static constexpr int kLoadsA = BM / (4 * kRowsPerLoad);  // per wave per stage
+  static constexpr int kLoadsB = BN / (4 * kRowsPerLoad);
+  static constexpr int kLoads = kLoadsA + kLoadsB;
+  static_assert(kKS % 2 == 0, "fragment double buffer needs an even K-step count");
+  static_assert(kLoads * (NS - 2 > 0 ? NS - 2 : 0) < 64, "vmcnt range");
 };
 
-// Issue the global->LDS copies of one K stage.  Octet o (8 rows) of a
-// tile is loaded by wave (o % 4); lane l fills physical chunk (l & 7) of row
-// 8o + (l >> 3), i.e. logical chunk (l & 7) ^ swz(row).
-template <int BM, int BN>
-__device__ __forceinline__ void load_stage(const uint16_t* __restrict__ X,
-                                           const uint16_t* __restrict__ W, char* lds_stage,
-                                           int K, int k0, int wave, int lane,
-                                           const int* __restrict__ a_row,
-                                           const int* __restrict__ b_row) {
-  using T = Tile<BM, BN>;
-  const int r_in = lane >> 3;
-  const int pc = lane & 7;
-#pragma unroll
-  for (int j = 0; j < T::kOctA; ++j) {
-    const int o = wave + 4 * j;
-    const int r = 8 * o + r_in;
-    const uint16_t* src = X + (int64_t)a_row[j] * K + k0 + 8 * (pc ^ swz(r));
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(lds_stage + o * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int j = 0; j < T::kOctB; ++j) {
-    const int o = wave + 4 * j;
-    const int r = 8 * o + r_in;
-    const uint16_t* src = W + (int64_t)b_row[j] * K + k0 + 8 * (pc ^ swz(r));
-    __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(lds_stage + T::kStageA + o * 1024), 16,
-                                     0, 0);
-  }
+// XOR swizzle of 16-byte chunks, a function of (row mod 16): every group of
+// 8 (or 16) consecutive fragment rows read at one logical chunk hits distinct
+// LDS banks.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64)
+    return (r & 7) ^ ((r >> 3) & 1);
+  else
+    return ((r >> 1) ^ (r >> 3)) & 3;
 }
 
-__device__ __forceinline__ bf16x8 read_frag(const char* lds_tile, int row, int chunk) {
-  return *reinterpret_cast<const bf16x8*>(lds_tile + row * kRowBytes +
-                                          ((chunk ^ swz(row)) << 4));
+// Wait until at most VM of this wave's vector-memory operations are pending
+// and all of its LDS reads returned, then synchronize the workgroup.  No
+// global-memory fence: the stage hand-over only needs LDS.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
 }
 
-template <int BM, int BN>
-__global__ __launch_bounds__(kThreads) void gemm_publish_kernel(GemmArgs a) {
-  using T = Tile<BM, BN>;
+__device__ __forceinline__ bf16x8 lds_frag(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// One stage of global->LDS copies for this wave: load group o = wave + 4j of
+// X's slab, then of W's.  voff is the lane's byte offset (row and swizzled
+// chunk); soffset adds the group's rows and the stage's K offset.
+template <class S>
+__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            char* lds, int voff, int group_step, int kbyte,
+                                            int wave) {
+#pragma unroll
+  for (int j = 0; j < S::kLoadsA; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + 4 * j) * 1024), 16,
+                                             voff, j * group_step + kbyte, 0, 0);
+#pragma unroll
+  for (int j = 0; j < S::kLoadsB; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + S::kA + (wave + 4 * j) * 1024),
+                                             16, voff, j * group_step + kbyte, 0, 0);
+}
+
+template <class S>
+struct Frags {
+  bf16x8 b[S::kNT];  // W fragments (MFMA rows = output columns)
+  bf16x8 a[S::kMT];  // X fragments (MFMA cols = output rows)
+};
+
+template <class S>
+__device__ __forceinline__ void read_frags(Frags<S>& f, const char* stage, int a_off, int b_off) {
+#pragma unroll
+  for (int j = 0; j < S::kNT; ++j) f.b[j] = lds_frag(stage + S::kA + b_off + j * 32 * S::kRow);
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i) f.a[i] = lds_frag(stage + a_off + i * 32 * S::kRow);
+}
+
+template <class S>
+struct Acc {
+  f32x16 c[S::kMT][S::kNT];
+};
+
+template <class S>
+__device__ __forceinline__ void mfma_step(Acc<S>& acc, const Frags<S>& f) {
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
+}
+
+template <int BM, int BN, int BK, int NS>
+__global__ __launch_bounds__(kThreads, 1) void gemm_publish_kernel(GemmArgs a) {
+  using S = Shape<BM, BN, BK, NS>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x;
@@ -102,115 +150,180 @@ __global__ __launch_bounds__(kThreads) void gemm_publish_kernel(GemmArgs a) {
 
   const int4 blk = reinterpret_cast<const int4*>(a.blocks)[blockIdx.x];
   const int d = blk.x, br = blk.y, bc = blk.z, t_first = blk.w;
-  const int row_base = br * BM;  // within the partition
-  const int col_base = bc * BN;
+  const int row0 = br * BM;  // within the partition
+  const int col0 = bc * BN;
+  const int K = a.K;
+  const int kbytes = K * 2;
 
-  // Source rows of this lane's load octets, clamped to the partition / N.
-  int a_row[T::kOctA], b_row[T::kOctB];
-#pragma unroll
-  for (int j = 0; j < T::kOctA; ++j) {
-    const int r = 8 * (wave + 4 * j) + (lane >> 3);
-    a_row[j] = d * a.R + min(row_base + r, a.R - 1);
-  }
-#pragma unroll
-  for (int j = 0; j < T::kOctB; ++j) {
-    const int r = 8 * (wave + 4 * j) + (lane >> 3);
-    b_row[j] = min(col_base + r, a.N - 1);
-  }
+  // Buffer descriptors bound the block's rows: X rows of partition d from
+  // row0, W rows (output columns) from col0.  Out-of-range rows read 0.
+  const int rows_a = min(BM, a.R - row0);
+  const int rows_b = min(BN, a.N - col0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + ((int64_t)d * a.R + row0) * K), (short)0, rows_a * kbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + (int64_t)col0 * K), (short)0, rows_b * kbytes, kRsrcWord3);
 
-  f32x16 acc[T::kMT][T::kNT];
-#pragma unroll
-  for (int i = 0; i < T::kMT; ++i)
-#pragma unroll
-    for (int j = 0; j < T::kNT; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
+  // Global source of this lane: row wave*RPL + lane/LPR of each group of
+  // 4*RPL rows, logical chunk (lane % LPR) ^ swz(row).
+  const int lrow = wave * S::kRowsPerLoad + lane / S::kLanesPerRow;
+  const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK>(lrow);
+  const int voff = lrow * kbytes + lchunk * 16;
+  const int group_step = 4 * S::kRowsPerLoad * kbytes;
 
-  const int nk = a.K / kBK;
-  load_stage<BM, BN>(a.X, a.W, smem, a.K, 0, wave, lane, a_row, b_row);
-  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's stage-0 copies landed
-  __syncthreads();
-
-  const int a_row0 = wm * T::kWM + (lane & 31);
-  const int b_row0 = wn * T::kWN + (lane & 31);
+  // LDS fragment offsets: MFMA lane l reads row (l & 31) of a 32-row group,
+  // logical chunk 2*ks + (l >> 5).
+  const int frow = lane & 31;
   const int khalf = lane >> 5;
+  int a_off[S::kKS], b_off[S::kKS];
+#pragma unroll
+  for (int ks = 0; ks < S::kKS; ++ks) {
+    const int c = ((2 * ks + khalf) ^ swz<BK>(frow)) << 4;
+    a_off[ks] = (wm * S::kWM + frow) * S::kRow + c;
+    b_off[ks] = (wn * S::kWN + frow) * S::kRow + c;
+  }
+
+  Acc<S> acc;
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+
+  // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, then stage NS-1.
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue_stage<S>(ra, rb, smem + s * S::kStage, voff, group_step, s * S::kRow, wave);
+  if (nk >= NS - 1)
+    stage_barrier<S::kLoads * (NS - 2)>();
+  else
+    stage_barrier<0>();
+  if (NS - 1 < nk)
+    issue_stage<S>(ra, rb, smem + (NS - 1) * S::kStage, voff, group_step, (NS - 1) * S::kRow,
+                   wave);
+
+  Frags<S> f0, f1;
+  read_frags<S>(f0, smem, a_off[0], b_off[0]);
 
   for (int kt = 0; kt < nk; ++kt) {
-    char* cur = smem + (kt & 1) * T::kStage;
-    if (kt + 1 < nk)
-      load_stage<BM, BN>(a.X, a.W, smem + ((kt + 1) & 1) * T::kStage, a.K, (kt + 1) * kBK,
-                         wave, lane, a_row, b_row);
-    const char* As = cur;
-    const char* Bs = cur + T::kStageA;
+    const int buf = kt % NS;
+    const char* cur = smem + buf * S::kStage;
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int chunk = 2 * ks + khalf;
-      bf16x8 af[T::kMT], bfr[T::kNT];
-#pragma unroll
-      for (int i = 0; i < T::kMT; ++i) af[i] = read_frag(As, a_row0 + 32 * i, chunk);
-#pragma unroll
-      for (int j = 0; j < T::kNT; ++j) bfr[j] = read_frag(Bs, b_row0 + 32 * j, chunk);
-#pragma unroll
-      for (int i = 0; i < T::kMT; ++i)
-#pragma unroll
-        for (int j = 0; j < T::kNT; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-    }
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): next stage's copies landed
-    __syncthreads();                      // and every wave is done with `cur`
-  }
-
-  // Epilogue.  Accumulator element v of lane l holds row
-  // 8*(v/4) + 4*(l/32) + (v%4) and column l%32 of its 32x32 MFMA tile.
-  const int col_l = lane & 31;
-  const int row_l = 4 * (lane >> 5);
-  const bool local = (d == a.rank);
-#pragma unroll
-  for (int i = 0; i < T::kMT; ++i) {
-#pragma unroll
-    for (int j = 0; j < T::kNT; ++j) {
-      const int col = col_base + wn * T::kWN + 32 * j + col_l;
-      if (col >= a.N) continue;
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int prow = row_base + wm * T::kWM + 32 * i + 8 * (v >> 2) + row_l + (v & 3);
-        if (prow >= a.R) continue;
-        const float x = acc[i][j][v];
-        if (local) {
-          a.own[(int64_t)prow * a.N + col] = x;
-        } else {
-          const int64_t e = (int64_t)(d * a.R + prow) * a.N + col;
-          if (a.outgoing_f32)
-            static_cast<float*>(a.outgoing)[e] = x;
-          else
-            static_cast<__bf16*>(a.outgoing)[e] = static_cast<__bf16>(x);
-        }
+    for (int ks = 0; ks + 1 < S::kKS; ks += 2) {
+      read_frags<S>(f1, cur, a_off[ks + 1], b_off[ks + 1]);
+      mfma_step<S>(acc, f0);
+      if (ks + 2 < S::kKS) {
+        read_frags<S>(f0, cur, a_off[ks + 2], b_off[ks + 2]);
+        mfma_step<S>(acc, f1);
       }
     }
+    if (kt + 1 < nk) {
+      // Stage kt+1 must have landed (stages up to kt+NS-1 were issued), and
+      // every wave must be done reading `cur`, which then takes stage kt+NS.
+      if (kt + NS - 1 < nk)
+        stage_barrier<S::kLoads * (NS - 2)>();
+      else
+        stage_barrier<0>();
+      if (kt + NS < nk)
+        issue_stage<S>(ra, rb, smem + buf * S::kStage, voff, group_step, (kt + NS) * S::kRow,
+                       wave);
+      read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, a_off[0], b_off[0]);
+    }
+    mfma_step<S>(acc, f1);
   }
 
-  // Publish (Sec. 4.2): all stores of the block, then the tiles' flags.
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  // Epilogue.  With the W fragment as the MFMA's row operand, accumulator
+  // element v of lane l holds output row (l & 31) of its 32 x 32 tile and
+  // columns 8*(v/4) + 4*(l/32) + v%4.  Each 32-row strip of the wave's
+  // sub-block is staged through the wave's own LDS area (rows padded by 16
+  // bytes so the transposed writes spread over the banks) and read back
+  // row-contiguous, so every global store instruction covers whole 128-byte
+  // lines: 16-byte fp32 stores for the local partition, 8-byte bf16 (or
+  // 16-byte fp32) stores for the outgoing contributions.
+  constexpr int kPitch = S::kWN * 4 + 16;
+  constexpr int kLanesPerRow = S::kWN / 4;
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  static_assert(4 * 32 * kPitch <= S::kLds, "epilogue staging exceeds LDS");
+  __syncthreads();  // every wave is done with the pipeline buffers
+  char* wbuf = smem + wave * 32 * kPitch;
+  const bool local = (d == a.rank);
+  const int rsub = lane / kLanesPerRow;
+  const int csub = (lane % kLanesPerRow) * 4;
+  const int col = col0 + wn * S::kWN + csub;
+  const bool col_ok = col < a.N;
+  float* const own_base = a.own + col;
+  const int64_t og_base = (int64_t)d * a.R * a.N + col;
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i) {
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+        v[0] = acc.c[i][j][4 * g + 0];
+        v[1] = acc.c[i][j][4 * g + 1];
+        v[2] = acc.c[i][j][4 * g + 2];
+        v[3] = acc.c[i][j][4 * g + 3];
+        *reinterpret_cast<f32x4*>(wbuf + frow * kPitch + (32 * j + 8 * g + 4 * khalf) * 4) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the strip is in LDS
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int q = 0; q < 32 / kRowsPerStore; ++q) {
+      const int r = q * kRowsPerStore + rsub;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(wbuf + r * kPitch + csub * 4);
+      const int prow = row0 + wm * S::kWM + 32 * i + r;
+      if (prow >= a.R || !col_ok) continue;
+      const int64_t e = (int64_t)prow * a.N;
+      if (local) {
+        *reinterpret_cast<f32x4*>(own_base + e) = v;
+      } else if (a.outgoing_f32) {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.outgoing) + og_base + e) = v;
+      } else {
+        bf16x4 h;
+        h[0] = static_cast<__bf16>(v[0]);
+        h[1] = static_cast<__bf16>(v[1]);
+        h[2] = static_cast<__bf16>(v[2]);
+        h[3] = static_cast<__bf16>(v[3]);
+        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.outgoing) + og_base + e) = h;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // strip read back before the next overwrites it
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Publish (Sec. 4.2): all stores of the block, then the tiles' flags.  The
+  // workgroup barrier waits until every wave's stores are acknowledged; one
+  // agent-scope release fence by thread 0 then writes the block's data back
+  // from this XCD's L2 so that a consumer on any XCD sees it, and thread 0
+  // stores the covered tiles' flags.  Data that no kernel on this device
+  // reads (contributions bound for peers) only needs its flags as progress
+  // markers unless every tile is to be released (publish == 2).
   __syncthreads();
-  const int sub_m = BM / a.tm, sub_n = BN / a.tn;
-  const int vm = min(sub_m, a.Rt - br * sub_m);
-  const int vn = min(sub_n, a.Ct - bc * sub_n);
-  if (tid < vm * vn)
-    __hip_atomic_store(a.flags + (int64_t)d * a.Q + t_first + tid, a.epoch, __ATOMIC_RELEASE,
-                       __HIP_MEMORY_SCOPE_AGENT);
+  if (a.publish != 0 && tid == 0) {
+    if (local || a.publish == 2) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    const int sub_m = BM / a.tm, sub_n = BN / a.tn;
+    const int vm = min(sub_m, a.Rt - br * sub_m);
+    const int vn = min(sub_n, a.Ct - bc * sub_n);
+    uint32_t* f = a.flags + (int64_t)d * a.Q + t_first;
+    for (int t = 0; t < vm * vn; ++t)
+      __hip_atomic_store(f + t, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int BK, int NS>
 hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
-  using T = Tile<BM, BN>;
+  using S = Shape<BM, BN, BK, NS>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, T::kLds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm_publish_kernel<BM, BN><<<num_blocks, kThreads, T::kLds, s>>>(a);
+  gemm_publish_kernel<BM, BN, BK, NS><<<num_blocks, kThreads, S::kLds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -218,10 +331,15 @@ hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
 
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream) {
-  if (bm == 128 && bn == 128) return launch_shape<128, 128>(a, num_blocks, stream);
-  if (bm == 128 && bn == 256) return launch_shape<128, 256>(a, num_blocks, stream);
-  if (bm == 256 && bn == 128) return launch_shape<256, 128>(a, num_blocks, stream);
-  if (bm == 256 && bn == 256) return launch_shape<256, 256>(a, num_blocks, stream);
+  const int v = a.variant;
+  if (bm == 128 && bn == 128) return launch_shape<128, 128, 64, 2>(a, num_blocks, stream);
+  if (bm == 128 && bn == 256) return launch_shape<128, 256, 64, 2>(a, num_blocks, stream);
+  if (bm == 256 && bn == 128) return launch_shape<256, 128, 64, 2>(a, num_blocks, stream);
+  if (bm == 256 && bn == 256) {
+    if (v == 1) return launch_shape<256, 256, 32, 4>(a, num_blocks, stream);
+    if (v == 2) return launch_shape<256, 256, 32, 3>(a, num_blocks, stream);
+    return launch_shape<256, 256, 64, 2>(a, num_blocks, stream);
+  }
   return hipErrorInvalidValue;
 }
 

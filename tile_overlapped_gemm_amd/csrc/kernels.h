@@ -28,6 +28,8 @@ struct GemmArgs {
   int32_t Rt, Ct;           // tile rows / cols per partition
   int32_t tm, tn;           // reduction tile
   int32_t outgoing_f32;     // outgoing partials in fp32 (else bf16)
+  int32_t variant;          // GEMM pipeline variant (0 = default for the shape)
+  int32_t publish;          // 0: no flags; 1: release local tiles, mark the rest; 2: release all
   uint32_t epoch;
 };
 
@@ -36,10 +38,11 @@ struct ReduceArgs {
   const void* peers[kMaxRanks];     // peer dtype [R][N]; [rank] unused
   void* out;                        // out dtype [R][N]
   const uint32_t* flags;            // [P][Q]
-  const int32_t* waits;             // [Q][P] flag index or -1
+  const int32_t* waits;             // [Q][wait_slots] flag index or -1
   const int32_t* tiles;             // [Q][2] tile row, tile col
   int32_t* error;                   // sticky device error word
   int32_t R, N, P, rank, Q;
+  int32_t wait_slots;               // P source ranks + 1 release-group slot
   int32_t tm, tn;
   int32_t slabs;                    // row slabs per tile (task = tile x slab)
   int32_t ntasks;                   // Q * slabs
@@ -53,8 +56,9 @@ struct ReduceArgs {
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream);
 
-// peer / out dtype: 0 = bf16, 1 = fp32.  threads in {128, 256, 512}.
+// peer / out dtype: 0 = bf16, 1 = fp32.  threads in {128, 256, 512}.  flat:
+// reduce the whole partition without flags (after the GEMM has finished).
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
-                              int grid, hipStream_t stream);
+                              bool flat, int grid, hipStream_t stream);
 
 }  // namespace entwine

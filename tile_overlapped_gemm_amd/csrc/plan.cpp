@@ -190,17 +190,19 @@ int build_plan(const Geometry& g, int rank, int order, int peer_ready, int relea
     return (int32_t)(d * g.Q + tt);
   };
 
-  pl.waits.assign((size_t)g.Q * g.P, -1);
+  // Wait slots per tile: one per source rank, then one for the release
+  // group.  The local slot is always the tile's own flag: it is what makes the
+  // tile's data safe to read.  A release group (Sec. 5.3.2) additionally holds
+  // the tile back until the block at the group's last logical position is
+  // done, i.e. the group is released when its last tile is produced.
+  const int slots = g.P + 1;
+  pl.wait_slots = slots;
+  pl.waits.assign((size_t)g.Q * slots, -1);
   for (int64_t tt = 0; tt < g.Q; ++tt) {
+    int32_t* w = &pl.waits[tt * slots];
     for (int r = 0; r < g.P; ++r) {
-      int32_t w = -1;
       if (r == rank) {
-        // The local contribution: this GPU's own flag for tile tt of its
-        // partition, or the flag that closes tt's release group.
-        if (release_group == ENTWINE_RELEASE_TILE)
-          w = (int32_t)(rank * g.Q + tt);
-        else
-          w = flag_at_position(release_position(rank, tt), tt);
+        w[r] = (int32_t)(rank * g.Q + tt);
       } else if (peer_ready == ENTWINE_PEERS_SYMMETRIC) {
         // Peer r produces tile tt (block tile_block[tt] of partition `rank`)
         // at its own logical position; this GPU's block at that position
@@ -208,10 +210,11 @@ int build_plan(const Geometry& g, int rank, int order, int peer_ready, int relea
         const int64_t p = release_group == ENTWINE_RELEASE_TILE
                               ? position_of(g, r, order, rank, tile_block[tt])
                               : release_position(r, tt);
-        w = flag_at_position(p, tt);
+        w[r] = flag_at_position(p, tt);
       }
-      pl.waits[tt * g.P + r] = w;
     }
+    if (release_group != ENTWINE_RELEASE_TILE)
+      w[g.P] = flag_at_position(release_position(rank, tt), tt);
   }
   *out = std::move(pl);
   return ENTWINE_OK;

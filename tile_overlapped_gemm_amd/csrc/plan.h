@@ -46,7 +46,8 @@ struct Plan {
   int rank = 0, order = 0, peer_ready = 0, release_group = 1;
   std::vector<int32_t> blocks;   // [NB][4]: d, br, bc, first tile
   std::vector<int32_t> tiles;    // [Q][2]: tile row, tile col
-  std::vector<int32_t> waits;    // [Q][P]: flag index or -1
+  int wait_slots = 0;            // P + 1
+  std::vector<int32_t> waits;    // [Q][wait_slots]: flag index or -1
   std::vector<int32_t> first_tile;  // [Bd]: number of block i's first tile
 };
 
