@@ -1,27 +1,32 @@
 #!/usr/bin/env python3
 """Benchmark of the tile-overlapped GEMM-ReduceScatter on one MI355X.
 
-One step = one entwine_gemm_rs call: the rank's whole share of the operation
-(the GEMM producing every tile with its ready flag, and the concurrent
-reduction of the rank's partition) on inputs already resident in HBM.
+A step is one entwine_gemm_rs call: the rank's whole share of the operation
+(the GEMM producing every output tile and publishing its flag, and the
+concurrent reduction of the rank's partition with the peers' contributions)
+on inputs already resident in HBM.  Steps are replayed from a captured HIP
+graph, as the pages' prototype does with CUDA Graphs, so the timed loop
+measures device time rather than host launch overhead.
 
 Default workload: the MLP down-projection slice, M = N = 4096, K_local =
 1792, P = 8 simulated ranks, rank 0, bf16 inputs, fp32 accumulation, bf16
-output, with the tuning table's choice of order, budget and block shape.
+output, with the tuning table's order, budget and block shape.  Timing
+follows the pages' protocol (Sec. 5.1): warm-up iterations, then timed
+iterations bracketed by HIP events, median reported.
 
-Reported (one JSON line on stdout):
-  value        TFLOP/s of the overlapped step (2*M*N*K_local / latency)
-  ms_per_step  mean step time over the timed steps
-  latency_us_median   median per-step latency (the pages' protocol: 120
-               warm-up and 200 timed iterations, median)
-  sequential   the same kernels run back to back (budget 0) and the
-               speedup of the overlapped schedule over it
-  roofline     the GEMM kernel (the dominant kernel) against the bf16 MFMA
-               dense peak, its duration timed with HIP events on the stream
-               it runs on
-  reducer      the reduction kernel alone (sequential schedule), GB/s of
-               algorithmic bytes against HBM peak
-  cpu_baseline the CPU oracle timed on a bounded sample of the same workload
+One JSON line on stdout:
+  value, ms_per_step   TFLOP/s (2*M*N*K_local / step time) and step time of
+                       the overlapped schedule
+  latency_us_median    median of per-step event pairs
+  sequential           the non-overlapped schedule (GEMM, then reduction) on
+                       the same GPU, and the speedup over it
+  roofline             the GEMM kernel inside the overlapped step against the
+                       bf16 MFMA dense peak; its duration comes from HIP
+                       events recorded on the stream the GEMM runs on
+  reducer              the reduction kernel alone (sequential schedule):
+                       algorithmic bytes / duration against HBM peak, with
+                       the peers' buffers warm and scrubbed from the caches
+  cpu_baseline         the CPU oracle on a bounded row sample of the workload
 """
 from __future__ import annotations
 
@@ -55,8 +60,8 @@ def kernel_sources_digest() -> str:
 
 
 def traffic_for(workload: str, kernel: str):
-    """HBM bytes per launch from committed rocprofv3 counter summaries, if they
-    were taken on the current kernel sources (else None)."""
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
@@ -68,24 +73,29 @@ def traffic_for(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
-def cpu_baseline(w, X, W, peers, target_s: float):
-    """Time the CPU oracle on the first S rows of the partition (S chosen so
-    the run takes about target_s seconds), scaled to TFLOP/s."""
+def cpu_baseline(w, X, W, target_s: float):
+    """The CPU oracle's fp64 partial GEMM on the first S rows of the M-row
+    product (S sized so the run takes about target_s seconds), as TFLOP/s."""
     from oracle import oracle as orc
 
     threads = orc.num_threads(0)
+    probe = max(1, min(w.M, 64))
     t0 = time.perf_counter()
-    orc.gemm_rs(X, W, peers, w.P, w.rank, row_begin=0, row_end=1, threads=threads)
-    one = max(time.perf_counter() - t0, 1e-4)
-    rows = int(max(1, min(w.rows, target_s / one)))
-    t0 = time.perf_counter()
-    orc.gemm_rs(X, W, peers, w.P, w.rank, row_begin=0, row_end=rows, threads=threads)
-    dt = time.perf_counter() - t0
-    flops = 2.0 * rows * w.N * w.K
+    orc.partial_gemm(X, W, row_begin=0, row_end=probe, threads=threads)
+    per_row = max((time.perf_counter() - t0) / probe, 1e-6)
+    rows = int(max(1, min(w.M, target_s / per_row)))
+    # Whole passes over the sampled rows until about target_s of CPU work.
+    runs, dt = 0, 0.0
+    while runs == 0 or (dt < 0.8 * target_s and runs < 64):
+        t0 = time.perf_counter()
+        orc.partial_gemm(X, W, row_begin=0, row_end=rows, threads=threads)
+        dt += time.perf_counter() - t0
+        runs += 1
+    flops = 2.0 * rows * w.N * w.K * runs
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"rows 0..{rows - 1} of the rank's {w.rows}-row partition, all {w.N} columns, "
-                      f"full K_local={w.K}, plus the {w.P - 1} peer adds; fp64 plain loops; "
-                      f"{dt:.1f} s wall"}
+            "sample": f"{runs} pass(es) over rows 0..{rows - 1} of the {w.M}-row partial product "
+                      f"X*W (N={w.N}, K_local={w.K}) in fp64 plain loops on {threads} threads, "
+                      f"{dt:.1f} s wall; the reduction's adds are negligible next to it"}
 
 
 def main() -> int:
@@ -95,18 +105,24 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=120)
     ap.add_argument("--workload", default="mlp")
     ap.add_argument("--order", default="auto", help="auto|row|partition|interleaved|col")
-    ap.add_argument("--budget", type=int, default=-1)
-    ap.add_argument("--block", default="", help="BMxBN, e.g. 128x256 (default: tuning table)")
-    ap.add_argument("--threads", type=int, default=0)
+    ap.add_argument("--budget", type=int, default=-1, help="comm budget x (-1: tuning table)")
+    ap.add_argument("--block", default="", help="BMxBN, e.g. 256x256 (default: tuning table)")
+    ap.add_argument("--threads", type=int, default=0, help="reduction threads (0: tuning table)")
+    ap.add_argument("--slabs", type=int, default=0, help="row slabs per task (0: tuning table)")
+    ap.add_argument("--peers", default="preseeded", help="preseeded|symmetric")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
-    ap.add_argument("--no-seq", action="store_true")
+    ap.add_argument("--profile", action="store_true",
+                    help="only run --warmup + --steps eager calls (for rocprofv3), print nothing")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-sized device buffer --steps times (the reference "
+                         "kernel for scaling FETCH_SIZE / WRITE_SIZE)")
     args = ap.parse_args()
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the operation is built "
-              "at one GPU's share of the work, with peer contributions as seeded buffers; "
-              "no multi-GPU path exists.", file=sys.stderr)
+              "at one GPU's share of the work, with the peers' contributions as seeded device "
+              "buffers; there is no multi-GPU path to launch.", file=sys.stderr)
         return 2
 
     import numpy as np
@@ -119,6 +135,15 @@ def main() -> int:
         log("bench.py needs a GPU")
         return 1
     dev = torch.device("cuda:0")
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        for _ in range(args.steps):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copied {args.copy_calibration} MiB x {args.steps}")
+        return 0
     tog.load()
     tog.entwine_load_tuning(os.path.join(ROOT, "tile_overlapped_gemm_amd", "tuning.txt"))
     w = wl.BY_NAME[args.workload]
@@ -135,57 +160,125 @@ def main() -> int:
     pd = [None if p is None else up(p) for p in peers]
     out = torch.empty((w.rows, w.N), dtype=torch.float32 if w.fp32_io else torch.bfloat16,
                       device=dev)
-    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, reducer_threads=args.threads)
+    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, reducer_threads=args.threads,
+                  task_slabs=args.slabs,
+                  peer_ready=tog.PEERS_SYMMETRIC if args.peers == "symmetric" else tog.PEERS_PRESEEDED)
     if w.fp32_io:
         cfg_kw.update(peer_dtype=tog.F32, out_dtype=tog.F32)
     if args.block:
         bm, bn = (int(v) for v in args.block.lower().split("x"))
         cfg_kw.update(block_m=bm, block_n=bn)
     cfg = tog.config(**cfg_kw)
+    cfg_gemm = tog.config(**cfg_kw, stages=tog.STAGES_GEMM)
+    cfg_red = tog.config(**cfg_kw, stages=tog.STAGES_REDUCE)
     order = tog.ORDER_AUTO if args.order == "auto" else tog.ORDERS[args.order]
-    stream = torch.cuda.current_stream(dev)
-
-    def step(budget):
-        tog.gemm_rs(Xd, Wd, pd, out, w.P, w.rank, order, budget, cfg=cfg, stream=stream)
-
-    def timed(budget, steps, warmup):
-        for _ in range(warmup):
-            step(budget)
-        torch.cuda.synchronize()
-        st = tog.entwine_device_status(stream.cuda_stream)
-        if st != tog.ENTWINE_OK:
-            raise RuntimeError(f"device status {st} after warm-up")
-        tog.entwine_timing_read()
-        tog.entwine_timing(True)
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        evs[0].record(stream)
-        for i in range(steps):
-            step(budget)
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        tog.entwine_timing(False)
-        gemm_ms, red_ms, calls = tog.entwine_timing_read()
-        st = tog.entwine_device_status(stream.cuda_stream)
-        if st != tog.ENTWINE_OK:
-            raise RuntimeError(f"device status {st} in the timed region")
-        per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
-        total = evs[0].elapsed_time(evs[-1])
-        return dict(ms_per_step=total / steps, median_ms=statistics.median(per),
-                    p10_ms=sorted(per)[len(per) // 10], p90_ms=sorted(per)[(9 * len(per)) // 10],
-                    gemm_ms=gemm_ms / calls, reduce_ms=red_ms / calls, wall_s=wall)
-
+    stream = torch.cuda.Stream(dev)
     budget = args.budget
-    log(f"overlapped: {args.warmup} warm-up + {args.steps} timed steps")
-    ov = timed(budget, args.steps, args.warmup)
+
+    def call(budget, c=cfg):
+        tog.gemm_rs(Xd, Wd, pd, out, w.P, w.rank, order, budget, cfg=c, stream=stream)
+
+    def check_status(where):
+        st = tog.entwine_device_status(stream.cuda_stream)
+        if st != tog.ENTWINE_OK:
+            raise RuntimeError(f"device status {st} {where}")
+
+    if args.profile:
+        for _ in range(args.warmup + args.steps):
+            call(budget)
+        stream.synchronize()
+        check_status("in the profiled calls")
+        log(f"profiled {args.warmup + args.steps} calls, budget {budget}")
+        return 0
+
+    def graph_of(body):
+        with torch.cuda.stream(stream):
+            body()  # workspace and schedule exist before the capture
+        stream.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            body()
+        return g
+
+    def timed_graph(body, steps, warmup, per_step=True):
+        """Per-replay and total device time of graph replays of `body`."""
+        g = graph_of(body)
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                g.replay()
+        stream.synchronize()
+        check_status("after warm-up")
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            evs[0].record(stream)
+            for i in range(steps):
+                g.replay()
+                if per_step:
+                    evs[i + 1].record(stream)
+            evs[-1].record(stream)
+        torch.cuda.synchronize()
+        check_status("in the timed region")
+        total = evs[0].elapsed_time(evs[-1])
+        res = dict(ms_per_step=total / steps)
+        if per_step:
+            per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+            res.update(median_ms=statistics.median(per), p10_ms=per[len(per) // 10],
+                       p90_ms=per[(9 * len(per)) // 10])
+        return res
+
+    log(f"overlapped step: {args.warmup} warm-up + {args.steps} timed graph replays")
+    ov = timed_graph(lambda: call(budget), args.steps, args.warmup)
+    log("sequential step (budget 0): same protocol")
+    sq = timed_graph(lambda: call(0), args.steps, args.warmup)
+
+    # Kernels alone: GEMM without flags; the reduction of the workspace's
+    # partial, flat (sequential schedule) and tiled at the step's budget.  Ten
+    # launches per graph replay amortize the replay's launch latency; the cold
+    # reduction subtracts a graph holding only the cache scrub.
+    reps, ksteps = 10, max(10, min(args.steps, 50))
+    scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+
+    def rep(body):
+        def f():
+            for _ in range(reps):
+                body()
+        return f
+
+    log("kernels alone")
+    g_alone = timed_graph(rep(lambda: call(0, cfg_gemm)), ksteps, 3, False)["ms_per_step"] / reps
+    r_flat = timed_graph(rep(lambda: call(0, cfg_red)), ksteps, 3, False)["ms_per_step"] / reps
+    r_tile = timed_graph(rep(lambda: call(budget, cfg_red)), ksteps, 3, False)["ms_per_step"] / reps
+    t_scrub = timed_graph(lambda: scrub.fill_(1), ksteps, 3, False)["ms_per_step"]
+    t_both = timed_graph(lambda: (scrub.fill_(1), call(0, cfg_red)), ksteps, 3,
+                         False)["ms_per_step"]
+    r_cold = max(t_both - t_scrub, 1e-6)
+    del scrub
+
+    # The GEMM and the reduction inside the overlapped step, from HIP events
+    # recorded on each kernel's own stream around eager calls.
+    for _ in range(3):
+        call(budget)
+    stream.synchronize()
+    tog.entwine_timing_read()
+    tog.entwine_timing(True)
+    for _ in range(ksteps):
+        call(budget)
+    stream.synchronize()
+    tog.entwine_timing(False)
+    gm, rm, n = tog.entwine_timing_read()
+    check_status("in the kernel timing loop")
+    g_ov, r_ov = gm / n, rm / n
+
     flops = float(w.flops)
     red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
                                        else (4 + 2 * (w.P - 1) + 2))
+    tflops = flops / (ov["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (g_ov * 1e-3) / 1e12
+    gbps = lambda ms: red_bytes / (ms * 1e-3) / 1e9
     res = {
         "metric": METRIC,
-        "value": flops / (ov["ms_per_step"] * 1e-3) / 1e12,
+        "value": tflops,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -200,42 +293,44 @@ def main() -> int:
                    "rank": w.rank, "tile_order": args.order, "comm_budget": budget,
                    "block": args.block or "tuning table", "tile": w.tile,
                    "reducer_threads": args.threads or "tuning table",
-                   "peer_ready": "preseeded"},
+                   "task_slabs": args.slabs or "tuning table", "peer_ready": args.peers,
+                   "launch": "HIP graph replay"},
         "latency_us": ov["ms_per_step"] * 1e3,
         "latency_us_median": ov["median_ms"] * 1e3,
         "latency_us_p10_p90": [ov["p10_ms"] * 1e3, ov["p90_ms"] * 1e3],
-        "pct_bf16_peak": 100.0 * flops / (ov["ms_per_step"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-        "gemm_in_overlap_us": ov["gemm_ms"] * 1e3,
-        "reduce_kernel_in_overlap_us": ov["reduce_ms"] * 1e3,
-    }
-    gemm_ms = ov["gemm_ms"]
-    if not args.no_seq:
-        log("sequential (budget 0): same steps")
-        sq = timed(0, args.steps, args.warmup)
-        res["sequential"] = {
+        "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        "sequential": {
             "latency_us": sq["ms_per_step"] * 1e3,
             "latency_us_median": sq["median_ms"] * 1e3,
-            "gemm_us": sq["gemm_ms"] * 1e3,
-            "reduce_us": sq["reduce_ms"] * 1e3,
-        }
-        res["speedup_vs_sequential"] = sq["ms_per_step"] / ov["ms_per_step"]
-        res["overlap_efficiency"] = sq["gemm_ms"] / ov["ms_per_step"]
-        res["reducer"] = {
+        },
+        "speedup_vs_sequential": sq["ms_per_step"] / ov["ms_per_step"],
+        "gemm_alone_us": g_alone * 1e3,
+        "gemm_alone_tflops": flops / (g_alone * 1e-3) / 1e12,
+        "gemm_in_overlap_us": g_ov * 1e3,
+        "reduce_kernel_in_overlap_us": r_ov * 1e3,
+        "overlap_efficiency": g_alone / ov["ms_per_step"],
+        "tail_us": (ov["ms_per_step"] - g_ov) * 1e3,
+        "reducer": {
             "bytes": red_bytes,
-            "standalone_gbps": red_bytes / (sq["reduce_ms"] * 1e-3) / 1e9,
-            "pct_hbm_peak": 100.0 * red_bytes / (sq["reduce_ms"] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-            "in_overlap_gbps_incl_waits": red_bytes / (ov["reduce_ms"] * 1e-3) / 1e9,
-        }
-        res["gemm_standalone_tflops"] = flops / (sq["gemm_ms"] * 1e-3) / 1e12
-    achieved = flops / (gemm_ms * 1e-3) / 1e12
-    res["roofline"] = {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
-                       "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                       "traffic": traffic_for(w.name, "gemm_publish"),
-                       "kernel": "gemm_publish (in the overlapped step)",
-                       "algorithmic_flops_per_launch": flops}
+            "flat_warm_us": r_flat * 1e3,
+            "flat_warm_gbps": gbps(r_flat),
+            "flat_cold_us": r_cold * 1e3,
+            "flat_cold_gbps": gbps(r_cold),
+            "pct_hbm_peak_cold": 100.0 * gbps(r_cold) / HBM_PEAK_GBPS,
+            "tiled_at_budget_us": r_tile * 1e3,
+            "tiled_at_budget_gbps": gbps(r_tile),
+            "required_gbps_eq4": gbps(g_alone),
+        },
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
+                     "traffic": traffic_for(w.name, "gemm_publish"),
+                     "kernel": "gemm_publish_kernel (inside the overlapped step)",
+                     "kernel_us": g_ov * 1e3,
+                     "algorithmic_flops_per_launch": flops},
+    }
     if not args.no_cpu:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
-        res["cpu_baseline"] = cpu_baseline(w, X, W, peers, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(w, X, W, args.cpu_seconds)
     print(json.dumps(res), flush=True)
     return 0
 

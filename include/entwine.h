@@ -91,6 +91,8 @@ enum {
   ENTWINE_W_KN = 1  /* [K_local][N] row-major: N contiguous (reserved; not built yet) */
 };
 
+enum { ENTWINE_STAGES_ALL = 0, ENTWINE_STAGES_GEMM = 1, ENTWINE_STAGES_REDUCE = 2 };
+
 /* Release granularity (Sec. 5.3.2): tiles released together. */
 #define ENTWINE_RELEASE_TILE 1       /* each tile on its own flag (the method) */
 #define ENTWINE_RELEASE_PARTITION 0  /* a tile waits for the last tile of its partition */
@@ -153,7 +155,13 @@ typedef struct entwine_config {
   int32_t publish_all;     /* 0: agent-scope release only for tiles a kernel on this device
                               reads (the rank's partition), progress flags for the rest;
                               1: release every tile (the cost of publishing to peers) */
-  int32_t reserved[5];
+  int32_t stages;          /* measurement: ENTWINE_STAGES_ALL (0), or one kernel alone:
+                              ENTWINE_STAGES_GEMM (the GEMM without flags) or
+                              ENTWINE_STAGES_REDUCE (the reduction of whatever the workspace
+                              holds, with every flag treated as ready; the budget picks the
+                              schedule as usual).  A single stage leaves `out` (GEMM) or the
+                              partials (reduction) as they were: for timing only. */
+  int32_t reserved[4];
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);
@@ -228,8 +236,9 @@ int entwine_timing(int enable);
 int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls);
 
 /* Load an offline tuning table (text; one entry per line:
- * "M N K_local P tile_order comm_budget block_m block_n reducer_threads").
- * Entries are consulted by the AUTO settings. */
+ * "M N K_local P tile_order comm_budget block_m block_n reducer_threads
+ * [task_slabs]", '#' starts a comment line).  Entries are consulted by the
+ * AUTO settings (tile_order -1, comm_budget -1, zero config fields). */
 int entwine_load_tuning(const char* path);
 
 /* Frees the current device's workspace; the next call re-creates it. */

@@ -68,24 +68,37 @@ def test_parity_and_schedule_invariance(dev, w):
 @pytest.mark.parametrize("w", SMALL[:2], ids=lambda w: w.name)
 def test_reducer_variants_bit_identical(dev, w):
     case, ref = case_for(w, dev)
-    base = down(case.run(tog.ORDER_INTERLEAVED, 4))
+    blk = dict(block_m=128, block_n=128)
+    base = down(case.run(tog.ORDER_INTERLEAVED, 4, **blk))
     for threads in (128, 256, 512):
         for mode in (tog.PEERS_PRESEEDED, tog.PEERS_SYMMETRIC):
             for order in (tog.ORDER_INTERLEAVED, tog.ORDER_PARTITION_MAJOR):
                 for group in (tog.RELEASE_TILE, 3, tog.RELEASE_PARTITION, tog.RELEASE_OUTPUT):
                     print(f"case {w.name} b={threads} mode={mode} order={order} g={group}", flush=True)
                     out = down(case.run(order, 5, reducer_threads=threads, peer_ready=mode,
-                                        release_group=group))
+                                        release_group=group, **blk))
                     np.testing.assert_array_equal(out, base)
     for slabs in (1, 2, 8):
         for budget in (1, 5, 64):
-            out = down(case.run(tog.ORDER_INTERLEAVED, budget, task_slabs=slabs))
+            out = down(case.run(tog.ORDER_INTERLEAVED, budget, task_slabs=slabs, **blk))
             np.testing.assert_array_equal(out, base)
     for publish_all in (0, 1):
-        out = down(case.run(tog.ORDER_COL_MAJOR, 3, publish_all=publish_all))
+        out = down(case.run(tog.ORDER_COL_MAJOR, 3, publish_all=publish_all, **blk))
         np.testing.assert_array_equal(out, base)
-    out = down(case.run(tog.ORDER_INTERLEAVED, 0))
+    out = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
     np.testing.assert_array_equal(out, base)
+
+
+def test_reducer_that_cannot_share_a_cu_is_rejected(dev):
+    """A 512-thread reduction workgroup beside a 256x256 GEMM block would need
+    more registers than a SIMD holds, so waiting reducers could starve the
+    GEMM of CUs: the call is refused before anything is enqueued."""
+    case, _ = case_for(SMALL[0], dev)
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, 4, reducer_threads=512, block_m=256, block_n=256)
+    assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+    # the sequential schedule has no waiting reducers and stays available
+    case.run(tog.ORDER_INTERLEAVED, 0, reducer_threads=512, block_m=256, block_n=256)
 
 
 @pytest.mark.parametrize("w", SMALL, ids=lambda w: w.name)

@@ -30,6 +30,7 @@ BF16, F32 = 0, 1
 PEERS_PRESEEDED, PEERS_SYMMETRIC = 0, 1
 W_NK, W_KN = 0, 1
 RELEASE_TILE, RELEASE_PARTITION, RELEASE_OUTPUT = 1, 0, -1
+STAGES_ALL, STAGES_GEMM, STAGES_REDUCE = 0, 1, 2
 
 # Names exported by the library (one per declaration in include/entwine.h).
 EXPORTS = [
@@ -65,7 +66,8 @@ class entwine_config(ctypes.Structure):
         ("withhold_tile", ctypes.c_int32),
         ("gemm_variant", ctypes.c_int32),
         ("publish_all", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 5),
+        ("stages", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 4),
     ]
 
 

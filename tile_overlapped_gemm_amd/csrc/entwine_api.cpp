@@ -75,6 +75,9 @@ struct Workspace {
   int wall_khz = 100000;
   hipStream_t s_gemm = nullptr, s_red = nullptr;
   hipEvent_t ev_fork = nullptr, ev_gemm = nullptr, ev_red = nullptr;
+  // Separate events for calls made while the caller's stream is being
+  // captured into a graph, so that eager calls never wait on a captured record.
+  hipEvent_t cap_fork = nullptr, cap_gemm = nullptr, cap_red = nullptr;
   bool have_prev = false;
   float* own = nullptr;
   size_t own_bytes = 0;
@@ -83,14 +86,14 @@ struct Workspace {
   uint32_t* flags = nullptr;
   size_t flag_count = 0;
   int32_t* error = nullptr;
-  uint32_t epoch = 0;
+  uint32_t* ctl = nullptr;  // kCtlWords device words: epoch and check-out counters
   std::map<PlanKey, std::unique_ptr<DevicePlan>> plans;
   std::vector<TimingPair> timing_live;
   std::vector<TimingPair> timing_free;
 };
 
 struct TuneEntry {
-  int order, budget, bm, bn, threads;
+  int order, budget, bm, bn, threads, slabs;
 };
 
 std::mutex g_mu;
@@ -124,6 +127,9 @@ void destroy_workspace(Workspace* w) {
   if (w->outgoing) (void)hipFree(w->outgoing);
   if (w->flags) (void)hipFree(w->flags);
   if (w->error) (void)hipFree(w->error);
+  if (w->ctl) (void)hipFree(w->ctl);
+  for (hipEvent_t e : {w->cap_fork, w->cap_gemm, w->cap_red})
+    if (e) (void)hipEventDestroy(e);
   if (w->ev_fork) (void)hipEventDestroy(w->ev_fork);
   if (w->ev_gemm) (void)hipEventDestroy(w->ev_gemm);
   if (w->ev_red) (void)hipEventDestroy(w->ev_red);
@@ -151,8 +157,15 @@ int get_workspace(Workspace** out) {
   HIP_TRY(hipEventCreateWithFlags(&w->ev_fork, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&w->ev_gemm, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&w->ev_red, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&w->cap_fork, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&w->cap_gemm, hipEventDisableTiming));
+  HIP_TRY(hipEventCreateWithFlags(&w->cap_red, hipEventDisableTiming));
   HIP_TRY(hipMalloc(&w->error, sizeof(int32_t)));
   HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
+  // The first call's epoch is 1: freshly allocated flags hold 0.
+  const uint32_t ctl_init[kCtlWords] = {1, 0, 0, 0};
+  HIP_TRY(hipMalloc(&w->ctl, sizeof ctl_init));
+  HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
   *out = w.get();
   g_ws[dev] = std::move(w);
   return ENTWINE_OK;
@@ -249,7 +262,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile, variant, publish_all;
+      slabs, withhold_tile, variant, publish_all, stages;
   uint32_t timeout_ms;
 };
 
@@ -296,8 +309,9 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->out_f32 = c.out_dtype == ENTWINE_F32;
   r->peer_ready = c.peer_ready;
   r->release_group = c.release_group;
-  r->slabs = c.task_slabs;
+  r->slabs = c.task_slabs ? c.task_slabs : (te ? te->slabs : 1);
   r->publish_all = c.publish_all;
+  r->stages = c.stages;
   r->timeout_ms = c.poll_timeout_ms ? c.poll_timeout_ms : 2000;
   r->withhold_tile = c.withhold_tile - 1;
   r->variant = c.gemm_variant;
@@ -305,6 +319,8 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
   if (c.publish_all != 0 && c.publish_all != 1)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "publish_all must be 0 or 1");
+  if (c.stages < ENTWINE_STAGES_ALL || c.stages > ENTWINE_STAGES_REDUCE)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "stages %d out of range", c.stages);
   return ENTWINE_OK;
 }
 
@@ -338,32 +354,66 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "out overlaps peer_partials[%d]", r);
   }
 
+  hipStream_t stream = static_cast<hipStream_t>(stream_);
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  HIP_TRY(hipStreamIsCapturing(stream, &cap));
+  const bool capturing = cap != hipStreamCaptureStatusNone;
+
   std::lock_guard<std::mutex> lock(g_mu);
+  if (capturing) {
+    int dev = 0;
+    HIP_TRY(hipGetDevice(&dev));
+    if (g_ws.find(dev) == g_ws.end())
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT,
+                  "no workspace on this device: make the same call once outside the capture");
+    if (g_timing)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "entwine_timing cannot record inside a capture");
+  }
   Workspace* w = nullptr;
   if ((rc = get_workspace(&w))) return rc;
   if (rs.budget >= w->cus)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT,
                 "comm_budget %d must stay below the device's %d compute units", rs.budget, w->cus);
-  const int x = (int)std::min<int64_t>(rs.budget, g.Q);
 
-  if ((rc = ensure(w, (void**)&w->own, &w->own_bytes, (size_t)g.R * N * 4, false))) return rc;
-  if ((rc = ensure(w, &w->outgoing, &w->outgoing_bytes, (size_t)M * N * peer_sz, false))) return rc;
-  size_t flag_bytes = w->flag_count * 4;
+  const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
+  if (!sequential && rs.stages == ENTWINE_STAGES_ALL) {
+    // The reduction workgroups wait for GEMM blocks, so a CU holding one
+    // must still fit a GEMM block: otherwise reduction workgroups spread
+    // over the device could starve the GEMM until the watchdog fires.
+    const int waves_per_simd = (rs.threads / 64 + 3) / 4;
+    const int gr = gemm_registers(g.bm, g.bn, rs.variant);
+    const int rr = reduce_registers(rs.threads, rs.peer_f32, rs.out_f32);
+    auto up8 = [](int v) { return (v + 7) / 8 * 8; };
+    if (gr <= 0 || rr <= 0)
+      return fail(ENTWINE_ERR_HIP, "kernel register counts unavailable");
+    if (up8(gr) + waves_per_simd * up8(rr) > 512)
+      return fail(ENTWINE_ERR_UNSUPPORTED,
+                  "a %d-thread reduction workgroup (%d registers per lane) cannot share a CU "
+                  "with a %dx%d GEMM block (%d registers per lane)",
+                  rs.threads, rr, g.bm, g.bn, gr);
+  }
+
+  const size_t own_need = (size_t)g.R * N * 4, og_need = (size_t)M * N * peer_sz;
   // One slot past the P x Q flags is never written by any GEMM (failure injection).
-  if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, ((size_t)g.P * g.Q + 1) * 4, true))) return rc;
+  const size_t flag_need = ((size_t)g.P * g.Q + 1) * 4;
+  if (capturing) {
+    // Allocation, upload and synchronization are not allowed while capturing.
+    PlanKey key{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, rs.order, rs.peer_ready,
+                rs.release_group};
+    if (w->own_bytes < own_need || w->outgoing_bytes < og_need || w->flag_count * 4 < flag_need ||
+        w->plans.find(key) == w->plans.end())
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT,
+                  "the workspace and schedule for this shape must exist before a graph capture: "
+                  "make the same call once outside the capture");
+  }
+  if ((rc = ensure(w, (void**)&w->own, &w->own_bytes, own_need, false))) return rc;
+  if ((rc = ensure(w, &w->outgoing, &w->outgoing_bytes, og_need, false))) return rc;
+  size_t flag_bytes = w->flag_count * 4;
+  if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, flag_need, true))) return rc;
   w->flag_count = flag_bytes / 4;
 
   DevicePlan* dp = nullptr;
   if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, &dp))) return rc;
-
-  hipStream_t stream = static_cast<hipStream_t>(stream_);
-  // Epochs skip 0 (the value of freshly cleared flags).  On wrap-around the
-  // flags are cleared once so that no flag left from 2^32 calls ago matches.
-  bool clear_flags = false;
-  if (++w->epoch == 0) {
-    w->epoch = 1;
-    clear_flags = true;
-  }
 
   TimingPair tp{};
   if (g_timing && (rc = take_timing_pair(w, &tp))) return rc;
@@ -387,7 +437,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ga.tn = g.tn;
   ga.outgoing_f32 = rs.peer_f32;
   ga.variant = rs.variant;
-  ga.epoch = w->epoch;
+  ga.ctl = w->ctl;
 
   ReduceArgs ra{};
   ra.own = w->own;
@@ -405,24 +455,28 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ra.wait_slots = dp->plan.wait_slots;
   ra.tm = g.tm;
   ra.tn = g.tn;
-  ra.epoch = w->epoch;
+  ra.ctl = w->ctl;
   ra.timeout_ticks = (uint64_t)rs.timeout_ms * (uint64_t)w->wall_khz;
   ra.withhold_tile = rs.withhold_tile;
   ra.never_flag = (int32_t)(g.P * g.Q);
 
   // Fork: both internal streams start after the caller's prior work and after
-  // this workspace's previous call.
-  HIP_TRY(hipEventRecord(w->ev_fork, stream));
-  HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_fork, 0));
-  HIP_TRY(hipStreamWaitEvent(w->s_red, w->ev_fork, 0));
-  if (w->have_prev) HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_red, 0));
-  if (clear_flags) HIP_TRY(hipMemsetAsync(w->flags, 0, w->flag_count * 4, w->s_gemm));
+  // this workspace's previous eager call.  Inside a capture the graph's own
+  // edges order the work and the capture events are used instead.
+  hipEvent_t ev_fork = capturing ? w->cap_fork : w->ev_fork;
+  hipEvent_t ev_gemm = capturing ? w->cap_gemm : w->ev_gemm;
+  hipEvent_t ev_red = capturing ? w->cap_red : w->ev_red;
+  // The sequential schedule uses the GEMM stream only (a stream that joins a
+  // capture must be joined back, so the idle one stays out of it).
+  HIP_TRY(hipEventRecord(ev_fork, stream));
+  HIP_TRY(hipStreamWaitEvent(w->s_gemm, ev_fork, 0));
+  if (!sequential) HIP_TRY(hipStreamWaitEvent(w->s_red, ev_fork, 0));
+  if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_red, 0));
 
   // Sequential schedule (budget 0): the GEMM publishes nothing and the
   // reduction streams the whole partition after the GEMM kernel has ended.
   // Overlapped schedule: the GEMM releases its tiles and x persistent
   // reduction workgroups consume them as they become ready.
-  const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
   hipStream_t s_red = sequential ? w->s_gemm : w->s_red;
   int grid;
   if (sequential) {
@@ -437,24 +491,37 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     ga.publish = rs.publish_all ? 2 : 1;
     ra.slabs = rs.slabs ? rs.slabs : 1;
     ra.ntasks = (int32_t)(g.Q * ra.slabs);
-    grid = (int)std::min<int64_t>(rs.budget, ra.ntasks);
+    grid = (int)std::min<int64_t>(rs.budget, ra.ntasks);  // x, capped by the task count
   }
 
+  // Measurement stages: one kernel alone, outside the flag protocol.
+  const bool run_gemm = rs.stages != ENTWINE_STAGES_REDUCE;
+  const bool run_red = rs.stages != ENTWINE_STAGES_GEMM;
+  if (rs.stages != ENTWINE_STAGES_ALL) {
+    ga.publish = 0;
+    ra.nowait = 1;
+  }
   if (g_timing) HIP_TRY(hipEventRecord(tp.g0, w->s_gemm));
-  hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, w->s_gemm);
-  if (e != hipSuccess) return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  if (run_gemm) {
+    hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, w->s_gemm);
+    if (e != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+  }
   if (g_timing) HIP_TRY(hipEventRecord(tp.g1, w->s_gemm));
-  HIP_TRY(hipEventRecord(w->ev_gemm, w->s_gemm));
+  HIP_TRY(hipEventRecord(ev_gemm, w->s_gemm));
   if (g_timing) HIP_TRY(hipEventRecord(tp.r0, s_red));
-  e = launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, sequential, grid, s_red);
-  if (e != hipSuccess)
-    return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
+  if (run_red) {
+    hipError_t e =
+        launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, sequential, grid, s_red);
+    if (e != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
+  }
   if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));
-  HIP_TRY(hipEventRecord(w->ev_red, s_red));
-  w->have_prev = true;
+  HIP_TRY(hipEventRecord(ev_red, s_red));
+  if (!capturing) w->have_prev = true;
   // Join: the caller's stream continues after both kernels.
-  HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
-  HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+  HIP_TRY(hipStreamWaitEvent(stream, ev_gemm, 0));
+  HIP_TRY(hipStreamWaitEvent(stream, ev_red, 0));
   if (g_timing) w->timing_live.push_back(tp);
   return ENTWINE_OK;
 }
@@ -652,14 +719,15 @@ int entwine_load_tuning(const char* path) {
     ++lineno;
     if (line[0] == '#' || line[0] == '\n') continue;
     long long M, N, K;
-    int P, order, budget, bm, bn, threads;
-    if (std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d", &M, &N, &K, &P, &order, &budget,
-                    &bm, &bn, &threads) != 9) {
+    int P, order, budget, bm, bn, threads, slabs = 1;
+    const int n = std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d %d", &M, &N, &K, &P, &order,
+                              &budget, &bm, &bn, &threads, &slabs);
+    if (n != 9 && n != 10) {
       std::fclose(f);
-      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "%s:%d: expected 9 integers", path, lineno);
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "%s:%d: expected 9 or 10 integers", path, lineno);
     }
     table[std::make_tuple((int64_t)M, (int64_t)N, (int64_t)K, P)] =
-        TuneEntry{order, budget, bm, bn, threads};
+        TuneEntry{order, budget, bm, bn, threads, slabs};
   }
   std::fclose(f);
   std::lock_guard<std::mutex> lock(g_mu);

@@ -307,9 +307,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_publish_kernel(GemmArgs a) {
     const int sub_m = BM / a.tm, sub_n = BN / a.tn;
     const int vm = min(sub_m, a.Rt - br * sub_m);
     const int vn = min(sub_n, a.Ct - bc * sub_n);
+    const uint32_t epoch = a.ctl[kEpoch];
     uint32_t* f = a.flags + (int64_t)d * a.Q + t_first;
     for (int t = 0; t < vm * vn; ++t)
-      __hip_atomic_store(f + t, a.epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(f + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    check_out(a.ctl, kGemmDone, epoch);
   }
 }
 
@@ -328,6 +330,26 @@ hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
 }
 
 }  // namespace
+
+template <int BM, int BN, int BK, int NS>
+int regs_of() {
+  hipFuncAttributes at{};
+  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS>) != hipSuccess)
+    return 0;
+  return at.numRegs;
+}
+
+int gemm_registers(int bm, int bn, int variant) {
+  if (bm == 128 && bn == 128) return regs_of<128, 128, 64, 2>();
+  if (bm == 128 && bn == 256) return regs_of<128, 256, 64, 2>();
+  if (bm == 256 && bn == 128) return regs_of<256, 128, 64, 2>();
+  if (bm == 256 && bn == 256) {
+    if (variant == 1) return regs_of<256, 256, 32, 4>();
+    if (variant == 2) return regs_of<256, 256, 32, 3>();
+    return regs_of<256, 256, 64, 2>();
+  }
+  return 0;
+}
 
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream) {

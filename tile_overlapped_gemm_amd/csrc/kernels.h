@@ -30,7 +30,7 @@ struct GemmArgs {
   int32_t outgoing_f32;     // outgoing partials in fp32 (else bf16)
   int32_t variant;          // GEMM pipeline variant (0 = default for the shape)
   int32_t publish;          // 0: no flags; 1: release local tiles, mark the rest; 2: release all
-  uint32_t epoch;
+  uint32_t* ctl;            // device control words (see check_out)
 };
 
 struct ReduceArgs {
@@ -46,11 +46,37 @@ struct ReduceArgs {
   int32_t tm, tn;
   int32_t slabs;                    // row slabs per tile (task = tile x slab)
   int32_t ntasks;                   // Q * slabs
-  uint32_t epoch;
+  uint32_t* ctl;                    // device control words (see check_out)
   uint64_t timeout_ticks;           // watchdog, in wall-clock ticks
   int32_t withhold_tile;            // -1, or a tile whose local wait watches `never_flag`
   int32_t never_flag;               // a flag slot that no GEMM of this call writes
+  int32_t nowait;                   // 1: every flag counts as ready, no epoch check-out
 };
+
+// Epochs.  A flag is ready when it equals the call's epoch, which both
+// kernels read from ctl[kEpoch] at run time (so a captured graph replays
+// correctly).  The epoch must not change while any workgroup of the call can
+// still read it, so every workgroup of both kernels checks out when it is
+// done; the last workgroup of a kernel checks the kernel out, and the second
+// kernel to finish advances the epoch (skipping 0, the value of flags never
+// written) and clears the counters for the next call.
+enum { kEpoch = 0, kReduceDone = 1, kGemmDone = 2, kKernelsDone = 3, kCtlWords = 4 };
+
+__device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
+
+// Called by one thread per workgroup after the workgroup's last use of the
+// epoch.  `counter` is kReduceDone or kGemmDone.
+__device__ __forceinline__ void check_out(uint32_t* ctl, int counter, uint32_t epoch) {
+  const uint32_t n = __hip_atomic_fetch_add(ctl + counter, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  if (n + 1 != gridDim.x) return;
+  __hip_atomic_store(ctl + counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const uint32_t k = __hip_atomic_fetch_add(ctl + kKernelsDone, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT);
+  if (k + 1 != 2) return;
+  __hip_atomic_store(ctl + kKernelsDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 // GEMM block shapes built: (bm, bn) in {128, 256}^2.
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
@@ -60,5 +86,10 @@ hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks
 // reduce the whole partition without flags (after the GEMM has finished).
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
                               bool flat, int grid, hipStream_t stream);
+
+// Registers per lane (VGPRs + AGPRs) of the kernels a launch would use, for
+// the co-residency check; 0 if unknown.
+int gemm_registers(int bm, int bn, int variant);
+int reduce_registers(int threads, int peer_f32, int out_f32);
 
 }  // namespace entwine

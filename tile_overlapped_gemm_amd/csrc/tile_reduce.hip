@@ -145,7 +145,7 @@ __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t
 // Wave 0 waits until every flag that task tile t depends on equals `epoch`.
 // Lane k (< P + 1) watches wait slot k.  Returns false if the watchdog
 // expired (uniform across the wave).
-__device__ bool wait_tile(const ReduceArgs& a, int t, int lane) {
+__device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int t, int lane) {
   int32_t idx = -1;
   if (lane < a.wait_slots) idx = a.waits[t * a.wait_slots + lane];
   if (t == a.withhold_tile && lane == a.rank) idx = a.never_flag;
@@ -153,7 +153,7 @@ __device__ bool wait_tile(const ReduceArgs& a, int t, int lane) {
   const uint64_t start = wall_clock64();
   while (true) {
     bool ready = true;
-    if (f) ready = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == a.epoch;
+    if (f) ready = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
     if (__all(ready)) break;
     if (wall_clock64() - start > a.timeout_ticks) {
       if (lane == 0)
@@ -174,6 +174,7 @@ template <int THREADS, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   __shared__ int s_abort[2];
   const int tid = threadIdx.x;
+  const uint32_t epoch = a.ctl[kEpoch];
   const int chunks_per_row = a.tn >> 3;
   const int slab_rows = a.tm / a.slabs;
   int parity = 0;
@@ -181,14 +182,14 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
     const int t = task / a.slabs;
     const int slab = task - t * a.slabs;
     if (tid < 64) {
-      const bool ok = wait_tile(a, t, tid);
+      const bool ok = a.nowait || wait_tile(a, epoch, t, tid);
       if (tid == 0) s_abort[parity] = ok ? 0 : 1;
     }
     // The flag wait is ordered before every wave's reads of the tile.  The
     // abort word alternates between two slots, so wave 0 can write the next
     // task's word while a slower wave still reads this one.
     __syncthreads();
-    if (s_abort[parity]) return;  // uniform: every thread read the same value
+    if (s_abort[parity]) break;  // uniform: every thread read the same value
 
     const int row0 = a.tiles[2 * t] * a.tm + slab * slab_rows;
     const int col0 = a.tiles[2 * t + 1] * a.tn;
@@ -209,6 +210,8 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
       reduce_chunks<kUnroll, PEER_F32, OUT_F32>(a, e, ok);
     }
   }
+  // Every workgroup, finished or timed out, checks out.
+  if (tid == 0 && !a.nowait) check_out(a.ctl, kReduceDone, epoch);
 }
 
 // The sequential schedule's reduction: no flags; the partition is one flat
@@ -253,7 +256,33 @@ hipError_t launch_threads(const ReduceArgs& a, int peer_f32, int out_f32, bool f
   return hipGetLastError();
 }
 
+template <int THREADS, bool PEER_F32, bool OUT_F32>
+int regs_typed() {
+  hipFuncAttributes at{};
+  if (hipFuncGetAttributes(&at, (const void*)tile_reduce_kernel<THREADS, PEER_F32, OUT_F32>) !=
+      hipSuccess)
+    return 0;
+  return at.numRegs;
+}
+
+template <int THREADS>
+int regs_threads(int peer_f32, int out_f32) {
+  if (!peer_f32 && !out_f32) return regs_typed<THREADS, false, false>();
+  if (!peer_f32 && out_f32) return regs_typed<THREADS, false, true>();
+  if (peer_f32 && !out_f32) return regs_typed<THREADS, true, false>();
+  return regs_typed<THREADS, true, true>();
+}
+
 }  // namespace
+
+int reduce_registers(int threads, int peer_f32, int out_f32) {
+  switch (threads) {
+    case 128: return regs_threads<128>(peer_f32, out_f32);
+    case 256: return regs_threads<256>(peer_f32, out_f32);
+    case 512: return regs_threads<512>(peer_f32, out_f32);
+    default: return 0;
+  }
+}
 
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
                               bool flat, int grid, hipStream_t stream) {
