@@ -155,13 +155,15 @@ typedef struct entwine_config {
   int32_t publish_all;     /* 0: agent-scope release only for tiles a kernel on this device
                               reads (the rank's partition), progress flags for the rest;
                               1: release every tile (the cost of publishing to peers) */
+  int32_t linear_dispatch; /* 0: XCD-aware dispatch within each window of co-resident blocks
+                              (entwine_plan_dispatch); 1: workgroup b computes logical block b */
   int32_t stages;          /* measurement: ENTWINE_STAGES_ALL (0), or one kernel alone:
                               ENTWINE_STAGES_GEMM (the GEMM without flags) or
                               ENTWINE_STAGES_REDUCE (the reduction of whatever the workspace
                               holds, with every flag treated as ready; the budget picks the
                               schedule as usual).  A single stage leaves `out` (GEMM) or the
                               partials (reduction) as they were: for timing only. */
-  int32_t reserved[4];
+  int32_t reserved[3];
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);
@@ -189,6 +191,16 @@ int entwine_plan_shape(int64_t M, int64_t N, int P, int block_m, int block_n, in
  * partition d).  `capacity` = number of int32 elements available. */
 int entwine_plan_blocks(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
                         int block_n, int tile_m, int tile_n, int32_t* blocks, int64_t capacity);
+
+/* The GEMM's dispatch permutation: workgroup b computes logical position
+ * dispatch[b].  Workgroups run on XCD b % 8 in order, so inside each window of
+ * `window` consecutive positions (the blocks resident at once: CUs times
+ * blocks per CU; 0 = identity) the positions are dealt so that each XCD gets a
+ * compact rectangle of the block grid.  The production order across windows
+ * is unchanged.  `capacity` = number of int32 elements available (>= blocks). */
+int entwine_plan_dispatch(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                          int block_n, int tile_m, int tile_n, int64_t window, int32_t* dispatch,
+                          int64_t capacity);
 
 /* Tile t of a partition (numbered in N-major producer order, Sec. 3.1
  * "Matching task order") sits at tile row tiles[2t], tile col tiles[2t+1]. */

@@ -24,7 +24,7 @@ SMALL = [
     wl.custom("odd_n", 512, 1160, 256, 2, rank=1, index=302),        # N = 9*128 + 8
     wl.BY_NAME["tiny"],                                              # fp32 peers/out, 64x64 tiles
 ]
-BLOCKS = [(128, 128), (128, 256), (256, 128)]
+BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256)]
 
 
 @pytest.fixture(scope="module")
@@ -48,21 +48,27 @@ def case_for(w, dev):
 def test_parity_and_schedule_invariance(dev, w):
     case, ref = case_for(w, dev)
     _, _, q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
-    first = None
+    first = {}
     runs = 0
     for bm, bn in BLOCKS:
-        for order in ORDERS:
-            for budget in (0, 1, 3, min(q, 64)):
-                print(f"case {w.name} block {bm}x{bn} order {order} budget {budget}", flush=True)
-                out = down(case.run(order, budget, block_m=bm, block_n=bn))
-                runs += 1
-                if first is None:
-                    first = out
+        if w.tile == 64 and bm == 256:
+            continue
+        for variant in (0, 3):
+            for order in ORDERS:
+                for budget in (0, 1, 3, min(q, 64)):
+                    print(f"case {w.name} block {bm}x{bn} v{variant} order {order} budget {budget}",
+                          flush=True)
+                    out = down(case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant))
+                    runs += 1
                     r = err_ratio(out, ref)
                     assert r <= 1.0, f"max err/tol {r:.3f}"
-                else:
-                    np.testing.assert_array_equal(out, first)
-    assert runs == len(BLOCKS) * len(ORDERS) * 4
+                    # one result per block shape and variant (accumulation order)
+                    key = (bm, bn, variant)
+                    if key not in first:
+                        first[key] = out
+                    else:
+                        np.testing.assert_array_equal(out, first[key])
+    assert runs >= 2 * 2 * len(ORDERS) * 4
 
 
 @pytest.mark.parametrize("w", SMALL[:2], ids=lambda w: w.name)

@@ -153,3 +153,53 @@ def test_tasks_partition_the_tiles(q, x):
     assert flat == list(range(q))
     for j, s in enumerate(seqs):
         assert s == list(range(j, q, min(x, q))) if j < min(x, q) else s == []
+
+
+def _panels(blocks, positions, Rb):
+    rows = {blocks[p][0] * Rb + blocks[p][1] for p in positions}
+    cols = {blocks[p][2] for p in positions}
+    return len(rows) + len(cols)
+
+
+@pytest.mark.parametrize("shape,window", [
+    ((4096, 4096, 8, 256, 256, 128, 128), 256),     # one window: the whole grid
+    ((8192, 8192, 8, 256, 256, 128, 128), 256),     # four windows
+    ((16384, 5120, 4, 256, 256, 128, 128), 256),    # five windows
+    ((1000, 12288, 8, 128, 128, 128, 128), 512),    # two blocks per CU
+    ((1000, 1536, 8, 128, 128, 128, 128), 40),      # a partial last window
+])
+def test_dispatch_is_windowed_permutation(shape, window):
+    """Workgroup b computes logical position dispatch[b]: a permutation that
+    keeps every window of consecutive positions on the same window of
+    workgroups (production order is kept across windows) and gives every XCD
+    (workgroups b with equal b % 8) a compact set of blocks."""
+    M, N, P, bm, bn, tm, tn = shape
+    nb, bd, q = tog.entwine_plan_shape(*shape)
+    for order in ORDERS:
+        disp = tog.entwine_plan_dispatch(M, N, P, 0, order, bm, bn, tm, tn, window)
+        assert sorted(disp) == list(range(nb))
+        w = window - window % 8
+        for b, p in enumerate(disp):
+            assert b // w == p // w
+        assert tog.entwine_plan_dispatch(M, N, P, 0, order, bm, bn, tm, tn, 0) == list(range(nb))
+        # the busiest XCD of each window touches no more panels than with the
+        # identity dispatch
+        blocks = tog.entwine_plan_blocks(M, N, P, 0, order, bm, bn, tm, tn)
+        Rb = -(-(M // P) // bm)
+        for w0 in range(0, nb, w):
+            span = range(w0, min(nb, w0 + w))
+            mine = max(_panels(blocks, [disp[b] for b in span if b % 8 == x], Rb) for x in range(8))
+            ident = max(_panels(blocks, [b for b in span if b % 8 == x], Rb) for x in range(8))
+            assert mine <= ident
+
+
+def test_dispatch_panel_counts_mlp():
+    """MLP slice, 256x256 blocks, one window of 256: interleaved order gives XCD
+    x the 32 blocks of partition x (2 row panels + 16 column panels); the
+    XCD-aware deal gives each XCD a 4 x 8 rectangle (12 panels)."""
+    M, N, P, bm, bn, tm, tn = 4096, 4096, 8, 256, 256, 128, 128
+    blocks = tog.entwine_plan_blocks(M, N, P, 0, tog.ORDER_INTERLEAVED, bm, bn, tm, tn)
+    disp = tog.entwine_plan_dispatch(M, N, P, 0, tog.ORDER_INTERLEAVED, bm, bn, tm, tn, 256)
+    for x in range(8):
+        assert _panels(blocks, [b for b in range(256) if b % 8 == x], 2) == 18
+        assert _panels(blocks, [disp[b] for b in range(256) if b % 8 == x], 2) == 12

@@ -35,7 +35,7 @@ STAGES_ALL, STAGES_GEMM, STAGES_REDUCE = 0, 1, 2
 # Names exported by the library (one per declaration in include/entwine.h).
 EXPORTS = [
     "entwine_gemm_rs", "entwine_config_init", "entwine_gemm_rs_ex", "entwine_plan_shape",
-    "entwine_plan_blocks", "entwine_plan_tiles", "entwine_plan_waits", "entwine_plan_tasks",
+    "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
     "entwine_workspace", "entwine_timing", "entwine_timing_read", "entwine_load_tuning",
     "entwine_release", "entwine_device_cus",
@@ -66,8 +66,9 @@ class entwine_config(ctypes.Structure):
         ("withhold_tile", ctypes.c_int32),
         ("gemm_variant", ctypes.c_int32),
         ("publish_all", ctypes.c_int32),
+        ("linear_dispatch", ctypes.c_int32),
         ("stages", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 4),
+        ("reserved", ctypes.c_int32 * 3),
     ]
 
 
@@ -98,6 +99,7 @@ def load(path: str = LIB):
         "entwine_config_init": ([pcfg], None),
         "entwine_plan_shape": ([i64, i64, i32, i32, i32, i32, i32, pi64, pi64, pi64], i32),
         "entwine_plan_blocks": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, pi32, i64], i32),
+        "entwine_plan_dispatch": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, i64, pi32, i64], i32),
         "entwine_plan_tiles": ([i64, i64, i32, i32, i32, i32, i32, pi32, i64], i32),
         "entwine_plan_waits": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32, pi32, i64], i32),
         "entwine_plan_tasks": ([i64, i32, i32, pi32, i64, pi64], i32),
@@ -210,6 +212,15 @@ def entwine_plan_blocks(M, N, P, rank, tile_order, block_m, block_n, tile_m, til
     _check(load().entwine_plan_blocks(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
                                       buf, 4 * nb))
     return [tuple(buf[4 * p:4 * p + 4]) for p in range(nb)]
+
+
+def entwine_plan_dispatch(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n, window):
+    """Logical position computed by each GEMM workgroup (XCD-aware within windows)."""
+    nb, _, _ = entwine_plan_shape(M, N, P, block_m, block_n, tile_m, tile_n)
+    buf = _i32_array(nb)
+    _check(load().entwine_plan_dispatch(M, N, P, rank, tile_order, block_m, block_n, tile_m,
+                                        tile_n, window, buf, nb))
+    return list(buf[:nb])
 
 
 def entwine_plan_tiles(M, N, P, block_m, block_n, tile_m, tile_n):

@@ -63,7 +63,7 @@ struct DevicePlan {
   int32_t* d_waits = nullptr;
 };
 
-using PlanKey = std::tuple<int64_t, int64_t, int, int, int, int, int, int, int, int, int>;
+using PlanKey = std::tuple<int64_t, int64_t, int, int, int, int, int, int, int, int, int, int64_t>;
 
 struct TimingPair {
   hipEvent_t g0, g1, r0, r1;
@@ -193,8 +193,9 @@ int ensure(Workspace* w, void** buf, size_t* have, size_t need, bool zero) {
 }
 
 int get_plan(Workspace* w, const Geometry& g, int rank, int order, int peer_ready,
-             int release_group, DevicePlan** out) {
-  PlanKey key{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, order, peer_ready, release_group};
+             int release_group, int64_t window, DevicePlan** out) {
+  PlanKey key{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, order, peer_ready, release_group,
+              window};
   auto it = w->plans.find(key);
   if (it != w->plans.end()) {
     *out = it->second.get();
@@ -203,13 +204,14 @@ int get_plan(Workspace* w, const Geometry& g, int rank, int order, int peer_read
   auto dp = std::make_unique<DevicePlan>();
   int rc = build_plan(g, rank, order, peer_ready, release_group, &dp->plan);
   if (rc != ENTWINE_OK) return fail(rc, "schedule construction failed");
+  assign_dispatch(&dp->plan, window);
   const Plan& p = dp->plan;
   auto upload = [&](const std::vector<int32_t>& v, int32_t** d) -> int {
     HIP_TRY(hipMalloc(d, v.size() * sizeof(int32_t)));
     HIP_TRY(hipMemcpy(*d, v.data(), v.size() * sizeof(int32_t), hipMemcpyHostToDevice));
     return ENTWINE_OK;
   };
-  if ((rc = upload(p.blocks, &dp->d_blocks)) != ENTWINE_OK ||
+  if ((rc = upload(p.launch, &dp->d_blocks)) != ENTWINE_OK ||
       (rc = upload(p.tiles, &dp->d_tiles)) != ENTWINE_OK ||
       (rc = upload(p.waits, &dp->d_waits)) != ENTWINE_OK) {
     free_plan(dp.get());
@@ -262,7 +264,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile, variant, publish_all, stages;
+      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch;
   uint32_t timeout_ms;
 };
 
@@ -312,6 +314,7 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->slabs = c.task_slabs ? c.task_slabs : (te ? te->slabs : 1);
   r->publish_all = c.publish_all;
   r->stages = c.stages;
+  r->linear_dispatch = c.linear_dispatch;
   r->timeout_ms = c.poll_timeout_ms ? c.poll_timeout_ms : 2000;
   r->withhold_tile = c.withhold_tile - 1;
   r->variant = c.gemm_variant;
@@ -319,6 +322,8 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
   if (c.publish_all != 0 && c.publish_all != 1)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "publish_all must be 0 or 1");
+  if (c.linear_dispatch != 0 && c.linear_dispatch != 1)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "linear_dispatch must be 0 or 1");
   if (c.stages < ENTWINE_STAGES_ALL || c.stages > ENTWINE_STAGES_REDUCE)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "stages %d out of range", c.stages);
   return ENTWINE_OK;
@@ -380,17 +385,25 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     // The reduction workgroups wait for GEMM blocks, so a CU holding one
     // must still fit a GEMM block: otherwise reduction workgroups spread
     // over the device could starve the GEMM until the watchdog fires.
-    const int waves_per_simd = (rs.threads / 64 + 3) / 4;
+    const int red_waves_per_simd = (rs.threads / 64 + 3) / 4;
+    const int gemm_waves_per_simd = (gemm_waves(g.bm, g.bn, rs.variant) + 3) / 4;
     const int gr = gemm_registers(g.bm, g.bn, rs.variant);
     const int rr = reduce_registers(rs.threads, rs.peer_f32, rs.out_f32);
     auto up8 = [](int v) { return (v + 7) / 8 * 8; };
     if (gr <= 0 || rr <= 0)
       return fail(ENTWINE_ERR_HIP, "kernel register counts unavailable");
-    if (up8(gr) + waves_per_simd * up8(rr) > 512)
+    if (gemm_waves_per_simd * up8(gr) + red_waves_per_simd * up8(rr) > 512)
       return fail(ENTWINE_ERR_UNSUPPORTED,
                   "a %d-thread reduction workgroup (%d registers per lane) cannot share a CU "
                   "with a %dx%d GEMM block (%d registers per lane)",
                   rs.threads, rr, g.bm, g.bn, gr);
+  }
+
+  // Blocks resident at once: the window inside which dispatch is XCD-aware.
+  int64_t window = 0;
+  if (!rs.linear_dispatch) {
+    const int per_cu = gemm_blocks_per_cu(g.bm, g.bn, rs.variant);
+    window = (int64_t)std::max(per_cu, 1) * w->cus;
   }
 
   const size_t own_need = (size_t)g.R * N * 4, og_need = (size_t)M * N * peer_sz;
@@ -399,7 +412,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   if (capturing) {
     // Allocation, upload and synchronization are not allowed while capturing.
     PlanKey key{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, rs.order, rs.peer_ready,
-                rs.release_group};
+                rs.release_group, window};
     if (w->own_bytes < own_need || w->outgoing_bytes < og_need || w->flag_count * 4 < flag_need ||
         w->plans.find(key) == w->plans.end())
       return fail(ENTWINE_ERR_INVALID_ARGUMENT,
@@ -413,7 +426,8 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   w->flag_count = flag_bytes / 4;
 
   DevicePlan* dp = nullptr;
-  if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, &dp))) return rc;
+  if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, window, &dp)))
+    return rc;
 
   TimingPair tp{};
   if (g_timing && (rc = take_timing_pair(w, &tp))) return rc;
@@ -587,6 +601,21 @@ int entwine_plan_blocks(int64_t M, int64_t N, int P, int rank, int tile_order, i
   if (!blocks || capacity < (int64_t)p.blocks.size())
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "blocks needs %zu entries", p.blocks.size());
   std::copy(p.blocks.begin(), p.blocks.end(), blocks);
+  return ENTWINE_OK;
+}
+
+int entwine_plan_dispatch(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                          int block_n, int tile_m, int tile_n, int64_t window, int32_t* dispatch,
+                          int64_t capacity) {
+  Plan p;
+  int rc = plan_for(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
+                    ENTWINE_PEERS_PRESEEDED, ENTWINE_RELEASE_TILE, &p);
+  if (rc) return rc;
+  if (window < 0) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "window must be >= 0");
+  assign_dispatch(&p, window);
+  if (!dispatch || capacity < (int64_t)p.dispatch.size())
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "dispatch needs %zu entries", p.dispatch.size());
+  std::copy(p.dispatch.begin(), p.dispatch.end(), dispatch);
   return ENTWINE_OK;
 }
 

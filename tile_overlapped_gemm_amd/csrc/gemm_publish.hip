@@ -12,11 +12,13 @@
 //    flags of every reduction tile it covers with release semantics.
 //
 // MI355X (gfx950) design.
-//  * 256 threads = 4 waves of 64 in a 2 x 2 arrangement; a wave owns a
-//    (BM/2) x (BN/2) sub-block computed with v_mfma_f32_32x32x16_bf16 into
-//    fp32 accumulators.  The MFMA's first operand is the W fragment and the
-//    second the X fragment, so each lane ends up holding runs of 4
-//    consecutive output columns (16-byte fp32 / 8-byte bf16 stores).
+//  * 512 threads = 8 waves of 64 (two per SIMD, so one wave's waits are
+//    covered by the other's MFMAs) in a 2 x 4 (or 4 x 2) arrangement; a wave
+//    owns a (BM/WGM) x (BN/WGN) sub-block computed with
+//    v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  A 4-wave (2 x 2)
+//    instance remains as variant 3.  The MFMA's first operand is the W
+//    fragment and the second the X fragment, so each lane holds runs of 4
+//    consecutive output columns.
 //  * K advances in stages of 64 (128 bytes per row).  X and W are both
 //    K-contiguous, so each stage is a BM x 128 B and a BN x 128 B slab.  Slabs
 //    move from global memory straight into LDS with buffer_load_dwordx4 ...
@@ -48,23 +50,28 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
-constexpr int kThreads = 256;
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-// Block BM x BN, K stage BK (32 or 64), NS LDS stages.
-template <int BM, int BN, int BK, int NS>
+// Block BM x BN, K stage BK (32 or 64), NS LDS stages, WGM x WGN waves.
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
 struct Shape {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWavesN = WGN;
   static constexpr int kRow = BK * 2;                 // bytes per slab row
   static constexpr int kRowsPerLoad = 1024 / kRow;    // rows per 1 KiB wave load
   static constexpr int kLanesPerRow = kRow / 16;
   static constexpr int kKS = BK / 16;                 // MFMA K steps per stage
-  static constexpr int kWM = BM / 2, kWN = BN / 2;    // wave sub-block
+  static constexpr int kWM = BM / WGM, kWN = BN / WGN;  // wave sub-block
   static constexpr int kMT = kWM / 32, kNT = kWN / 32;
   static constexpr int kA = BM * kRow, kB = BN * kRow;  // stage slabs
   static constexpr int kStage = kA + kB;
   static constexpr int kLds = NS * kStage;
-  static constexpr int kLoadsA = BM / (4 * kRowsPerLoad);  // per wave per stage
-  static constexpr int kLoadsB = BN / (4 * kRowsPerLoad);
+  static constexpr int kLoadsA = BM / (kWaves * kRowsPerLoad);  // per wave per stage
+  static constexpr int kLoadsB = BN / (kWaves * kRowsPerLoad);
+  static_assert(kLoadsA * kWaves * kRowsPerLoad == BM && kLoadsB * kWaves * kRowsPerLoad == BN,
+                "slab rows must split evenly over the waves");
+  static_assert(kWaves % 2 == 0, "load groups keep the row parity of the swizzle");
   static constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(kKS % 2 == 0, "fragment double buffer needs an even K-step count");
   static_assert(kLoads * (NS - 2 > 0 ? NS - 2 : 0) < 64, "vmcnt range");
@@ -102,12 +109,13 @@ __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_
                                             int wave) {
 #pragma unroll
   for (int j = 0; j < S::kLoadsA; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + 4 * j) * 1024), 16,
-                                             voff, j * group_step + kbyte, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + S::kWaves * j) * 1024),
+                                             16, voff, j * group_step + kbyte, 0, 0);
 #pragma unroll
   for (int j = 0; j < S::kLoadsB; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_ptr_t)(lds + S::kA + (wave + 4 * j) * 1024),
-                                             16, voff, j * group_step + kbyte, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_ptr_t)(lds + S::kA + (wave + S::kWaves * j) * 1024), 16, voff,
+        j * group_step + kbyte, 0, 0);
 }
 
 template <class S>
@@ -138,15 +146,15 @@ __device__ __forceinline__ void mfma_step(Acc<S>& acc, const Frags<S>& f) {
       acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
 }
 
-template <int BM, int BN, int BK, int NS>
-__global__ __launch_bounds__(kThreads, 1) void gemm_publish_kernel(GemmArgs a) {
-  using S = Shape<BM, BN, BK, NS>;
+template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArgs a) {
+  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = wave >> 1, wn = wave & 1;
+  const int wm = wave / WGN, wn = wave % WGN;
 
   const int4 blk = reinterpret_cast<const int4*>(a.blocks)[blockIdx.x];
   const int d = blk.x, br = blk.y, bc = blk.z, t_first = blk.w;
@@ -165,11 +173,11 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_publish_kernel(GemmArgs a) {
       (void*)(a.W + (int64_t)col0 * K), (short)0, rows_b * kbytes, kRsrcWord3);
 
   // Global source of this lane: row wave*RPL + lane/LPR of each group of
-  // 4*RPL rows, logical chunk (lane % LPR) ^ swz(row).
+  // kWaves*RPL rows, logical chunk (lane % LPR) ^ swz(row).
   const int lrow = wave * S::kRowsPerLoad + lane / S::kLanesPerRow;
   const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK>(lrow);
   const int voff = lrow * kbytes + lchunk * 16;
-  const int group_step = 4 * S::kRowsPerLoad * kbytes;
+  const int group_step = S::kWaves * S::kRowsPerLoad * kbytes;
 
   // LDS fragment offsets: MFMA lane l reads row (l & 31) of a 32-row group,
   // logical chunk 2*ks + (l >> 5).
@@ -245,7 +253,7 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_publish_kernel(GemmArgs a) {
   constexpr int kPitch = S::kWN * 4 + 16;
   constexpr int kLanesPerRow = S::kWN / 4;
   constexpr int kRowsPerStore = 64 / kLanesPerRow;
-  static_assert(4 * 32 * kPitch <= S::kLds, "epilogue staging exceeds LDS");
+  static_assert(S::kWaves * 32 * kPitch <= S::kLds, "epilogue staging exceeds LDS");
   __syncthreads();  // every wave is done with the pipeline buffers
   char* wbuf = smem + wave * 32 * kPitch;
   const bool local = (d == a.rank);
@@ -315,54 +323,108 @@ __global__ __launch_bounds__(kThreads, 1) void gemm_publish_kernel(GemmArgs a) {
   }
 }
 
-template <int BM, int BN, int BK, int NS>
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
 hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
-  using S = Shape<BM, BN, BK, NS>;
+  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm_publish_kernel<BM, BN, BK, NS><<<num_blocks, kThreads, S::kLds, s>>>(a);
+  gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN><<<num_blocks, S::kThreads, S::kLds, s>>>(a);
   return hipGetLastError();
 }
 
-}  // namespace
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+int occupancy_of() {
+  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
+          &n, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN>, S::kThreads,
+          S::kLds) != hipSuccess)
+    return 0;
+  return n;
+}
 
-template <int BM, int BN, int BK, int NS>
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
 int regs_of() {
   hipFuncAttributes at{};
-  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS>) != hipSuccess)
+  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN>) !=
+      hipSuccess)
     return 0;
   return at.numRegs;
 }
 
-int gemm_registers(int bm, int bn, int variant) {
-  if (bm == 128 && bn == 128) return regs_of<128, 128, 64, 2>();
-  if (bm == 128 && bn == 256) return regs_of<128, 256, 64, 2>();
-  if (bm == 256 && bn == 128) return regs_of<256, 128, 64, 2>();
-  if (bm == 256 && bn == 256) {
-    if (variant == 1) return regs_of<256, 256, 32, 4>();
-    if (variant == 2) return regs_of<256, 256, 32, 3>();
-    return regs_of<256, 256, 64, 2>();
+// The kernel instance for a block shape and variant, handed to `f` as a
+// template functor call f.template operator()<BM, BN, BK, NS, WGM, WGN>().
+template <class F>
+auto with_instance(int bm, int bn, int variant, F&& f) -> decltype(f.template run<128, 128, 64, 2, 2, 2>()) {
+  if (bm == 128 && bn == 128) {
+    if (variant == 3) return f.template run<128, 128, 64, 2, 2, 4>();
+    return f.template run<128, 128, 64, 2, 2, 2>();
   }
-  return 0;
+  if (bm == 128 && bn == 256) {
+    if (variant == 3) return f.template run<128, 256, 64, 2, 2, 2>();
+    return f.template run<128, 256, 64, 2, 2, 4>();
+  }
+  if (bm == 256 && bn == 128) {
+    if (variant == 3) return f.template run<256, 128, 64, 2, 2, 2>();
+    return f.template run<256, 128, 64, 2, 4, 2>();
+  }
+  if (bm == 256 && bn == 256) {
+    if (variant == 1) return f.template run<256, 256, 32, 4, 2, 2>();
+    if (variant == 2) return f.template run<256, 256, 32, 3, 2, 2>();
+    if (variant == 3) return f.template run<256, 256, 64, 2, 2, 2>();
+    return f.template run<256, 256, 64, 2, 2, 4>();
+  }
+  return f.template run<0, 0, 0, 0, 0, 0>();
 }
+
+struct Launch {
+  const GemmArgs& a;
+  int num_blocks;
+  hipStream_t s;
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  hipError_t run() {
+    if constexpr (BM == 0) return hipErrorInvalidValue;
+    else return launch_shape<BM, BN, BK, NS, WGM, WGN>(a, num_blocks, s);
+  }
+};
+struct Occupancy {
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  int run() {
+    if constexpr (BM == 0) return 0;
+    else return occupancy_of<BM, BN, BK, NS, WGM, WGN>();
+  }
+};
+struct Registers {
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  int run() {
+    if constexpr (BM == 0) return 0;
+    else return regs_of<BM, BN, BK, NS, WGM, WGN>();
+  }
+};
+
+}  // namespace
+
+int gemm_registers(int bm, int bn, int variant) { return with_instance(bm, bn, variant, Registers{}); }
+
+int gemm_blocks_per_cu(int bm, int bn, int variant) {
+  return with_instance(bm, bn, variant, Occupancy{});
+}
+
+struct Waves {
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  int run() { return WGM * WGN; }
+};
+
+int gemm_waves(int bm, int bn, int variant) { return with_instance(bm, bn, variant, Waves{}); }
 
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream) {
-  const int v = a.variant;
-  if (bm == 128 && bn == 128) return launch_shape<128, 128, 64, 2>(a, num_blocks, stream);
-  if (bm == 128 && bn == 256) return launch_shape<128, 256, 64, 2>(a, num_blocks, stream);
-  if (bm == 256 && bn == 128) return launch_shape<256, 128, 64, 2>(a, num_blocks, stream);
-  if (bm == 256 && bn == 256) {
-    if (v == 1) return launch_shape<256, 256, 32, 4>(a, num_blocks, stream);
-    if (v == 2) return launch_shape<256, 256, 32, 3>(a, num_blocks, stream);
-    return launch_shape<256, 256, 64, 2>(a, num_blocks, stream);
-  }
-  return hipErrorInvalidValue;
+  return with_instance(bm, bn, a.variant, Launch{a, num_blocks, stream});
 }
 
 }  // namespace entwine

@@ -90,6 +90,10 @@ hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, in
 // Registers per lane (VGPRs + AGPRs) of the kernels a launch would use, for
 // the co-residency check; 0 if unknown.
 int gemm_registers(int bm, int bn, int variant);
+// GEMM workgroups of a block shape resident per CU at once (0 if unknown).
+int gemm_blocks_per_cu(int bm, int bn, int variant);
+// Waves per GEMM workgroup (64 lanes each).
+int gemm_waves(int bm, int bn, int variant);
 int reduce_registers(int threads, int peer_f32, int out_f32);
 
 }  // namespace entwine

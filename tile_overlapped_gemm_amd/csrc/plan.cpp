@@ -20,6 +20,7 @@
 #include "plan.h"
 
 #include <algorithm>
+#include <numeric>
 
 #include "entwine.h"
 
@@ -218,6 +219,109 @@ int build_plan(const Geometry& g, int rank, int order, int peer_ready, int relea
   }
   *out = std::move(pl);
   return ENTWINE_OK;
+}
+
+// Distinct X row panels plus W column panels touched by a set of blocks.
+static int64_t panels(const std::vector<std::pair<int64_t, int64_t>>& rc, size_t lo, size_t hi) {
+  std::vector<int64_t> rows, cols;
+  for (size_t k = lo; k < hi; ++k) {
+    rows.push_back(rc[k].first);
+    cols.push_back(rc[k].second);
+  }
+  std::sort(rows.begin(), rows.end());
+  std::sort(cols.begin(), cols.end());
+  return (int64_t)(std::unique(rows.begin(), rows.end()) - rows.begin()) +
+         (int64_t)(std::unique(cols.begin(), cols.end()) - cols.begin());
+}
+
+void assign_dispatch(Plan* plan, int64_t window) {
+  const Geometry& g = plan->g;
+  const int64_t NB = g.NB;
+  plan->dispatch.resize(NB);
+  std::iota(plan->dispatch.begin(), plan->dispatch.end(), 0);
+  if (window >= kXcds) {
+    window -= window % kXcds;
+    for (int64_t w0 = 0; w0 < NB; w0 += window) {
+      const int64_t w1 = std::min(NB, w0 + window), n = w1 - w0;
+      // Global block coordinates of the window's positions.
+      std::vector<std::pair<int64_t, int64_t>> rc(n);
+      for (int64_t k = 0; k < n; ++k) {
+        const int32_t* b = &plan->blocks[4 * (w0 + k)];
+        rc[k] = {(int64_t)b[0] * g.Rb + b[1], (int64_t)b[2]};
+      }
+      std::vector<int64_t> urows, ucols;
+      for (auto& v : rc) {
+        urows.push_back(v.first);
+        ucols.push_back(v.second);
+      }
+      std::sort(urows.begin(), urows.end());
+      urows.erase(std::unique(urows.begin(), urows.end()), urows.end());
+      std::sort(ucols.begin(), ucols.end());
+      ucols.erase(std::unique(ucols.begin(), ucols.end()), ucols.end());
+      // Slots of each XCD inside the window: workgroups b in [w0, w1) with
+      // b % kXcds == x, in order (w0 is a multiple of kXcds).
+      std::vector<int64_t> slots(kXcds, 0);
+      for (int64_t b = w0; b < w1; ++b) ++slots[b % kXcds];
+      // The identity deal (XCD x takes positions w0 + x + kXcds*k) as written
+      // in deal order, then splits of the window's rows into a groups and its
+      // columns into kXcds / a groups; keep the deal whose busiest XCD touches
+      // the fewest panels.
+      std::vector<int64_t> best_order;
+      int64_t best_cost = -1;
+      {
+        std::vector<int64_t> order;
+        std::vector<std::pair<int64_t, int64_t>> sorted;
+        for (int x = 0; x < kXcds; ++x)
+          for (int64_t k = x; k < n; k += kXcds) {
+            order.push_back(k);
+            sorted.push_back(rc[k]);
+          }
+        size_t lo = 0;
+        best_cost = 0;
+        for (int x = 0; x < kXcds; ++x) {
+          best_cost = std::max(best_cost, panels(sorted, lo, lo + slots[x]));
+          lo += slots[x];
+        }
+        best_order = order;
+      }
+      for (int a = 1; a <= kXcds; a *= 2) {
+        const int bgrp = kXcds / a;
+        std::vector<int64_t> order(n);
+        std::iota(order.begin(), order.end(), 0);
+        auto key = [&](int64_t k) {
+          const int64_t ri = std::lower_bound(urows.begin(), urows.end(), rc[k].first) - urows.begin();
+          const int64_t ci = std::lower_bound(ucols.begin(), ucols.end(), rc[k].second) - ucols.begin();
+          const int64_t grp = (ri * a / (int64_t)urows.size()) * bgrp + ci * bgrp / (int64_t)ucols.size();
+          return std::make_tuple(grp, rc[k].first, rc[k].second);
+        };
+        std::stable_sort(order.begin(), order.end(),
+                         [&](int64_t u, int64_t v) { return key(u) < key(v); });
+        std::vector<std::pair<int64_t, int64_t>> sorted(n);
+        for (int64_t k = 0; k < n; ++k) sorted[k] = rc[order[k]];
+        int64_t cost = 0;
+        size_t lo = 0;
+        for (int x = 0; x < kXcds; ++x) {
+          cost = std::max(cost, panels(sorted, lo, lo + slots[x]));
+          lo += slots[x];
+        }
+        if (cost < best_cost) {
+          best_cost = cost;
+          best_order = order;
+        }
+      }
+      // XCD x takes the next slots[x] positions of the chosen order; its
+      // k-th workgroup in the window is b = w0 + x + kXcds * k.
+      int64_t lo = 0;
+      for (int x = 0; x < kXcds; ++x) {
+        for (int64_t k = 0; k < slots[x]; ++k)
+          plan->dispatch[w0 + x + kXcds * k] = (int32_t)(w0 + best_order[lo + k]);
+        lo += slots[x];
+      }
+    }
+  }
+  plan->launch.resize(4 * NB);
+  for (int64_t b = 0; b < NB; ++b)
+    for (int f = 0; f < 4; ++f) plan->launch[4 * b + f] = plan->blocks[4 * plan->dispatch[b] + f];
 }
 
 }  // namespace entwine

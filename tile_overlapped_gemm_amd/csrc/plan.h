@@ -44,7 +44,9 @@ void block_valid_tiles(const Geometry& g, int64_t i, int* vm, int* vn);
 struct Plan {
   Geometry g;
   int rank = 0, order = 0, peer_ready = 0, release_group = 1;
-  std::vector<int32_t> blocks;   // [NB][4]: d, br, bc, first tile
+  std::vector<int32_t> blocks;   // [NB][4]: d, br, bc, first tile, by logical position
+  std::vector<int32_t> dispatch; // [NB]: logical position computed by workgroup b
+  std::vector<int32_t> launch;   // [NB][4]: blocks[dispatch[b]], what the GEMM reads
   std::vector<int32_t> tiles;    // [Q][2]: tile row, tile col
   int wait_slots = 0;            // P + 1
   std::vector<int32_t> waits;    // [Q][wait_slots]: flag index or -1
@@ -53,5 +55,16 @@ struct Plan {
 
 int build_plan(const Geometry& g, int rank, int order, int peer_ready, int release_group,
                Plan* out);
+
+// The devices this is built for dispatch workgroup b of a grid to XCD
+// b % kXcds, each XCD's workgroups in order.  Blocks resident at the same
+// time (a window of `window` consecutive logical positions) run concurrently,
+// so within each window the positions are dealt to XCDs such that every XCD
+// gets a compact rectangle of the global block grid: its L2 then holds few X
+// row panels and W column panels.  Across windows the production order is
+// unchanged.  window = 0 (or 1) keeps the identity (workgroup b computes
+// position b).  Fills plan->dispatch and plan->launch.
+constexpr int kXcds = 8;
+void assign_dispatch(Plan* plan, int64_t window);
 
 }  // namespace entwine
