@@ -36,9 +36,9 @@
 //    cover the barrier and the next stage's first fragment reads.
 //  * Epilogue: accumulators leave through LDS in 32-row strips so that the
 //    global stores write whole cache lines.
-//  * Publication: the workgroup synchronizes after its stores, then thread 0
-//    issues one agent-scope release fence and stores the call's epoch into the
-//    flag of every tile the block covers.
+//  * Publication: tiles read on this device are written with device-coherent
+//    (SC1) stores; the workgroup synchronizes after its stores, then thread 0
+//    stores the call's epoch into the flag of every tile the block covers.
 #include "kernels.h"
 
 namespace entwine {
@@ -94,6 +94,16 @@ __device__ __forceinline__ int swz(int r) {
 template <int VM>
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
+// Device-coherent global stores (buffer cache policy SC1) through a
+// wave-uniform buffer descriptor; `off` is the lane's byte offset.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kCoherent = 16;  // SC1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
 }
 
 __device__ __forceinline__ bf16x8 lds_frag(const char* p) {
@@ -250,6 +260,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
   // row-contiguous, so every global store instruction covers whole 128-byte
   // lines: 16-byte fp32 stores for the local partition, 8-byte bf16 (or
   // 16-byte fp32) stores for the outgoing contributions.
+  //
+  // Tiles that are released to a consumer are written with device-coherent
+  // stores (cache policy SC1, the encoding of a relaxed agent-scope atomic
+  // store): the data is written through this XCD's L2, so once a store is
+  // acknowledged a reader on any XCD sees it and the release needs no
+  // write-back of the whole L2.
   constexpr int kPitch = S::kWN * 4 + 16;
   constexpr int kLanesPerRow = S::kWN / 4;
   constexpr int kRowsPerStore = 64 / kLanesPerRow;
@@ -261,8 +277,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
   const int csub = (lane % kLanesPerRow) * 4;
   const int col = col0 + wn * S::kWN + csub;
   const bool col_ok = col < a.N;
-  float* const own_base = a.own + col;
-  const int64_t og_base = (int64_t)d * a.R * a.N + col;
+  const bool coherent = local ? a.publish != 0 : a.publish == 2;
+  const int strip_bytes = 32 * a.N * (local || a.outgoing_f32 ? 4 : 2);
 #pragma unroll
   for (int i = 0; i < S::kMT; ++i) {
 #pragma unroll
@@ -278,24 +294,38 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
       }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the strip is in LDS
     __builtin_amdgcn_wave_barrier();
+    // The strip's first row (wave-uniform) in the partition, and the output
+    // it lands in: the fp32 local partial or the outgoing contributions.
+    const int srow = row0 + wm * S::kWM + 32 * i;
+    float* const own_strip = a.own + (int64_t)srow * a.N;
+    const int64_t og_row = (int64_t)d * a.R + srow;
+    float* const og32_strip = static_cast<float*>(a.outgoing) + og_row * a.N;
+    __bf16* const og16_strip = static_cast<__bf16*>(a.outgoing) + og_row * a.N;
 #pragma unroll
     for (int q = 0; q < 32 / kRowsPerStore; ++q) {
       const int r = q * kRowsPerStore + rsub;
       const f32x4 v = *reinterpret_cast<const f32x4*>(wbuf + r * kPitch + csub * 4);
-      const int prow = row0 + wm * S::kWM + 32 * i + r;
-      if (prow >= a.R || !col_ok) continue;
-      const int64_t e = (int64_t)prow * a.N;
-      if (local) {
-        *reinterpret_cast<f32x4*>(own_base + e) = v;
-      } else if (a.outgoing_f32) {
-        *reinterpret_cast<f32x4*>(static_cast<float*>(a.outgoing) + og_base + e) = v;
+      if (srow + r >= a.R || !col_ok) continue;
+      const int e = r * a.N + col;  // element offset inside the strip
+      if (local || a.outgoing_f32) {
+        float* const base = local ? own_strip : og32_strip;
+        if (coherent)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v),
+                                                 rsrc_of(base, strip_bytes), e * 4, 0, kCoherent);
+        else
+          *reinterpret_cast<f32x4*>(base + e) = v;
       } else {
         bf16x4 h;
         h[0] = static_cast<__bf16>(v[0]);
         h[1] = static_cast<__bf16>(v[1]);
         h[2] = static_cast<__bf16>(v[2]);
         h[3] = static_cast<__bf16>(v[3]);
-        *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(a.outgoing) + og_base + e) = h;
+        if (coherent)
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h),
+                                                rsrc_of(og16_strip, strip_bytes), e * 2, 0,
+                                                kCoherent);
+        else
+          *reinterpret_cast<bf16x4*>(og16_strip + e) = h;
       }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // strip read back before the next overwrites it
@@ -303,15 +333,14 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
   }
 
   // Publish (Sec. 4.2): all stores of the block, then the tiles' flags.  The
-  // workgroup barrier waits until every wave's stores are acknowledged; one
-  // agent-scope release fence by thread 0 then writes the block's data back
-  // from this XCD's L2 so that a consumer on any XCD sees it, and thread 0
-  // stores the covered tiles' flags.  Data that no kernel on this device
+  // workgroup barrier waits until every wave's stores are acknowledged (its
+  // workgroup-scope fence waits for vmcnt 0), and the released tiles' stores
+  // were device-coherent, so their data is visible device-wide before thread
+  // 0 stores the covered tiles' flags.  Data that no kernel on this device
   // reads (contributions bound for peers) only needs its flags as progress
   // markers unless every tile is to be released (publish == 2).
   __syncthreads();
   if (a.publish != 0 && tid == 0) {
-    if (local || a.publish == 2) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
     const int sub_m = BM / a.tm, sub_n = BN / a.tn;
     const int vm = min(sub_m, a.Rt - br * sub_m);
     const int vn = min(sub_n, a.Ct - bc * sub_n);

@@ -54,14 +54,19 @@ struct Raw8<true> {
 
 template <bool F32>
 __device__ __forceinline__ Raw8<F32> load_raw8(const void* base, int64_t e);
+// Every input element is read exactly once: nontemporal (streaming) loads
+// keep the partials from displacing the concurrent GEMM's operands in the
+// caches.
 template <>
 __device__ __forceinline__ Raw8<false> load_raw8<false>(const void* base, int64_t e) {
-  return Raw8<false>{*reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + e)};
+  return Raw8<false>{__builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + e))};
 }
 template <>
 __device__ __forceinline__ Raw8<true> load_raw8<true>(const void* base, int64_t e) {
   const float* p = static_cast<const float*>(base) + e;
-  return Raw8<true>{*reinterpret_cast<const f32x4*>(p), *reinterpret_cast<const f32x4*>(p + 4)};
+  return Raw8<true>{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+                    __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
 }
 
 // bf16 -> fp32 is exact: the bf16 bits are the upper half of the binary32.
