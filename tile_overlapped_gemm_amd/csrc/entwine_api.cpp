@@ -163,7 +163,7 @@ int get_workspace(Workspace** out) {
   HIP_TRY(hipMalloc(&w->error, sizeof(int32_t)));
   HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
   // The first call's epoch is 1: freshly allocated flags hold 0.
-  const uint32_t ctl_init[kCtlWords] = {1, 0, 0, 0};
+  const uint32_t ctl_init[kCtlWords] = {1, 0, 0, 0};  // epoch 1, count 0
   HIP_TRY(hipMalloc(&w->ctl, sizeof ctl_init));
   HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
   *out = w.get();
@@ -503,6 +503,10 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                                                         (int64_t)8 * w->cus));
   } else {
     ga.publish = rs.publish_all ? 2 : 1;
+    // Flags of peer-bound tiles are read by symmetric-peer and release-group
+    // waits only.
+    ga.flag_all = rs.publish_all || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
+                  rs.release_group != ENTWINE_RELEASE_TILE;
     ra.slabs = rs.slabs ? rs.slabs : 1;
     ra.ntasks = (int32_t)(g.Q * ra.slabs);
     grid = (int)std::min<int64_t>(rs.budget, ra.ntasks);  // x, capped by the task count
@@ -671,7 +675,12 @@ int entwine_device_status(void* stream) {
   int32_t err = 0;
   HIP_TRY(hipMemcpy(&err, w->error, sizeof err, hipMemcpyDeviceToHost));
   if (err != 0) {
+    // An aborted reduction advanced the epoch while GEMM blocks may still
+    // have been publishing; with every stream idle, start the flags afresh.
+    const uint32_t ctl_init[kCtlWords] = {1, 0, 0, 0};
     HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
+    if (w->flags) HIP_TRY(hipMemset(w->flags, 0, w->flag_count * sizeof(uint32_t)));
+    HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
     return fail(err, "a reduction workgroup timed out waiting for a tile flag");
   }
   return ENTWINE_OK;

@@ -336,19 +336,19 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
   // workgroup barrier waits until every wave's stores are acknowledged (its
   // workgroup-scope fence waits for vmcnt 0), and the released tiles' stores
   // were device-coherent, so their data is visible device-wide before thread
-  // 0 stores the covered tiles' flags.  Data that no kernel on this device
-  // reads (contributions bound for peers) only needs its flags as progress
-  // markers unless every tile is to be released (publish == 2).
-  __syncthreads();
-  if (a.publish != 0 && tid == 0) {
-    const int sub_m = BM / a.tm, sub_n = BN / a.tn;
-    const int vm = min(sub_m, a.Rt - br * sub_m);
-    const int vn = min(sub_n, a.Ct - bc * sub_n);
-    const uint32_t epoch = a.ctl[kEpoch];
-    uint32_t* f = a.flags + (int64_t)d * a.Q + t_first;
-    for (int t = 0; t < vm * vn; ++t)
-      __hip_atomic_store(f + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    check_out(a.ctl, kGemmDone, epoch);
+  // 0 stores the covered tiles' flags.  Flags of tiles bound for peers only
+  // mark progress; they are stored when some wait reads them (flag_all).
+  if (a.publish != 0 && (local || a.flag_all)) {
+    __syncthreads();
+    if (tid == 0) {
+      const int sub_m = BM / a.tm, sub_n = BN / a.tn;
+      const int vm = min(sub_m, a.Rt - br * sub_m);
+      const int vn = min(sub_n, a.Ct - bc * sub_n);
+      const uint32_t epoch = a.ctl[kEpoch];
+      uint32_t* f = a.flags + (int64_t)d * a.Q + t_first;
+      for (int t = 0; t < vm * vn; ++t)
+        __hip_atomic_store(f + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 

@@ -30,6 +30,7 @@ struct GemmArgs {
   int32_t outgoing_f32;     // outgoing partials in fp32 (else bf16)
   int32_t variant;          // GEMM pipeline variant (0 = default for the shape)
   int32_t publish;          // 0: no flags; 1: release local tiles, mark the rest; 2: release all
+  int32_t flag_all;         // 1: every block stores its flags (else only the local ones)
   uint32_t* ctl;            // device control words (see check_out)
 };
 
@@ -55,26 +56,24 @@ struct ReduceArgs {
 
 // Epochs.  A flag is ready when it equals the call's epoch, which both
 // kernels read from ctl[kEpoch] at run time (so a captured graph replays
-// correctly).  The epoch must not change while any workgroup of the call can
-// still read it, so every workgroup of both kernels checks out when it is
-// done; the last workgroup of a kernel checks the kernel out, and the second
-// kernel to finish advances the epoch (skipping 0, the value of flags never
-// written) and clears the counters for the next call.
-enum { kEpoch = 0, kReduceDone = 1, kGemmDone = 2, kKernelsDone = 3, kCtlWords = 4 };
+// correctly).  The last reduction workgroup to finish advances the epoch
+// (skipping 0, the value of flags never written).  Every tile the reduction
+// reads was published before it finished, so the data dependencies of the
+// call are complete; a GEMM block that publishes later (a tile bound for a
+// peer, whose flag only marks progress) may write the next epoch into its
+// flags, which the next call can only read as progress markers too: the
+// tile's own flag is always a wait slot of its own.
+enum { kEpoch = 0, kReduceDone = 1, kCtlWords = 4 };
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
 
-// Called by one thread per workgroup after the workgroup's last use of the
-// epoch.  `counter` is kReduceDone or kGemmDone.
-__device__ __forceinline__ void check_out(uint32_t* ctl, int counter, uint32_t epoch) {
-  const uint32_t n = __hip_atomic_fetch_add(ctl + counter, 1u, __ATOMIC_RELAXED,
+// Counts this workgroup out of a grid of gridDim.x; the last one resets the
+// count and advances the epoch.
+__device__ __forceinline__ void check_out(uint32_t* ctl, uint32_t epoch) {
+  const uint32_t n = __hip_atomic_fetch_add(ctl + kReduceDone, 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
   if (n + 1 != gridDim.x) return;
-  __hip_atomic_store(ctl + counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  const uint32_t k = __hip_atomic_fetch_add(ctl + kKernelsDone, 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT);
-  if (k + 1 != 2) return;
-  __hip_atomic_store(ctl + kKernelsDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(ctl + kReduceDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

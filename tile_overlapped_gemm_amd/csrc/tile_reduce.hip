@@ -216,7 +216,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
     }
   }
   // Every workgroup, finished or timed out, checks out.
-  if (tid == 0 && !a.nowait) check_out(a.ctl, kReduceDone, epoch);
+  if (tid == 0 && !a.nowait) check_out(a.ctl, epoch);
 }
 
 // The sequential schedule's reduction: no flags; the partition is one flat
