@@ -73,6 +73,18 @@ def traffic_for(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
+def tuned_schedule(w) -> int:
+    """The schedule column of the tuning table's entry for the workload (0 if none)."""
+    with open(os.path.join(ROOT, "tile_overlapped_gemm_amd", "tuning.txt")) as f:
+        for line in f:
+            v = line.split()
+            if not v or v[0].startswith("#"):
+                continue
+            if [int(x) for x in v[:4]] == [w.M, w.N, w.K, w.P] and len(v) >= 11:
+                return int(v[10])
+    return 0
+
+
 def cpu_baseline(w, X, W, target_s: float):
     """The CPU oracle's fp64 partial GEMM on the first S rows of the M-row
     product (S sized so the run takes about target_s seconds), as TFLOP/s."""
@@ -110,6 +122,8 @@ def main() -> int:
     ap.add_argument("--threads", type=int, default=0, help="reduction threads (0: tuning table)")
     ap.add_argument("--slabs", type=int, default=0, help="row slabs per task (0: tuning table)")
     ap.add_argument("--peers", default="preseeded", help="preseeded|symmetric")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "streams", "fused"],
+                    help="overlapped schedule: two streams, one fused kernel, or the tuning table's")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
@@ -160,7 +174,12 @@ def main() -> int:
     pd = [None if p is None else up(p) for p in peers]
     out = torch.empty((w.rows, w.N), dtype=torch.float32 if w.fp32_io else torch.bfloat16,
                       device=dev)
-    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, reducer_threads=args.threads,
+    schedule = {"auto": tog.SCHEDULE_AUTO, "streams": tog.SCHEDULE_STREAMS,
+                "fused": tog.SCHEDULE_FUSED}[args.schedule]
+    if schedule == tog.SCHEDULE_AUTO:
+        schedule = tuned_schedule(w) or tog.SCHEDULE_STREAMS
+    fused = schedule == tog.SCHEDULE_FUSED and args.budget != 0
+    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, reducer_threads=args.threads, schedule=schedule,
                   task_slabs=args.slabs,
                   peer_ready=tog.PEERS_SYMMETRIC if args.peers == "symmetric" else tog.PEERS_PRESEEDED)
     if w.fp32_io:
@@ -227,10 +246,17 @@ def main() -> int:
                        p90_ms=per[(9 * len(per)) // 10])
         return res
 
-    log(f"overlapped step: {args.warmup} warm-up + {args.steps} timed graph replays")
+    log(f"overlapped step ({'fused' if fused else 'two streams'}): {args.warmup} warm-up + "
+        f"{args.steps} timed graph replays")
     ov = timed_graph(lambda: call(budget), args.steps, args.warmup)
     log("sequential step (budget 0): same protocol")
     sq = timed_graph(lambda: call(0), args.steps, args.warmup)
+    other = None
+    if budget != 0:
+        other_cfg = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS if fused
+                                      else tog.SCHEDULE_FUSED))
+        log(f"overlapped step, {'two streams' if fused else 'fused'}: same protocol")
+        other = timed_graph(lambda: call(budget, other_cfg), args.steps, args.warmup)
 
     # Kernels alone: GEMM without flags; the reduction of the workspace's
     # partial, flat (sequential schedule) and tiled at the step's budget.  Ten
@@ -294,6 +320,7 @@ def main() -> int:
                    "block": args.block or "tuning table", "tile": w.tile,
                    "reducer_threads": args.threads or "tuning table",
                    "task_slabs": args.slabs or "tuning table", "peer_ready": args.peers,
+                   "schedule": args.schedule,
                    "launch": "HIP graph replay"},
         "latency_us": ov["ms_per_step"] * 1e3,
         "latency_us_median": ov["median_ms"] * 1e3,
@@ -304,12 +331,20 @@ def main() -> int:
             "latency_us_median": sq["median_ms"] * 1e3,
         },
         "speedup_vs_sequential": sq["ms_per_step"] / ov["ms_per_step"],
+        "schedule": "fused" if fused else "streams",
+        ("streams" if fused else "fused"): None if other is None else {
+            "latency_us": other["ms_per_step"] * 1e3,
+            "latency_us_median": other["median_ms"] * 1e3,
+        },
         "gemm_alone_us": g_alone * 1e3,
         "gemm_alone_tflops": flops / (g_alone * 1e-3) / 1e12,
-        "gemm_in_overlap_us": g_ov * 1e3,
-        "reduce_kernel_in_overlap_us": r_ov * 1e3,
+        # Fused: one kernel does both, so its duration is reported once and the
+        # tail is what it takes beyond the GEMM alone.
+        "gemm_in_overlap_us": None if fused else g_ov * 1e3,
+        "reduce_kernel_in_overlap_us": None if fused else r_ov * 1e3,
+        "fused_kernel_us": g_ov * 1e3 if fused else None,
         "overlap_efficiency": g_alone / ov["ms_per_step"],
-        "tail_us": (ov["ms_per_step"] - g_ov) * 1e3,
+        "tail_us": ((g_ov - g_alone) if fused else (ov["ms_per_step"] - g_ov)) * 1e3,
         "reducer": {
             "bytes": red_bytes,
             "flat_warm_us": r_flat * 1e3,
@@ -323,8 +358,9 @@ def main() -> int:
         },
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                     "traffic": traffic_for(w.name, "gemm_publish"),
-                     "kernel": "gemm_publish_kernel (inside the overlapped step)",
+                     "traffic": traffic_for(w.name, "gemm_rs_fused" if fused else "gemm_publish"),
+                     "kernel": ("gemm_rs_fused_kernel (the whole step: GEMM and reduction)"
+                                if fused else "gemm_publish_kernel (inside the overlapped step)"),
                      "kernel_us": g_ov * 1e3,
                      "algorithmic_flops_per_launch": flops},
     }

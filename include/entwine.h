@@ -93,6 +93,19 @@ enum {
 
 enum { ENTWINE_STAGES_ALL = 0, ENTWINE_STAGES_GEMM = 1, ENTWINE_STAGES_REDUCE = 2 };
 
+/* How an overlapped call (comm_budget >= 1) runs producer and consumer:
+ *  STREAMS  two kernels on two internal streams forked from and joined back
+ *           to the caller's stream (Sec. 4.3): the GEMM, and x persistent
+ *           reduction workgroups that poll the tiles' flags concurrently.
+ *  FUSED    one kernel on the caller's stream.  Its workgroups take GEMM
+ *           blocks (in the same production order, with the same per-tile
+ *           flags) until every block is taken; then at most x of them take
+ *           reduction tasks in production order.  No fork or join.
+ *  AUTO     the tuning table's choice for the shape, else STREAMS.
+ * Both give bit-identical output.  The sequential schedule (comm_budget 0)
+ * and single stages ignore this field. */
+enum { ENTWINE_SCHEDULE_AUTO = 0, ENTWINE_SCHEDULE_STREAMS = 1, ENTWINE_SCHEDULE_FUSED = 2 };
+
 /* Release granularity (Sec. 5.3.2): tiles released together. */
 #define ENTWINE_RELEASE_TILE 1       /* each tile on its own flag (the method) */
 #define ENTWINE_RELEASE_PARTITION 0  /* a tile waits for the last tile of its partition */
@@ -163,7 +176,9 @@ typedef struct entwine_config {
                               holds, with every flag treated as ready; the budget picks the
                               schedule as usual).  A single stage leaves `out` (GEMM) or the
                               partials (reduction) as they were: for timing only. */
-  int32_t reserved[3];
+  int32_t schedule;        /* ENTWINE_SCHEDULE_*; FUSED is built for the variant-0 pipelines
+                              of every block shape and variant 3 of 256x256 */
+  int32_t reserved[2];
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);
@@ -217,6 +232,17 @@ int entwine_plan_waits(int64_t M, int64_t N, int P, int rank, int tile_order, in
                        int block_n, int tile_m, int tile_n, int peer_ready, int release_group,
                        int32_t* waits, int64_t capacity);
 
+/* The fused schedule's task order (Sec. 3.1 "Matching task order"): task
+ * k = tile * task_slabs + slab of partition `rank`, sorted by the dispatch
+ * index of the last GEMM block it waits for (its own tile's block, and under
+ * SYMMETRIC peers or release groups the blocks standing for the other flags
+ * of its wait slots), ties by task number.  Dispatch as entwine_plan_dispatch
+ * with `window`.  `capacity` = int32 elements available (>= Q * task_slabs). */
+int entwine_plan_task_order(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                            int block_n, int tile_m, int tile_n, int peer_ready,
+                            int release_group, int64_t window, int task_slabs,
+                            int32_t* task_order, int64_t capacity);
+
 /* Consumer j's task sequence j, j+x, j+2x, ... < Q (Sec. 3.1 "Matching task
  * order") with x = min(comm_budget, Q).  Writes at most `capacity` entries
  * and stores the sequence length in *count. */
@@ -229,7 +255,10 @@ int entwine_plan_tasks(int64_t Q, int comm_budget, int consumer, int32_t* tasks,
 
 /* Synchronizes `stream`, then returns and clears the sticky device error of
  * the current device (ENTWINE_ERR_TIMEOUT if a reduction workgroup's
- * watchdog fired since the last query, else ENTWINE_OK). */
+ * watchdog fired since the last query, else ENTWINE_OK).  While the error is
+ * set, reduction workgroups stop waiting for flags, so the output of the
+ * failed call and of any later call is undefined until this query has
+ * returned the error; the query also clears the flags and the epoch. */
 int entwine_device_status(void* stream);
 
 const char* entwine_status_string(int status);
@@ -243,13 +272,14 @@ int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* 
 /* Per-kernel timing with HIP events recorded on the stream each kernel is
  * launched on.  entwine_timing(1) starts recording every call; reading
  * synchronizes the recorded events and returns the summed kernel durations
- * (ms) and the number of calls since the last read. */
+ * (ms) and the number of calls since the last read.  Under the FUSED
+ * schedule both durations are the fused kernel's. */
 int entwine_timing(int enable);
 int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls);
 
 /* Load an offline tuning table (text; one entry per line:
  * "M N K_local P tile_order comm_budget block_m block_n reducer_threads
- * [task_slabs]", '#' starts a comment line).  Entries are consulted by the
+ * [task_slabs [schedule]]", '#' starts a comment line).  Entries are consulted by the
  * AUTO settings (tile_order -1, comm_budget -1, zero config fields). */
 int entwine_load_tuning(const char* path);
 

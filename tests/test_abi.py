@@ -96,6 +96,8 @@ def test_validation_before_any_device_call(lib, kw, status):
     ("release_group", -2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("task_slabs", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("publish_all", 2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("schedule", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("schedule", -1, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("struct_size", 4, tog.ENTWINE_ERR_INVALID_ARGUMENT),
 ])
 def test_config_validation(lib, field, value, status):
@@ -107,10 +109,13 @@ def test_tuning_table_parsing(lib, tmp_path):
     good = tmp_path / "t.txt"
     good.write_text("# M N K P order budget bm bn threads\n4096 4096 1792 8 2 32 256 128 256\n")
     tog.entwine_load_tuning(str(good))
+    good.write_text("4096 4096 1792 8 2 32 256 128 256 4 2\n")  # with slabs and schedule
+    tog.entwine_load_tuning(str(good))
     bad = tmp_path / "b.txt"
-    bad.write_text("4096 4096 1792 8 2\n")
-    with pytest.raises(tog.EntwineError):
-        tog.entwine_load_tuning(str(bad))
+    for text in ("4096 4096 1792 8 2\n", "4096 4096 1792 8 2 32 256 128 256 4 7\n"):
+        bad.write_text(text)
+        with pytest.raises(tog.EntwineError):
+            tog.entwine_load_tuning(str(bad))
     with pytest.raises(tog.EntwineError):
         tog.entwine_load_tuning(str(tmp_path / "missing.txt"))
     empty = tmp_path / "e.txt"

@@ -35,8 +35,12 @@ def test_full_size_sampled_parity(w):
     out = case.run(tog.ORDER_AUTO, tog.BUDGET_AUTO)
     print(f"workload {w.name}: sequential run", flush=True)
     seq = case.run(tog.ORDER_AUTO, tog.BUDGET_SEQUENTIAL)
-    assert torch.equal(out.view(torch.int16) if out.dtype == torch.bfloat16 else out,
-                       seq.view(torch.int16) if seq.dtype == torch.bfloat16 else seq)
+    bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t  # noqa: E731
+    assert torch.equal(bits(out), bits(seq))
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
+        print(f"workload {w.name}: overlapped run (AUTO), schedule {sched}", flush=True)
+        assert torch.equal(bits(case.run(tog.ORDER_AUTO, tog.BUDGET_AUTO, schedule=sched)),
+                           bits(seq))
     got = down(out)
     worst = 0.0
     for r in sample_rows(w.rows):

@@ -13,7 +13,8 @@ from gpu_util import device, down, up
 pytestmark = pytest.mark.gpu
 
 
-def test_graph_replays_match_eager():
+@pytest.mark.parametrize("sched", [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED])
+def test_graph_replays_match_eager(sched):
     dev = device()
     w = wl.custom("graph", 2048, 1536, 512, 4, rank=2, index=320)
     Xa, W = wl.operands(w)
@@ -21,7 +22,7 @@ def test_graph_replays_match_eager():
     peers = wl.peer_partials(w)
     Wd = up(W, dev)
     pd = [None if p is None else up(p, dev) for p in peers]
-    cfg = tog.config(block_m=256, block_n=128)
+    cfg = tog.config(block_m=256, block_n=128, schedule=sched)
     srcs = [up(Xa, dev), up(Xb, dev)]
     X = srcs[0].clone()
 

@@ -2,9 +2,9 @@
 
 Bar: |out - ref| <= 1e-2 * max(1, |ref|) element by element against the fp64
 oracle; bit-identical output across production orders, budgets (sequential
-included), reducer thread counts, peer-readiness modes and release groups;
-bit-exact on integer inputs; bit-exact reduction given the device's own fp32
-partial.
+included), schedules (two streams or one fused kernel), reducer thread
+counts, peer-readiness modes and release groups; bit-exact on integer
+inputs; bit-exact reduction given the device's own fp32 partial.
 """
 import numpy as np
 import pytest
@@ -25,6 +25,12 @@ SMALL = [
     wl.BY_NAME["tiny"],                                              # fp32 peers/out, 64x64 tiles
 ]
 BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256)]
+SCHEDULES = [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED]
+
+
+def fused_built(bm, bn, variant):
+    """The fused kernel is built for variant 0 of every shape and variant 3 of 256x256."""
+    return variant == 0 or (bm, bn) == (256, 256)
 
 
 @pytest.fixture(scope="module")
@@ -55,10 +61,13 @@ def test_parity_and_schedule_invariance(dev, w):
             continue
         for variant in (0, 3):
             for order in ORDERS:
-                for budget in (0, 1, 3, min(q, 64)):
-                    print(f"case {w.name} block {bm}x{bn} v{variant} order {order} budget {budget}",
-                          flush=True)
-                    out = down(case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant))
+                for budget, sched in [(b, s) for b in (0, 1, 3, min(q, 64)) for s in SCHEDULES]:
+                    if sched == tog.SCHEDULE_FUSED and (budget == 0 or not fused_built(bm, bn, variant)):
+                        continue
+                    print(f"case {w.name} block {bm}x{bn} v{variant} order {order} budget {budget} "
+                          f"schedule {sched}", flush=True)
+                    out = down(case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant,
+                                        schedule=sched))
                     runs += 1
                     r = err_ratio(out, ref)
                     assert r <= 1.0, f"max err/tol {r:.3f}"
@@ -68,7 +77,7 @@ def test_parity_and_schedule_invariance(dev, w):
                         first[key] = out
                     else:
                         np.testing.assert_array_equal(out, first[key])
-    assert runs >= 2 * 2 * len(ORDERS) * 4
+    assert runs >= 2 * len(ORDERS) * (4 + 3 + 4)  # two shapes: v0 both schedules, v3 streams
 
 
 @pytest.mark.parametrize("w", SMALL[:2], ids=lambda w: w.name)
@@ -93,6 +102,62 @@ def test_reducer_variants_bit_identical(dev, w):
         np.testing.assert_array_equal(out, base)
     out = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
     np.testing.assert_array_equal(out, base)
+
+
+@pytest.mark.parametrize("w", SMALL[:2], ids=lambda w: w.name)
+def test_fused_schedule_variants_bit_identical(dev, w):
+    """The fused kernel under every peer-readiness mode, release group, slab
+    count, budget and publication setting gives the two-stream result."""
+    case, ref = case_for(w, dev)
+    blk = dict(block_m=128, block_n=128)
+    base = down(case.run(tog.ORDER_INTERLEAVED, 4, **blk))
+    fused = dict(schedule=tog.SCHEDULE_FUSED, **blk)
+    for mode in (tog.PEERS_PRESEEDED, tog.PEERS_SYMMETRIC):
+        for order in (tog.ORDER_INTERLEAVED, tog.ORDER_PARTITION_MAJOR, tog.ORDER_COL_MAJOR):
+            for group in (tog.RELEASE_TILE, 3, tog.RELEASE_PARTITION, tog.RELEASE_OUTPUT):
+                print(f"case {w.name} fused mode={mode} order={order} g={group}", flush=True)
+                out = down(case.run(order, 5, peer_ready=mode, release_group=group, **fused))
+                np.testing.assert_array_equal(out, base)
+    for slabs in (1, 2, 8):
+        for budget in (1, 5, 64, 255):
+            budget = min(budget, tog.entwine_device_cus() - 1)
+            out = down(case.run(tog.ORDER_INTERLEAVED, budget, task_slabs=slabs, **fused))
+            np.testing.assert_array_equal(out, base)
+    for publish_all in (0, 1):
+        out = down(case.run(tog.ORDER_ROW_MAJOR, 3, publish_all=publish_all, **fused))
+        np.testing.assert_array_equal(out, base)
+    # the two schedules alternating on one workspace
+    for sched in SCHEDULES * 2:
+        out = down(case.run(tog.ORDER_INTERLEAVED, 6, schedule=sched, **blk))
+        np.testing.assert_array_equal(out, base)
+
+
+def test_fused_many_rounds_bit_identical(dev):
+    """More GEMM blocks than resident workgroups: workgroups take several
+    blocks each (and take blocks from other XCDs' lists) before reducing."""
+    w = wl.custom("rounds", 8192, 4096, 128, 4, rank=3, index=306)
+    X, W = wl.operands(w)
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    blk = dict(block_m=128, block_n=128)
+    seq = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
+    for order in ORDERS:
+        for budget in (1, 16, 200):
+            print(f"case rounds order {order} budget {budget}", flush=True)
+            out = down(case.run(order, budget, schedule=tog.SCHEDULE_FUSED, **blk))
+            np.testing.assert_array_equal(out, seq)
+    got = seq
+    for r in (0, w.rows // 2, w.rows - 1):
+        ref = orc.gemm_rs(X, W, peers, w.P, w.rank, row_begin=r, row_end=r + 1)
+        assert err_ratio(got[r:r + 1], ref) <= 1.0
+
+
+def test_fused_unbuilt_variant_rejected(dev):
+    case, _ = case_for(SMALL[0], dev)
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, 4, schedule=tog.SCHEDULE_FUSED, block_m=256, block_n=256,
+                 gemm_variant=1)
+    assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
 
 
 def test_reducer_that_cannot_share_a_cu_is_rejected(dev):
@@ -183,18 +248,20 @@ def test_repeated_calls_and_release(dev):
     np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 7)), a)
 
 
-def test_watchdog_reports_timeout_then_recovers(dev):
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_watchdog_reports_timeout_then_recovers(dev, sched):
     """A tile whose flag never arrives (forced from the host) makes its
     reduction workgroup give up after the poll timeout; the device status
     reports ENTWINE_ERR_TIMEOUT once, and the next call is correct."""
     w = SMALL[0]
     case, ref = case_for(w, dev)
-    good = down(case.run(tog.ORDER_INTERLEAVED, 4))
-    case.run(tog.ORDER_INTERLEAVED, 4, check_status=False, withhold_tile=3, poll_timeout_ms=20)
+    good = down(case.run(tog.ORDER_INTERLEAVED, 4, schedule=sched))
+    case.run(tog.ORDER_INTERLEAVED, 4, check_status=False, withhold_tile=3, poll_timeout_ms=20,
+             schedule=sched)
     st = tog.entwine_device_status(torch.cuda.current_stream().cuda_stream)
     assert st == tog.ENTWINE_ERR_TIMEOUT
     assert tog.entwine_device_status(torch.cuda.current_stream().cuda_stream) == tog.ENTWINE_OK
-    np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 4)), good)
+    np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 4, schedule=sched)), good)
 
 
 def test_timing_api(dev):
@@ -204,9 +271,10 @@ def test_timing_api(dev):
     tog.entwine_timing(True)
     for b in (0, 4):
         case.run(tog.ORDER_INTERLEAVED, b)
+    case.run(tog.ORDER_INTERLEAVED, 4, schedule=tog.SCHEDULE_FUSED)
     tog.entwine_timing(False)
     g, r, n = tog.entwine_timing_read()
-    assert n == 2 and g > 0 and r > 0
+    assert n == 3 and g > 0 and r > 0
 
 
 def test_budget_at_cu_count_rejected(dev):

@@ -203,3 +203,53 @@ def test_dispatch_panel_counts_mlp():
     for x in range(8):
         assert _panels(blocks, [b for b in range(256) if b % 8 == x], 2) == 18
         assert _panels(blocks, [disp[b] for b in range(256) if b % 8 == x], 2) == 12
+
+
+@pytest.mark.parametrize("shape", SHAPES[:3] + [(4096, 4096, 8, 256, 256, 128, 128)])
+@pytest.mark.parametrize("mode,group", [(tog.PEERS_PRESEEDED, tog.RELEASE_TILE),
+                                        (tog.PEERS_SYMMETRIC, tog.RELEASE_TILE),
+                                        (tog.PEERS_PRESEEDED, 3),
+                                        (tog.PEERS_SYMMETRIC, tog.RELEASE_PARTITION)])
+def test_fused_task_order_follows_production(shape, mode, group):
+    """The fused kernel's tasks: a permutation of tile x slab, each tile's
+    slabs together and in order, tiles sorted by the dispatch index of the
+    last block that their wait slots depend on (ties by tile number)."""
+    M, N, P, bm, bn, tm, tn = shape
+    nb, _, q = tog.entwine_plan_shape(M, N, P, bm, bn, tm, tn)
+    rank = P - 1
+    window = 16
+    for order in ORDERS:
+        blocks = tog.entwine_plan_blocks(M, N, P, rank, order, bm, bn, tm, tn)
+        dispatch = tog.entwine_plan_dispatch(M, N, P, rank, order, bm, bn, tm, tn, window)
+        at = {p: b for b, p in enumerate(dispatch)}
+        pos = {tuple(blocks[p][:3]): p for p in range(nb)}
+        tiles = tog.entwine_plan_tiles(M, N, P, bm, bn, tm, tn)
+        waits = tog.entwine_plan_waits(M, N, P, rank, order, bm, bn, tm, tn, mode, group)
+
+        def ready(t):
+            last = -1
+            for f in waits[t]:
+                if f >= 0:
+                    d, tt = divmod(f, q)
+                    tr, tc = tiles[tt]
+                    last = max(last, at[pos[(d, tr // (bm // tm), tc // (bn // tn))]])
+            return last
+
+        for slabs in (1, 4):
+            got = tog.entwine_plan_task_order(M, N, P, rank, order, bm, bn, tm, tn, mode, group,
+                                              window, slabs)
+            assert sorted(got) == list(range(q * slabs))
+            seq = [got[k] // slabs for k in range(0, len(got), slabs)]
+            for k, t in enumerate(seq):
+                assert got[k * slabs:(k + 1) * slabs] == [t * slabs + s for s in range(slabs)]
+            keys = [(ready(t), t) for t in seq]
+            assert keys == sorted(keys)
+
+
+def test_fused_task_order_errors():
+    with pytest.raises(tog.EntwineError):
+        tog.entwine_plan_task_order(512, 768, 4, 0, tog.ORDER_INTERLEAVED, 128, 256, 128, 128,
+                                    task_slabs=3)
+    with pytest.raises(tog.EntwineError):
+        tog.entwine_plan_task_order(512, 768, 4, 0, tog.ORDER_INTERLEAVED, 128, 256, 128, 128,
+                                    window=-1)

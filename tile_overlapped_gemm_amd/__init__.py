@@ -31,11 +31,13 @@ PEERS_PRESEEDED, PEERS_SYMMETRIC = 0, 1
 W_NK, W_KN = 0, 1
 RELEASE_TILE, RELEASE_PARTITION, RELEASE_OUTPUT = 1, 0, -1
 STAGES_ALL, STAGES_GEMM, STAGES_REDUCE = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_STREAMS, SCHEDULE_FUSED = 0, 1, 2
 
 # Names exported by the library (one per declaration in include/entwine.h).
 EXPORTS = [
     "entwine_gemm_rs", "entwine_config_init", "entwine_gemm_rs_ex", "entwine_plan_shape",
-    "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits", "entwine_plan_tasks",
+    "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
+    "entwine_plan_task_order", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
     "entwine_workspace", "entwine_timing", "entwine_timing_read", "entwine_load_tuning",
     "entwine_release", "entwine_device_cus",
@@ -68,7 +70,8 @@ class entwine_config(ctypes.Structure):
         ("publish_all", ctypes.c_int32),
         ("linear_dispatch", ctypes.c_int32),
         ("stages", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 3),
+        ("schedule", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 2),
     ]
 
 
@@ -102,6 +105,8 @@ def load(path: str = LIB):
         "entwine_plan_dispatch": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, i64, pi32, i64], i32),
         "entwine_plan_tiles": ([i64, i64, i32, i32, i32, i32, i32, pi32, i64], i32),
         "entwine_plan_waits": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32, pi32, i64], i32),
+        "entwine_plan_task_order": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, i32, i32, i64,
+                                     i32, pi32, i64], i32),
         "entwine_plan_tasks": ([i64, i32, i32, pi32, i64, pi64], i32),
         "entwine_device_status": ([vp], i32),
         "entwine_status_string": ([i32], ctypes.c_char_p),
@@ -238,6 +243,19 @@ def entwine_plan_waits(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile
     _check(load().entwine_plan_waits(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
                                      peer_ready, release_group, buf, q * S))
     return [list(buf[t * S:(t + 1) * S]) for t in range(q)]
+
+
+def entwine_plan_task_order(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n,
+                            peer_ready=PEERS_PRESEEDED, release_group=RELEASE_TILE, window=0,
+                            task_slabs=1):
+    """The fused schedule's reduction tasks in the order workgroups take them."""
+    _, _, q = entwine_plan_shape(M, N, P, block_m, block_n, tile_m, tile_n)
+    n = q * task_slabs
+    buf = _i32_array(n)
+    _check(load().entwine_plan_task_order(M, N, P, rank, tile_order, block_m, block_n, tile_m,
+                                          tile_n, peer_ready, release_group, window, task_slabs,
+                                          buf, n))
+    return list(buf[:n])
 
 
 def entwine_plan_tasks(Q, comm_budget, consumer):

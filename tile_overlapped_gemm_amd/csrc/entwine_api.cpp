@@ -61,6 +61,7 @@ struct DevicePlan {
   int32_t* d_blocks = nullptr;
   int32_t* d_tiles = nullptr;
   int32_t* d_waits = nullptr;
+  std::map<int, int32_t*> d_task_order;  // fused schedule, by task_slabs
 };
 
 using PlanKey = std::tuple<int64_t, int64_t, int, int, int, int, int, int, int, int, int, int64_t>;
@@ -93,7 +94,7 @@ struct Workspace {
 };
 
 struct TuneEntry {
-  int order, budget, bm, bn, threads, slabs;
+  int order, budget, bm, bn, threads, slabs, schedule;
 };
 
 std::mutex g_mu;
@@ -106,6 +107,8 @@ void free_plan(DevicePlan* p) {
   if (p->d_tiles) (void)hipFree(p->d_tiles);
   if (p->d_waits) (void)hipFree(p->d_waits);
   p->d_blocks = p->d_tiles = p->d_waits = nullptr;
+  for (auto& kv : p->d_task_order) (void)hipFree(kv.second);
+  p->d_task_order.clear();
 }
 
 void destroy_workspace(Workspace* w) {
@@ -114,6 +117,7 @@ void destroy_workspace(Workspace* w) {
   (void)hipSetDevice(w->device);
   if (w->s_gemm) (void)hipStreamSynchronize(w->s_gemm);
   if (w->s_red) (void)hipStreamSynchronize(w->s_red);
+  if (w->have_prev) (void)hipEventSynchronize(w->ev_red);  // work on a caller's stream
   for (auto& kv : w->plans) free_plan(kv.second.get());
   w->plans.clear();
   for (auto* v : {&w->timing_live, &w->timing_free})
@@ -163,7 +167,7 @@ int get_workspace(Workspace** out) {
   HIP_TRY(hipMalloc(&w->error, sizeof(int32_t)));
   HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
   // The first call's epoch is 1: freshly allocated flags hold 0.
-  const uint32_t ctl_init[kCtlWords] = {1, 0, 0, 0};  // epoch 1, count 0
+  const uint32_t ctl_init[kCtlWords] = {1};  // epoch 1; counters and tickets 0
   HIP_TRY(hipMalloc(&w->ctl, sizeof ctl_init));
   HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
   *out = w.get();
@@ -176,6 +180,9 @@ int ensure(Workspace* w, void** buf, size_t* have, size_t need, bool zero) {
   if (*have >= need && *buf) return ENTWINE_OK;
   HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
+  // The previous eager call's last kernel, which may have run on a caller's
+  // stream.
+  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
   if (*buf) {
     HIP_TRY(hipFree(*buf));
     *buf = nullptr;
@@ -264,7 +271,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch;
+      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch, schedule;
   uint32_t timeout_ms;
 };
 
@@ -312,6 +319,9 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->peer_ready = c.peer_ready;
   r->release_group = c.release_group;
   r->slabs = c.task_slabs ? c.task_slabs : (te ? te->slabs : 1);
+  r->schedule = c.schedule != ENTWINE_SCHEDULE_AUTO
+                    ? c.schedule
+                    : (te && te->schedule ? te->schedule : ENTWINE_SCHEDULE_STREAMS);
   r->publish_all = c.publish_all;
   r->stages = c.stages;
   r->linear_dispatch = c.linear_dispatch;
@@ -326,6 +336,8 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "linear_dispatch must be 0 or 1");
   if (c.stages < ENTWINE_STAGES_ALL || c.stages > ENTWINE_STAGES_REDUCE)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "stages %d out of range", c.stages);
+  if (r->schedule < ENTWINE_SCHEDULE_STREAMS || r->schedule > ENTWINE_SCHEDULE_FUSED)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "schedule %d out of range", r->schedule);
   return ENTWINE_OK;
 }
 
@@ -381,7 +393,16 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                 "comm_budget %d must stay below the device's %d compute units", rs.budget, w->cus);
 
   const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
-  if (!sequential && rs.stages == ENTWINE_STAGES_ALL) {
+  const bool fused = !sequential && rs.stages == ENTWINE_STAGES_ALL &&
+                     rs.schedule == ENTWINE_SCHEDULE_FUSED;
+  int fused_per_cu = 0;
+  if (fused) {
+    fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32);
+    if (fused_per_cu <= 0)
+      return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
+                  "GEMM variant %d", g.bm, g.bn, rs.variant);
+  }
+  if (!sequential && !fused && rs.stages == ENTWINE_STAGES_ALL) {
     // The reduction workgroups wait for GEMM blocks, so a CU holding one
     // must still fit a GEMM block: otherwise reduction workgroups spread
     // over the device could starve the GEMM until the watchdog fires.
@@ -413,8 +434,10 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     // Allocation, upload and synchronization are not allowed while capturing.
     PlanKey key{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, rs.order, rs.peer_ready,
                 rs.release_group, window};
+    auto pit = w->plans.find(key);
     if (w->own_bytes < own_need || w->outgoing_bytes < og_need || w->flag_count * 4 < flag_need ||
-        w->plans.find(key) == w->plans.end())
+        pit == w->plans.end() ||
+        (fused && !pit->second->d_task_order.count(rs.slabs ? rs.slabs : 1)))
       return fail(ENTWINE_ERR_INVALID_ARGUMENT,
                   "the workspace and schedule for this shape must exist before a graph capture: "
                   "make the same call once outside the capture");
@@ -428,6 +451,21 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   DevicePlan* dp = nullptr;
   if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, window, &dp)))
     return rc;
+
+  int32_t* d_task_order = nullptr;
+  if (fused) {
+    const int slabs = rs.slabs ? rs.slabs : 1;
+    auto it = dp->d_task_order.find(slabs);
+    if (it == dp->d_task_order.end()) {
+      const std::vector<int32_t> order = fused_task_order(dp->plan, slabs);
+      HIP_TRY(hipMalloc(&d_task_order, order.size() * sizeof(int32_t)));
+      dp->d_task_order[slabs] = d_task_order;
+      HIP_TRY(hipMemcpy(d_task_order, order.data(), order.size() * sizeof(int32_t),
+                        hipMemcpyHostToDevice));
+    } else {
+      d_task_order = it->second;
+    }
+  }
 
   TimingPair tp{};
   if (g_timing && (rc = take_timing_pair(w, &tp))) return rc;
@@ -474,24 +512,48 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ra.withhold_tile = rs.withhold_tile;
   ra.never_flag = (int32_t)(g.P * g.Q);
 
-  // Fork: both internal streams start after the caller's prior work and after
-  // this workspace's previous eager call.  Inside a capture the graph's own
-  // edges order the work and the capture events are used instead.
-  hipEvent_t ev_fork = capturing ? w->cap_fork : w->ev_fork;
-  hipEvent_t ev_gemm = capturing ? w->cap_gemm : w->ev_gemm;
-  hipEvent_t ev_red = capturing ? w->cap_red : w->ev_red;
-  // The sequential schedule uses the GEMM stream only (a stream that joins a
-  // capture must be joined back, so the idle one stays out of it).
-  HIP_TRY(hipEventRecord(ev_fork, stream));
-  HIP_TRY(hipStreamWaitEvent(w->s_gemm, ev_fork, 0));
-  if (!sequential) HIP_TRY(hipStreamWaitEvent(w->s_red, ev_fork, 0));
-  if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(w->s_gemm, w->ev_red, 0));
+  if (fused) {
+    // One kernel on the caller's stream, after this workspace's previous
+    // eager call (which may have run on other streams).
+    ga.publish = rs.publish_all ? 2 : 1;
+    ga.flag_all = rs.publish_all || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
+                  rs.release_group != ENTWINE_RELEASE_TILE;
+    ra.slabs = rs.slabs ? rs.slabs : 1;
+    ra.ntasks = (int32_t)(g.Q * ra.slabs);
+    FusedArgs fa{};
+    fa.g = ga;
+    fa.r = ra;
+    fa.nb = (int32_t)g.NB;
+    fa.workers = (int32_t)std::min<int64_t>(rs.budget, ra.ntasks);
+    fa.task_order = d_task_order;
+    // Resident workgroups, but no more than there is work for.
+    const int64_t grid =
+        std::min<int64_t>((int64_t)fused_per_cu * w->cus, g.NB + (int64_t)fa.workers);
+    if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+    if (g_timing) {
+      HIP_TRY(hipEventRecord(tp.g0, stream));
+      HIP_TRY(hipEventRecord(tp.r0, stream));
+    }
+    hipError_t e = launch_gemm_rs_fused(fa, g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32,
+                                        (int)grid, stream);
+    if (e != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "fused launch failed: %s", hipGetErrorString(e));
+    if (g_timing) {
+      HIP_TRY(hipEventRecord(tp.g1, stream));
+      HIP_TRY(hipEventRecord(tp.r1, stream));
+      w->timing_live.push_back(tp);
+    }
+    if (!capturing) {
+      HIP_TRY(hipEventRecord(w->ev_red, stream));
+      w->have_prev = true;
+    }
+    return ENTWINE_OK;
+  }
 
   // Sequential schedule (budget 0): the GEMM publishes nothing and the
   // reduction streams the whole partition after the GEMM kernel has ended.
   // Overlapped schedule: the GEMM releases its tiles and x persistent
   // reduction workgroups consume them as they become ready.
-  hipStream_t s_red = sequential ? w->s_gemm : w->s_red;
   int grid;
   if (sequential) {
     ga.publish = 0;
@@ -519,14 +581,34 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     ga.publish = 0;
     ra.nowait = 1;
   }
-  if (g_timing) HIP_TRY(hipEventRecord(tp.g0, w->s_gemm));
+
+  // Kernels that do not run concurrently (the sequential schedule, a single
+  // stage) run on the caller's stream: no fork, no join.  The overlapped
+  // schedule forks both internal streams from the caller's stream and joins
+  // them back.  Either way the work starts after this workspace's previous
+  // eager call.  Inside a capture the graph's own edges order the work and
+  // the capture events are used instead.
+  const bool forked = !sequential && rs.stages == ENTWINE_STAGES_ALL;
+  hipStream_t s_gemm = forked ? w->s_gemm : stream;
+  hipStream_t s_red = forked ? w->s_red : stream;
+  hipEvent_t ev_fork = capturing ? w->cap_fork : w->ev_fork;
+  hipEvent_t ev_gemm = capturing ? w->cap_gemm : w->ev_gemm;
+  hipEvent_t ev_red = capturing ? w->cap_red : w->ev_red;
+  if (forked) {
+    HIP_TRY(hipEventRecord(ev_fork, stream));
+    HIP_TRY(hipStreamWaitEvent(w->s_gemm, ev_fork, 0));
+    HIP_TRY(hipStreamWaitEvent(w->s_red, ev_fork, 0));
+  }
+  if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(s_gemm, w->ev_red, 0));
+
+  if (g_timing) HIP_TRY(hipEventRecord(tp.g0, s_gemm));
   if (run_gemm) {
-    hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, w->s_gemm);
+    hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, s_gemm);
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
   }
-  if (g_timing) HIP_TRY(hipEventRecord(tp.g1, w->s_gemm));
-  HIP_TRY(hipEventRecord(ev_gemm, w->s_gemm));
+  if (g_timing) HIP_TRY(hipEventRecord(tp.g1, s_gemm));
+  if (forked) HIP_TRY(hipEventRecord(ev_gemm, s_gemm));
   if (g_timing) HIP_TRY(hipEventRecord(tp.r0, s_red));
   if (run_red) {
     hipError_t e =
@@ -535,11 +617,13 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
   }
   if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));
-  HIP_TRY(hipEventRecord(ev_red, s_red));
+  if (forked || !capturing) HIP_TRY(hipEventRecord(ev_red, s_red));
   if (!capturing) w->have_prev = true;
-  // Join: the caller's stream continues after both kernels.
-  HIP_TRY(hipStreamWaitEvent(stream, ev_gemm, 0));
-  HIP_TRY(hipStreamWaitEvent(stream, ev_red, 0));
+  if (forked) {
+    // Join: the caller's stream continues after both kernels.
+    HIP_TRY(hipStreamWaitEvent(stream, ev_gemm, 0));
+    HIP_TRY(hipStreamWaitEvent(stream, ev_red, 0));
+  }
   if (g_timing) w->timing_live.push_back(tp);
   return ENTWINE_OK;
 }
@@ -648,6 +732,25 @@ int entwine_plan_waits(int64_t M, int64_t N, int P, int rank, int tile_order, in
   return ENTWINE_OK;
 }
 
+int entwine_plan_task_order(int64_t M, int64_t N, int P, int rank, int tile_order, int block_m,
+                            int block_n, int tile_m, int tile_n, int peer_ready,
+                            int release_group, int64_t window, int task_slabs,
+                            int32_t* task_order, int64_t capacity) {
+  Plan p;
+  int rc = plan_for(M, N, P, rank, tile_order, block_m, block_n, tile_m, tile_n, peer_ready,
+                    release_group, &p);
+  if (rc) return rc;
+  if (window < 0) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "window must be >= 0");
+  if (task_slabs < 1 || tile_m % task_slabs != 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
+  assign_dispatch(&p, window);
+  const std::vector<int32_t> order = fused_task_order(p, task_slabs);
+  if (!task_order || capacity < (int64_t)order.size())
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_order needs %zu entries", order.size());
+  std::copy(order.begin(), order.end(), task_order);
+  return ENTWINE_OK;
+}
+
 int entwine_plan_tasks(int64_t Q, int comm_budget, int consumer, int32_t* tasks, int64_t capacity,
                        int64_t* count) {
   if (Q < 0 || comm_budget < 1 || consumer < 0)
@@ -672,12 +775,13 @@ int entwine_device_status(void* stream) {
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
   HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
   int32_t err = 0;
   HIP_TRY(hipMemcpy(&err, w->error, sizeof err, hipMemcpyDeviceToHost));
   if (err != 0) {
     // An aborted reduction advanced the epoch while GEMM blocks may still
     // have been publishing; with every stream idle, start the flags afresh.
-    const uint32_t ctl_init[kCtlWords] = {1, 0, 0, 0};
+    const uint32_t ctl_init[kCtlWords] = {1};
     HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
     if (w->flags) HIP_TRY(hipMemset(w->flags, 0, w->flag_count * sizeof(uint32_t)));
     HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
@@ -757,15 +861,16 @@ int entwine_load_tuning(const char* path) {
     ++lineno;
     if (line[0] == '#' || line[0] == '\n') continue;
     long long M, N, K;
-    int P, order, budget, bm, bn, threads, slabs = 1;
-    const int n = std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d %d", &M, &N, &K, &P, &order,
-                              &budget, &bm, &bn, &threads, &slabs);
-    if (n != 9 && n != 10) {
+    int P, order, budget, bm, bn, threads, slabs = 1, schedule = ENTWINE_SCHEDULE_AUTO;
+    const int n = std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d %d %d", &M, &N, &K, &P,
+                              &order, &budget, &bm, &bn, &threads, &slabs, &schedule);
+    if (n < 9 || schedule < ENTWINE_SCHEDULE_AUTO || schedule > ENTWINE_SCHEDULE_FUSED) {
       std::fclose(f);
-      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "%s:%d: expected 9 or 10 integers", path, lineno);
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT,
+                  "%s:%d: expected 9 to 11 integers (schedule 0, 1 or 2)", path, lineno);
     }
     table[std::make_tuple((int64_t)M, (int64_t)N, (int64_t)K, P)] =
-        TuneEntry{order, budget, bm, bn, threads, slabs};
+        TuneEntry{order, budget, bm, bn, threads, slabs, schedule};
   }
   std::fclose(f);
   std::lock_guard<std::mutex> lock(g_mu);

@@ -1,0 +1,326 @@
+// gemm_block.h -- device code of one GEMM block with per-tile release,
+// shared by the stand-alone GEMM kernel and the fused GEMM + reduction
+// kernel.
+//
+// Method: "Entwine: Coordinating Tiled Computation and Fine-Grained
+// Communication across GPUs" (paperpeel.com/paper/2609.11562), Sec. 2.1,
+// Sec. 3.1 and Sec. 4.2; the MI355X design is described in gemm_publish.hip.
+#pragma once
+
+#include "kernels.h"
+
+namespace entwine {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+
+// Block BM x BN, K stage BK (32 or 64), NS LDS stages, WGM x WGN waves.
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+struct Shape {
+  static constexpr int kWaves = WGM * WGN;
+  static constexpr int kThreads = 64 * kWaves;
+  static constexpr int kWavesN = WGN;
+  static constexpr int kRow = BK * 2;                 // bytes per slab row
+  static constexpr int kRowsPerLoad = 1024 / kRow;    // rows per 1 KiB wave load
+  static constexpr int kLanesPerRow = kRow / 16;
+  static constexpr int kKS = BK / 16;                 // MFMA K steps per stage
+  static constexpr int kWM = BM / WGM, kWN = BN / WGN;  // wave sub-block
+  static constexpr int kMT = kWM / 32, kNT = kWN / 32;
+  static constexpr int kA = BM * kRow, kB = BN * kRow;  // stage slabs
+  static constexpr int kStage = kA + kB;
+  static constexpr int kLds = NS * kStage;
+  static constexpr int kLoadsA = BM / (kWaves * kRowsPerLoad);  // per wave per stage
+  static constexpr int kLoadsB = BN / (kWaves * kRowsPerLoad);
+  static_assert(kLoadsA * kWaves * kRowsPerLoad == BM && kLoadsB * kWaves * kRowsPerLoad == BN,
+                "slab rows must split evenly over the waves");
+  static_assert(kWaves % 2 == 0, "load groups keep the row parity of the swizzle");
+  static constexpr int kLoads = kLoadsA + kLoadsB;
+  static_assert(kKS % 2 == 0, "fragment double buffer needs an even K-step count");
+  static_assert(kLoads * (NS - 2 > 0 ? NS - 2 : 0) < 64, "vmcnt range");
+};
+
+// XOR swizzle of 16-byte chunks, a function of (row mod 16): every group of
+// 8 (or 16) consecutive fragment rows read at one logical chunk hits distinct
+// LDS banks.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (BK == 64)
+    return (r & 7) ^ ((r >> 3) & 1);
+  else
+    return ((r >> 1) ^ (r >> 3)) & 3;
+}
+
+// Wait until at most VM of this wave's vector-memory operations are pending
+// and all of its LDS reads returned, then synchronize the workgroup.  No
+// global-memory fence: the stage hand-over only needs LDS.
+template <int VM>
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(VM) : "memory");
+}
+
+// Device-coherent global stores (buffer cache policy SC1) through a
+// wave-uniform buffer descriptor; `off` is the lane's byte offset.
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+constexpr int kCoherent = 16;  // SC1
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc_of(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, kRsrcWord3);
+}
+
+__device__ __forceinline__ bf16x8 lds_frag(const char* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+
+// One stage of global->LDS copies for this wave: load group o = wave + 4j of
+// X's slab, then of W's.  voff is the lane's byte offset (row and swizzled
+// chunk); soffset adds the group's rows and the stage's K offset.
+template <class S>
+__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
+                                            char* lds, int voff, int group_step, int kbyte,
+                                            int wave) {
+#pragma unroll
+  for (int j = 0; j < S::kLoadsA; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + S::kWaves * j) * 1024),
+                                             16, voff, j * group_step + kbyte, 0, 0);
+#pragma unroll
+  for (int j = 0; j < S::kLoadsB; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_ptr_t)(lds + S::kA + (wave + S::kWaves * j) * 1024), 16, voff,
+        j * group_step + kbyte, 0, 0);
+}
+
+template <class S>
+struct Frags {
+  bf16x8 b[S::kNT];  // W fragments (MFMA rows = output columns)
+  bf16x8 a[S::kMT];  // X fragments (MFMA cols = output rows)
+};
+
+template <class S>
+__device__ __forceinline__ void read_frags(Frags<S>& f, const char* stage, int a_off, int b_off) {
+#pragma unroll
+  for (int j = 0; j < S::kNT; ++j) f.b[j] = lds_frag(stage + S::kA + b_off + j * 32 * S::kRow);
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i) f.a[i] = lds_frag(stage + a_off + i * 32 * S::kRow);
+}
+
+template <class S>
+struct Acc {
+  f32x16 c[S::kMT][S::kNT];
+};
+
+template <class S>
+__device__ __forceinline__ void mfma_step(Acc<S>& acc, const Frags<S>& f) {
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j)
+      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
+}
+
+// One BM x BN block of C_r = X_r W_r: main loop, epilogue stores and the
+// block's flags.  `blk` = (partition d, block row, block column, first tile);
+// `smem` is the workgroup's S::kLds bytes of LDS.  Every thread of the
+// workgroup calls it; it contains workgroup barriers.
+template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+__device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, char* smem) {
+  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WGN, wn = wave % WGN;
+
+  const int d = blk.x, br = blk.y, bc = blk.z, t_first = blk.w;
+  const int row0 = br * BM;  // within the partition
+  const int col0 = bc * BN;
+  const int K = a.K;
+  const int kbytes = K * 2;
+
+  // Buffer descriptors bound the block's rows: X rows of partition d from
+  // row0, W rows (output columns) from col0.  Out-of-range rows read 0.
+  const int rows_a = min(BM, a.R - row0);
+  const int rows_b = min(BN, a.N - col0);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.X + ((int64_t)d * a.R + row0) * K), (short)0, rows_a * kbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(a.W + (int64_t)col0 * K), (short)0, rows_b * kbytes, kRsrcWord3);
+
+  // Global source of this lane: row wave*RPL + lane/LPR of each group of
+  // kWaves*RPL rows, logical chunk (lane % LPR) ^ swz(row).
+  const int lrow = wave * S::kRowsPerLoad + lane / S::kLanesPerRow;
+  const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK>(lrow);
+  const int voff = lrow * kbytes + lchunk * 16;
+  const int group_step = S::kWaves * S::kRowsPerLoad * kbytes;
+
+  // LDS fragment offsets: MFMA lane l reads row (l & 31) of a 32-row group,
+  // logical chunk 2*ks + (l >> 5).
+  const int frow = lane & 31;
+  const int khalf = lane >> 5;
+  int a_off[S::kKS], b_off[S::kKS];
+#pragma unroll
+  for (int ks = 0; ks < S::kKS; ++ks) {
+    const int c = ((2 * ks + khalf) ^ swz<BK>(frow)) << 4;
+    a_off[ks] = (wm * S::kWM + frow) * S::kRow + c;
+    b_off[ks] = (wn * S::kWN + frow) * S::kRow + c;
+  }
+
+  Acc<S> acc;
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i)
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+
+  // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, then stage NS-1.
+  const int nk = K / BK;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) issue_stage<S>(ra, rb, smem + s * S::kStage, voff, group_step, s * S::kRow, wave);
+  if (nk >= NS - 1)
+    stage_barrier<S::kLoads * (NS - 2)>();
+  else
+    stage_barrier<0>();
+  if (NS - 1 < nk)
+    issue_stage<S>(ra, rb, smem + (NS - 1) * S::kStage, voff, group_step, (NS - 1) * S::kRow,
+                   wave);
+
+  Frags<S> f0, f1;
+  read_frags<S>(f0, smem, a_off[0], b_off[0]);
+
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt % NS;
+    const char* cur = smem + buf * S::kStage;
+#pragma unroll
+    for (int ks = 0; ks + 1 < S::kKS; ks += 2) {
+      read_frags<S>(f1, cur, a_off[ks + 1], b_off[ks + 1]);
+      mfma_step<S>(acc, f0);
+      if (ks + 2 < S::kKS) {
+        read_frags<S>(f0, cur, a_off[ks + 2], b_off[ks + 2]);
+        mfma_step<S>(acc, f1);
+      }
+    }
+    if (kt + 1 < nk) {
+      // Stage kt+1 must have landed (stages up to kt+NS-1 were issued), and
+      // every wave must be done reading `cur`, which then takes stage kt+NS.
+      if (kt + NS - 1 < nk)
+        stage_barrier<S::kLoads * (NS - 2)>();
+      else
+        stage_barrier<0>();
+      if (kt + NS < nk)
+        issue_stage<S>(ra, rb, smem + buf * S::kStage, voff, group_step, (kt + NS) * S::kRow,
+                       wave);
+      read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, a_off[0], b_off[0]);
+    }
+    mfma_step<S>(acc, f1);
+  }
+
+  // Epilogue.  With the W fragment as the MFMA's row operand, accumulator
+  // element v of lane l holds output row (l & 31) of its 32 x 32 tile and
+  // columns 8*(v/4) + 4*(l/32) + v%4.  Each 32-row strip of the wave's
+  // sub-block is staged through the wave's own LDS area (rows padded by 16
+  // bytes so the transposed writes spread over the banks) and read back
+  // row-contiguous, so every global store instruction covers whole 128-byte
+  // lines: 16-byte fp32 stores for the local partition, 8-byte bf16 (or
+  // 16-byte fp32) stores for the outgoing contributions.
+  //
+  // Tiles that are released to a consumer are written with device-coherent
+  // stores (cache policy SC1, the encoding of a relaxed agent-scope atomic
+  // store): the data is written through this XCD's L2, so once a store is
+  // acknowledged a reader on any XCD sees it and the release needs no
+  // write-back of the whole L2.
+  constexpr int kPitch = S::kWN * 4 + 16;
+  constexpr int kLanesPerRow = S::kWN / 4;
+  constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  static_assert(S::kWaves * 32 * kPitch <= S::kLds, "epilogue staging exceeds LDS");
+  __syncthreads();  // every wave is done with the pipeline buffers
+  char* wbuf = smem + wave * 32 * kPitch;
+  const bool local = (d == a.rank);
+  const int rsub = lane / kLanesPerRow;
+  const int csub = (lane % kLanesPerRow) * 4;
+  const int col = col0 + wn * S::kWN + csub;
+  const bool col_ok = col < a.N;
+  const bool coherent = local ? a.publish != 0 : a.publish == 2;
+  const int strip_bytes = 32 * a.N * (local || a.outgoing_f32 ? 4 : 2);
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i) {
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        f32x4 v;
+        v[0] = acc.c[i][j][4 * g + 0];
+        v[1] = acc.c[i][j][4 * g + 1];
+        v[2] = acc.c[i][j][4 * g + 2];
+        v[3] = acc.c[i][j][4 * g + 3];
+        *reinterpret_cast<f32x4*>(wbuf + frow * kPitch + (32 * j + 8 * g + 4 * khalf) * 4) = v;
+      }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the strip is in LDS
+    __builtin_amdgcn_wave_barrier();
+    // The strip's first row (wave-uniform) in the partition, and the output
+    // it lands in: the fp32 local partial or the outgoing contributions.
+    const int srow = row0 + wm * S::kWM + 32 * i;
+    float* const own_strip = a.own + (int64_t)srow * a.N;
+    const int64_t og_row = (int64_t)d * a.R + srow;
+    float* const og32_strip = static_cast<float*>(a.outgoing) + og_row * a.N;
+    __bf16* const og16_strip = static_cast<__bf16*>(a.outgoing) + og_row * a.N;
+#pragma unroll
+    for (int q = 0; q < 32 / kRowsPerStore; ++q) {
+      const int r = q * kRowsPerStore + rsub;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(wbuf + r * kPitch + csub * 4);
+      if (srow + r >= a.R || !col_ok) continue;
+      const int e = r * a.N + col;  // element offset inside the strip
+      if (local || a.outgoing_f32) {
+        float* const base = local ? own_strip : og32_strip;
+        if (coherent)
+          __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v),
+                                                 rsrc_of(base, strip_bytes), e * 4, 0, kCoherent);
+        else
+          *reinterpret_cast<f32x4*>(base + e) = v;
+      } else {
+        bf16x4 h;
+        h[0] = static_cast<__bf16>(v[0]);
+        h[1] = static_cast<__bf16>(v[1]);
+        h[2] = static_cast<__bf16>(v[2]);
+        h[3] = static_cast<__bf16>(v[3]);
+        if (coherent)
+          __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, h),
+                                                rsrc_of(og16_strip, strip_bytes), e * 2, 0,
+                                                kCoherent);
+        else
+          *reinterpret_cast<bf16x4*>(og16_strip + e) = h;
+      }
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // strip read back before the next overwrites it
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // Publish (Sec. 4.2): all stores of the block, then the tiles' flags.  The
+  // workgroup barrier waits until every wave's stores are acknowledged (its
+  // workgroup-scope fence waits for vmcnt 0), and the released tiles' stores
+  // were device-coherent, so their data is visible device-wide before thread
+  // 0 stores the covered tiles' flags.  Flags of tiles bound for peers only
+  // mark progress; they are stored when some wait reads them (flag_all).
+  if (a.publish != 0 && (local || a.flag_all)) {
+    __syncthreads();
+    if (tid == 0) {
+      const int sub_m = BM / a.tm, sub_n = BN / a.tn;
+      const int vm = min(sub_m, a.Rt - br * sub_m);
+      const int vn = min(sub_n, a.Ct - bc * sub_n);
+      const uint32_t epoch = a.ctl[kEpoch];
+      uint32_t* f = a.flags + (int64_t)d * a.Q + t_first;
+      for (int t = 0; t < vm * vn; ++t)
+        __hip_atomic_store(f + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace
+}  // namespace entwine

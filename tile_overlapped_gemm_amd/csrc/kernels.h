@@ -63,7 +63,23 @@ struct ReduceArgs {
 // peer, whose flag only marks progress) may write the next epoch into its
 // flags, which the next call can only read as progress markers too: the
 // tile's own flag is always a wait slot of its own.
-enum { kEpoch = 0, kReduceDone = 1, kCtlWords = 4 };
+//
+// The fused kernel (GEMM blocks and reduction tasks taken from tickets) keeps
+// its tickets and its own check-out count in further control words; its
+// last workgroup clears them and advances the epoch.  Every counter that many
+// workgroups update has a 128-byte line of its own: atomics to one line are
+// serialized, and with the eight block tickets in one line a multi-round
+// 768-block GEMM ran 30 % slower.
+enum {
+  kLine = 32,  // control words per 128-byte line
+  kEpoch = 0,
+  kReduceDone = 1 * kLine,
+  kFusedDone = 2 * kLine,
+  kWorkerTicket = 3 * kLine,
+  kTaskTicket = 4 * kLine,
+  kBlockTicket = 5 * kLine,  // ticket of XCD y at kBlockTicket + y * kLine
+  kCtlWords = 13 * kLine
+};
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
 
@@ -76,6 +92,18 @@ __device__ __forceinline__ void check_out(uint32_t* ctl, uint32_t epoch) {
   __hip_atomic_store(ctl + kReduceDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+
+// The fused schedule: one kernel on the caller's stream.  Its workgroups take
+// GEMM blocks from per-XCD lists (block b of the dispatch order belongs to
+// XCD b % 8) until all are taken, then up to `workers` of them take reduction
+// tasks in `task_order`.
+struct FusedArgs {
+  GemmArgs g;
+  ReduceArgs r;
+  int32_t nb;                 // GEMM blocks
+  int32_t workers;            // workgroups that may reduce (the comm budget)
+  const int32_t* task_order;  // [r.ntasks]: task ids in production order
+};
 
 // GEMM block shapes built: (bm, bn) in {128, 256}^2.
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
@@ -94,5 +122,12 @@ int gemm_blocks_per_cu(int bm, int bn, int variant);
 // Waves per GEMM workgroup (64 lanes each).
 int gemm_waves(int bm, int bn, int variant);
 int reduce_registers(int threads, int peer_f32, int out_f32);
+
+// Fused kernel instances: the variant-0 pipelines of every block shape and
+// variant 3 of 256 x 256.  Returns hipErrorInvalidValue for other shapes.
+hipError_t launch_gemm_rs_fused(const FusedArgs& a, int bm, int bn, int variant, int peer_f32,
+                                int out_f32, int grid, hipStream_t stream);
+// Fused workgroups resident per CU (0 if the instance is not built).
+int fused_blocks_per_cu(int bm, int bn, int variant, int peer_f32, int out_f32);
 
 }  // namespace entwine

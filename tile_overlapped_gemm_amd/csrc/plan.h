@@ -67,4 +67,10 @@ int build_plan(const Geometry& g, int rank, int order, int peer_ready, int relea
 constexpr int kXcds = 8;
 void assign_dispatch(Plan* plan, int64_t window);
 
+// The fused schedule's task order (Sec. 3.1 "Matching task order"): tasks
+// t * slabs + s of the rank's partition, sorted by the dispatch index of the
+// last block any of the tile's wait slots depends on, ties by task number.
+// Needs plan->dispatch (assign_dispatch).
+std::vector<int32_t> fused_task_order(const Plan& plan, int slabs);
+
 }  // namespace entwine

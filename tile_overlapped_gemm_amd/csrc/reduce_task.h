@@ -1,0 +1,189 @@
+// reduce_task.h -- device code of one reduction task (wait for its flags,
+// then local + peers in rank order), shared by the persistent reduction
+// kernel and the fused GEMM + reduction kernel.
+//
+// Method: "Entwine: Coordinating Tiled Computation and Fine-Grained
+// Communication across GPUs" (paperpeel.com/paper/2609.11562), Sec. 4.2
+// (Consumer); the MI355X design is described in tile_reduce.hip.
+#pragma once
+
+#include "kernels.h"
+
+namespace entwine {
+namespace {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+struct F8 {
+  float v[8];
+};
+
+// Raw chunk of 8 elements: 16 bytes of bf16 or 32 bytes of fp32.
+template <bool F32>
+struct Raw8;
+template <>
+struct Raw8<false> {
+  u32x4 w;
+};
+template <>
+struct Raw8<true> {
+  f32x4 a, b;
+};
+
+template <bool F32>
+__device__ __forceinline__ Raw8<F32> load_raw8(const void* base, int64_t e);
+// Every input element is read exactly once: nontemporal (streaming) loads
+// keep the partials from displacing the concurrent GEMM's operands in the
+// caches.
+template <>
+__device__ __forceinline__ Raw8<false> load_raw8<false>(const void* base, int64_t e) {
+  return Raw8<false>{__builtin_nontemporal_load(
+      reinterpret_cast<const u32x4*>(static_cast<const uint16_t*>(base) + e))};
+}
+template <>
+__device__ __forceinline__ Raw8<true> load_raw8<true>(const void* base, int64_t e) {
+  const float* p = static_cast<const float*>(base) + e;
+  return Raw8<true>{__builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p)),
+                    __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
+}
+
+// bf16 -> fp32 is exact: the bf16 bits are the upper half of the binary32.
+__device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ F8 widen(const Raw8<true>& r) {
+  F8 f;
+  f.v[0] = r.a[0]; f.v[1] = r.a[1]; f.v[2] = r.a[2]; f.v[3] = r.a[3];
+  f.v[4] = r.b[0]; f.v[5] = r.b[1]; f.v[6] = r.b[2]; f.v[7] = r.b[3];
+  return f;
+}
+
+__device__ __forceinline__ void add8(F8& acc, const Raw8<false>& r) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    acc.v[2 * i] += lo_bf16(r.w[i]);
+    acc.v[2 * i + 1] += hi_bf16(r.w[i]);
+  }
+}
+__device__ __forceinline__ void add8(F8& acc, const Raw8<true>& r) {
+  acc.v[0] += r.a[0]; acc.v[1] += r.a[1]; acc.v[2] += r.a[2]; acc.v[3] += r.a[3];
+  acc.v[4] += r.b[0]; acc.v[5] += r.b[1]; acc.v[6] += r.b[2]; acc.v[7] += r.b[3];
+}
+
+// fp32 -> bf16, round to nearest even (the hardware conversion on gfx950).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const __bf16 l = static_cast<__bf16>(lo);
+  const __bf16 h = static_cast<__bf16>(hi);
+  return (uint32_t)__builtin_bit_cast(uint16_t, l) |
+         ((uint32_t)__builtin_bit_cast(uint16_t, h) << 16);
+}
+
+template <bool F32>
+__device__ __forceinline__ void store8(void* base, int64_t e, const F8& acc);
+template <>
+__device__ __forceinline__ void store8<false>(void* base, int64_t e, const F8& acc) {
+  u32x4 o;
+  o[0] = pack_bf16x2(acc.v[0], acc.v[1]);
+  o[1] = pack_bf16x2(acc.v[2], acc.v[3]);
+  o[2] = pack_bf16x2(acc.v[4], acc.v[5]);
+  o[3] = pack_bf16x2(acc.v[6], acc.v[7]);
+  *reinterpret_cast<u32x4*>(static_cast<uint16_t*>(base) + e) = o;
+}
+template <>
+__device__ __forceinline__ void store8<true>(void* base, int64_t e, const F8& acc) {
+  float* p = static_cast<float*>(base) + e;
+  f32x4 lo, hi;
+  lo[0] = acc.v[0]; lo[1] = acc.v[1]; lo[2] = acc.v[2]; lo[3] = acc.v[3];
+  hi[0] = acc.v[4]; hi[1] = acc.v[5]; hi[2] = acc.v[6]; hi[3] = acc.v[7];
+  *reinterpret_cast<f32x4*>(p) = lo;
+  *reinterpret_cast<f32x4*>(p + 4) = hi;
+}
+
+// Reduce U chunks at element offsets e[0..U): all loads first, then the
+// fixed-order fp32 sums, then the stores.  ok[u] masks chunks past the end.
+template <int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t (&e)[U],
+                                              const bool (&ok)[U]) {
+  Raw8<true> own[U];
+  Raw8<PEER_F32> pv[U][kMaxRanks];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!ok[u]) continue;
+    own[u] = load_raw8<true>(a.own, e[u]);
+#pragma unroll
+    for (int q = 0; q < kMaxRanks; ++q)
+      if (q < a.P && q != a.rank) pv[u][q] = load_raw8<PEER_F32>(a.peers[q], e[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!ok[u]) continue;
+    F8 acc = widen(own[u]);
+#pragma unroll
+    for (int q = 0; q < kMaxRanks; ++q)
+      if (q < a.P && q != a.rank) add8(acc, pv[u][q]);
+    store8<OUT_F32>(a.out, e[u], acc);
+  }
+}
+
+// Wave 0 waits until every flag that task tile t depends on equals `epoch`.
+// Lane k (< P + 1) watches wait slot k.  Returns false (uniform across the
+// wave) if the watchdog expired, or if the sticky error word is set: once one
+// workgroup has timed out, the others stop waiting too, so a failed call ends
+// within one timeout whatever its task count.
+__device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int t, int lane) {
+  int32_t idx = -1;
+  if (lane < a.wait_slots) idx = a.waits[t * a.wait_slots + lane];
+  if (t == a.withhold_tile && lane == a.rank) idx = a.never_flag;
+  const uint32_t* f = idx >= 0 ? a.flags + idx : nullptr;
+  const uint64_t start = wall_clock64();
+  while (true) {
+    bool ready = true;
+    if (f) ready = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
+    if (__all(ready)) break;
+    if (__builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+      return false;
+    if (wall_clock64() - start > a.timeout_ticks) {
+      if (lane == 0)
+        __hip_atomic_store(a.error, (int32_t)5 /* ENTWINE_ERR_TIMEOUT */, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+  // One acquire per task: later reads of the tile see the producers' stores.
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  return true;
+}
+
+constexpr int kUnroll = 2;
+
+// Reduce row slab `slab` of task tile t: thread tid of THREADS takes chunks
+// tid, tid + THREADS, ... of the slab (8 elements each).
+template <int THREADS, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void reduce_slab(const ReduceArgs& a, int t, int slab, int tid) {
+  const int chunks_per_row = a.tn >> 3;
+  const int slab_rows = a.tm / a.slabs;
+  const int row0 = a.tiles[2 * t] * a.tm + slab * slab_rows;
+  const int col0 = a.tiles[2 * t + 1] * a.tn;
+  const int rows = min(slab_rows, a.R - row0);
+  const int cols = min(a.tn, a.N - col0);
+  const int n_chunks = rows > 0 ? rows * chunks_per_row : 0;
+  for (int c0 = tid; c0 < n_chunks; c0 += kUnroll * THREADS) {
+    int64_t e[kUnroll];
+    bool ok[kUnroll];
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const int c = c0 + u * THREADS;
+      const int r = c / chunks_per_row;
+      const int col = (c - r * chunks_per_row) << 3;
+      ok[u] = c < n_chunks && col < cols;
+      e[u] = (int64_t)(row0 + r) * a.N + col0 + col;
+    }
+    reduce_chunks<kUnroll, PEER_F32, OUT_F32>(a, e, ok);
+  }
+}
+
+}  // namespace
+}  // namespace entwine
