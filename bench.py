@@ -2,30 +2,34 @@
 """Benchmark of the tile-overlapped GEMM-ReduceScatter on one MI355X.
 
 A step is one entwine_gemm_rs call: the rank's whole share of the operation
-(the GEMM producing every output tile and publishing its flag, and the
-concurrent reduction of the rank's partition with the peers' contributions)
-on inputs already resident in HBM.  Steps are replayed from a captured HIP
-graph, as the pages' prototype does with CUDA Graphs, so the timed loop
-measures device time rather than host launch overhead.
+(the GEMM producing every output tile, and the reduction of the rank's
+partition with the peers' contributions) on inputs already resident in HBM.
+Steps are replayed from a captured HIP graph, as the pages' prototype does with
+CUDA Graphs, so the timed loop measures device time rather than host launch
+overhead.
 
 Default workload: the MLP down-projection slice, M = N = 4096, K_local =
 1792, P = 8 simulated ranks, rank 0, bf16 inputs, fp32 accumulation, bf16
-output, with the tuning table's order, budget and block shape.  Timing
-follows the pages' protocol (Sec. 5.1): warm-up iterations, then timed
-iterations bracketed by HIP events, median reported.
+output, in the configuration the offline tuning table picks for the shape
+(block shape, order, budget -- 0 when no overlapped schedule beat the
+sequential one --, schedule).  Timing follows the pages' protocol (Sec. 5.1):
+warm-up iterations, then timed iterations bracketed by HIP events, median
+reported.
 
 One JSON line on stdout:
   value, ms_per_step   TFLOP/s (2*M*N*K_local / step time) and step time of
-                       the overlapped schedule
-  latency_us_median    median of per-step event pairs
-  sequential           the non-overlapped schedule (GEMM, then reduction) on
-                       the same GPU, and the speedup over it
-  roofline             the GEMM kernel inside the overlapped step against the
-                       bf16 MFMA dense peak; its duration comes from HIP
-                       events recorded on the stream the GEMM runs on
-  reducer              the reduction kernel alone (sequential schedule):
-                       algorithmic bytes / duration against HBM peak, with
-                       the peers' buffers warm and scrubbed from the caches
+                       the tuned step
+  sequential           the non-overlapped schedule (GEMM, then reduction)
+  overlapped           both overlapped schedules (two streams, fused) at the
+                       tuned budget (or 128 if the tuned step is sequential)
+  symmetric_all_ranks  the tuned step for every rank under symmetric peer
+                       readiness; the slowest rank bounds a P-GPU step
+  roofline             the step's dominant kernel against the bf16 MFMA
+                       dense peak; its duration comes from HIP events
+                       recorded on the stream the kernel runs on
+  reducer              the reduction kernel alone: algorithmic bytes /
+                       duration against HBM peak, with the peers' buffers
+                       warm and scrubbed from the caches
   cpu_baseline         the CPU oracle on a bounded row sample of the workload
 """
 from __future__ import annotations
@@ -73,16 +77,18 @@ def traffic_for(workload: str, kernel: str):
     return e.get("bytes_per_launch")
 
 
-def tuned_schedule(w) -> int:
-    """The schedule column of the tuning table's entry for the workload (0 if none)."""
+def tuned_entry(w):
+    """The tuning table's entry for the workload's shape as a dict, or None."""
+    names = ["order", "budget", "bm", "bn", "threads", "slabs", "schedule"]
     with open(os.path.join(ROOT, "tile_overlapped_gemm_amd", "tuning.txt")) as f:
         for line in f:
             v = line.split()
             if not v or v[0].startswith("#"):
                 continue
-            if [int(x) for x in v[:4]] == [w.M, w.N, w.K, w.P] and len(v) >= 11:
-                return int(v[10])
-    return 0
+            if [int(x) for x in v[:4]] == [w.M, w.N, w.K, w.P]:
+                vals = [int(x) for x in v[4:]] + [1, 0][len(v) - 9:]
+                return dict(zip(names, vals))
+    return None
 
 
 def cpu_baseline(w, X, W, target_s: float):
@@ -174,28 +180,40 @@ def main() -> int:
     pd = [None if p is None else up(p) for p in peers]
     out = torch.empty((w.rows, w.N), dtype=torch.float32 if w.fp32_io else torch.bfloat16,
                       device=dev)
-    schedule = {"auto": tog.SCHEDULE_AUTO, "streams": tog.SCHEDULE_STREAMS,
-                "fused": tog.SCHEDULE_FUSED}[args.schedule]
-    if schedule == tog.SCHEDULE_AUTO:
-        schedule = tuned_schedule(w) or tog.SCHEDULE_STREAMS
-    fused = schedule == tog.SCHEDULE_FUSED and args.budget != 0
-    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, reducer_threads=args.threads, schedule=schedule,
-                  task_slabs=args.slabs,
+    # The step's configuration, every field explicit: flags first, then the
+    # tuning table's entry for the shape, then the library's defaults.
+    tuned = tuned_entry(w) or {}
+    _, _, q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
+    cus = tog.entwine_device_cus()
+    if args.block:
+        bm, bn = (int(v) for v in args.block.lower().split("x"))
+    else:
+        bm, bn = tuned.get("bm", 256), tuned.get("bn", 256)
+    order = (tog.ORDERS[args.order] if args.order != "auto"
+             else tuned.get("order", tog.ORDER_INTERLEAVED))
+    budget = args.budget if args.budget >= 0 else tuned.get("budget", 32)
+    threads = args.threads or tuned.get("threads", 256)
+    slabs = args.slabs or tuned.get("slabs", 1)
+    schedule = ({"streams": tog.SCHEDULE_STREAMS, "fused": tog.SCHEDULE_FUSED}[args.schedule]
+                if args.schedule != "auto" else (tuned.get("schedule") or tog.SCHEDULE_STREAMS))
+    # The overlapped schedules are also timed when the tuned step is sequential.
+    ov_budget = budget if budget > 0 else min(128, q, cus - 1)
+    kind = "sequential" if budget == 0 else ("fused" if schedule == tog.SCHEDULE_FUSED
+                                             else "streams")
+    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, block_m=bm, block_n=bn, reducer_threads=threads,
+                  task_slabs=slabs, schedule=schedule,
                   peer_ready=tog.PEERS_SYMMETRIC if args.peers == "symmetric" else tog.PEERS_PRESEEDED)
     if w.fp32_io:
         cfg_kw.update(peer_dtype=tog.F32, out_dtype=tog.F32)
-    if args.block:
-        bm, bn = (int(v) for v in args.block.lower().split("x"))
-        cfg_kw.update(block_m=bm, block_n=bn)
     cfg = tog.config(**cfg_kw)
     cfg_gemm = tog.config(**cfg_kw, stages=tog.STAGES_GEMM)
     cfg_red = tog.config(**cfg_kw, stages=tog.STAGES_REDUCE)
-    order = tog.ORDER_AUTO if args.order == "auto" else tog.ORDERS[args.order]
+    cfg_streams = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS))
+    cfg_fused = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED))
     stream = torch.cuda.Stream(dev)
-    budget = args.budget
 
-    def call(budget, c=cfg):
-        tog.gemm_rs(Xd, Wd, pd, out, w.P, w.rank, order, budget, cfg=c, stream=stream)
+    def call(b, c=cfg, rank=w.rank, peers=pd):
+        tog.gemm_rs(Xd, Wd, peers, out, w.P, rank, order, b, cfg=c, stream=stream)
 
     def check_status(where):
         st = tog.entwine_device_status(stream.cuda_stream)
@@ -207,7 +225,8 @@ def main() -> int:
             call(budget)
         stream.synchronize()
         check_status("in the profiled calls")
-        log(f"profiled {args.warmup + args.steps} calls, budget {budget}")
+        log(f"profiled {args.warmup + args.steps} calls: {kind}, block {bm}x{bn}, order {order}, "
+            f"budget {budget}")
         return 0
 
     def graph_of(body):
@@ -246,22 +265,35 @@ def main() -> int:
                        p90_ms=per[(9 * len(per)) // 10])
         return res
 
-    log(f"overlapped step ({'fused' if fused else 'two streams'}): {args.warmup} warm-up + "
-        f"{args.steps} timed graph replays")
-    ov = timed_graph(lambda: call(budget), args.steps, args.warmup)
+    def lat(r):
+        return {"latency_us": r["ms_per_step"] * 1e3, "latency_us_median": r["median_ms"] * 1e3}
+
+    log(f"step ({kind}, block {bm}x{bn}, order {order}, budget {budget}): {args.warmup} warm-up "
+        f"+ {args.steps} timed graph replays")
+    st = timed_graph(lambda: call(budget), args.steps, args.warmup)
     log("sequential step (budget 0): same protocol")
     sq = timed_graph(lambda: call(0), args.steps, args.warmup)
-    other = None
-    if budget != 0:
-        other_cfg = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS if fused
-                                      else tog.SCHEDULE_FUSED))
-        log(f"overlapped step, {'two streams' if fused else 'fused'}: same protocol")
-        other = timed_graph(lambda: call(budget, other_cfg), args.steps, args.warmup)
+    log(f"overlapped steps at budget {ov_budget}, two streams and fused: same protocol")
+    ov_s = timed_graph(lambda: call(ov_budget, cfg_streams), args.steps, args.warmup)
+    ov_f = timed_graph(lambda: call(ov_budget, cfg_fused), args.steps, args.warmup)
+
+    # Every rank's step under symmetric peer readiness (each peer's tile counts
+    # as ready once this GPU has produced the block at the position where the
+    # peer produces it): the slowest rank bounds the step of the P-GPU operation.
+    log("every rank, symmetric peer readiness: same protocol")
+    sym_cfg = tog.config(**dict(cfg_kw, peer_ready=tog.PEERS_SYMMETRIC))
+    seeded = [p for p in pd if p is not None]
+    per_rank = []
+    for r in range(w.P):
+        it = iter(seeded)
+        pr = [None if k == r else next(it) for k in range(w.P)]
+        body = (lambda r=r, pr=pr: call(budget, sym_cfg, r, pr))
+        per_rank.append(timed_graph(body, args.steps, args.warmup)["median_ms"] * 1e3)
 
     # Kernels alone: GEMM without flags; the reduction of the workspace's
-    # partial, flat (sequential schedule) and tiled at the step's budget.  Ten
-    # launches per graph replay amortize the replay's launch latency; the cold
-    # reduction subtracts a graph holding only the cache scrub.
+    # partial, flat (sequential schedule) and tiled at the overlapped budget.
+    # Ten launches per graph replay amortize the replay's launch latency; the
+    # cold reduction subtracts a graph holding only the cache scrub.
     reps, ksteps = 10, max(10, min(args.steps, 50))
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
 
@@ -274,15 +306,17 @@ def main() -> int:
     log("kernels alone")
     g_alone = timed_graph(rep(lambda: call(0, cfg_gemm)), ksteps, 3, False)["ms_per_step"] / reps
     r_flat = timed_graph(rep(lambda: call(0, cfg_red)), ksteps, 3, False)["ms_per_step"] / reps
-    r_tile = timed_graph(rep(lambda: call(budget, cfg_red)), ksteps, 3, False)["ms_per_step"] / reps
+    r_tile = timed_graph(rep(lambda: call(ov_budget, cfg_red)), ksteps, 3,
+                         False)["ms_per_step"] / reps
     t_scrub = timed_graph(lambda: scrub.fill_(1), ksteps, 3, False)["ms_per_step"]
     t_both = timed_graph(lambda: (scrub.fill_(1), call(0, cfg_red)), ksteps, 3,
                          False)["ms_per_step"]
     r_cold = max(t_both - t_scrub, 1e-6)
     del scrub
 
-    # The GEMM and the reduction inside the overlapped step, from HIP events
-    # recorded on each kernel's own stream around eager calls.
+    # The step's kernels, from HIP events recorded on each kernel's own stream
+    # around eager calls: GEMM and reduction (sequential: one after the other;
+    # two streams: concurrently), or the fused kernel twice.
     for _ in range(3):
         call(budget)
     stream.synchronize()
@@ -294,14 +328,18 @@ def main() -> int:
     tog.entwine_timing(False)
     gm, rm, n = tog.entwine_timing_read()
     check_status("in the kernel timing loop")
-    g_ov, r_ov = gm / n, rm / n
+    k_gemm, k_red = gm / n, rm / n
 
     flops = float(w.flops)
     red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
                                        else (4 + 2 * (w.P - 1) + 2))
-    tflops = flops / (ov["ms_per_step"] * 1e-3) / 1e12
-    achieved = flops / (g_ov * 1e-3) / 1e12
+    tflops = flops / (st["ms_per_step"] * 1e-3) / 1e12
+    achieved = flops / (k_gemm * 1e-3) / 1e12
     gbps = lambda ms: red_bytes / (ms * 1e-3) / 1e9
+    kernel = {"sequential": "gemm_publish_kernel (the step's GEMM)",
+              "streams": "gemm_publish_kernel (inside the overlapped step)",
+              "fused": "gemm_rs_fused_kernel (the whole step: GEMM and reduction)"}[kind]
+    traffic_key = "gemm_rs_fused" if kind == "fused" else "gemm_publish"
     res = {
         "metric": METRIC,
         "value": tflops,
@@ -309,42 +347,37 @@ def main() -> int:
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": ov["ms_per_step"],
+        "ms_per_step": st["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K_local": w.K, "P": w.P,
-                   "rank": w.rank, "tile_order": args.order, "comm_budget": budget,
-                   "block": args.block or "tuning table", "tile": w.tile,
-                   "reducer_threads": args.threads or "tuning table",
-                   "task_slabs": args.slabs or "tuning table", "peer_ready": args.peers,
-                   "schedule": args.schedule,
+                   "rank": w.rank, "schedule": kind, "block": f"{bm}x{bn}", "tile": w.tile,
+                   "tile_order": order, "comm_budget": budget, "reducer_threads": threads,
+                   "task_slabs": slabs, "peer_ready": args.peers,
+                   "source": "tuning table" if tuned and args.budget < 0 else "flags",
                    "launch": "HIP graph replay"},
-        "latency_us": ov["ms_per_step"] * 1e3,
-        "latency_us_median": ov["median_ms"] * 1e3,
-        "latency_us_p10_p90": [ov["p10_ms"] * 1e3, ov["p90_ms"] * 1e3],
+        "latency_us": st["ms_per_step"] * 1e3,
+        "latency_us_median": st["median_ms"] * 1e3,
+        "latency_us_p10_p90": [st["p10_ms"] * 1e3, st["p90_ms"] * 1e3],
         "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
-        "sequential": {
-            "latency_us": sq["ms_per_step"] * 1e3,
-            "latency_us_median": sq["median_ms"] * 1e3,
-        },
-        "speedup_vs_sequential": sq["ms_per_step"] / ov["ms_per_step"],
-        "schedule": "fused" if fused else "streams",
-        ("streams" if fused else "fused"): None if other is None else {
-            "latency_us": other["ms_per_step"] * 1e3,
-            "latency_us_median": other["median_ms"] * 1e3,
-        },
+        "sequential": lat(sq),
+        "speedup_vs_sequential": sq["ms_per_step"] / st["ms_per_step"],
+        "overlapped": {"budget": ov_budget, "streams": lat(ov_s), "fused": lat(ov_f),
+                       "best_speedup_vs_sequential":
+                           sq["ms_per_step"] / min(ov_s["ms_per_step"], ov_f["ms_per_step"])},
+        "symmetric_all_ranks": {"latency_us_median_max": max(per_rank),
+                                "latency_us_median_per_rank": per_rank,
+                                "speedup_vs_sequential": sq["median_ms"] * 1e3 / max(per_rank)},
         "gemm_alone_us": g_alone * 1e3,
         "gemm_alone_tflops": flops / (g_alone * 1e-3) / 1e12,
-        # Fused: one kernel does both, so its duration is reported once and the
-        # tail is what it takes beyond the GEMM alone.
-        "gemm_in_overlap_us": None if fused else g_ov * 1e3,
-        "reduce_kernel_in_overlap_us": None if fused else r_ov * 1e3,
-        "fused_kernel_us": g_ov * 1e3 if fused else None,
-        "overlap_efficiency": g_alone / ov["ms_per_step"],
-        "tail_us": ((g_ov - g_alone) if fused else (ov["ms_per_step"] - g_ov)) * 1e3,
+        "step_kernels_us": ({"fused": k_gemm * 1e3} if kind == "fused"
+                            else {"gemm": k_gemm * 1e3, "reduction": k_red * 1e3}),
+        "overlap_efficiency": g_alone / st["ms_per_step"],
+        # after the GEMM alone would have ended: the reduction's exposed part
+        "tail_us": (st["ms_per_step"] - g_alone) * 1e3,
         "reducer": {
             "bytes": red_bytes,
             "flat_warm_us": r_flat * 1e3,
@@ -358,10 +391,9 @@ def main() -> int:
         },
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
-                     "traffic": traffic_for(w.name, "gemm_rs_fused" if fused else "gemm_publish"),
-                     "kernel": ("gemm_rs_fused_kernel (the whole step: GEMM and reduction)"
-                                if fused else "gemm_publish_kernel (inside the overlapped step)"),
-                     "kernel_us": g_ov * 1e3,
+                     "traffic": traffic_for(w.name, traffic_key),
+                     "kernel": kernel,
+                     "kernel_us": k_gemm * 1e3,
                      "algorithmic_flops_per_launch": flops},
     }
     if not args.no_cpu:

@@ -37,10 +37,10 @@ def test_full_size_sampled_parity(w):
     seq = case.run(tog.ORDER_AUTO, tog.BUDGET_SEQUENTIAL)
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t  # noqa: E731
     assert torch.equal(bits(out), bits(seq))
+    # both overlapped schedules at a budget of 128 (the tuned step may be sequential)
     for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
-        print(f"workload {w.name}: overlapped run (AUTO), schedule {sched}", flush=True)
-        assert torch.equal(bits(case.run(tog.ORDER_AUTO, tog.BUDGET_AUTO, schedule=sched)),
-                           bits(seq))
+        print(f"workload {w.name}: overlapped run, budget 128, schedule {sched}", flush=True)
+        assert torch.equal(bits(case.run(tog.ORDER_AUTO, 128, schedule=sched)), bits(seq))
     got = down(out)
     worst = 0.0
     for r in sample_rows(w.rows):
