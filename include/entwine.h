@@ -178,7 +178,13 @@ typedef struct entwine_config {
                               partials (reduction) as they were: for timing only. */
   int32_t schedule;        /* ENTWINE_SCHEDULE_*; FUSED is built for the variant-0 pipelines
                               of every block shape and variant 3 of 256x256 */
-  int32_t reserved[2];
+  int32_t reducer_cus;     /* static CU partitioning (Sec. 5.3.3): 0 = shared pool, the only
+                              mode built (both kernels may use every CU).  n in [1, CUs) asks
+                              for the reduction on n CUs and the GEMM on the others through
+                              CU-masked streams, which the HIP runtime on MI355X did not
+                              support reliably: ENTWINE_ERR_UNSUPPORTED (n >= CUs:
+                              ENTWINE_ERR_INVALID_ARGUMENT) for overlapped calls */
+  int32_t reserved[1];
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);

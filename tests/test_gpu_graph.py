@@ -80,3 +80,4 @@ def test_capture_requires_prepared_workspace():
         pass  # an empty capture may be rejected by torch; the library error is what matters
     assert err is not None and err.status == tog.ENTWINE_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
+

@@ -71,7 +71,8 @@ class entwine_config(ctypes.Structure):
         ("linear_dispatch", ctypes.c_int32),
         ("stages", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 2),
+        ("reducer_cus", ctypes.c_int32),
+        ("reserved", ctypes.c_int32 * 1),
     ]
 
 

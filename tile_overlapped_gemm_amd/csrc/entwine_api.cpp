@@ -139,6 +139,7 @@ void destroy_workspace(Workspace* w) {
   if (w->ev_red) (void)hipEventDestroy(w->ev_red);
   if (w->s_gemm) (void)hipStreamDestroy(w->s_gemm);
   if (w->s_red) (void)hipStreamDestroy(w->s_red);
+
   if (prev >= 0) (void)hipSetDevice(prev);
 }
 
@@ -271,7 +272,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch, schedule;
+      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch, schedule, reducer_cus;
   uint32_t timeout_ms;
 };
 
@@ -338,6 +339,9 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "stages %d out of range", c.stages);
   if (r->schedule < ENTWINE_SCHEDULE_STREAMS || r->schedule > ENTWINE_SCHEDULE_FUSED)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "schedule %d out of range", r->schedule);
+  r->reducer_cus = c.reducer_cus;
+  if (c.reducer_cus < 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "reducer_cus %d is negative", c.reducer_cus);
   return ENTWINE_OK;
 }
 
@@ -401,6 +405,16 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     if (fused_per_cu <= 0)
       return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
                   "GEMM variant %d", g.bm, g.bn, rs.variant);
+  }
+  if (rs.reducer_cus > 0 && !sequential && rs.stages == ENTWINE_STAGES_ALL) {
+    if (rs.reducer_cus >= w->cus)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "reducer_cus %d must stay below the device's "
+                  "%d compute units", rs.reducer_cus, w->cus);
+    // Static partitioning needs streams whose CU masks enable part of the
+    // device; creating such streams failed or crashed inside the HIP runtime
+    // on MI355X, so this build does not attempt it.
+    return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning (reducer_cus > 0) is not "
+                "available in this build: partial CU masks are not supported by the runtime");
   }
   if (!sequential && !fused && rs.stages == ENTWINE_STAGES_ALL) {
     // The reduction workgroups wait for GEMM blocks, so a CU holding one
@@ -596,8 +610,8 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   hipEvent_t ev_red = capturing ? w->cap_red : w->ev_red;
   if (forked) {
     HIP_TRY(hipEventRecord(ev_fork, stream));
-    HIP_TRY(hipStreamWaitEvent(w->s_gemm, ev_fork, 0));
-    HIP_TRY(hipStreamWaitEvent(w->s_red, ev_fork, 0));
+    HIP_TRY(hipStreamWaitEvent(s_gemm, ev_fork, 0));
+    HIP_TRY(hipStreamWaitEvent(s_red, ev_fork, 0));
   }
   if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(s_gemm, w->ev_red, 0));
 
