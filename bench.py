@@ -276,6 +276,11 @@ def main() -> int:
     log(f"overlapped steps at budget {ov_budget}, two streams and fused: same protocol")
     ov_s = timed_graph(lambda: call(ov_budget, cfg_streams), args.steps, args.warmup)
     ov_f = timed_graph(lambda: call(ov_budget, cfg_fused), args.steps, args.warmup)
+    log("the same with every peer-bound tile also pushed to the staging buffer")
+    cfg_push_s = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, push_outgoing=1))
+    cfg_push_f = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED, push_outgoing=1))
+    pu_s = timed_graph(lambda: call(ov_budget, cfg_push_s), args.steps, args.warmup)
+    pu_f = timed_graph(lambda: call(ov_budget, cfg_push_f), args.steps, args.warmup)
 
     # Every rank's step under symmetric peer readiness (each peer's tile counts
     # as ready once this GPU has produced the block at the position where the
@@ -367,7 +372,10 @@ def main() -> int:
         "speedup_vs_sequential": sq["ms_per_step"] / st["ms_per_step"],
         "overlapped": {"budget": ov_budget, "streams": lat(ov_s), "fused": lat(ov_f),
                        "best_speedup_vs_sequential":
-                           sq["ms_per_step"] / min(ov_s["ms_per_step"], ov_f["ms_per_step"])},
+                           sq["ms_per_step"] / min(ov_s["ms_per_step"], ov_f["ms_per_step"]),
+                       # the sender's side of a push-based transfer: every
+                       # peer-bound tile also copied, (M - M/P) * N * 2 * 2 bytes more
+                       "push_outgoing": {"streams": lat(pu_s), "fused": lat(pu_f)}},
         "symmetric_all_ranks": {"latency_us_median_max": max(per_rank),
                                 "latency_us_median_per_rank": per_rank,
                                 "speedup_vs_sequential": sq["median_ms"] * 1e3 / max(per_rank)},

@@ -184,7 +184,12 @@ typedef struct entwine_config {
                               CU-masked streams, which the HIP runtime on MI355X did not
                               support reliably: ENTWINE_ERR_UNSUPPORTED (n >= CUs:
                               ENTWINE_ERR_INVALID_ARGUMENT) for overlapped calls */
-  int32_t reserved[1];
+  int32_t push_outgoing;   /* 0: pull only (the method); 1: the reduction workgroups also push
+                              every peer-bound tile, once its flag is set, from the outgoing
+                              partials into a staging buffer (entwine_staging), in production
+                              order with the reductions: the sender's side of a push-based
+                              transfer, on one GPU.  Overlapped schedules only (comm_budget 0:
+                              ENTWINE_ERR_UNSUPPORTED); releases every tile like publish_all */
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);
@@ -274,6 +279,12 @@ const char* entwine_last_error_message(void);
  * own-partition partial [M/P][N] and the outgoing contributions [M][N]
  * (peer dtype) written by the last call.  Any pointer may be NULL. */
 int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* bytes);
+
+/* Device pointer of the current device's staging buffer (for tests and
+ * measurements): peer dtype [M][N], whose rows of partition d != rank hold
+ * the copies pushed by the last call with push_outgoing = 1 (the rank's own
+ * rows are unused).  NULL before any pushing call. */
+int entwine_staging(const void** staging, int64_t* bytes);
 
 /* Per-kernel timing with HIP events recorded on the stream each kernel is
  * launched on.  entwine_timing(1) starts recording every call; reading

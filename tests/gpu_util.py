@@ -21,6 +21,8 @@ def hip():
         _hip = ctypes.CDLL("libamdhip64.so.7")
         _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
         _hip.hipMemcpy.restype = ctypes.c_int
+        _hip.hipMemset.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t]
+        _hip.hipMemset.restype = ctypes.c_int
     return _hip
 
 

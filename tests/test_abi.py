@@ -99,6 +99,7 @@ def test_validation_before_any_device_call(lib, kw, status):
     ("schedule", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("schedule", -1, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("reducer_cus", -4, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("push_outgoing", 2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("struct_size", 4, tog.ENTWINE_ERR_INVALID_ARGUMENT),
 ])
 def test_config_validation(lib, field, value, status):

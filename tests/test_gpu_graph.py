@@ -13,8 +13,9 @@ from gpu_util import device, down, up
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("sched", [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED])
-def test_graph_replays_match_eager(sched):
+@pytest.mark.parametrize("sched,push", [(tog.SCHEDULE_STREAMS, 0), (tog.SCHEDULE_FUSED, 0),
+                                        (tog.SCHEDULE_FUSED, 1)])
+def test_graph_replays_match_eager(sched, push):
     dev = device()
     w = wl.custom("graph", 2048, 1536, 512, 4, rank=2, index=320)
     Xa, W = wl.operands(w)
@@ -22,13 +23,14 @@ def test_graph_replays_match_eager(sched):
     peers = wl.peer_partials(w)
     Wd = up(W, dev)
     pd = [None if p is None else up(p, dev) for p in peers]
-    cfg = tog.config(block_m=256, block_n=128, schedule=sched)
+    cfg = tog.config(block_m=256, block_n=128, schedule=sched, push_outgoing=push)
     srcs = [up(Xa, dev), up(Xb, dev)]
     X = srcs[0].clone()
 
     def eager(Xin, budget):
         o = torch.empty((w.rows, w.N), dtype=torch.bfloat16, device=dev)
-        tog.gemm_rs(Xin, Wd, pd, o, w.P, w.rank, tog.ORDER_INTERLEAVED, budget, cfg=cfg)
+        c = cfg if budget else tog.config(block_m=256, block_n=128)  # sequential: no push
+        tog.gemm_rs(Xin, Wd, pd, o, w.P, w.rank, tog.ORDER_INTERLEAVED, budget, cfg=c)
         torch.cuda.synchronize()
         return down(o)
 

@@ -12,7 +12,7 @@ import torch
 
 import tile_overlapped_gemm_amd as tog
 import workloads as wl
-from gpu_util import Case, as_f64, device, down, err_ratio, read_workspace
+from gpu_util import Case, as_f64, device, down, err_ratio, hip, read_workspace
 from oracle import oracle as orc
 
 pytestmark = pytest.mark.gpu
@@ -132,6 +132,46 @@ def test_fused_schedule_variants_bit_identical(dev, w):
         np.testing.assert_array_equal(out, base)
 
 
+def read_staging(M, N, f32):
+    ptr, nbytes = tog.entwine_staging()
+    st = np.empty((M, N), dtype=np.float32 if f32 else np.uint16)
+    assert ptr and nbytes >= st.nbytes
+    assert hip().hipMemcpy(st.ctypes.data, ptr, st.nbytes, 2) == 0
+    return st
+
+
+@pytest.mark.parametrize("w", [SMALL[1], SMALL[3]], ids=lambda w: w.name)
+def test_push_outgoing_copies_every_peer_tile(dev, w):
+    """With push_outgoing the reduction workgroups also copy every peer-bound
+    tile into the staging buffer: the output is unchanged and the staging rows
+    of every other partition equal the outgoing partials bit for bit."""
+    case, ref = case_for(w, dev)
+    blk = dict(block_m=128, block_n=128)
+    base = down(case.run(tog.ORDER_INTERLEAVED, 4, **blk))
+    rows = np.ones(w.M, dtype=bool)
+    rows[w.rank * w.rows:(w.rank + 1) * w.rows] = False
+    for sched in SCHEDULES:
+        for order, budget, slabs, mode in ((tog.ORDER_INTERLEAVED, 4, 1, tog.PEERS_PRESEEDED),
+                                           (tog.ORDER_PARTITION_MAJOR, 1, 2, tog.PEERS_SYMMETRIC),
+                                           (tog.ORDER_COL_MAJOR, 64, 4, tog.PEERS_PRESEEDED)):
+            print(f"case {w.name} push schedule {sched} order {order} budget {budget} "
+                  f"slabs {slabs} mode {mode}", flush=True)
+            # a stale staging buffer must be fully overwritten
+            st_ptr, st_bytes = tog.entwine_staging()
+            if st_ptr:
+                torch.cuda.synchronize()
+                assert hip().hipMemset(st_ptr, 0x7f, st_bytes) == 0
+            out = down(case.run(order, budget, push_outgoing=1, schedule=sched, task_slabs=slabs,
+                                peer_ready=mode, **blk))
+            np.testing.assert_array_equal(out, base)
+            _, outgoing = read_workspace(w.rows, w.N, w.M, w.fp32_io)
+            staging = read_staging(w.M, w.N, w.fp32_io)
+            np.testing.assert_array_equal(staging[rows], outgoing[rows])
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, 0, push_outgoing=1, **blk)
+    assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+
+
 def test_fused_many_rounds_bit_identical(dev):
     """More GEMM blocks than resident workgroups: workgroups take several
     blocks each (and take blocks from other XCDs' lists) before reducing."""
@@ -146,6 +186,9 @@ def test_fused_many_rounds_bit_identical(dev):
             print(f"case rounds order {order} budget {budget}", flush=True)
             out = down(case.run(order, budget, schedule=tog.SCHEDULE_FUSED, **blk))
             np.testing.assert_array_equal(out, seq)
+    out = down(case.run(tog.ORDER_INTERLEAVED, 128, schedule=tog.SCHEDULE_FUSED, push_outgoing=1,
+                        **blk))
+    np.testing.assert_array_equal(out, seq)
     got = seq
     for r in (0, w.rows // 2, w.rows - 1):
         ref = orc.gemm_rs(X, W, peers, w.P, w.rank, row_begin=r, row_end=r + 1)

@@ -39,7 +39,7 @@ EXPORTS = [
     "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
     "entwine_plan_task_order", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
-    "entwine_workspace", "entwine_timing", "entwine_timing_read", "entwine_load_tuning",
+    "entwine_workspace", "entwine_staging", "entwine_timing", "entwine_timing_read", "entwine_load_tuning",
     "entwine_release", "entwine_device_cus",
 ]
 
@@ -72,7 +72,7 @@ class entwine_config(ctypes.Structure):
         ("stages", ctypes.c_int32),
         ("schedule", ctypes.c_int32),
         ("reducer_cus", ctypes.c_int32),
-        ("reserved", ctypes.c_int32 * 1),
+        ("push_outgoing", ctypes.c_int32),
     ]
 
 
@@ -113,6 +113,7 @@ def load(path: str = LIB):
         "entwine_status_string": ([i32], ctypes.c_char_p),
         "entwine_last_error_message": ([], ctypes.c_char_p),
         "entwine_workspace": ([ctypes.POINTER(vp), ctypes.POINTER(vp), pi64], i32),
+        "entwine_staging": ([ctypes.POINTER(vp), pi64], i32),
         "entwine_timing": ([i32], i32),
         "entwine_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), pi64],
                                 i32),
@@ -186,6 +187,13 @@ def entwine_workspace():
     own, outg, nb = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int64()
     _check(load().entwine_workspace(ctypes.byref(own), ctypes.byref(outg), ctypes.byref(nb)))
     return own.value, outg.value, nb.value
+
+
+def entwine_staging():
+    """(device pointer, bytes) of the staging buffer that pushing calls fill."""
+    st, nb = ctypes.c_void_p(), ctypes.c_int64()
+    _check(load().entwine_staging(ctypes.byref(st), ctypes.byref(nb)))
+    return st.value, nb.value
 
 
 def entwine_load_tuning(path: str) -> None:

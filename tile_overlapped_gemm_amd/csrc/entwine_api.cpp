@@ -61,7 +61,9 @@ struct DevicePlan {
   int32_t* d_blocks = nullptr;
   int32_t* d_tiles = nullptr;
   int32_t* d_waits = nullptr;
-  std::map<int, int32_t*> d_task_order;  // fused schedule, by task_slabs
+  // Task lists in production order, by (task_slabs, push): the fused
+  // schedule's, and the two-stream reducer's when it also pushes.
+  std::map<std::pair<int, int>, int32_t*> d_task_list;
 };
 
 using PlanKey = std::tuple<int64_t, int64_t, int, int, int, int, int, int, int, int, int, int64_t>;
@@ -84,6 +86,8 @@ struct Workspace {
   size_t own_bytes = 0;
   void* outgoing = nullptr;
   size_t outgoing_bytes = 0;
+  void* staging = nullptr;  // pushed copies of the outgoing partials
+  size_t staging_bytes = 0;
   uint32_t* flags = nullptr;
   size_t flag_count = 0;
   int32_t* error = nullptr;
@@ -107,8 +111,8 @@ void free_plan(DevicePlan* p) {
   if (p->d_tiles) (void)hipFree(p->d_tiles);
   if (p->d_waits) (void)hipFree(p->d_waits);
   p->d_blocks = p->d_tiles = p->d_waits = nullptr;
-  for (auto& kv : p->d_task_order) (void)hipFree(kv.second);
-  p->d_task_order.clear();
+  for (auto& kv : p->d_task_list) (void)hipFree(kv.second);
+  p->d_task_list.clear();
 }
 
 void destroy_workspace(Workspace* w) {
@@ -129,6 +133,7 @@ void destroy_workspace(Workspace* w) {
     }
   if (w->own) (void)hipFree(w->own);
   if (w->outgoing) (void)hipFree(w->outgoing);
+  if (w->staging) (void)hipFree(w->staging);
   if (w->flags) (void)hipFree(w->flags);
   if (w->error) (void)hipFree(w->error);
   if (w->ctl) (void)hipFree(w->ctl);
@@ -272,7 +277,8 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch, schedule, reducer_cus;
+      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch, schedule, reducer_cus,
+      push;
   uint32_t timeout_ms;
 };
 
@@ -281,7 +287,7 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   entwine_config c;
   entwine_config_init(&c);
   if (cfg) {
-    if (cfg->struct_size < (int32_t)offsetof(entwine_config, reserved))
+    if (cfg->struct_size < (int32_t)offsetof(entwine_config, schedule))
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "entwine_config.struct_size too small");
     std::memcpy(&c, cfg, std::min<size_t>(sizeof c, (size_t)cfg->struct_size));
   }
@@ -340,6 +346,9 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   if (r->schedule < ENTWINE_SCHEDULE_STREAMS || r->schedule > ENTWINE_SCHEDULE_FUSED)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "schedule %d out of range", r->schedule);
   r->reducer_cus = c.reducer_cus;
+  r->push = c.push_outgoing;
+  if (c.push_outgoing != 0 && c.push_outgoing != 1)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "push_outgoing must be 0 or 1");
   if (c.reducer_cus < 0)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "reducer_cus %d is negative", c.reducer_cus);
   return ENTWINE_OK;
@@ -399,6 +408,13 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
   const bool fused = !sequential && rs.stages == ENTWINE_STAGES_ALL &&
                      rs.schedule == ENTWINE_SCHEDULE_FUSED;
+  if (rs.push && sequential)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "push_outgoing applies to the overlapped schedules "
+                "(comm_budget >= 1)");
+  // A list of tasks in production order: always for the fused kernel, and for
+  // the two-stream reducer when it also pushes.
+  const bool listed = !sequential && (fused || rs.push);
+  const int slabs_eff = rs.slabs ? rs.slabs : 1;
   int fused_per_cu = 0;
   if (fused) {
     fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32);
@@ -450,14 +466,15 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                 rs.release_group, window};
     auto pit = w->plans.find(key);
     if (w->own_bytes < own_need || w->outgoing_bytes < og_need || w->flag_count * 4 < flag_need ||
-        pit == w->plans.end() ||
-        (fused && !pit->second->d_task_order.count(rs.slabs ? rs.slabs : 1)))
+        (rs.push && w->staging_bytes < og_need) || pit == w->plans.end() ||
+        (listed && !pit->second->d_task_list.count({slabs_eff, rs.push})))
       return fail(ENTWINE_ERR_INVALID_ARGUMENT,
                   "the workspace and schedule for this shape must exist before a graph capture: "
                   "make the same call once outside the capture");
   }
   if ((rc = ensure(w, (void**)&w->own, &w->own_bytes, own_need, false))) return rc;
   if ((rc = ensure(w, &w->outgoing, &w->outgoing_bytes, og_need, false))) return rc;
+  if (rs.push && (rc = ensure(w, &w->staging, &w->staging_bytes, og_need, false))) return rc;
   size_t flag_bytes = w->flag_count * 4;
   if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, flag_need, true))) return rc;
   w->flag_count = flag_bytes / 4;
@@ -466,18 +483,17 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, window, &dp)))
     return rc;
 
-  int32_t* d_task_order = nullptr;
-  if (fused) {
-    const int slabs = rs.slabs ? rs.slabs : 1;
-    auto it = dp->d_task_order.find(slabs);
-    if (it == dp->d_task_order.end()) {
-      const std::vector<int32_t> order = fused_task_order(dp->plan, slabs);
-      HIP_TRY(hipMalloc(&d_task_order, order.size() * sizeof(int32_t)));
-      dp->d_task_order[slabs] = d_task_order;
-      HIP_TRY(hipMemcpy(d_task_order, order.data(), order.size() * sizeof(int32_t),
+  int32_t* d_task_list = nullptr;
+  if (listed) {
+    auto it = dp->d_task_list.find({slabs_eff, rs.push});
+    if (it == dp->d_task_list.end()) {
+      const std::vector<int32_t> order = task_list(dp->plan, slabs_eff, rs.push != 0);
+      HIP_TRY(hipMalloc(&d_task_list, order.size() * sizeof(int32_t)));
+      dp->d_task_list[{slabs_eff, rs.push}] = d_task_list;
+      HIP_TRY(hipMemcpy(d_task_list, order.data(), order.size() * sizeof(int32_t),
                         hipMemcpyHostToDevice));
     } else {
-      d_task_order = it->second;
+      d_task_list = it->second;
     }
   }
 
@@ -525,21 +541,23 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ra.timeout_ticks = (uint64_t)rs.timeout_ms * (uint64_t)w->wall_khz;
   ra.withhold_tile = rs.withhold_tile;
   ra.never_flag = (int32_t)(g.P * g.Q);
+  ra.outgoing = w->outgoing;
+  ra.staging = rs.push ? w->staging : nullptr;
+  ra.task_list = d_task_list;
 
   if (fused) {
     // One kernel on the caller's stream, after this workspace's previous
     // eager call (which may have run on other streams).
-    ga.publish = rs.publish_all ? 2 : 1;
-    ga.flag_all = rs.publish_all || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
+    ga.publish = rs.publish_all || rs.push ? 2 : 1;
+    ga.flag_all = rs.publish_all || rs.push || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
                   rs.release_group != ENTWINE_RELEASE_TILE;
-    ra.slabs = rs.slabs ? rs.slabs : 1;
-    ra.ntasks = (int32_t)(g.Q * ra.slabs);
+    ra.slabs = slabs_eff;
+    ra.ntasks = (int32_t)(g.Q * ra.slabs * (rs.push ? g.P : 1));
     FusedArgs fa{};
     fa.g = ga;
     fa.r = ra;
     fa.nb = (int32_t)g.NB;
     fa.workers = (int32_t)std::min<int64_t>(rs.budget, ra.ntasks);
-    fa.task_order = d_task_order;
     // Resident workgroups, but no more than there is work for.
     const int64_t grid =
         std::min<int64_t>((int64_t)fused_per_cu * w->cus, g.NB + (int64_t)fa.workers);
@@ -578,13 +596,15 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + per_wg - 1) / per_wg,
                                                         (int64_t)8 * w->cus));
   } else {
-    ga.publish = rs.publish_all ? 2 : 1;
-    // Flags of peer-bound tiles are read by symmetric-peer and release-group
-    // waits only.
-    ga.flag_all = rs.publish_all || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
+    // Pushing reads the peer-bound tiles on this device: they are released
+    // like the own ones.
+    ga.publish = rs.publish_all || rs.push ? 2 : 1;
+    // Flags of peer-bound tiles are read by send tasks, symmetric-peer and
+    // release-group waits only.
+    ga.flag_all = rs.publish_all || rs.push || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
                   rs.release_group != ENTWINE_RELEASE_TILE;
-    ra.slabs = rs.slabs ? rs.slabs : 1;
-    ra.ntasks = (int32_t)(g.Q * ra.slabs);
+    ra.slabs = slabs_eff;
+    ra.ntasks = (int32_t)(g.Q * ra.slabs * (rs.push ? g.P : 1));
     grid = (int)std::min<int64_t>(rs.budget, ra.ntasks);  // x, capped by the task count
   }
 
@@ -758,10 +778,12 @@ int entwine_plan_task_order(int64_t M, int64_t N, int P, int rank, int tile_orde
   if (task_slabs < 1 || tile_m % task_slabs != 0)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
   assign_dispatch(&p, window);
-  const std::vector<int32_t> order = fused_task_order(p, task_slabs);
+  const std::vector<int32_t> order = task_list(p, task_slabs, false);
   if (!task_order || capacity < (int64_t)order.size())
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_order needs %zu entries", order.size());
-  std::copy(order.begin(), order.end(), task_order);
+  // Global ids (rank * Q + t) * slabs + s -> the partition's own numbering.
+  for (size_t k = 0; k < order.size(); ++k)
+    task_order[k] = order[k] - (int32_t)(rank * p.g.Q * task_slabs);
   return ENTWINE_OK;
 }
 
@@ -827,9 +849,26 @@ int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* 
   Workspace* w = it->second.get();
   HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
   if (own_partial) *own_partial = w->own;
   if (outgoing) *outgoing = w->outgoing;
-  if (bytes) *bytes = (int64_t)(w->own_bytes + w->outgoing_bytes + w->flag_count * 4);
+  if (bytes)
+    *bytes = (int64_t)(w->own_bytes + w->outgoing_bytes + w->staging_bytes + w->flag_count * 4);
+  return ENTWINE_OK;
+}
+
+int entwine_staging(const void** staging, int64_t* bytes) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end()) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no workspace on this device yet");
+  Workspace* w = it->second.get();
+  HIP_TRY(hipStreamSynchronize(w->s_gemm));
+  HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
+  if (staging) *staging = w->staging;
+  if (bytes) *bytes = (int64_t)w->staging_bytes;
   return ENTWINE_OK;
 }
 

@@ -120,22 +120,24 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     while (true) {
       if (tid == 0) {
         const uint32_t k = take(ctl + kTaskTicket);
-        s_pick[parity] = k < (uint32_t)f.r.ntasks ? f.task_order[k] : -1;
+        s_pick[parity] = k < (uint32_t)f.r.ntasks ? (int)k : -1;
       }
       __syncthreads();
       const int task = __builtin_amdgcn_readfirstlane(s_pick[parity]);
       parity ^= 1;
       if (task < 0) break;
-      const int t = task / f.r.slabs;
-      const int slab = task - t * f.r.slabs;
+      const TaskRef k = task_ref(f.r, task);
       if (tid < 64) {
-        const bool ok = wait_tile(f.r, epoch, t, tid);
+        const bool ok = wait_tile(f.r, epoch, k.d, k.t, tid);
         if (tid == 0) s_abort = ok ? 0 : 1;
       }
       // The flag wait is ordered before every wave's reads of the tile.
       __syncthreads();
       if (s_abort) break;  // uniform
-      reduce_slab<kThreads, PEER_F32, OUT_F32>(f.r, t, slab, tid);
+      if (k.d == f.r.rank)
+        reduce_slab<kThreads, PEER_F32, OUT_F32>(f.r, k.t, k.slab, tid);
+      else
+        push_slab<kThreads, PEER_F32>(f.r, k.d, k.t, k.slab, tid);
     }
   }
   if (tid == 0) fused_check_out(ctl, epoch);

@@ -46,7 +46,14 @@ struct ReduceArgs {
   int32_t wait_slots;               // P source ranks + 1 release-group slot
   int32_t tm, tn;
   int32_t slabs;                    // row slabs per tile (task = tile x slab)
-  int32_t ntasks;                   // Q * slabs
+  int32_t ntasks;                   // tasks in the call (Q * slabs without a task list)
+  // Task list: entry j is the global task id (d * Q + t) * slabs + slab of
+  // partition d's tile t.  d == rank: reduce the slab into `out`; d != rank:
+  // push the outgoing slab into `staging` (a send task).  nullptr: task j is
+  // slab j % slabs of own tile j / slabs.
+  const int32_t* task_list;
+  const void* outgoing;             // peer dtype [M][N]: the GEMM's outgoing partials
+  void* staging;                    // peer dtype [M][N]: pushed copies (rows of partition d)
   uint32_t* ctl;                    // device control words (see check_out)
   uint64_t timeout_ticks;           // watchdog, in wall-clock ticks
   int32_t withhold_tile;            // -1, or a tile whose local wait watches `never_flag`
@@ -95,14 +102,13 @@ __device__ __forceinline__ void check_out(uint32_t* ctl, uint32_t epoch) {
 
 // The fused schedule: one kernel on the caller's stream.  Its workgroups take
 // GEMM blocks from per-XCD lists (block b of the dispatch order belongs to
-// XCD b % 8) until all are taken, then up to `workers` of them take reduction
-// tasks in `task_order`.
+// XCD b % 8) until all are taken, then up to `workers` of them take the tasks
+// of r.task_list in order.
 struct FusedArgs {
   GemmArgs g;
-  ReduceArgs r;
+  ReduceArgs r;               // r.task_list: the tasks in production order
   int32_t nb;                 // GEMM blocks
   int32_t workers;            // workgroups that may reduce (the comm budget)
-  const int32_t* task_order;  // [r.ntasks]: task ids in production order
 };
 
 // GEMM block shapes built: (bm, bn) in {128, 256}^2.

@@ -324,7 +324,7 @@ void assign_dispatch(Plan* plan, int64_t window) {
     for (int f = 0; f < 4; ++f) plan->launch[4 * b + f] = plan->blocks[4 * plan->dispatch[b] + f];
 }
 
-std::vector<int32_t> fused_task_order(const Plan& plan, int slabs) {
+std::vector<int32_t> task_list(const Plan& plan, int slabs, bool push) {
   const Geometry& g = plan.g;
   // Dispatch index of each logical position, and of each flag's block.
   std::vector<int64_t> at(g.NB);
@@ -333,25 +333,40 @@ std::vector<int32_t> fused_task_order(const Plan& plan, int slabs) {
     return (int64_t)(std::upper_bound(plan.first_tile.begin(), plan.first_tile.end(),
                                       (int32_t)tt) - plan.first_tile.begin()) - 1;
   };
-  auto flag_dispatch = [&](int32_t flag) -> int64_t {
+  auto flag_dispatch = [&](int64_t flag) -> int64_t {
     const int d = (int)(flag / g.Q);
     const int64_t tt = flag % g.Q;
     return at[position_of(g, plan.rank, plan.order, d, block_of_tile(tt))];
   };
-  std::vector<std::pair<int64_t, int64_t>> key(g.Q);  // (ready at, tile)
-  for (int64_t tt = 0; tt < g.Q; ++tt) {
-    int64_t last = -1;
-    for (int s = 0; s < plan.wait_slots; ++s) {
-      const int32_t f = plan.waits[tt * plan.wait_slots + s];
-      if (f >= 0) last = std::max(last, flag_dispatch(f));
+  struct Key {
+    int64_t ready;
+    int d;
+    int64_t t;
+    bool operator<(const Key& o) const {
+      return ready != o.ready ? ready < o.ready : d != o.d ? d < o.d : t < o.t;
     }
-    key[tt] = {last, tt};
+  };
+  std::vector<Key> keys;
+  for (int d = 0; d < g.P; ++d) {
+    if (d != plan.rank && !push) continue;
+    for (int64_t tt = 0; tt < g.Q; ++tt) {
+      int64_t last = -1;
+      if (d == plan.rank) {
+        for (int s = 0; s < plan.wait_slots; ++s) {
+          const int32_t f = plan.waits[tt * plan.wait_slots + s];
+          if (f >= 0) last = std::max(last, flag_dispatch(f));
+        }
+      } else {
+        last = flag_dispatch((int64_t)d * g.Q + tt);
+      }
+      keys.push_back(Key{last, d, tt});
+    }
   }
-  std::sort(key.begin(), key.end());
+  std::sort(keys.begin(), keys.end());
   std::vector<int32_t> order;
-  order.reserve((size_t)g.Q * slabs);
-  for (const auto& k : key)
-    for (int s = 0; s < slabs; ++s) order.push_back((int32_t)(k.second * slabs + s));
+  order.reserve(keys.size() * slabs);
+  for (const auto& k : keys)
+    for (int s = 0; s < slabs; ++s) order.push_back((int32_t)((k.d * g.Q + k.t) * slabs + s));
   return order;
 }
 

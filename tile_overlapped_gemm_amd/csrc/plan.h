@@ -67,10 +67,12 @@ int build_plan(const Geometry& g, int rank, int order, int peer_ready, int relea
 constexpr int kXcds = 8;
 void assign_dispatch(Plan* plan, int64_t window);
 
-// The fused schedule's task order (Sec. 3.1 "Matching task order"): tasks
-// t * slabs + s of the rank's partition, sorted by the dispatch index of the
-// last block any of the tile's wait slots depends on, ties by task number.
-// Needs plan->dispatch (assign_dispatch).
-std::vector<int32_t> fused_task_order(const Plan& plan, int slabs);
+// Tasks in production order (Sec. 3.1 "Matching task order") as global ids
+// (d * Q + t) * slabs + s: the reductions of the rank's tiles and, with
+// `push`, the send tasks of every other partition's tiles.  Tiles are sorted
+// by the dispatch index of the last block they wait for (a reduction: any of
+// its wait slots; a send task: the tile's own block), ties by partition, then
+// tile.  Needs plan->dispatch (assign_dispatch).
+std::vector<int32_t> task_list(const Plan& plan, int slabs, bool push);
 
 }  // namespace entwine

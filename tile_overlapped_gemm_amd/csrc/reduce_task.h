@@ -126,15 +126,20 @@ __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t
   }
 }
 
-// Wave 0 waits until every flag that task tile t depends on equals `epoch`.
-// Lane k (< P + 1) watches wait slot k.  Returns false (uniform across the
+// Wave 0 waits until every flag that tile t of partition d depends on equals
+// `epoch`.  For the own partition lane k (< P + 1) watches wait slot k; a
+// send task (d != rank) waits for the tile's own flag only.  Returns false (uniform across the
 // wave) if the watchdog expired, or if the sticky error word is set: once one
 // workgroup has timed out, the others stop waiting too, so a failed call ends
 // within one timeout whatever its task count.
-__device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int t, int lane) {
+__device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int d, int t, int lane) {
   int32_t idx = -1;
-  if (lane < a.wait_slots) idx = a.waits[t * a.wait_slots + lane];
-  if (t == a.withhold_tile && lane == a.rank) idx = a.never_flag;
+  if (d != a.rank) {
+    idx = lane == 0 ? d * a.Q + t : -1;  // a send task: the tile's own flag
+  } else {
+    if (lane < a.wait_slots) idx = a.waits[t * a.wait_slots + lane];
+    if (t == a.withhold_tile && lane == a.rank) idx = a.never_flag;
+  }
   const uint32_t* f = idx >= 0 ? a.flags + idx : nullptr;
   const uint64_t start = wall_clock64();
   while (true) {
@@ -182,6 +187,43 @@ __device__ __forceinline__ void reduce_slab(const ReduceArgs& a, int t, int slab
       e[u] = (int64_t)(row0 + r) * a.N + col0 + col;
     }
     reduce_chunks<kUnroll, PEER_F32, OUT_F32>(a, e, ok);
+  }
+}
+
+// Global task id -> (partition, tile, slab).
+struct TaskRef {
+  int d, t, slab;
+};
+__device__ __forceinline__ TaskRef task_ref(const ReduceArgs& a, int j) {
+  const int g = a.task_list ? a.task_list[j] : a.rank * a.Q * a.slabs + j;
+  const int dt = g / a.slabs;
+  const int d = dt / a.Q;
+  return TaskRef{d, dt - d * a.Q, g - dt * a.slabs};
+}
+
+// Push row slab `slab` of partition d's tile t from the outgoing partials to
+// the staging buffer (the stand-in for the transfer to peer d): 16-byte
+// chunks, thread tid of THREADS takes chunks tid, tid + THREADS, ...
+template <int THREADS, bool PEER_F32>
+__device__ __forceinline__ void push_slab(const ReduceArgs& a, int d, int t, int slab, int tid) {
+  constexpr int kPerChunk = PEER_F32 ? 4 : 8;  // elements per 16 bytes
+  const int chunks_per_row = a.tn / kPerChunk;
+  const int slab_rows = a.tm / a.slabs;
+  const int row0 = a.tiles[2 * t] * a.tm + slab * slab_rows;
+  const int col0 = a.tiles[2 * t + 1] * a.tn;
+  const int rows = min(slab_rows, a.R - row0);
+  const int cols = min(a.tn, a.N - col0);
+  const int n_chunks = rows > 0 ? rows * chunks_per_row : 0;
+  const int64_t base = ((int64_t)d * a.R + row0) * a.N + col0;
+  const char* src = static_cast<const char*>(a.outgoing);
+  char* dst = static_cast<char*>(a.staging);
+  for (int c = tid; c < n_chunks; c += THREADS) {
+    const int r = c / chunks_per_row;
+    const int col = (c - r * chunks_per_row) * kPerChunk;
+    if (col >= cols) continue;
+    const int64_t off = (base + (int64_t)r * a.N + col) * (PEER_F32 ? 4 : 2);
+    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
+    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + off));
   }
 }
 

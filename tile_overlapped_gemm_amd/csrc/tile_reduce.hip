@@ -40,10 +40,9 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   const uint32_t epoch = a.ctl[kEpoch];
   int parity = 0;
   for (int task = blockIdx.x; task < a.ntasks; task += gridDim.x, parity ^= 1) {
-    const int t = task / a.slabs;
-    const int slab = task - t * a.slabs;
+    const TaskRef k = task_ref(a, task);
     if (tid < 64) {
-      const bool ok = a.nowait || wait_tile(a, epoch, t, tid);
+      const bool ok = a.nowait || wait_tile(a, epoch, k.d, k.t, tid);
       if (tid == 0) s_abort[parity] = ok ? 0 : 1;
     }
     // The flag wait is ordered before every wave's reads of the tile.  The
@@ -52,7 +51,10 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
     __syncthreads();
     if (s_abort[parity]) break;  // uniform: every thread read the same value
 
-    reduce_slab<THREADS, PEER_F32, OUT_F32>(a, t, slab, tid);
+    if (k.d == a.rank)
+      reduce_slab<THREADS, PEER_F32, OUT_F32>(a, k.t, k.slab, tid);
+    else
+      push_slab<THREADS, PEER_F32>(a, k.d, k.t, k.slab, tid);
   }
   // Every workgroup, finished or timed out, checks out.
   if (tid == 0 && !a.nowait) check_out(a.ctl, epoch);
