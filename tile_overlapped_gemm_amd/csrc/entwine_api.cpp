@@ -76,11 +76,12 @@ struct Workspace {
   int device = -1;
   int cus = 0;
   int wall_khz = 100000;
-  hipStream_t s_gemm = nullptr, s_red = nullptr;
+  hipStream_t s_red = nullptr;  // the overlapped schedule's reducer
+  // ev_gemm / ev_red: the last eager call's GEMM and last reduction kernel.
   hipEvent_t ev_fork = nullptr, ev_gemm = nullptr, ev_red = nullptr;
   // Separate events for calls made while the caller's stream is being
   // captured into a graph, so that eager calls never wait on a captured record.
-  hipEvent_t cap_fork = nullptr, cap_gemm = nullptr, cap_red = nullptr;
+  hipEvent_t cap_fork = nullptr, cap_red = nullptr;
   bool have_prev = false;
   float* own = nullptr;
   size_t own_bytes = 0;
@@ -119,9 +120,11 @@ void destroy_workspace(Workspace* w) {
   int prev = -1;
   (void)hipGetDevice(&prev);
   (void)hipSetDevice(w->device);
-  if (w->s_gemm) (void)hipStreamSynchronize(w->s_gemm);
   if (w->s_red) (void)hipStreamSynchronize(w->s_red);
-  if (w->have_prev) (void)hipEventSynchronize(w->ev_red);  // work on a caller's stream
+  if (w->have_prev) {  // work on a caller's stream
+    (void)hipEventSynchronize(w->ev_gemm);
+    (void)hipEventSynchronize(w->ev_red);
+  }
   for (auto& kv : w->plans) free_plan(kv.second.get());
   w->plans.clear();
   for (auto* v : {&w->timing_live, &w->timing_free})
@@ -137,12 +140,11 @@ void destroy_workspace(Workspace* w) {
   if (w->flags) (void)hipFree(w->flags);
   if (w->error) (void)hipFree(w->error);
   if (w->ctl) (void)hipFree(w->ctl);
-  for (hipEvent_t e : {w->cap_fork, w->cap_gemm, w->cap_red})
+  for (hipEvent_t e : {w->cap_fork, w->cap_red})
     if (e) (void)hipEventDestroy(e);
   if (w->ev_fork) (void)hipEventDestroy(w->ev_fork);
   if (w->ev_gemm) (void)hipEventDestroy(w->ev_gemm);
   if (w->ev_red) (void)hipEventDestroy(w->ev_red);
-  if (w->s_gemm) (void)hipStreamDestroy(w->s_gemm);
   if (w->s_red) (void)hipStreamDestroy(w->s_red);
 
   if (prev >= 0) (void)hipSetDevice(prev);
@@ -162,13 +164,11 @@ int get_workspace(Workspace** out) {
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     w->wall_khz = khz;
-  HIP_TRY(hipStreamCreateWithFlags(&w->s_gemm, hipStreamNonBlocking));
   HIP_TRY(hipStreamCreateWithFlags(&w->s_red, hipStreamNonBlocking));
   HIP_TRY(hipEventCreateWithFlags(&w->ev_fork, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&w->ev_gemm, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&w->ev_red, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&w->cap_fork, hipEventDisableTiming));
-  HIP_TRY(hipEventCreateWithFlags(&w->cap_gemm, hipEventDisableTiming));
   HIP_TRY(hipEventCreateWithFlags(&w->cap_red, hipEventDisableTiming));
   HIP_TRY(hipMalloc(&w->error, sizeof(int32_t)));
   HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
@@ -184,11 +184,12 @@ int get_workspace(Workspace** out) {
 // Grow a device buffer; growth waits for all of this workspace's work.
 int ensure(Workspace* w, void** buf, size_t* have, size_t need, bool zero) {
   if (*have >= need && *buf) return ENTWINE_OK;
-  HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
-  // The previous eager call's last kernel, which may have run on a caller's
-  // stream.
-  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
+  // The previous eager call's kernels, which ran on a caller's stream too.
+  if (w->have_prev) {
+    HIP_TRY(hipEventSynchronize(w->ev_gemm));
+    HIP_TRY(hipEventSynchronize(w->ev_red));
+  }
   if (*buf) {
     HIP_TRY(hipFree(*buf));
     *buf = nullptr;
@@ -561,7 +562,10 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     // Resident workgroups, but no more than there is work for.
     const int64_t grid =
         std::min<int64_t>((int64_t)fused_per_cu * w->cus, g.NB + (int64_t)fa.workers);
-    if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+    if (w->have_prev && !capturing) {
+      HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
+      HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+    }
     if (g_timing) {
       HIP_TRY(hipEventRecord(tp.g0, stream));
       HIP_TRY(hipEventRecord(tp.r0, stream));
@@ -576,6 +580,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       w->timing_live.push_back(tp);
     }
     if (!capturing) {
+      HIP_TRY(hipEventRecord(w->ev_gemm, stream));
       HIP_TRY(hipEventRecord(w->ev_red, stream));
       w->have_prev = true;
     }
@@ -616,33 +621,34 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     ra.nowait = 1;
   }
 
-  // Kernels that do not run concurrently (the sequential schedule, a single
-  // stage) run on the caller's stream: no fork, no join.  The overlapped
-  // schedule forks both internal streams from the caller's stream and joins
-  // them back.  Either way the work starts after this workspace's previous
-  // eager call.  Inside a capture the graph's own edges order the work and
-  // the capture events are used instead.
+  // Everything but the overlapped schedule's reducer runs on the caller's
+  // stream: the GEMM, the sequential reduction, a single stage.  The reducer
+  // runs on an internal stream forked from the caller's stream just before
+  // the GEMM, and the caller's stream joins it after the GEMM; cross-stream
+  // waits cost several µs each, so no other stream is forked.  The work
+  // starts after this workspace's previous eager call.  Inside a capture the
+  // graph's own edges order the work and the capture events are used instead.
   const bool forked = !sequential && rs.stages == ENTWINE_STAGES_ALL;
-  hipStream_t s_gemm = forked ? w->s_gemm : stream;
   hipStream_t s_red = forked ? w->s_red : stream;
   hipEvent_t ev_fork = capturing ? w->cap_fork : w->ev_fork;
-  hipEvent_t ev_gemm = capturing ? w->cap_gemm : w->ev_gemm;
   hipEvent_t ev_red = capturing ? w->cap_red : w->ev_red;
+  if (w->have_prev && !capturing) {
+    HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
+    HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+  }
   if (forked) {
     HIP_TRY(hipEventRecord(ev_fork, stream));
-    HIP_TRY(hipStreamWaitEvent(s_gemm, ev_fork, 0));
     HIP_TRY(hipStreamWaitEvent(s_red, ev_fork, 0));
   }
-  if (w->have_prev && !capturing) HIP_TRY(hipStreamWaitEvent(s_gemm, w->ev_red, 0));
 
-  if (g_timing) HIP_TRY(hipEventRecord(tp.g0, s_gemm));
+  if (g_timing) HIP_TRY(hipEventRecord(tp.g0, stream));
   if (run_gemm) {
-    hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, s_gemm);
+    hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, stream);
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
   }
-  if (g_timing) HIP_TRY(hipEventRecord(tp.g1, s_gemm));
-  if (forked) HIP_TRY(hipEventRecord(ev_gemm, s_gemm));
+  if (g_timing) HIP_TRY(hipEventRecord(tp.g1, stream));
+  if (!capturing) HIP_TRY(hipEventRecord(w->ev_gemm, stream));
   if (g_timing) HIP_TRY(hipEventRecord(tp.r0, s_red));
   if (run_red) {
     hipError_t e =
@@ -653,11 +659,8 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));
   if (forked || !capturing) HIP_TRY(hipEventRecord(ev_red, s_red));
   if (!capturing) w->have_prev = true;
-  if (forked) {
-    // Join: the caller's stream continues after both kernels.
-    HIP_TRY(hipStreamWaitEvent(stream, ev_gemm, 0));
-    HIP_TRY(hipStreamWaitEvent(stream, ev_red, 0));
-  }
+  // Join: the caller's stream continues after the reducer too.
+  if (forked) HIP_TRY(hipStreamWaitEvent(stream, ev_red, 0));
   if (g_timing) w->timing_live.push_back(tp);
   return ENTWINE_OK;
 }
@@ -809,9 +812,11 @@ int entwine_device_status(void* stream) {
   int rc = get_workspace(&w);
   if (rc) return rc;
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
-  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
+  if (w->have_prev) {
+    HIP_TRY(hipEventSynchronize(w->ev_gemm));
+    HIP_TRY(hipEventSynchronize(w->ev_red));
+  }
   int32_t err = 0;
   HIP_TRY(hipMemcpy(&err, w->error, sizeof err, hipMemcpyDeviceToHost));
   if (err != 0) {
@@ -847,9 +852,11 @@ int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* 
   auto it = g_ws.find(dev);
   if (it == g_ws.end()) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no workspace on this device yet");
   Workspace* w = it->second.get();
-  HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
-  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
+  if (w->have_prev) {
+    HIP_TRY(hipEventSynchronize(w->ev_gemm));
+    HIP_TRY(hipEventSynchronize(w->ev_red));
+  }
   if (own_partial) *own_partial = w->own;
   if (outgoing) *outgoing = w->outgoing;
   if (bytes)
@@ -864,9 +871,11 @@ int entwine_staging(const void** staging, int64_t* bytes) {
   auto it = g_ws.find(dev);
   if (it == g_ws.end()) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no workspace on this device yet");
   Workspace* w = it->second.get();
-  HIP_TRY(hipStreamSynchronize(w->s_gemm));
   HIP_TRY(hipStreamSynchronize(w->s_red));
-  if (w->have_prev) HIP_TRY(hipEventSynchronize(w->ev_red));
+  if (w->have_prev) {
+    HIP_TRY(hipEventSynchronize(w->ev_gemm));
+    HIP_TRY(hipEventSynchronize(w->ev_red));
+  }
   if (staging) *staging = w->staging;
   if (bytes) *bytes = (int64_t)w->staging_bytes;
   return ENTWINE_OK;
