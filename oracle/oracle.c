@@ -19,6 +19,8 @@
  *   - Sec. 4.2 (Producer Traversal, Publication, and Reduction), ReduceTile:
  *     the accumulator starts from the local contribution and the peers'
  *     values are added in rank order.
+ *   - Sec. 5.2.2 (Layer-Level Performance): the layer chain continues the
+ *     ReduceScatter with a residual addition and an RMSNorm.
  *
  * Everything here is evaluated in fp64 from the exact values that the device
  * receives (bf16 or fp32 inputs widened exactly), with plain loops and no
@@ -249,16 +251,20 @@ static uint16_t round_to_bf16(float f)
 /*
  * The ReduceTile closed form (Sec. 4.2) evaluated in binary32:
  *   acc = own[e];  for r ascending, r != rank: acc = fl32(acc + V_r[e]);
+ *   with a residual (the layer chain of Sec. 5.2.2, added as one more term
+ *   after the peers): acc = fl32(acc + residual[e]);
  *   out[e] = acc rounded to out_dtype (bf16 with round-to-nearest-even, or
  *            fp32 unchanged).
- * `own` is the rank's own fp32 partial for its partition ([rows][N]).
+ * `own` is the rank's own fp32 partial for its partition ([rows][N]);
+ * `residual` is NULL or [rows][N] in res_dtype.
  */
 int oracle_reduce_f32(const float *own, const void *const *peers, int peer_dtype,
-                      int P, int rank, int64_t rows, int64_t N, int out_dtype,
-                      void *out)
+                      int P, int rank, int64_t rows, int64_t N, const void *residual,
+                      int res_dtype, int out_dtype, void *out)
 {
     if (!own || !out || P < 1 || rank < 0 || rank >= P || rows < 0 || N < 0 ||
         (peer_dtype != ORACLE_BF16 && peer_dtype != ORACLE_F32) ||
+        (res_dtype != ORACLE_BF16 && res_dtype != ORACLE_F32) ||
         (out_dtype != ORACLE_BF16 && out_dtype != ORACLE_F32))
         return ORACLE_EINVAL;
     for (int r = 0; r < P; ++r)
@@ -272,10 +278,39 @@ int oracle_reduce_f32(const float *own, const void *const *peers, int peer_dtype
             float v = (float)load_elem(peers[r], peer_dtype, e);
             acc = acc + v;
         }
+        if (residual)
+            acc = acc + (float)load_elem(residual, res_dtype, e);
         if (out_dtype == ORACLE_BF16)
             ((uint16_t *)out)[e] = round_to_bf16(acc);
         else
             ((float *)out)[e] = acc;
+    }
+    return ORACLE_OK;
+}
+
+/*
+ * RMSNorm of each row (Sec. 5.2.2: the layer chain's normalization after the
+ * residual addition), in fp64 from the stored values h:
+ *   ms_i = (1/N) * sum_j h[i][j]^2
+ *   y[i][j] = gamma[j] * h[i][j] / sqrt(ms_i + eps)
+ * h is [rows][N] and gamma [N], each bf16 bits or fp32; y is [rows][N] double.
+ */
+int oracle_rmsnorm(const void *h, int h_dtype, const void *gamma, int g_dtype, double eps,
+                   int64_t rows, int64_t N, double *y)
+{
+    if (!h || !gamma || !y || rows < 0 || N <= 0 || !(eps >= 0.0) ||
+        (h_dtype != ORACLE_BF16 && h_dtype != ORACLE_F32) ||
+        (g_dtype != ORACLE_BF16 && g_dtype != ORACLE_F32))
+        return ORACLE_EINVAL;
+    for (int64_t i = 0; i < rows; ++i) {
+        double ss = 0.0;
+        for (int64_t j = 0; j < N; ++j) {
+            double v = load_elem(h, h_dtype, i * N + j);
+            ss += v * v;
+        }
+        double scale = 1.0 / sqrt(ss / (double)N + eps);
+        for (int64_t j = 0; j < N; ++j)
+            y[i * N + j] = load_elem(gamma, g_dtype, j) * load_elem(h, h_dtype, i * N + j) * scale;
     }
     return ORACLE_OK;
 }

@@ -10,8 +10,9 @@ receives (bf16 as uint16 bit patterns, or float32) and returns fp64 results,
 except :func:`reduce_f32`, the bit-exact fp32 closed form of the reduction.
 
 Source: "Entwine: Coordinating Tiled Computation and Fine-Grained
-Communication across GPUs" (paperpeel.com/paper/2609.11562), Sec. 2.1, 3.1 and
-4.2 (ReduceTile); see oracle.c for the definitions.
+Communication across GPUs" (paperpeel.com/paper/2609.11562), Sec. 2.1, 3.1,
+4.2 (ReduceTile) and 5.2.2 (the layer chain); see oracle.c for the
+definitions.
 """
 from __future__ import annotations
 
@@ -56,8 +57,10 @@ def load(path: str = LIB):
                                    i32, i32, i64, i64, i32, vp]
     lib.oracle_gemm_rs.restype = i32
     lib.oracle_reduce_f32.argtypes = [vp, ctypes.POINTER(vp), i32, i32, i32, i64, i64,
-                                      i32, vp]
+                                      vp, i32, i32, vp]
     lib.oracle_reduce_f32.restype = i32
+    lib.oracle_rmsnorm.argtypes = [vp, i32, vp, i32, ctypes.c_double, i64, i64, vp]
+    lib.oracle_rmsnorm.restype = i32
     lib.oracle_num_threads.argtypes = [i32]
     lib.oracle_num_threads.restype = i32
     if path == LIB:
@@ -141,8 +144,9 @@ def gemm_rs(X: np.ndarray, W: np.ndarray, peers: list, P: int, rank: int,
 
 
 def reduce_f32(own: np.ndarray, peers: list, P: int, rank: int,
-               out_dtype: int = BF16, lib=None) -> np.ndarray:
-    """Bit-exact fp32 reduction: acc = own, += peers ascending, round to out."""
+               out_dtype: int = BF16, lib=None, residual: np.ndarray | None = None) -> np.ndarray:
+    """Bit-exact fp32 reduction: acc = own, += peers ascending, += residual
+    (if given), round to out."""
     lib = lib or load()
     own = np.ascontiguousarray(own, dtype=np.float32)
     rows, N = own.shape
@@ -160,6 +164,26 @@ def reduce_f32(own: np.ndarray, peers: list, P: int, rank: int,
         keep.append(v)
         arr[r] = _ptr(v)
     out = np.empty((rows, N), dtype=np.uint16 if out_dtype == BF16 else np.float32)
-    _check(lib.oracle_reduce_f32(_ptr(own), arr, pdt, P, rank, rows, N, out_dtype,
-                                 _ptr(out)), "reduce_f32")
+    res_ptr, res_dt = None, BF16
+    if residual is not None:
+        residual = np.ascontiguousarray(residual)
+        if residual.shape != (rows, N):
+            raise ValueError(f"residual has shape {residual.shape}, expected {(rows, N)}")
+        res_ptr, res_dt = _ptr(residual), _dtype_code(residual)
+    _check(lib.oracle_reduce_f32(_ptr(own), arr, pdt, P, rank, rows, N, res_ptr, res_dt,
+                                 out_dtype, _ptr(out)), "reduce_f32")
     return out
+
+
+def rmsnorm(h: np.ndarray, gamma: np.ndarray, eps: float, lib=None) -> np.ndarray:
+    """fp64 RMSNorm of each row: gamma * h / sqrt(mean(h^2) + eps)."""
+    lib = lib or load()
+    h = np.ascontiguousarray(h)
+    gamma = np.ascontiguousarray(gamma)
+    rows, N = h.shape
+    if gamma.shape != (N,):
+        raise ValueError(f"gamma has shape {gamma.shape}, expected {(N,)}")
+    y = np.empty((rows, N), dtype=np.float64)
+    _check(lib.oracle_rmsnorm(_ptr(h), _dtype_code(h), _ptr(gamma), _dtype_code(gamma),
+                              float(eps), rows, N, _ptr(y)), "rmsnorm")
+    return y

@@ -177,6 +177,69 @@ def pin_reduce_matches_fp64_when_exact(lib):
     np.testing.assert_array_equal(bf16_to_f32(got).astype(np.float64), ref)
 
 
+def pin_residual_is_added_last(lib):
+    """With a residual, the fp32 reduction adds it as one more term after the
+    peers: the same as a reduction over one more rank whose contribution is the
+    residual, at a rank index above all others.  The values are chosen so that
+    adding the residual first (or in fp64) gives other bits:
+      own = 2^24, V_0 = 1, residual = -2^24  ->  ((2^24 + 1) - 2^24) = 0."""
+    own = np.array([[2.0 ** 24, 1.0, 3.0, -7.25]], dtype=np.float32)
+    v0 = np.array([[1.0, 2.0 ** -30, -1.0, 0.25]], dtype=np.float32)
+    res = np.array([[-(2.0 ** 24), 0.0, 0.5, 7.0]], dtype=np.float32)
+    got = orc.reduce_f32(own, [v0, None], 2, 1, orc.F32, lib=lib, residual=res)
+    np.testing.assert_array_equal(got, np.array([[0.0, 1.0, 2.5, 0.0]], dtype=np.float32))
+    as_rank = orc.reduce_f32(own, [v0, None, res], 3, 1, orc.F32, lib=lib)
+    np.testing.assert_array_equal(got, as_rank)
+    # bf16 operands and output on random data: the same identity
+    g = rng(906, 0, 0)
+    own = g.standard_normal((8, 40), dtype=np.float32)
+    peers = [_rand_bf16(g, (8, 40)) if r != 2 else None for r in range(4)]
+    res = _rand_bf16(g, (8, 40), 4.0)
+    got = orc.reduce_f32(own, peers, 4, 2, orc.BF16, lib=lib, residual=res)
+    np.testing.assert_array_equal(got, orc.reduce_f32(own, peers + [res], 5, 2, orc.BF16, lib=lib))
+    zero = np.zeros((8, 40), dtype=np.uint16)
+    np.testing.assert_array_equal(orc.reduce_f32(own, peers, 4, 2, orc.BF16, lib=lib, residual=zero),
+                                  orc.reduce_f32(own, peers, 4, 2, orc.BF16, lib=lib))
+
+
+def pin_rmsnorm_handworked(lib):
+    """RMSNorm by hand (tests/golden/rmsnorm_handworked.json): h = [1, 2, 3, 4],
+    mean of squares 30/4 = 7.5; with eps = 0.5 the divisor is sqrt(8), so
+    y = gamma * h / (2 sqrt 2)."""
+    with open(os.path.join(GOLDEN, "rmsnorm_handworked.json")) as f:
+        fx = json.load(f)
+    for case in fx["cases"]:
+        h = np.array(case["h"], dtype=np.float32)
+        gamma = np.array(case["gamma"], dtype=np.float32)
+        got = orc.rmsnorm(h, gamma, case["eps"], lib=lib)
+        np.testing.assert_allclose(got, np.array(case["y"]), rtol=1e-15, atol=0)
+        got = orc.rmsnorm(bf16_bits(h), bf16_bits(gamma), case["eps"], lib=lib)
+        np.testing.assert_allclose(got, np.array(case["y"]), rtol=1e-15, atol=0)
+
+
+def pin_rmsnorm_invariants(lib):
+    """Closed forms: a constant row c gives gamma * c / sqrt(c^2 + eps); with
+    eps = 0 the result does not change when a row is scaled by a > 0 and flips
+    sign for a < 0; every output row has mean square mean(gamma^2 h^2)/ms."""
+    g = rng(907, 0, 0)
+    N = 96
+    gamma = g.standard_normal(N, dtype=np.float32)
+    for c, eps in ((3.0, 1e-5), (-0.125, 0.25), (1e-3, 1e-6)):
+        h = np.full((1, N), c, dtype=np.float32)
+        c = float(h[0, 0])  # the value stored
+        got = orc.rmsnorm(h, gamma, eps, lib=lib)
+        want = gamma.astype(np.float64) * c / np.sqrt(c * c + eps)
+        np.testing.assert_allclose(got[0], want, rtol=1e-14, atol=0)
+    h = g.standard_normal((5, N), dtype=np.float32)
+    base = orc.rmsnorm(h, gamma, 0.0, lib=lib)
+    for a in (2.0, 0.5, -4.0):
+        got = orc.rmsnorm((h * np.float32(a)).astype(np.float32), gamma, 0.0, lib=lib)
+        np.testing.assert_allclose(got, np.sign(a) * base, rtol=1e-13, atol=1e-15)
+    ones = np.ones(N, dtype=np.float32)
+    y = orc.rmsnorm(h, ones, 0.0, lib=lib)
+    np.testing.assert_allclose((y ** 2).mean(axis=1), np.ones(5), rtol=1e-13)
+
+
 ALL_PINS = [
     pin_single_rank_is_matmul,
     pin_identity_X,
@@ -186,4 +249,7 @@ ALL_PINS = [
     pin_reduce_rounding,
     pin_reduce_order,
     pin_reduce_matches_fp64_when_exact,
+    pin_residual_is_added_last,
+    pin_rmsnorm_handworked,
+    pin_rmsnorm_invariants,
 ]

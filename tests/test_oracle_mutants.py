@@ -43,6 +43,24 @@ MUTANTS = {
     "rounding": ("(u + 0x7fffu + lsb) >> 16", "(u + 0x8000u) >> 16"),
     # the local contribution is left out of the reduction
     "reduce_no_local": ("float acc = own[e];", "float acc = 0.0f * own[e];"),
+    # the residual is added before the peers
+    "residual_first": ("""        float acc = own[e];
+        for (int r = 0; r < P; ++r) {""", """        float acc = own[e];
+        if (residual)
+            acc = acc + (float)load_elem(residual, res_dtype, e);
+        for (int r = 0; r < P; ++r) {"""),
+    # the residual is not added
+    "residual_dropped": ("            acc = acc + (float)load_elem(residual, res_dtype, e);",
+                         "            acc = acc + 0.0f;"),
+    # RMSNorm: sum of squares instead of the mean
+    "rms_sum": ("sqrt(ss / (double)N + eps)", "sqrt(ss + eps)"),
+    # RMSNorm: eps left out
+    "rms_eps": ("sqrt(ss / (double)N + eps)", "sqrt(ss / (double)N)"),
+    # RMSNorm: no square root
+    "rms_sqrt": ("1.0 / sqrt(ss / (double)N + eps)", "1.0 / (ss / (double)N + eps)"),
+    # RMSNorm: gamma not applied
+    "rms_gamma": ("load_elem(gamma, g_dtype, j) * load_elem(h, h_dtype, i * N + j) * scale",
+                  "load_elem(h, h_dtype, i * N + j) * scale"),
 }
 
 
