@@ -200,6 +200,33 @@ int entwine_gemm_rs_ex(const void* X, const void* W, const void* const* peer_par
                        int tile_order, int comm_budget, void* stream,
                        const entwine_config* cfg);
 
+/*
+ * entwine_gemm_rs_rmsnorm -- the layer chain of Sec. 5.2.2 (Layer-Level
+ * Performance): the GEMM-ReduceScatter above, then a residual addition and an
+ * RMSNorm over the rank's rows, in one call with the same schedules.
+ *
+ *   residual  device, out dtype [M/P][N]: the residual stream's rows of
+ *             partition `rank`.  May be h_out itself (in-place update);
+ *             otherwise it must not overlap h_out.
+ *   gamma     device, out dtype [N]: the norm weight.
+ *   eps       finite, >= 0 (added to the mean of squares).
+ *   h_out     device, out dtype [M/P][N]: h = RS + residual.  The residual is
+ *             added in fp32 after the peers, before the single rounding to the
+ *             output type, so h is what the reduction alone would give with one
+ *             more contribution.
+ *   y_out     device, out dtype [M/P][N]: y[i][j] = gamma[j] * h[i][j] /
+ *             sqrt(mean_j(h[i][j]^2) + eps), from the rounded h, in fp32,
+ *             rounded once.  Must not overlap any other operand.
+ * All other arguments and all errors are those of entwine_gemm_rs_ex; a NULL,
+ * misaligned or overlapping chain operand, or a bad eps, is
+ * ENTWINE_ERR_INVALID_ARGUMENT.  16-byte alignment throughout.
+ */
+int entwine_gemm_rs_rmsnorm(const void* X, const void* W, const void* const* peer_partials,
+                            const void* residual, const void* gamma, float eps, void* h_out,
+                            void* y_out, int64_t M, int64_t N, int64_t K_local, int P, int rank,
+                            int tile_order, int comm_budget, void* stream,
+                            const entwine_config* cfg);
+
 /* ------------------------------------------------------------------------
  * Schedule queries (host only, no GPU needed).  They return the tables that
  * the kernels receive, for inspection and testing.

@@ -132,3 +132,26 @@ def test_plan_query_errors(lib):
         tog.entwine_plan_shape(512, 256, 4, 96, 128, 128, 128)
     with pytest.raises(tog.EntwineError):
         tog.entwine_plan_blocks(512, 256, 4, 4, tog.ORDER_INTERLEAVED, 128, 128, 128, 128)
+
+
+def chain_call(residual=FAKE * 8, gamma=FAKE * 9, eps=1e-5, h_out=FAKE * 3, y_out=FAKE * 10,
+               M=512, N=256, K=128, P=4, rank=0):
+    lib = tog.load()
+    peers = [None if r == rank else FAKE * (4 + r) for r in range(P)]
+    arr = (ctypes.c_void_p * P)(*peers)
+    return lib.entwine_gemm_rs_rmsnorm(FAKE, FAKE * 2, arr, residual, gamma, eps, h_out, y_out,
+                                       M, N, K, P, rank, tog.ORDER_INTERLEAVED, 4, None, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(residual=0), dict(gamma=0), dict(y_out=0),
+    dict(gamma=FAKE * 9 + 4),                         # misaligned
+    dict(eps=-1.0), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(y_out=FAKE * 3),                             # y aliases h
+    dict(y_out=FAKE * 8),                             # y aliases the residual
+    dict(residual=FAKE * 3 + 1024),                   # residual partly overlaps h
+    dict(gamma=FAKE * 3 + 256),                       # gamma inside h
+])
+def test_chain_validation_before_any_device_call(lib, kw):
+    assert chain_call(**kw) == tog.ENTWINE_ERR_INVALID_ARGUMENT
+    assert lib.entwine_last_error_message().decode()

@@ -35,7 +35,8 @@ SCHEDULE_AUTO, SCHEDULE_STREAMS, SCHEDULE_FUSED = 0, 1, 2
 
 # Names exported by the library (one per declaration in include/entwine.h).
 EXPORTS = [
-    "entwine_gemm_rs", "entwine_config_init", "entwine_gemm_rs_ex", "entwine_plan_shape",
+    "entwine_gemm_rs", "entwine_config_init", "entwine_gemm_rs_ex", "entwine_gemm_rs_rmsnorm",
+    "entwine_plan_shape",
     "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
     "entwine_plan_task_order", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
@@ -101,6 +102,8 @@ def load(path: str = LIB):
         "entwine_gemm_rs_ex": ([vp, vp, ctypes.POINTER(vp), vp, i64, i64, i64, i32, i32, i32, i32, vp,
                                 pcfg], i32),
         "entwine_config_init": ([pcfg], None),
+        "entwine_gemm_rs_rmsnorm": ([vp, vp, ctypes.POINTER(vp), vp, vp, ctypes.c_float, vp, vp,
+                                     i64, i64, i64, i32, i32, i32, i32, vp, pcfg], i32),
         "entwine_plan_shape": ([i64, i64, i32, i32, i32, i32, i32, pi64, pi64, pi64], i32),
         "entwine_plan_blocks": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, pi32, i64], i32),
         "entwine_plan_dispatch": ([i64, i64, i32, i32, i32, i32, i32, i32, i32, i64, pi32, i64], i32),
@@ -277,14 +280,22 @@ def entwine_plan_tasks(Q, comm_budget, consumer):
 
 # ----------------------------------------------------------- torch helper --
 
-def gemm_rs(X, W, peers, out, P: int, rank: int, tile_order: int = ORDER_AUTO,
-            comm_budget: int = BUDGET_AUTO, cfg: entwine_config | None = None, stream=None):
-    """torch front end: checks devices, dtypes, shapes and contiguity, then
-    calls entwine_gemm_rs(_ex) on the current (or given) stream.
+def entwine_gemm_rs_rmsnorm(X: int, W: int, peer_partials: list, residual: int, gamma: int,
+                            eps: float, h_out: int, y_out: int, M: int, N: int, K_local: int,
+                            P: int, rank: int, tile_order: int, comm_budget: int, stream: int,
+                            cfg: entwine_config | None = None) -> int:
+    """Raw pointers in, status out (raises EntwineError on failure)."""
+    lib = load()
+    arr = (ctypes.c_void_p * max(P, 1))(*[p or None for p in peer_partials])
+    rc = lib.entwine_gemm_rs_rmsnorm(X, W, arr, residual, gamma, eps, h_out, y_out, M, N,
+                                     K_local, P, rank, tile_order, comm_budget, stream,
+                                     ctypes.byref(cfg) if cfg is not None else None)
+    return _check(rc)
 
-    X [M][K] bf16, W [N][K] bf16, peers[r] [M/P][N] (None at `rank`),
-    out [M/P][N]; all CUDA tensors on one device.
-    """
+
+def _check_operands(X, W, peers, out, P, rank, cfg):
+    """Shapes, dtypes, devices and contiguity of the operation's operands;
+    returns (M, N, K, peer pointers)."""
     import torch
 
     if not (X.is_cuda and W.is_cuda and out.is_cuda):
@@ -315,7 +326,44 @@ def gemm_rs(X, W, peers, out, P: int, rank: int, tile_order: int = ORDER_AUTO,
         if p.dtype != want_peer:
             raise TypeError(f"peer {r} must be {want_peer} for this configuration")
         ptrs.append(p.data_ptr())
+    return M, N, K, ptrs
+
+
+def gemm_rs(X, W, peers, out, P: int, rank: int, tile_order: int = ORDER_AUTO,
+            comm_budget: int = BUDGET_AUTO, cfg: entwine_config | None = None, stream=None):
+    """torch front end: checks devices, dtypes, shapes and contiguity, then
+    calls entwine_gemm_rs(_ex) on the current (or given) stream.
+
+    X [M][K] bf16, W [N][K] bf16, peers[r] [M/P][N] (None at `rank`),
+    out [M/P][N]; all CUDA tensors on one device.
+    """
+    import torch
+
+    M, N, K, ptrs = _check_operands(X, W, peers, out, P, rank, cfg)
     if stream is None:
         stream = torch.cuda.current_stream(X.device)
     return entwine_gemm_rs(X.data_ptr(), W.data_ptr(), ptrs, out.data_ptr(), M, N, K, P, rank,
                            tile_order, comm_budget, stream.cuda_stream, cfg)
+
+
+def gemm_rs_rmsnorm(X, W, peers, residual, gamma, eps: float, h_out, y_out, P: int, rank: int,
+                    tile_order: int = ORDER_AUTO, comm_budget: int = BUDGET_AUTO,
+                    cfg: entwine_config | None = None, stream=None):
+    """torch front end of the layer chain: h_out = RS + residual, y_out =
+    RMSNorm(h_out) * gamma.  residual and h_out [M/P][N] (may be the same
+    tensor), gamma [N], y_out [M/P][N], all in the output dtype."""
+    import torch
+
+    M, N, K, ptrs = _check_operands(X, W, peers, h_out, P, rank, cfg)
+    for name, t, shape in (("residual", residual, (M // P, N)), ("gamma", gamma, (N,)),
+                           ("y_out", y_out, (M // P, N))):
+        if not t.is_cuda or not t.is_contiguous() or tuple(t.shape) != shape:
+            raise ValueError(f"{name} must be a contiguous device tensor of shape {shape}")
+        if t.dtype != h_out.dtype:
+            raise TypeError(f"{name} must be {h_out.dtype}")
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    return entwine_gemm_rs_rmsnorm(X.data_ptr(), W.data_ptr(), ptrs, residual.data_ptr(),
+                                   gamma.data_ptr(), eps, h_out.data_ptr(), y_out.data_ptr(), M,
+                                   N, K, P, rank, tile_order, comm_budget, stream.cuda_stream,
+                                   cfg)

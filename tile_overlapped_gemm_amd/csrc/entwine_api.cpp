@@ -355,9 +355,18 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   return ENTWINE_OK;
 }
 
+// The layer chain after the ReduceScatter (Sec. 5.2.2): `out` receives
+// h = RS + residual, and y = RMSNorm(h) with weight gamma.
+struct Chain {
+  const void* residual = nullptr;
+  const void* gamma = nullptr;
+  void* y = nullptr;
+  float eps = 0.0f;
+};
+
 int run(const void* X, const void* W, const void* const* peers, void* out, int64_t M, int64_t N,
         int64_t K, int P, int rank, int tile_order, int comm_budget, void* stream_,
-        const entwine_config* cfg) {
+        const entwine_config* cfg, const Chain* chain = nullptr) {
   int rc = check_shape(M, N, K, P, rank);
   if (rc) return rc;
   Resolved rs;
@@ -383,6 +392,27 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_partials[%d] is not 16-byte aligned", r);
     if (overlaps(out, out_bytes, peers[r], (size_t)g.R * N * peer_sz))
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "out overlaps peer_partials[%d]", r);
+  }
+  if (chain) {
+    if (!chain->residual || !chain->gamma || !chain->y)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "residual, gamma and y_out must be non-NULL");
+    if (!aligned16(chain->residual) || !aligned16(chain->gamma) || !aligned16(chain->y))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "residual, gamma and y_out must be 16-byte aligned");
+    if (!(chain->eps >= 0.0f) || chain->eps > 3.0e38f)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "eps must be finite and >= 0");
+    const size_t g_bytes = (size_t)N * out_sz;
+    const void* y = chain->y;
+    if (overlaps(y, out_bytes, X, (size_t)M * K * 2) || overlaps(y, out_bytes, W, (size_t)N * K * 2) ||
+        overlaps(y, out_bytes, out, out_bytes) || overlaps(y, out_bytes, chain->residual, out_bytes) ||
+        overlaps(y, out_bytes, chain->gamma, g_bytes))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "y_out overlaps another operand");
+    for (int r = 0; r < P; ++r)
+      if (r != rank && overlaps(y, out_bytes, peers[r], (size_t)g.R * N * peer_sz))
+        return fail(ENTWINE_ERR_INVALID_ARGUMENT, "y_out overlaps peer_partials[%d]", r);
+    if (chain->residual != out && overlaps(chain->residual, out_bytes, out, out_bytes))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "residual must be h_out itself or not overlap it");
+    if (overlaps(chain->gamma, g_bytes, out, out_bytes))
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "gamma overlaps h_out");
   }
 
   hipStream_t stream = static_cast<hipStream_t>(stream_);
@@ -544,6 +574,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ra.never_flag = (int32_t)(g.P * g.Q);
   ra.outgoing = w->outgoing;
   ra.staging = rs.push ? w->staging : nullptr;
+  ra.residual = chain ? chain->residual : nullptr;
   ra.task_list = d_task_list;
 
   if (fused) {
@@ -574,6 +605,9 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                                         (int)grid, stream);
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "fused launch failed: %s", hipGetErrorString(e));
+    if (chain && (e = launch_rmsnorm(out, chain->gamma, chain->y, (int)g.R, (int)N, chain->eps,
+                                     rs.out_f32, stream)) != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "RMSNorm launch failed: %s", hipGetErrorString(e));
     if (g_timing) {
       HIP_TRY(hipEventRecord(tp.g1, stream));
       HIP_TRY(hipEventRecord(tp.r1, stream));
@@ -655,6 +689,10 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
         launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, sequential, grid, s_red);
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
+    // The chain's normalization needs whole rows: after the reduction.
+    if (chain && (e = launch_rmsnorm(out, chain->gamma, chain->y, (int)g.R, (int)N, chain->eps,
+                                     rs.out_f32, s_red)) != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "RMSNorm launch failed: %s", hipGetErrorString(e));
   }
   if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));
   if (forked || !capturing) HIP_TRY(hipEventRecord(ev_red, s_red));
@@ -692,6 +730,20 @@ int entwine_gemm_rs_ex(const void* X, const void* W, const void* const* peer_par
                        int comm_budget, void* stream, const entwine_config* cfg) {
   return run(X, W, peer_partials, out, M, N, K_local, P, rank, tile_order, comm_budget, stream,
              cfg);
+}
+
+int entwine_gemm_rs_rmsnorm(const void* X, const void* W, const void* const* peer_partials,
+                            const void* residual, const void* gamma, float eps, void* h_out,
+                            void* y_out, int64_t M, int64_t N, int64_t K_local, int P, int rank,
+                            int tile_order, int comm_budget, void* stream,
+                            const entwine_config* cfg) {
+  Chain c;
+  c.residual = residual;
+  c.gamma = gamma;
+  c.y = y_out;
+  c.eps = eps;
+  return run(X, W, peer_partials, h_out, M, N, K_local, P, rank, tile_order, comm_budget, stream,
+             cfg, &c);
 }
 
 int entwine_plan_shape(int64_t M, int64_t N, int P, int block_m, int block_n, int tile_m,

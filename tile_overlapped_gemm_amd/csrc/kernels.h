@@ -52,6 +52,11 @@ struct ReduceArgs {
   // push the outgoing slab into `staging` (a send task).  nullptr: task j is
   // slab j % slabs of own tile j / slabs.
   const int32_t* task_list;
+  // Layer chain (residual addition before the RMSNorm): out dtype [R][N]
+  // added after the peers, before the rounding; nullptr for the plain
+  // operation.  May be `out` itself (each element is read, then written, by
+  // the same thread).
+  const void* residual;
   const void* outgoing;             // peer dtype [M][N]: the GEMM's outgoing partials
   void* staging;                    // peer dtype [M][N]: pushed copies (rows of partition d)
   uint32_t* ctl;                    // device control words (see check_out)
@@ -128,6 +133,11 @@ int gemm_blocks_per_cu(int bm, int bn, int variant);
 // Waves per GEMM workgroup (64 lanes each).
 int gemm_waves(int bm, int bn, int variant);
 int reduce_registers(int threads, int peer_f32, int out_f32);
+
+// RMSNorm of each of `rows` rows of h (out dtype [rows][N], N % 8 == 0):
+// y = gamma * h / sqrt(mean(h^2) + eps), one 256-thread workgroup per row.
+hipError_t launch_rmsnorm(const void* h, const void* gamma, void* y, int rows, int N, float eps,
+                          int out_f32, hipStream_t stream);
 
 // Fused kernel instances: the variant-0 pipelines of every block shape and
 // variant 3 of 256 x 256.  Returns hipErrorInvalidValue for other shapes.

@@ -101,12 +101,15 @@ __device__ __forceinline__ void store8<true>(void* base, int64_t e, const F8& ac
 }
 
 // Reduce U chunks at element offsets e[0..U): all loads first, then the
-// fixed-order fp32 sums, then the stores.  ok[u] masks chunks past the end.
+// fixed-order fp32 sums (own, peers ascending, then the residual if any),
+// then the stores.  ok[u] masks chunks past the end.
 template <int U, bool PEER_F32, bool OUT_F32>
 __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t (&e)[U],
                                               const bool (&ok)[U]) {
   Raw8<true> own[U];
   Raw8<PEER_F32> pv[U][kMaxRanks];
+  Raw8<OUT_F32> res[U];
+  const bool with_res = a.residual != nullptr;  // uniform
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!ok[u]) continue;
@@ -114,6 +117,7 @@ __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t
 #pragma unroll
     for (int q = 0; q < kMaxRanks; ++q)
       if (q < a.P && q != a.rank) pv[u][q] = load_raw8<PEER_F32>(a.peers[q], e[u]);
+    if (with_res) res[u] = load_raw8<OUT_F32>(a.residual, e[u]);
   }
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -122,6 +126,7 @@ __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t
 #pragma unroll
     for (int q = 0; q < kMaxRanks; ++q)
       if (q < a.P && q != a.rank) add8(acc, pv[u][q]);
+    if (with_res) add8(acc, res[u]);
     store8<OUT_F32>(a.out, e[u], acc);
   }
 }

@@ -24,7 +24,12 @@ peers drawn from N(0, 1), as stated for it.
 
 Seeds: numpy PCG64 over SeedSequence(20261202, spawn_key=(workload index,
 rank, tensor id)) with tensor id 0 = X, 1 = W, 2 = peer noise, 3 = exact-case
-draws.
+draws, 4 = the layer chain's residual and norm weight.
+
+Layer chain (residual addition and RMSNorm after the ReduceScatter): the
+residual stream's rows of the rank's partition are N(0, 1), and the norm
+weight is N(1, 0.1^2) per column; both in the output type (bf16, or fp32 for
+fp32-I/O workloads).
 
 W is handed over K-contiguous, [N][K] (element (k, n) at W[n*K + k]), the
 layout in which a row-parallel linear layer keeps its weight; the [K][N]
@@ -37,7 +42,7 @@ from dataclasses import dataclass
 import numpy as np
 
 SEED = 20261202
-X_ID, W_ID, PEER_ID, EXACT_ID = 0, 1, 2, 3
+X_ID, W_ID, PEER_ID, EXACT_ID, CHAIN_ID = 0, 1, 2, 3, 4
 
 
 @dataclass(frozen=True)
@@ -161,3 +166,15 @@ def exact_operands(w: Workload, r: int | None = None, nnz_per_row: int = 48,
         v = g.integers(-peer_mag, peer_mag + 1, size=(w.rows, w.N)).astype(np.float32)
         peers.append(v if w.fp32_io else bf16_bits(v))
     return bf16_bits(X), bf16_bits(W), peers
+
+
+def chain_inputs(w: Workload, rank: int | None = None):
+    """(residual [M/P][N], gamma [N]) of the layer chain for rank `rank`: bf16
+    bit patterns, or float32 for fp32-I/O workloads."""
+    rank = w.rank if rank is None else rank
+    g = rng(w.index, rank, CHAIN_ID)
+    residual = g.standard_normal((w.rows, w.N), dtype=np.float32)
+    gamma = (1.0 + 0.1 * g.standard_normal(w.N, dtype=np.float32)).astype(np.float32)
+    if w.fp32_io:
+        return residual, gamma
+    return bf16_bits(residual), bf16_bits(gamma)
