@@ -295,6 +295,20 @@ def main() -> int:
         body = (lambda r=r, pr=pr: call(budget, sym_cfg, r, pr))
         per_rank.append(timed_graph(body, args.steps, args.warmup)["median_ms"] * 1e3)
 
+    # The layer chain (Sec. 5.2.2): the same step followed by the residual
+    # addition (in the reduction's store) and an RMSNorm of the rank's rows.
+    log("layer chain (residual + RMSNorm): tuned step and sequential, same protocol")
+    res_h, gamma_h = wl.chain_inputs(w)
+    res_d, gamma_d = up(res_h), up(gamma_h)
+    h_buf, y_buf = torch.empty_like(out), torch.empty_like(out)
+
+    def chain(b):
+        tog.gemm_rs_rmsnorm(Xd, Wd, pd, res_d, gamma_d, 1e-5, h_buf, y_buf, w.P, w.rank, order, b,
+                            cfg=cfg, stream=stream)
+
+    ch = timed_graph(lambda: chain(budget), args.steps, args.warmup)
+    ch_sq = timed_graph(lambda: chain(0), args.steps, args.warmup)
+
     # Kernels alone: GEMM without flags; the reduction of the workspace's
     # partial, flat (sequential schedule) and tiled at the overlapped budget.
     # Ten launches per graph replay amortize the replay's launch latency; the
@@ -376,6 +390,11 @@ def main() -> int:
                        # the sender's side of a push-based transfer: every
                        # peer-bound tile also copied, (M - M/P) * N * 2 * 2 bytes more
                        "push_outgoing": {"streams": lat(pu_s), "fused": lat(pu_f)}},
+        "layer_chain": {"step": lat(ch), "sequential": lat(ch_sq),
+                        "speedup_vs_sequential": ch_sq["ms_per_step"] / ch["ms_per_step"],
+                        # beyond the plain step: the residual read and the norm's
+                        # h read + y write, (M/P)*N*3*2 bytes
+                        "extra_over_step_us": (ch["ms_per_step"] - st["ms_per_step"]) * 1e3},
         "symmetric_all_ranks": {"latency_us_median_max": max(per_rank),
                                 "latency_us_median_per_rank": per_rank,
                                 "speedup_vs_sequential": sq["median_ms"] * 1e3 / max(per_rank)},
