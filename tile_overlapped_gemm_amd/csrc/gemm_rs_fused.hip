@@ -15,12 +15,13 @@
 // stream, about as much as the whole reduction of a 4096 x 4096 output.  Here
 // one kernel on the caller's stream does both, so nothing forks or joins.
 //
-// Forward progress.  Roles come from device-wide tickets, not from blockIdx:
-// a workgroup takes GEMM blocks until every block has been taken and only
-// then may take reduction tasks.  A task waits only for flags of blocks that
-// running workgroups have already taken, and a workgroup computing a block
-// never waits, so every wait ends whatever the dispatch order and however
-// many workgroups are resident.  (Withheld flags end through the watchdog.)
+// Forward progress.  GEMM blocks come from device-wide tickets, not from
+// blockIdx: a workgroup takes blocks until every block has been taken and
+// only then works on its reduction tasks (workgroup w < x takes tasks w,
+// w + x, ...).  A task waits only for flags of blocks that running workgroups
+// have already taken, and a workgroup computing a block never waits, so every
+// wait ends whatever the dispatch order.  (Withheld flags end through the
+// watchdog.)
 //
 // XCD locality.  The host's dispatch order deals each window of concurrent
 // blocks to the 8 XCDs as compact rectangles (block b to XCD b % 8).  Each
@@ -75,8 +76,6 @@ __device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
     __hip_atomic_store(ctl + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
   for (int y = 0; y < 8; ++y) clear(kBlockTicket + y * kLine);
-  clear(kWorkerTicket);
-  clear(kTaskTicket);
   clear(kFusedDone);
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
@@ -88,7 +87,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   // Broadcast slots alternate so that thread 0 never overwrites a value a
   // slower wave has yet to read.
   __shared__ int s_pick[2];
-  __shared__ int s_abort;
+  __shared__ int s_abort[2];
   const int tid = threadIdx.x;
   uint32_t* const ctl = f.g.ctl;
   const uint32_t epoch = peek(ctl + kEpoch);
@@ -108,32 +107,20 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
                                          smem);
   }
 
-  // Reduction tasks, by at most f.workers workgroups, in production order.
-  bool worker = true;
-  if (f.workers < (int)gridDim.x) {
-    if (tid == 0) s_pick[parity] = take(ctl + kWorkerTicket) < (uint32_t)f.workers ? 1 : 0;
-    __syncthreads();
-    worker = s_pick[parity] != 0;
-    parity ^= 1;
-  }
-  if (worker) {
-    while (true) {
-      if (tid == 0) {
-        const uint32_t k = take(ctl + kTaskTicket);
-        s_pick[parity] = k < (uint32_t)f.r.ntasks ? (int)k : -1;
-      }
-      __syncthreads();
-      const int task = __builtin_amdgcn_readfirstlane(s_pick[parity]);
-      parity ^= 1;
-      if (task < 0) break;
+  // Reduction tasks: workgroup w < x (the budget) takes tasks w, w + x, ...
+  // of the production-ordered list (Sec. 3.1), once it has left the GEMM
+  // loop, i.e. once every block has been taken.  A static deal needs no
+  // per-task atomic: one ticket counter shared by all workers serialized them.
+  if ((int)blockIdx.x < f.workers) {
+    for (int task = blockIdx.x; task < f.r.ntasks; task += f.workers, parity ^= 1) {
       const TaskRef k = task_ref(f.r, task);
       if (tid < 64) {
         const bool ok = wait_tile(f.r, epoch, k.d, k.t, tid);
-        if (tid == 0) s_abort = ok ? 0 : 1;
+        if (tid == 0) s_abort[parity] = ok ? 0 : 1;
       }
       // The flag wait is ordered before every wave's reads of the tile.
       __syncthreads();
-      if (s_abort) break;  // uniform
+      if (s_abort[parity]) break;  // uniform
       if (k.d == f.r.rank)
         reduce_slab<kThreads, PEER_F32, OUT_F32>(f.r, k.t, k.slab, tid);
       else

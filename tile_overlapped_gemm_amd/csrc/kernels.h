@@ -87,10 +87,8 @@ enum {
   kEpoch = 0,
   kReduceDone = 1 * kLine,
   kFusedDone = 2 * kLine,
-  kWorkerTicket = 3 * kLine,
-  kTaskTicket = 4 * kLine,
-  kBlockTicket = 5 * kLine,  // ticket of XCD y at kBlockTicket + y * kLine
-  kCtlWords = 13 * kLine
+  kBlockTicket = 3 * kLine,  // ticket of XCD y at kBlockTicket + y * kLine
+  kCtlWords = 11 * kLine
 };
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
@@ -107,8 +105,8 @@ __device__ __forceinline__ void check_out(uint32_t* ctl, uint32_t epoch) {
 
 // The fused schedule: one kernel on the caller's stream.  Its workgroups take
 // GEMM blocks from per-XCD lists (block b of the dispatch order belongs to
-// XCD b % 8) until all are taken, then up to `workers` of them take the tasks
-// of r.task_list in order.
+// XCD b % 8) until all are taken; then workgroup w < `workers` takes tasks w,
+// w + workers, ... of r.task_list.
 struct FusedArgs {
   GemmArgs g;
   ReduceArgs r;               // r.task_list: the tasks in production order
