@@ -94,13 +94,14 @@ enum {
 enum { ENTWINE_STAGES_ALL = 0, ENTWINE_STAGES_GEMM = 1, ENTWINE_STAGES_REDUCE = 2 };
 
 /* How an overlapped call (comm_budget >= 1) runs producer and consumer:
- *  STREAMS  two kernels on two internal streams forked from and joined back
- *           to the caller's stream (Sec. 4.3): the GEMM, and x persistent
- *           reduction workgroups that poll the tiles' flags concurrently.
+ *  STREAMS  two concurrent kernels (Sec. 4.3): the GEMM on the caller's
+ *           stream, and x persistent reduction workgroups that poll the tiles'
+ *           flags on an internal stream forked from and joined back to it.
  *  FUSED    one kernel on the caller's stream.  Its workgroups take GEMM
  *           blocks (in the same production order, with the same per-tile
- *           flags) until every block is taken; then at most x of them take
- *           reduction tasks in production order.  No fork or join.
+ *           flags) until every block is taken; then workgroup w < x takes
+ *           reduction tasks w, w + x, ... in production order.  No fork or
+ *           join.
  *  AUTO     the tuning table's choice for the shape, else STREAMS.
  * Both give bit-identical output.  The sequential schedule (comm_budget 0)
  * and single stages ignore this field. */

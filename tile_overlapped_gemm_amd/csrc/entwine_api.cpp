@@ -11,10 +11,12 @@
 //
 // MI355X choices.  Flags hold the call's epoch instead of being cleared: a
 // flag is ready when it equals the current epoch, which is equivalent to
-// "reset, then set" without a clearing pass per call.  Both internal streams
-// run at the default priority; the fork/join uses HIP events.  Sequential
-// mode (budget 0) runs the same two kernels one after the other on one
-// stream.
+// "reset, then set" without a clearing pass per call.  Cross-stream waits cost
+// several µs each on this GPU, so only the two-stream schedule's reducer runs
+// on an internal stream (default priority), forked from and joined back to
+// the caller's stream with HIP events; the GEMM, the fused kernel, the
+// sequential reduction (budget 0) and the layer chain's RMSNorm run on the
+// caller's stream (the RMSNorm follows the reduction on its stream).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
