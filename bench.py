@@ -134,6 +134,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
                     help="only run --warmup + --steps eager calls (for rocprofv3), print nothing")
+    ap.add_argument("--chain", action="store_true",
+                    help="with --profile: the calls run the layer chain (residual + RMSNorm)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -220,9 +222,18 @@ def main() -> int:
         if st != tog.ENTWINE_OK:
             raise RuntimeError(f"device status {st} {where}")
 
+    # The layer chain's inputs (residual stream rows and norm weight).
+    res_h, gamma_h = wl.chain_inputs(w)
+    res_d, gamma_d = up(res_h), up(gamma_h)
+    h_buf, y_buf = torch.empty_like(out), torch.empty_like(out)
+
+    def chain(b):
+        tog.gemm_rs_rmsnorm(Xd, Wd, pd, res_d, gamma_d, 1e-5, h_buf, y_buf, w.P, w.rank, order, b,
+                            cfg=cfg, stream=stream)
+
     if args.profile:
         for _ in range(args.warmup + args.steps):
-            call(budget)
+            (chain if args.chain else call)(budget)
         stream.synchronize()
         check_status("in the profiled calls")
         log(f"profiled {args.warmup + args.steps} calls: {kind}, block {bm}x{bn}, order {order}, "
@@ -298,14 +309,6 @@ def main() -> int:
     # The layer chain (Sec. 5.2.2): the same step followed by the residual
     # addition (in the reduction's store) and an RMSNorm of the rank's rows.
     log("layer chain (residual + RMSNorm): tuned step and sequential, same protocol")
-    res_h, gamma_h = wl.chain_inputs(w)
-    res_d, gamma_d = up(res_h), up(gamma_h)
-    h_buf, y_buf = torch.empty_like(out), torch.empty_like(out)
-
-    def chain(b):
-        tog.gemm_rs_rmsnorm(Xd, Wd, pd, res_d, gamma_d, 1e-5, h_buf, y_buf, w.P, w.rank, order, b,
-                            cfg=cfg, stream=stream)
-
     ch = timed_graph(lambda: chain(budget), args.steps, args.warmup)
     ch_sq = timed_graph(lambda: chain(0), args.steps, args.warmup)
 
