@@ -349,3 +349,30 @@ def test_budget_at_cu_count_rejected(dev):
     with pytest.raises(tog.EntwineError) as e:
         case.run(tog.ORDER_INTERLEAVED, cus)
     assert e.value.status == tog.ENTWINE_ERR_INVALID_ARGUMENT
+
+
+@pytest.mark.parametrize("M,N,K,P,rank", [(4, 8, 64, 4, 2),      # one row per partition, one column chunk
+                                          (8, 16, 64, 8, 7),     # P = 8, last rank
+                                          (96, 264, 128, 3, 0),  # 32-row partitions, N = 33*8
+                                          (512, 8, 192, 2, 1)])  # a single 8-wide column
+def test_degenerate_shapes(dev, M, N, K, P, rank):
+    """Shapes at the smallest legal sizes: every block and tile is mostly
+    masked.  All schedules and both block extremes give the oracle's result,
+    and one bit pattern per block shape."""
+    w = wl.custom(f"deg_{M}_{N}_{K}_{P}", M, N, K, P, rank=rank, index=330 + M % 7 + N % 5)
+    X, W = wl.operands(w)
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    ref = orc.gemm_rs(X, W, peers, w.P, w.rank)
+    for bm, bn in ((128, 128), (256, 256)):
+        first = None
+        for budget, sched in ((0, tog.SCHEDULE_STREAMS), (1, tog.SCHEDULE_STREAMS),
+                              (3, tog.SCHEDULE_FUSED), (200, tog.SCHEDULE_FUSED)):
+            print(f"case deg {M}x{N}x{K} P{P} r{rank} block {bm}x{bn} budget {budget} "
+                  f"schedule {sched}", flush=True)
+            out = down(case.run(tog.ORDER_INTERLEAVED, budget, block_m=bm, block_n=bn,
+                                schedule=sched))
+            assert err_ratio(out, ref) <= 1.0
+            if first is None:
+                first = out
+            np.testing.assert_array_equal(out, first)
