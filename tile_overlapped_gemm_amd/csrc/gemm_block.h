@@ -96,6 +96,25 @@ __device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_
         j * group_step + kbyte, 0, 0);
 }
 
+// The X or the W half of issue_stage alone.
+template <class S>
+__device__ __forceinline__ void issue_x(__amdgpu_buffer_rsrc_t ra, char* lds, int voff,
+                                        int group_step, int kbyte, int wave) {
+#pragma unroll
+  for (int j = 0; j < S::kLoadsA; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + S::kWaves * j) * 1024),
+                                             16, voff, j * group_step + kbyte, 0, 0);
+}
+template <class S>
+__device__ __forceinline__ void issue_w(__amdgpu_buffer_rsrc_t rb, char* lds, int voff,
+                                        int group_step, int kbyte, int wave) {
+#pragma unroll
+  for (int j = 0; j < S::kLoadsB; ++j)
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(
+        rb, (lds_ptr_t)(lds + S::kA + (wave + S::kWaves * j) * 1024), 16, voff,
+        j * group_step + kbyte, 0, 0);
+}
+
 template <class S>
 struct Frags {
   bf16x8 b[S::kNT];  // W fragments (MFMA rows = output columns)
@@ -195,6 +214,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
   Frags<S> f0, f1;
   read_frags<S>(f0, smem, a_off[0], b_off[0]);
 
+  // Stage kt + NS is loaded in two halves: X's slab right after the barrier
+  // that frees its buffer, W's after the next stage's first MFMAs, so that
+  // the eight waves' loads do not all reach the address units and LDS at once
+  // (1.5-2 % on the 4-round shapes).
+  int pending_w = -1;  // stage whose W slab is still to be issued
   for (int kt = 0; kt < nk; ++kt) {
     const int buf = kt % NS;
     const char* cur = smem + buf * S::kStage;
@@ -202,6 +226,13 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
     for (int ks = 0; ks + 1 < S::kKS; ks += 2) {
       read_frags<S>(f1, cur, a_off[ks + 1], b_off[ks + 1]);
       mfma_step<S>(acc, f0);
+      if (ks == 0 && pending_w >= 0) {
+        // The buffer of stage pending_w is not `cur`: it was freed by the
+        // previous barrier.
+        issue_w<S>(rb, smem + (pending_w % NS) * S::kStage, voff, group_step,
+                   pending_w * S::kRow, wave);
+        pending_w = -1;
+      }
       if (ks + 2 < S::kKS) {
         read_frags<S>(f0, cur, a_off[ks + 2], b_off[ks + 2]);
         mfma_step<S>(acc, f1);
@@ -214,9 +245,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
         stage_barrier<S::kLoads * (NS - 2)>();
       else
         stage_barrier<0>();
-      if (kt + NS < nk)
-        issue_stage<S>(ra, rb, smem + buf * S::kStage, voff, group_step, (kt + NS) * S::kRow,
-                       wave);
+      if (kt + NS < nk) {
+        issue_x<S>(ra, smem + buf * S::kStage, voff, group_step, (kt + NS) * S::kRow, wave);
+        pending_w = kt + NS;
+      }
       read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, a_off[0], b_off[0]);
     }
     mfma_step<S>(acc, f1);
