@@ -279,6 +279,18 @@ def main() -> int:
     def lat(r):
         return {"latency_us": r["ms_per_step"] * 1e3, "latency_us_median": r["median_ms"] * 1e3}
 
+    # The GPU's clocks ramp over the first fraction of a second of work: about
+    # one second of untimed replays of the step settles them before any of
+    # the timed legs (each still runs its own W warm-up replays).
+    settle = graph_of(lambda: call(budget))
+    t_end = time.perf_counter() + 1.0
+    while time.perf_counter() < t_end:
+        with torch.cuda.stream(stream):
+            for _ in range(20):
+                settle.replay()
+        stream.synchronize()
+    check_status("while the clocks settle")
+    del settle
     log(f"step ({kind}, block {bm}x{bn}, order {order}, budget {budget}): {args.warmup} warm-up "
         f"+ {args.steps} timed graph replays")
     st = timed_graph(lambda: call(budget), args.steps, args.warmup)
