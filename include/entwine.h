@@ -150,7 +150,8 @@ int entwine_gemm_rs(const void* X, const void* W, const void* const* peer_partia
 typedef struct entwine_config {
   int32_t struct_size;     /* sizeof(entwine_config) */
   int32_t block_m;         /* GEMM block rows BM: 0 = auto, else 128 or 256 */
-  int32_t block_n;         /* GEMM block cols BN: 0 = auto, else 128 or 256 */
+  int32_t block_n;         /* GEMM block cols BN: 0 = auto, else 128 or 256, or 384 with
+                              block_m 128 (one round of blocks for short partitions) */
   int32_t tile_m;          /* reduction tile rows TM: 0 = 128, else 64 or 128; BM % TM == 0 */
   int32_t tile_n;          /* reduction tile cols TN: 0 = 128, else 64 or 128; BN % TN == 0 */
   int32_t reducer_threads; /* b: 0 = 256, else 128, 256 or 512 (Sec. 4.3) */
@@ -165,7 +166,13 @@ typedef struct entwine_config {
   int32_t withhold_tile;   /* failure injection for tests: 0 = off; t+1 makes tile t's local
                               wait watch a flag that no GEMM of the call sets, so that tile's
                               reduction workgroup times out (ENTWINE_ERR_TIMEOUT) */
-  int32_t gemm_variant;    /* GEMM main-loop variant for the block shape: 0 = default */
+  int32_t gemm_variant;    /* GEMM main-loop variant for the block shape: 0 = default
+                              (8 waves, K stages of 64, two LDS stages); 256x256 also has
+                              1 and 2 (4 waves, K stages of 32, 4 or 3 LDS stages), 3 (4 waves,
+                              K stages of 64) and 4 (8 waves in two groups that alternate
+                              between loading and MFMAs, K stages of 64, two LDS stages);
+                              128x128, 128x256 and 256x128 have 3 (the other wave count);
+                              unknown values select 0 */
   int32_t publish_all;     /* 0: agent-scope release only for tiles a kernel on this device
                               reads (the rank's partition), progress flags for the rest;
                               1: release every tile (the cost of publishing to peers) */
@@ -178,7 +185,7 @@ typedef struct entwine_config {
                               schedule as usual).  A single stage leaves `out` (GEMM) or the
                               partials (reduction) as they were: for timing only. */
   int32_t schedule;        /* ENTWINE_SCHEDULE_*; FUSED is built for the variant-0 pipelines
-                              of every block shape and variant 3 of 256x256 */
+                              of every block shape and variants 3 and 4 of 256x256 */
   int32_t reducer_cus;     /* static CU partitioning (Sec. 5.3.3): 0 = shared pool, the only
                               mode built (both kernels may use every CU).  n in [1, CUs) asks
                               for the reduction on n CUs and the GEMM on the others through

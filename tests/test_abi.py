@@ -107,6 +107,15 @@ def test_config_validation(lib, field, value, status):
     assert call(cfg=cfg) == status
 
 
+def test_block_shapes(lib):
+    """384-column blocks exist only with 128 rows; other widths are refused."""
+    for bm, bn in ((256, 384), (128, 512), (384, 128)):
+        assert call(cfg=tog.config(block_m=bm, block_n=bn)) == tog.ENTWINE_ERR_UNSUPPORTED
+    assert tog.entwine_plan_shape(1000, 12288, 8, 128, 384, 128, 128) == (256, 32, 96)
+    with pytest.raises(tog.EntwineError):
+        tog.entwine_plan_shape(1000, 12288, 8, 256, 384, 128, 128)
+
+
 def test_tuning_table_parsing(lib, tmp_path):
     good = tmp_path / "t.txt"
     good.write_text("# M N K P order budget bm bn threads\n4096 4096 1792 8 2 32 256 128 256\n")

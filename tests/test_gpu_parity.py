@@ -24,12 +24,13 @@ SMALL = [
     wl.custom("odd_n", 512, 1160, 256, 2, rank=1, index=302),        # N = 9*128 + 8
     wl.BY_NAME["tiny"],                                              # fp32 peers/out, 64x64 tiles
 ]
-BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256)]
+BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256), (128, 384)]
 SCHEDULES = [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED]
 
 
 def fused_built(bm, bn, variant):
-    """The fused kernel is built for variant 0 of every shape and variant 3 of 256x256."""
+    """The fused kernel is built for variant 0 of every shape and variants 3 and 4 of
+    256x256."""
     return variant == 0 or (bm, bn) == (256, 256)
 
 
@@ -59,13 +60,25 @@ def test_parity_and_schedule_invariance(dev, w):
     for bm, bn in BLOCKS:
         if w.tile == 64 and bm == 256:
             continue
-        for variant in (0, 3):
+        for variant in (0, 3, 4):
+            if variant == 4 and (bm, bn) != (256, 256):
+                continue  # the ping-pong pipeline is built for 256 x 256 blocks
+            if variant != 0 and (bm, bn) == (128, 384):
+                continue  # one pipeline for 128 x 384
             for order in ORDERS:
                 for budget, sched in [(b, s) for b in (0, 1, 3, min(q, 64)) for s in SCHEDULES]:
                     if sched == tog.SCHEDULE_FUSED and (budget == 0 or not fused_built(bm, bn, variant)):
                         continue
                     print(f"case {w.name} block {bm}x{bn} v{variant} order {order} budget {budget} "
                           f"schedule {sched}", flush=True)
+                    if variant == 4 and sched == tog.SCHEDULE_STREAMS and budget > 0:
+                        # 235 registers per lane leave no room for a reduction
+                        # workgroup on the GEMM's CUs: refused, nothing runs
+                        with pytest.raises(tog.EntwineError) as e:
+                            case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant,
+                                     schedule=sched)
+                        assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+                        continue
                     out = down(case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant,
                                         schedule=sched))
                     runs += 1

@@ -19,6 +19,7 @@ SHAPES = [
     (256, 256, 4, 128, 128, 64, 64),
     (2048, 640, 2, 256, 128, 128, 64),
     (96, 136, 3, 128, 128, 64, 128),
+    (1000, 1160, 8, 128, 384, 128, 128),   # three tiles per block, a ragged last column
 ]
 
 
@@ -166,6 +167,7 @@ def _panels(blocks, positions, Rb):
     ((8192, 8192, 8, 256, 256, 128, 128), 256),     # four windows
     ((16384, 5120, 4, 256, 256, 128, 128), 256),    # five windows
     ((1000, 12288, 8, 128, 128, 128, 128), 512),    # two blocks per CU
+    ((1000, 12288, 8, 128, 384, 128, 128), 256),    # one window of 128 x 384 blocks
     ((1000, 1536, 8, 128, 128, 128, 128), 40),      # a partial last window
 ])
 def test_dispatch_is_windowed_permutation(shape, window):

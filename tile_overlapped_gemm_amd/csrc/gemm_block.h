@@ -143,11 +143,100 @@ __device__ __forceinline__ void mfma_step(Acc<S>& acc, const Frags<S>& f) {
       acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
 }
 
+// Workgroup barrier that the compiler may not schedule any instruction across
+// (MFMAs included), after this wave's LDS reads and all but VM of its vector
+// memory operations have completed.
+template <int VM>
+__device__ __forceinline__ void phase_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  stage_barrier<VM>();
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// The same barrier without waiting for vector memory operations.
+__device__ __forceinline__ void phase_barrier_lds() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// phase_barrier<PER * n> for a wave-uniform n in [0, 2].
+template <int PER>
+__device__ __forceinline__ void phase_barrier_n(int n) {
+  if (n >= 2)
+    phase_barrier<2 * PER>();
+  else if (n == 1)
+    phase_barrier<PER>();
+  else
+    phase_barrier<0>();
+}
+
+// Ping-pong main loop for 8 waves.  The waves form two groups of four (waves
+// 0-3 and 4-7, one of each on every SIMD) that run the same sequence of
+// phases half a stage apart: in a memory phase a wave issues its share of a
+// future stage's global->LDS copies and reads all of the current stage's
+// fragments into registers; in the compute phase that follows it runs the
+// stage's MFMAs back to back on those registers, at raised issue priority.
+// While one group computes, the other loads, so every SIMD alternates between
+// the MFMAs of its two waves, and one workgroup barrier ends every phase.
+//
+// Stage i lives in LDS buffer i % NS and is read in phases 2i (group 0) and
+// 2i + 1 (group 1).  Its copies are issued in phase 2(i - L), L = NS - 1, by
+// both groups (group 1 at the start of a compute phase), into the buffer that
+// stage i - NS left at barrier 2(i - L); every wave has waited for its own
+// copies of stage j before barrier 2j.
+template <class S>
+__device__ __forceinline__ void pingpong_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_t ra,
+                                              __amdgpu_buffer_rsrc_t rb, char* smem, int voff,
+                                              int group_step, const int (&a_off)[S::kKS],
+                                              const int (&b_off)[S::kKS], int nk, int wave) {
+  constexpr int NS = S::kLds / S::kStage, L = NS - 1;
+  static_assert(S::kWaves == 8 && NS >= 2 && NS <= 4, "ping-pong: 8 waves, 2 to 4 stages");
+  constexpr int PER = S::kLoads;
+  static_assert(PER * (L - 1) < 64, "vmcnt range");
+  auto issue = [&](int st) {
+    issue_stage<S>(ra, rb, smem + (st % NS) * S::kStage, voff, group_step, st * S::kRow, wave);
+  };
+  const bool g1 = wave >= 4;  // wave-uniform
+  // Prologue: stages 0 .. L-1, then stage 0 landed for every wave.
+#pragma unroll
+  for (int st = 0; st < L; ++st)
+    if (st < nk) issue(st);
+  phase_barrier_n<PER>(min(L - 1, nk - 1));
+  if (g1) {
+    // Group 1's phase 0: the copies of stage L, and no compute.
+    if (L < nk) issue(L);
+    phase_barrier_lds();
+  }
+  Frags<S> fr[S::kKS];
+  for (int i = 0; i < nk; ++i) {
+    const char* cur = smem + (i % NS) * S::kStage;
+    // Memory phase of stage i.
+    if (!g1 && i + L < nk) issue(i + L);
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks) read_frags<S>(fr[ks], cur, a_off[ks], b_off[ks]);
+    if (g1)
+      phase_barrier_n<PER>(min(L - 1, nk - 2 - i));  // barrier 2(i+1): stage i+1 landed
+    else
+      phase_barrier_lds();
+    // Compute phase of stage i.
+    __builtin_amdgcn_s_setprio(1);
+    if (g1 && i + 1 + L < nk) issue(i + 1 + L);
+#pragma unroll
+    for (int ks = 0; ks < S::kKS; ++ks) mfma_step<S>(acc, fr[ks]);
+    __builtin_amdgcn_s_setprio(0);
+    if (!g1)
+      phase_barrier_n<PER>(min(L - 1, nk - 2 - i));  // barrier 2(i+1): stage i+1 landed
+    else if (i + 1 < nk)
+      phase_barrier_lds();
+  }
+}
+
 // One BM x BN block of C_r = X_r W_r: main loop, epilogue stores and the
 // block's flags.  `blk` = (partition d, block row, block column, first tile);
 // `smem` is the workgroup's S::kLds bytes of LDS.  Every thread of the
 // workgroup calls it; it contains workgroup barriers.
-template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP = false>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, char* smem) {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
 
@@ -198,8 +287,11 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
 
-  // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, then stage NS-1.
   const int nk = K / BK;
+  if constexpr (PP) {
+    pingpong_loop<S>(acc, ra, rb, smem, voff, group_step, a_off, b_off, nk, wave);
+  } else {
+  // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, then stage NS-1.
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
     if (s < nk) issue_stage<S>(ra, rb, smem + s * S::kStage, voff, group_step, s * S::kRow, wave);
@@ -253,6 +345,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
     }
     mfma_step<S>(acc, f1);
   }
+  }
 
   // Epilogue.  With the W fragment as the MFMA's row operand, accumulator
   // element v of lane l holds output row (l & 31) of its 32 x 32 tile and
@@ -270,7 +363,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
   // write-back of the whole L2.
   constexpr int kPitch = S::kWN * 4 + 16;
   constexpr int kLanesPerRow = S::kWN / 4;
+  // Rows one store instruction covers; with a 96-column sub-block 48 of the
+  // 64 lanes store (two rows) and the rest idle.
   constexpr int kRowsPerStore = 64 / kLanesPerRow;
+  static_assert(32 % kRowsPerStore == 0, "a strip splits into whole store rounds");
   static_assert(S::kWaves * 32 * kPitch <= S::kLds, "epilogue staging exceeds LDS");
   __syncthreads();  // every wave is done with the pipeline buffers
   char* wbuf = smem + wave * 32 * kPitch;
@@ -278,7 +374,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
   const int rsub = lane / kLanesPerRow;
   const int csub = (lane % kLanesPerRow) * 4;
   const int col = col0 + wn * S::kWN + csub;
-  const bool col_ok = col < a.N;
+  const bool col_ok = col < a.N && lane < kRowsPerStore * kLanesPerRow;
   const bool coherent = local ? a.publish != 0 : a.publish == 2;
   const int strip_bytes = 32 * a.N * (local || a.outgoing_f32 ? 4 : 2);
 #pragma unroll

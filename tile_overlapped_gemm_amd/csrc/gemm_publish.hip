@@ -16,9 +16,13 @@
 //    covered by the other's MFMAs) in a 2 x 4 (or 4 x 2) arrangement; a wave
 //    owns a (BM/WGM) x (BN/WGN) sub-block computed with
 //    v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  A 4-wave (2 x 2)
-//    instance remains as variant 3.  The MFMA's first operand is the W
-//    fragment and the second the X fragment, so each lane holds runs of 4
-//    consecutive output columns.
+//    instance remains as variant 3, and variant 4 of 256 x 256 runs the
+//    ping-pong schedule of gemm_block.h (the dispatcher places waves i and
+//    i + 4 of a workgroup on the same SIMD).  128 x 384 blocks (64 x 96 per
+//    wave) serve partitions of at most 128 rows: a third of the blocks of
+//    128 x 128, each with 1.5 times the MFMA work per byte loaded.  The MFMA's
+//    first operand is the W fragment and the second the X fragment, so each
+//    lane holds runs of 4 consecutive output columns.
 //  * K advances in stages of 64 (128 bytes per row).  X and W are both
 //    K-contiguous, so each stage is a BM x 128 B and a BN x 128 B slab.  Slabs
 //    move from global memory straight into LDS with buffer_load_dwordx4 ...
@@ -44,94 +48,97 @@
 namespace entwine {
 namespace {
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  gemm_block<BM, BN, BK, NS, WGM, WGN>(a, reinterpret_cast<const int4*>(a.blocks)[blockIdx.x],
-                                       smem);
+  gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(
+      a, reinterpret_cast<const int4*>(a.blocks)[blockIdx.x], smem);
 }
 
-template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN><<<num_blocks, S::kThreads, S::kLds, s>>>(a);
+  gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<num_blocks, S::kThreads, S::kLds, s>>>(a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 int occupancy_of() {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN>, S::kThreads,
+          &n, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>, S::kThreads,
           S::kLds) != hipSuccess)
     return 0;
   return n;
 }
 
-template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 int regs_of() {
   hipFuncAttributes at{};
-  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN>) !=
+  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>) !=
       hipSuccess)
     return 0;
   return at.numRegs;
 }
 
 // The kernel instance for a block shape and variant, handed to `f` as a
-// template functor call f.template operator()<BM, BN, BK, NS, WGM, WGN>().
+// template functor call f.template run<BM, BN, BK, NS, WGM, WGN, PP>() (PP: the
+// ping-pong main loop).
 template <class F>
-auto with_instance(int bm, int bn, int variant, F&& f) -> decltype(f.template run<128, 128, 64, 2, 2, 2>()) {
+auto with_instance(int bm, int bn, int variant, F&& f) -> decltype(f.template run<128, 128, 64, 2, 2, 2, false>()) {
   if (bm == 128 && bn == 128) {
-    if (variant == 3) return f.template run<128, 128, 64, 2, 2, 4>();
-    return f.template run<128, 128, 64, 2, 2, 2>();
+    if (variant == 3) return f.template run<128, 128, 64, 2, 2, 4, false>();
+    return f.template run<128, 128, 64, 2, 2, 2, false>();
   }
   if (bm == 128 && bn == 256) {
-    if (variant == 3) return f.template run<128, 256, 64, 2, 2, 2>();
-    return f.template run<128, 256, 64, 2, 2, 4>();
+    if (variant == 3) return f.template run<128, 256, 64, 2, 2, 2, false>();
+    return f.template run<128, 256, 64, 2, 2, 4, false>();
   }
+  if (bm == 128 && bn == 384) return f.template run<128, 384, 64, 2, 2, 4, false>();
   if (bm == 256 && bn == 128) {
-    if (variant == 3) return f.template run<256, 128, 64, 2, 2, 2>();
-    return f.template run<256, 128, 64, 2, 4, 2>();
+    if (variant == 3) return f.template run<256, 128, 64, 2, 2, 2, false>();
+    return f.template run<256, 128, 64, 2, 4, 2, false>();
   }
   if (bm == 256 && bn == 256) {
-    if (variant == 1) return f.template run<256, 256, 32, 4, 2, 2>();
-    if (variant == 2) return f.template run<256, 256, 32, 3, 2, 2>();
-    if (variant == 3) return f.template run<256, 256, 64, 2, 2, 2>();
-    return f.template run<256, 256, 64, 2, 2, 4>();
+    if (variant == 1) return f.template run<256, 256, 32, 4, 2, 2, false>();
+    if (variant == 2) return f.template run<256, 256, 32, 3, 2, 2, false>();
+    if (variant == 3) return f.template run<256, 256, 64, 2, 2, 2, false>();
+    if (variant == 4) return f.template run<256, 256, 64, 2, 2, 4, true>();
+    return f.template run<256, 256, 64, 2, 2, 4, false>();
   }
-  return f.template run<0, 0, 0, 0, 0, 0>();
+  return f.template run<0, 0, 0, 0, 0, 0, false>();
 }
 
 struct Launch {
   const GemmArgs& a;
   int num_blocks;
   hipStream_t s;
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   hipError_t run() {
     if constexpr (BM == 0) return hipErrorInvalidValue;
-    else return launch_shape<BM, BN, BK, NS, WGM, WGN>(a, num_blocks, s);
+    else return launch_shape<BM, BN, BK, NS, WGM, WGN, PP>(a, num_blocks, s);
   }
 };
 struct Occupancy {
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   int run() {
     if constexpr (BM == 0) return 0;
-    else return occupancy_of<BM, BN, BK, NS, WGM, WGN>();
+    else return occupancy_of<BM, BN, BK, NS, WGM, WGN, PP>();
   }
 };
 struct Registers {
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   int run() {
     if constexpr (BM == 0) return 0;
-    else return regs_of<BM, BN, BK, NS, WGM, WGN>();
+    else return regs_of<BM, BN, BK, NS, WGM, WGN, PP>();
   }
 };
 
@@ -144,7 +151,7 @@ int gemm_blocks_per_cu(int bm, int bn, int variant) {
 }
 
 struct Waves {
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   int run() { return WGM * WGN; }
 };
 

@@ -80,7 +80,7 @@ __device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PEER_F32, bool OUT_F32>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedArgs f) {
   constexpr int kThreads = 64 * WGM * WGN;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
@@ -103,8 +103,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     const int b = __builtin_amdgcn_readfirstlane(s_pick[parity]);
     parity ^= 1;
     if (b < 0) break;
-    gemm_block<BM, BN, BK, NS, WGM, WGN>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b],
-                                         smem);
+    gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b],
+                                             smem);
   }
 
   // Reduction tasks: workgroup w < x (the budget) takes tasks w, w + x, ...
@@ -130,10 +130,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   if (tid == 0) fused_check_out(ctl, epoch);
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PF, bool OF>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool PF, bool OF>
 struct Inst {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
-  static const void* fn() { return (const void*)gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PF, OF>; }
+  static const void* fn() { return (const void*)gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PP, PF, OF>; }
   static hipError_t launch(const FusedArgs& a, int grid, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
@@ -141,7 +141,7 @@ struct Inst {
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PF, OF><<<grid, S::kThreads, S::kLds, s>>>(a);
+    gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PP, PF, OF><<<grid, S::kThreads, S::kLds, s>>>(a);
     return hipGetLastError();
   }
   static int per_cu() {
@@ -156,11 +156,13 @@ struct Inst {
 // peer / output dtypes; f.none() if it is not built.
 template <bool PF, bool OF, class F>
 auto with_shape(int bm, int bn, int variant, F&& f) {
-  if (bm == 128 && bn == 128 && variant == 0) return f.template run<Inst<128, 128, 64, 2, 2, 2, PF, OF>>();
-  if (bm == 128 && bn == 256 && variant == 0) return f.template run<Inst<128, 256, 64, 2, 2, 4, PF, OF>>();
-  if (bm == 256 && bn == 128 && variant == 0) return f.template run<Inst<256, 128, 64, 2, 4, 2, PF, OF>>();
-  if (bm == 256 && bn == 256 && variant == 0) return f.template run<Inst<256, 256, 64, 2, 2, 4, PF, OF>>();
-  if (bm == 256 && bn == 256 && variant == 3) return f.template run<Inst<256, 256, 64, 2, 2, 2, PF, OF>>();
+  if (bm == 128 && bn == 128 && variant == 0) return f.template run<Inst<128, 128, 64, 2, 2, 2, false, PF, OF>>();
+  if (bm == 128 && bn == 256 && variant == 0) return f.template run<Inst<128, 256, 64, 2, 2, 4, false, PF, OF>>();
+  if (bm == 128 && bn == 384 && variant == 0) return f.template run<Inst<128, 384, 64, 2, 2, 4, false, PF, OF>>();
+  if (bm == 256 && bn == 128 && variant == 0) return f.template run<Inst<256, 128, 64, 2, 4, 2, false, PF, OF>>();
+  if (bm == 256 && bn == 256 && variant == 0) return f.template run<Inst<256, 256, 64, 2, 2, 4, false, PF, OF>>();
+  if (bm == 256 && bn == 256 && variant == 3) return f.template run<Inst<256, 256, 64, 2, 2, 2, false, PF, OF>>();
+  if (bm == 256 && bn == 256 && variant == 4) return f.template run<Inst<256, 256, 64, 2, 2, 4, true, PF, OF>>();
   return f.none();
 }
 

@@ -31,7 +31,7 @@ static int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int make_geometry(int64_t M, int64_t N, int P, int bm, int bn, int tm, int tn, Geometry* g) {
   if (M <= 0 || N <= 0 || P < 1 || M % P != 0) return ENTWINE_ERR_INVALID_ARGUMENT;
   if (P > 8) return ENTWINE_ERR_UNSUPPORTED;
-  if (!((bm == 128 || bm == 256) && (bn == 128 || bn == 256)))
+  if (!((bm == 128 || bm == 256) && (bn == 128 || bn == 256)) && !(bm == 128 && bn == 384))
     return ENTWINE_ERR_UNSUPPORTED;
   if (!((tm == 64 || tm == 128) && (tn == 64 || tn == 128)))
     return ENTWINE_ERR_UNSUPPORTED;

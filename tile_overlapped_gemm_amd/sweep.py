@@ -40,7 +40,7 @@ import sys
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 
-BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256)]
+BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256), (128, 384)]
 BUDGETS = [0, 1, 2, 4, 8, 12, 16, 24, 32, 48, 64, 96, 128, 192, 255]
 SLABS = [1, 2, 4]
 THREADS = [128, 256, 512]
