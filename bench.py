@@ -79,14 +79,14 @@ def traffic_for(workload: str, kernel: str):
 
 def tuned_entry(w):
     """The tuning table's entry for the workload's shape as a dict, or None."""
-    names = ["order", "budget", "bm", "bn", "threads", "slabs", "schedule"]
+    names = ["order", "budget", "bm", "bn", "threads", "slabs", "schedule", "variant"]
     with open(os.path.join(ROOT, "tile_overlapped_gemm_amd", "tuning.txt")) as f:
         for line in f:
             v = line.split()
             if not v or v[0].startswith("#"):
                 continue
             if [int(x) for x in v[:4]] == [w.M, w.N, w.K, w.P]:
-                vals = [int(x) for x in v[4:]] + [1, 0][len(v) - 9:]
+                vals = [int(x) for x in v[4:]] + [1, 0, 0][len(v) - 9:]
                 return dict(zip(names, vals))
     return None
 
@@ -127,6 +127,9 @@ def main() -> int:
     ap.add_argument("--block", default="", help="BMxBN, e.g. 256x256 (default: tuning table)")
     ap.add_argument("--threads", type=int, default=0, help="reduction threads (0: tuning table)")
     ap.add_argument("--slabs", type=int, default=0, help="row slabs per task (0: tuning table)")
+    ap.add_argument("--gemm-variant", type=int, default=0,
+                    help="GEMM pipeline (0: the tuning table's for its block shape, else 5 = "
+                         "base, 4 = ping-pong, ...)")
     ap.add_argument("--peers", default="preseeded", help="preseeded|symmetric")
     ap.add_argument("--schedule", default="auto", choices=["auto", "streams", "fused"],
                     help="overlapped schedule: two streams, one fused kernel, or the tuning table's")
@@ -202,8 +205,13 @@ def main() -> int:
     ov_budget = budget if budget > 0 else min(128, q, cus - 1)
     kind = "sequential" if budget == 0 else ("fused" if schedule == tog.SCHEDULE_FUSED
                                              else "streams")
+    # The pipeline the step's GEMM runs (tuning-table numbering, 0 = base).
+    if args.gemm_variant:
+        pipeline = 0 if args.gemm_variant == tog.GEMM_BASE else args.gemm_variant
+    else:
+        pipeline = tuned.get("variant", 0) if (tuned.get("bm"), tuned.get("bn")) == (bm, bn) else 0
     cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, block_m=bm, block_n=bn, reducer_threads=threads,
-                  task_slabs=slabs, schedule=schedule,
+                  task_slabs=slabs, schedule=schedule, gemm_variant=args.gemm_variant,
                   peer_ready=tog.PEERS_SYMMETRIC if args.peers == "symmetric" else tog.PEERS_PRESEEDED)
     if w.fp32_io:
         cfg_kw.update(peer_dtype=tog.F32, out_dtype=tog.F32)
@@ -390,7 +398,7 @@ def main() -> int:
         "config": {"workload": w.name, "M": w.M, "N": w.N, "K_local": w.K, "P": w.P,
                    "rank": w.rank, "schedule": kind, "block": f"{bm}x{bn}", "tile": w.tile,
                    "tile_order": order, "comm_budget": budget, "reducer_threads": threads,
-                   "task_slabs": slabs, "peer_ready": args.peers,
+                   "task_slabs": slabs, "gemm_pipeline": pipeline, "peer_ready": args.peers,
                    "source": "tuning table" if tuned and args.budget < 0 else "flags",
                    "launch": "HIP graph replay"},
         "latency_us": st["ms_per_step"] * 1e3,

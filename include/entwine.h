@@ -107,6 +107,23 @@ enum { ENTWINE_STAGES_ALL = 0, ENTWINE_STAGES_GEMM = 1, ENTWINE_STAGES_REDUCE = 
  * and single stages ignore this field. */
 enum { ENTWINE_SCHEDULE_AUTO = 0, ENTWINE_SCHEDULE_STREAMS = 1, ENTWINE_SCHEDULE_FUSED = 2 };
 
+/* GEMM main-loop pipeline (entwine_config.gemm_variant).  Every pipeline
+ * multiplies the K steps in the same order, so all give bit-identical output.
+ *  BASE (5)  8 waves in a 2 x 4 (or 4 x 2) arrangement, K stages of 64, two
+ *            LDS stages; the only pipeline of 128 x 384 blocks.
+ *  1, 2      256 x 256: 4 waves, K stages of 32, 4 or 3 LDS stages.
+ *  3         128 x 128, 128 x 256, 256 x 128 and 256 x 256: the other wave
+ *            count (4 or 8).
+ *  4         256 x 256: 8 waves in two groups that alternate between loading
+ *            and MFMAs (ping-pong), K stages of 64, two LDS stages.  It uses
+ *            235 registers per lane, so a two-stream reduction cannot share its
+ *            CUs (ENTWINE_ERR_UNSUPPORTED when requested explicitly).
+ *  AUTO (0)  the tuning table's pipeline when its entry names the block shape
+ *            in use, else BASE; BASE also replaces a pipeline the two-stream
+ *            reduction cannot share CUs with.
+ * Other values select BASE. */
+enum { ENTWINE_GEMM_AUTO = 0, ENTWINE_GEMM_PINGPONG = 4, ENTWINE_GEMM_BASE = 5 };
+
 /* Release granularity (Sec. 5.3.2): tiles released together. */
 #define ENTWINE_RELEASE_TILE 1       /* each tile on its own flag (the method) */
 #define ENTWINE_RELEASE_PARTITION 0  /* a tile waits for the last tile of its partition */
@@ -166,13 +183,7 @@ typedef struct entwine_config {
   int32_t withhold_tile;   /* failure injection for tests: 0 = off; t+1 makes tile t's local
                               wait watch a flag that no GEMM of the call sets, so that tile's
                               reduction workgroup times out (ENTWINE_ERR_TIMEOUT) */
-  int32_t gemm_variant;    /* GEMM main-loop variant for the block shape: 0 = default
-                              (8 waves, K stages of 64, two LDS stages); 256x256 also has
-                              1 and 2 (4 waves, K stages of 32, 4 or 3 LDS stages), 3 (4 waves,
-                              K stages of 64) and 4 (8 waves in two groups that alternate
-                              between loading and MFMAs, K stages of 64, two LDS stages);
-                              128x128, 128x256 and 256x128 have 3 (the other wave count);
-                              unknown values select 0 */
+  int32_t gemm_variant;    /* ENTWINE_GEMM_* pipeline (0 = AUTO) */
   int32_t publish_all;     /* 0: agent-scope release only for tiles a kernel on this device
                               reads (the rank's partition), progress flags for the rest;
                               1: release every tile (the cost of publishing to peers) */
@@ -331,8 +342,10 @@ int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls);
 
 /* Load an offline tuning table (text; one entry per line:
  * "M N K_local P tile_order comm_budget block_m block_n reducer_threads
- * [task_slabs [schedule]]", '#' starts a comment line).  Entries are consulted by the
- * AUTO settings (tile_order -1, comm_budget -1, zero config fields). */
+ * [task_slabs [schedule [gemm_variant]]]", '#' starts a comment line; the
+ * entry's gemm_variant is 0 for the base pipeline or 1 to 4).  Entries are
+ * consulted by the AUTO settings (tile_order -1, comm_budget -1, zero config
+ * fields). */
 int entwine_load_tuning(const char* path);
 
 /* Frees the current device's workspace; the next call re-creates it. */

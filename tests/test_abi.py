@@ -123,7 +123,10 @@ def test_tuning_table_parsing(lib, tmp_path):
     good.write_text("4096 4096 1792 8 2 32 256 128 256 4 2\n")  # with slabs and schedule
     tog.entwine_load_tuning(str(good))
     bad = tmp_path / "b.txt"
-    for text in ("4096 4096 1792 8 2\n", "4096 4096 1792 8 2 32 256 128 256 4 7\n"):
+    good.write_text("4096 4096 1792 8 2 32 256 256 256 1 1 4\n")  # with a GEMM pipeline
+    tog.entwine_load_tuning(str(good))
+    for text in ("4096 4096 1792 8 2\n", "4096 4096 1792 8 2 32 256 128 256 4 7\n",
+                 "4096 4096 1792 8 2 32 256 256 256 1 1 5\n"):
         bad.write_text(text)
         with pytest.raises(tog.EntwineError):
             tog.entwine_load_tuning(str(bad))

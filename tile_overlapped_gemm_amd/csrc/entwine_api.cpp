@@ -101,7 +101,7 @@ struct Workspace {
 };
 
 struct TuneEntry {
-  int order, budget, bm, bn, threads, slabs, schedule;
+  int order, budget, bm, bn, threads, slabs, schedule, variant;
 };
 
 std::mutex g_mu;
@@ -280,8 +280,8 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
-      slabs, withhold_tile, variant, publish_all, stages, linear_dispatch, schedule, reducer_cus,
-      push;
+      slabs, withhold_tile, variant, variant_auto, publish_all, stages, linear_dispatch, schedule,
+      reducer_cus, push;
   uint32_t timeout_ms;
 };
 
@@ -337,7 +337,13 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->linear_dispatch = c.linear_dispatch;
   r->timeout_ms = c.poll_timeout_ms ? c.poll_timeout_ms : 2000;
   r->withhold_tile = c.withhold_tile - 1;
-  r->variant = c.gemm_variant;
+  // GEMM pipeline: explicit, or the tuning table's when the entry's block
+  // shape is the one in use, else the base pipeline (internally 0).
+  r->variant_auto = c.gemm_variant == ENTWINE_GEMM_AUTO;
+  if (r->variant_auto)
+    r->variant = te && te->bm == r->bm && te->bn == r->bn ? te->variant : 0;
+  else
+    r->variant = c.gemm_variant == ENTWINE_GEMM_BASE ? 0 : c.gemm_variant;
   if (r->slabs < 0 || (r->slabs > 0 && r->tm % r->slabs != 0))
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
   if (c.publish_all != 0 && c.publish_all != 1)
@@ -470,13 +476,24 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     // must still fit a GEMM block: otherwise reduction workgroups spread
     // over the device could starve the GEMM until the watchdog fires.
     const int red_waves_per_simd = (rs.threads / 64 + 3) / 4;
-    const int gemm_waves_per_simd = (gemm_waves(g.bm, g.bn, rs.variant) + 3) / 4;
-    const int gr = gemm_registers(g.bm, g.bn, rs.variant);
     const int rr = reduce_registers(rs.threads, rs.peer_f32, rs.out_f32);
     auto up8 = [](int v) { return (v + 7) / 8 * 8; };
+    auto fits = [&](int variant, int* gr) {
+      *gr = gemm_registers(g.bm, g.bn, variant);
+      const int gemm_waves_per_simd = (gemm_waves(g.bm, g.bn, variant) + 3) / 4;
+      return gemm_waves_per_simd * up8(*gr) + red_waves_per_simd * up8(rr) <= 512;
+    };
+    int gr = 0;
+    bool ok = fits(rs.variant, &gr);
+    // An automatically chosen pipeline that leaves no room for the reducer
+    // gives way to the base pipeline (same accumulation order, same result).
+    if (!ok && rs.variant_auto && rs.variant != 0) {
+      rs.variant = 0;
+      ok = fits(0, &gr);
+    }
     if (gr <= 0 || rr <= 0)
       return fail(ENTWINE_ERR_HIP, "kernel register counts unavailable");
-    if (gemm_waves_per_simd * up8(gr) + red_waves_per_simd * up8(rr) > 512)
+    if (!ok)
       return fail(ENTWINE_ERR_UNSUPPORTED,
                   "a %d-thread reduction workgroup (%d registers per lane) cannot share a CU "
                   "with a %dx%d GEMM block (%d registers per lane)",
@@ -977,16 +994,18 @@ int entwine_load_tuning(const char* path) {
     ++lineno;
     if (line[0] == '#' || line[0] == '\n') continue;
     long long M, N, K;
-    int P, order, budget, bm, bn, threads, slabs = 1, schedule = ENTWINE_SCHEDULE_AUTO;
-    const int n = std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d %d %d", &M, &N, &K, &P,
-                              &order, &budget, &bm, &bn, &threads, &slabs, &schedule);
-    if (n < 9 || schedule < ENTWINE_SCHEDULE_AUTO || schedule > ENTWINE_SCHEDULE_FUSED) {
+    int P, order, budget, bm, bn, threads, slabs = 1, schedule = ENTWINE_SCHEDULE_AUTO, variant = 0;
+    const int n = std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d %d %d %d", &M, &N, &K, &P,
+                              &order, &budget, &bm, &bn, &threads, &slabs, &schedule, &variant);
+    if (n < 9 || schedule < ENTWINE_SCHEDULE_AUTO || schedule > ENTWINE_SCHEDULE_FUSED ||
+        variant < 0 || variant > 4) {
       std::fclose(f);
       return fail(ENTWINE_ERR_INVALID_ARGUMENT,
-                  "%s:%d: expected 9 to 11 integers (schedule 0, 1 or 2)", path, lineno);
+                  "%s:%d: expected 9 to 12 integers (schedule 0, 1 or 2; GEMM variant 0 to 4)",
+                  path, lineno);
     }
     table[std::make_tuple((int64_t)M, (int64_t)N, (int64_t)K, P)] =
-        TuneEntry{order, budget, bm, bn, threads, slabs, schedule};
+        TuneEntry{order, budget, bm, bn, threads, slabs, schedule, variant};
   }
   std::fclose(f);
   std::lock_guard<std::mutex> lock(g_mu);

@@ -15,9 +15,10 @@ produces it) and scored by the maximum over ranks.  `--objective preseeded`
 scores one rank with the peers' contributions ready from the start instead.
 
 The search is staged rather than exhaustive:
-  A. every GEMM block shape without overlap (x = 0, the order does not
-     matter), and every block shape x production order with the two-stream
-     and the fused schedule at budget min(128, Q);
+  A. every GEMM block shape and main-loop pipeline without overlap (x = 0,
+     the order does not matter), and every block shape x production order
+     with the two-stream schedule (base pipeline) and the fused schedule
+     (every pipeline) at budget min(128, Q);
   B. for the best two overlapped (block, order, schedule) points of A: every
      budget of the list x task slabs;
   C. at the best two-stream point: reduction threads 128 / 256 / 512 (the
@@ -25,7 +26,7 @@ The search is staged rather than exhaustive:
 Each measurement is one call captured in a HIP graph and replayed; a rank's
 latency is the median per-replay time.  Scores within `tie` of the best count
 as equal, and the tie goes to the smaller budget, then the smaller reduction
-thread count, then the smaller order enum.
+thread count, then the smaller order enum (then the base pipeline).
 
 Usage (one GPU):
     python -m tile_overlapped_gemm_amd.sweep --workloads mlp,large_mlp --out tuning.txt
@@ -47,37 +48,50 @@ THREADS = [128, 256, 512]
 
 
 class Candidate:
-    __slots__ = ("bm", "bn", "order", "budget", "threads", "slabs", "schedule", "us")
+    """One configuration; `variant` is the GEMM pipeline as the tuning table
+    numbers it (0 = the base pipeline, 4 = ping-pong)."""
+    __slots__ = ("bm", "bn", "order", "budget", "threads", "slabs", "schedule", "variant", "us")
 
-    def __init__(self, bm, bn, order, budget, threads=256, slabs=1, schedule=1, us=None):
+    def __init__(self, bm, bn, order, budget, threads=256, slabs=1, schedule=1, variant=0,
+                 us=None):
         self.bm, self.bn, self.order, self.budget = bm, bn, order, budget
         self.threads, self.slabs, self.schedule, self.us = threads, slabs, schedule, us
+        self.variant = variant
 
     def key(self):
-        return (self.bm, self.bn, self.order, self.budget, self.threads, self.slabs, self.schedule)
+        return (self.bm, self.bn, self.order, self.budget, self.threads, self.slabs, self.schedule,
+                self.variant)
 
     def __repr__(self):
         return (f"Candidate(block={self.bm}x{self.bn}, order={self.order}, x={self.budget}, "
-                f"b={self.threads}, slabs={self.slabs}, schedule={self.schedule}, us={self.us})")
+                f"b={self.threads}, slabs={self.slabs}, schedule={self.schedule}, "
+                f"variant={self.variant}, us={self.us})")
 
 
 def pick(cands: list[Candidate], tie: float = 0.01) -> Candidate:
     """The best measured candidate: the lowest latency, where latencies within
     a factor (1 + tie) of the lowest count as equal and the tie goes to the
     smaller budget, then fewer reduction threads, then the smaller order enum
-    (then fewer slabs and the two-stream schedule)."""
+    (then fewer slabs, the two-stream schedule and the base pipeline)."""
     done = [c for c in cands if c.us is not None]
     if not done:
         raise ValueError("no candidate was measured")
     best = min(c.us for c in done)
     close = [c for c in done if c.us <= best * (1.0 + tie)]
-    return min(close, key=lambda c: (c.budget, c.threads, c.order, c.slabs, c.schedule, c.us))
+    return min(close, key=lambda c: (c.budget, c.threads, c.order, c.slabs, c.schedule, c.variant,
+                                     c.us))
 
 
 def table_line(w, c: Candidate) -> str:
-    """One tuning-table entry: M N K_local P order budget bm bn threads slabs schedule."""
+    """One tuning-table entry: M N K_local P order budget bm bn threads slabs schedule
+    variant."""
     return (f"{w.M} {w.N} {w.K} {w.P} {c.order} {c.budget} {c.bm} {c.bn} {c.threads} "
-            f"{c.slabs} {c.schedule}")
+            f"{c.slabs} {c.schedule} {c.variant}")
+
+
+def pipelines_for(bm: int, bn: int) -> list[int]:
+    """GEMM pipelines worth timing for a block shape (tuning-table numbering)."""
+    return [0, 4] if (bm, bn) == (256, 256) else [0]
 
 
 def budgets_for(q: int, cus: int) -> list[int]:
@@ -126,7 +140,7 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     def time_rank(c: Candidate, rank: int):
         kw = dict(block_m=c.bm, block_n=c.bn, tile_m=w.tile, tile_n=w.tile,
                   reducer_threads=c.threads, task_slabs=c.slabs, schedule=c.schedule,
-                  peer_ready=mode)
+                  peer_ready=mode, gemm_variant=c.variant or tog.GEMM_BASE)
         if w.fp32_io:
             kw.update(peer_dtype=tog.F32, out_dtype=tog.F32)
         cfg = tog.config(**kw)
@@ -184,10 +198,12 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
               tog.ORDER_COL_MAJOR)
     # A: no overlap (every rank takes the same time), and the overlapped
     # schedules per block shape and order
-    seq = [run(Candidate(bm, bn, tog.ORDER_INTERLEAVED, 0), all_ranks=False) for bm, bn in blocks]
-    stage_a = [run(Candidate(bm, bn, order, x0, schedule=s))
+    seq = [run(Candidate(bm, bn, tog.ORDER_INTERLEAVED, 0, variant=v), all_ranks=False)
+           for bm, bn in blocks for v in pipelines_for(bm, bn)]
+    stage_a = [run(Candidate(bm, bn, order, x0, schedule=s, variant=v))
                for bm, bn in blocks for order in orders
-               for s in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED)]
+               for s in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED)
+               for v in (pipelines_for(bm, bn) if s == tog.SCHEDULE_FUSED else [0])]
     top = sorted((c for c in stage_a if c.us is not None), key=lambda c: c.us)[:2]
     log(f"stage A: no overlap {pick(seq)}; overlapped {top}")
     # B: budget x slabs at the two best overlapped points
@@ -199,7 +215,7 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
             for slabs in SLABS:
                 if w.tile % slabs == 0:
                     stage_b.append(run(Candidate(a.bm, a.bn, a.order, x, slabs=slabs,
-                                                 schedule=a.schedule)))
+                                                 schedule=a.schedule, variant=a.variant)))
     b = pick(stage_b)
     log(f"stage B: {b}")
     # C: reduction threads for the two-stream schedule
@@ -207,7 +223,7 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     if b.schedule == tog.SCHEDULE_STREAMS:
         for t in THREADS:
             stage_c.append(run(Candidate(b.bm, b.bn, b.order, b.budget, threads=t, slabs=b.slabs,
-                                         schedule=b.schedule)))
+                                         schedule=b.schedule, variant=b.variant)))
     best = pick(seq + stage_c)
     log(f"chosen: {best}; best without overlap {pick(seq)}")
     return best
@@ -245,7 +261,8 @@ def main(argv=None) -> int:
         "# Offline tuning table read by entwine_load_tuning(): the AUTO choices per shape,",
         "# written by tile_overlapped_gemm_amd/sweep.py from the median latency of",
         f"# graph-replayed steps on one MI355X (objective: {args.objective}).",
-        "# M N K_local P tile_order comm_budget block_m block_n reducer_threads task_slabs schedule",
+        "# M N K_local P tile_order comm_budget block_m block_n reducer_threads task_slabs schedule "
+        "gemm_variant",
     ]
     with open(args.out, "w") as f:
         f.write("\n".join(header + lines) + "\n")
