@@ -24,7 +24,8 @@ The search is staged rather than exhaustive:
   C. at the best two-stream point: reduction threads 128 / 256 / 512 (the
      fused kernel's workgroups are the GEMM's).
 Each measurement is one call captured in a HIP graph and replayed; a rank's
-latency is the median per-replay time.  Scores within `tie` of the best count
+latency is the median per-replay time (for the candidates without overlap, the
+better of two passes in opposite orders).  Scores within `tie` of the best count
 as equal, and the tie goes to the smaller budget, then the smaller reduction
 thread count, then the smaller order enum (then the base pipeline).
 
@@ -200,6 +201,14 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     # schedules per block shape and order
     seq = [run(Candidate(bm, bn, tog.ORDER_INTERLEAVED, 0, variant=v), all_ranks=False)
            for bm, bn in blocks for v in pipelines_for(bm, bn)]
+    # Candidates timed later in a run measure slightly faster: a second pass
+    # in reverse order, keeping each candidate's better time, evens that out
+    # between the block shapes and pipelines without overlap.
+    for c in reversed(seq):
+        if c.us is not None:
+            c.us = min(c.us, time_rank(c, ranks[0]))
+            cache[c.key()] = c.us
+            log(f"  again {c}")
     stage_a = [run(Candidate(bm, bn, order, x0, schedule=s, variant=v))
                for bm, bn in blocks for order in orders
                for s in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED)
