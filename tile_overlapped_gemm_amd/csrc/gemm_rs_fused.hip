@@ -7,7 +7,8 @@
 //    tasks are taken in production order ("matching task order").
 //  * Sec. 3.2: at most x workgroups (the communication budget) reduce.
 //  * Sec. 4.2: producers release each tile with a flag after the block's
-//    stores; a consumer acquires every flag of a task before reading it.
+//    stores; a consumer observes every flag of a task before reading it (with
+//    device-coherent loads in place of an acquire; see tile_reduce.hip).
 //
 // Why a single kernel on MI355X.  The paper runs producer and consumer as two
 // kernels on two streams.  On this GPU a step that forks to a second stream

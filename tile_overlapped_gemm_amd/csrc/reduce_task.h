@@ -48,6 +48,22 @@ __device__ __forceinline__ Raw8<true> load_raw8<true>(const void* base, int64_t 
                     __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p + 4))};
 }
 
+// Data that another workgroup of this device stored during the call and
+// released through a tile flag (the own partial, and the outgoing partials of
+// a send task) is read with device-coherent loads (cache policy SC1): no stale
+// L1 or L2 line can satisfy them, so the flag wait needs no acquire, which on
+// this GPU invalidates the XCD's whole L2 -- under a GEMM that is still
+// reading its operands from it.  The descriptor's base is the task's first
+// element (wave-uniform); offsets stay within the task's rows.
+constexpr int kSC1 = 16;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t coherent_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+__device__ __forceinline__ u32x4 load_coherent16(__amdgpu_buffer_rsrc_t r, int byte_off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kSC1));
+}
+
 // bf16 -> fp32 is exact: the bf16 bits are the upper half of the binary32.
 __device__ __forceinline__ float lo_bf16(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -102,18 +118,26 @@ __device__ __forceinline__ void store8<true>(void* base, int64_t e, const F8& ac
 
 // Reduce U chunks at element offsets e[0..U): all loads first, then the
 // fixed-order fp32 sums (own, peers ascending, then the residual if any),
-// then the stores.  ok[u] masks chunks past the end.
-template <int U, bool PEER_F32, bool OUT_F32>
+// then the stores.  ok[u] masks chunks past the end.  COH: the own partial is
+// read with device-coherent loads relative to element e0 (wave-uniform).
+template <int U, bool PEER_F32, bool OUT_F32, bool COH>
 __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t (&e)[U],
-                                              const bool (&ok)[U]) {
+                                              const bool (&ok)[U], int64_t e0) {
   Raw8<true> own[U];
   Raw8<PEER_F32> pv[U][kMaxRanks];
   Raw8<OUT_F32> res[U];
   const bool with_res = a.residual != nullptr;  // uniform
+  const __amdgpu_buffer_rsrc_t own_r = coherent_rsrc(a.own + e0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
     if (!ok[u]) continue;
-    own[u] = load_raw8<true>(a.own, e[u]);
+    if constexpr (COH) {
+      const int off = (int)((e[u] - e0) * 4);
+      own[u].a = __builtin_bit_cast(f32x4, load_coherent16(own_r, off));
+      own[u].b = __builtin_bit_cast(f32x4, load_coherent16(own_r, off + 16));
+    } else {
+      own[u] = load_raw8<true>(a.own, e[u]);
+    }
 #pragma unroll
     for (int q = 0; q < kMaxRanks; ++q)
       if (q < a.P && q != a.rank) pv[u][q] = load_raw8<PEER_F32>(a.peers[q], e[u]);
@@ -162,8 +186,8 @@ __device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int d, int t, int
     }
     __builtin_amdgcn_s_sleep(2);
   }
-  // One acquire per task: later reads of the tile see the producers' stores.
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  // No acquire: the tile's data is read with device-coherent loads, issued
+  // after this wait (program order, then the workgroup barrier that follows).
   return true;
 }
 
@@ -191,7 +215,7 @@ __device__ __forceinline__ void reduce_slab(const ReduceArgs& a, int t, int slab
       ok[u] = c < n_chunks && col < cols;
       e[u] = (int64_t)(row0 + r) * a.N + col0 + col;
     }
-    reduce_chunks<kUnroll, PEER_F32, OUT_F32>(a, e, ok);
+    reduce_chunks<kUnroll, PEER_F32, OUT_F32, true>(a, e, ok, (int64_t)row0 * a.N + col0);
   }
 }
 
@@ -219,16 +243,16 @@ __device__ __forceinline__ void push_slab(const ReduceArgs& a, int d, int t, int
   const int rows = min(slab_rows, a.R - row0);
   const int cols = min(a.tn, a.N - col0);
   const int n_chunks = rows > 0 ? rows * chunks_per_row : 0;
-  const int64_t base = ((int64_t)d * a.R + row0) * a.N + col0;
-  const char* src = static_cast<const char*>(a.outgoing);
-  char* dst = static_cast<char*>(a.staging);
+  constexpr int kSize = PEER_F32 ? 4 : 2;
+  const int64_t base = (((int64_t)d * a.R + row0) * a.N + col0) * kSize;
+  const __amdgpu_buffer_rsrc_t src = coherent_rsrc(static_cast<const char*>(a.outgoing) + base);
+  char* const dst = static_cast<char*>(a.staging) + base;
   for (int c = tid; c < n_chunks; c += THREADS) {
     const int r = c / chunks_per_row;
     const int col = (c - r * chunks_per_row) * kPerChunk;
     if (col >= cols) continue;
-    const int64_t off = (base + (int64_t)r * a.N + col) * (PEER_F32 ? 4 : 2);
-    const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src + off));
-    __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(dst + off));
+    const int off = (r * a.N + col) * kSize;  // within the slab's rows
+    __builtin_nontemporal_store(load_coherent16(src, off), reinterpret_cast<u32x4*>(dst + off));
   }
 }
 

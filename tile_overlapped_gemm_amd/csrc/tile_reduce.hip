@@ -16,10 +16,13 @@
 //    numbered tile-major, so the tiles' slabs spread over consecutive
 //    workgroups.
 //  * Wave 0 polls the task's flags in parallel, one lane per flag, with
-//    relaxed agent-scope loads and an s_sleep back-off, then issues one
-//    agent-scope acquire fence (it invalidates this XCD's L2 so that data
-//    written back by a producer on another XCD is read from memory); the
-//    other waves wait at the workgroup barrier meanwhile.
+//    relaxed agent-scope loads and an s_sleep back-off; the other waves wait
+//    at the workgroup barrier meanwhile.  The paper's acquire becomes
+//    device-coherent (SC1) loads of the released data: an agent-scope
+//    acquire fence on this GPU invalidates the XCD's whole L2, which a GEMM
+//    sharing the XCD is still reading its operands from.  The producers'
+//    SC1 stores were acknowledged before their flags were set, and SC1 loads
+//    issued after the wait cannot hit a stale line, so they see the stores.
 //  * The element loop moves 8 elements per thread step: two 16-byte fp32 loads
 //    of the local partial and one 16-byte load per bf16 peer.  Two steps are
 //    loaded before any add so that 2 * (P + 1) loads per thread are in flight.
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
       ok[u] = c < n_chunks;
       e[u] = c * 8;
     }
-    reduce_chunks<kUnroll, PEER_F32, OUT_F32>(a, e, ok);
+    reduce_chunks<kUnroll, PEER_F32, OUT_F32, false>(a, e, ok, 0);
   }
 }
 
