@@ -595,6 +595,10 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ra.staging = rs.push ? w->staging : nullptr;
   ra.residual = chain ? chain->residual : nullptr;
   ra.task_list = d_task_list;
+  // Preseeded peers (and the residual) exist before the call: a task may load
+  // them before its wait.  Under symmetric readiness they count as produced
+  // with the tiles, so they are read only after the wait.
+  ra.prefetch = rs.peer_ready == ENTWINE_PEERS_PRESEEDED;
 
   if (fused) {
     // One kernel on the caller's stream, after this workspace's previous

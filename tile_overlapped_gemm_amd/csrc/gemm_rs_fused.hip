@@ -18,7 +18,7 @@
 //
 // Forward progress.  GEMM blocks come from device-wide tickets, not from
 // blockIdx: a workgroup takes blocks until every block has been taken and
-// only then works on its reduction tasks (workgroup w < x takes tasks w,
+// only then waits for its reduction tasks (workgroup w < x takes tasks w,
 // w + x, ...).  A task waits only for flags of blocks that running workgroups
 // have already taken, and a workgroup computing a block never waits, so every
 // wait ends whatever the dispatch order.  (Withheld flags end through the
@@ -51,21 +51,34 @@ __device__ __forceinline__ uint32_t peek(const uint32_t* w) {
   return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Thread 0: the dispatch index of the next GEMM block for a workgroup on XCD
-// x, or -1 once every list is exhausted.  List y holds blocks y, y + 8, ...;
-// tickets only grow, so a list seen exhausted stays exhausted.
-__device__ int next_block(uint32_t* ctl, int nb, int x) {
-  for (int k = 0; k < 8; ++k) {
-    const int y = (x + k) & 7;
-    const uint32_t len = nb > y ? (uint32_t)((nb - y + 7) >> 3) : 0u;
-    uint32_t* const c = ctl + kBlockTicket + y * kLine;
-    // The own list is taken from directly; other lists are looked at first,
-    // so that exhausted lists cost a load rather than an atomic.
-    if (k > 0 && peek(c) >= len) continue;
-    const uint32_t i = take(c);
-    if (i < len) return y + 8 * (int)i;
+// Wave 0 (lane = 0..63): the dispatch index of the next GEMM block for a
+// workgroup on XCD x, or -1 once every list is exhausted (uniform).  List y
+// holds blocks y, y + 8, ...; tickets only grow, so a list seen exhausted
+// stays exhausted.  The own list is taken from directly; once it is empty,
+// lanes 0-7 look at all eight tickets at once, so finding that every list is
+// empty costs one load latency, not eight.
+__device__ int next_block(uint32_t* ctl, int nb, int x, int lane) {
+  auto len = [nb](int y) { return nb > y ? (uint32_t)((nb - y + 7) >> 3) : 0u; };
+  int got = -1;
+  if (lane == 0) {
+    const uint32_t i = take(ctl + kBlockTicket + x * kLine);
+    if (i < len(x)) got = x + 8 * (int)i;
   }
-  return -1;
+  got = __builtin_amdgcn_readfirstlane(got);
+  while (got < 0) {
+    const bool open = lane < 8 && lane != x && peek(ctl + kBlockTicket + lane * kLine) < len(lane);
+    const uint64_t m = __ballot(open);
+    if (m == 0) return -1;
+    // The first open list after x, cyclically.
+    const uint32_t rot = (uint32_t)(((m >> (x + 1)) | (m << (7 - x))) & 0xffu);
+    const int y = (x + 1 + __builtin_ctz(rot)) & 7;
+    if (lane == 0) {
+      const uint32_t i = take(ctl + kBlockTicket + y * kLine);
+      if (i < len(y)) got = y + 8 * (int)i;
+    }
+    got = __builtin_amdgcn_readfirstlane(got);
+  }
+  return got;
 }
 
 __device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
@@ -81,52 +94,115 @@ __device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// A reduction task begun but not completed: its slab and its U chunks per
+// thread (with the inputs loaded so far).
+template <int U, bool PEER_F32, bool OUT_F32>
+struct Pending {
+  static constexpr int kChunks = U;
+  Slab s;
+  Chunks<U, PEER_F32, OUT_F32> c;
+};
+
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedArgs f) {
   constexpr int kThreads = 64 * WGM * WGN;
+  // Chunks (8 elements) per thread prefetched for each of two tasks at once.
+  // One: with two, the 256 x 256 GEMM spills.  A task of 32 x 128 elements
+  // (a 128 x 128 tile in four slabs) is then one chunk per thread of a
+  // 512-thread workgroup.
+  constexpr int kU = 1;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  // Broadcast slots alternate so that thread 0 never overwrites a value a
-  // slower wave has yet to read.
-  __shared__ int s_pick[2];
-  __shared__ int s_abort[2];
+  // Thread 0's broadcast word.  Slots alternate: the next write to a slot
+  // comes after a barrier that every wave passes only once it has read it.
+  __shared__ int s_word[2];
   const int tid = threadIdx.x;
   uint32_t* const ctl = f.g.ctl;
+  const ReduceArgs& r = f.r;
   const uint32_t epoch = peek(ctl + kEpoch);
   int parity = 0;
-
-  // GEMM blocks, until every list is exhausted.
-  const int x = xcd_id();
-  while (true) {
-    if (tid == 0) s_pick[parity] = next_block(ctl, f.nb, x);
+  // Thread 0's v, for every thread, as a wave-uniform (scalar) value.
+  auto share = [&](int v) {
+    if (tid == 0) s_word[parity] = v;
     __syncthreads();
-    // Wave-uniform (scalar) values from here on: the block's descriptors and
-    // output addresses stay in scalar registers, with no waterfall loops.
-    const int b = __builtin_amdgcn_readfirstlane(s_pick[parity]);
+    const int out = __builtin_amdgcn_readfirstlane(s_word[parity]);
     parity ^= 1;
+    return out;
+  };
+
+  // Start of a reduction task: the slab's chunk placement and, when
+  // r.prefetch is set, the loads of the inputs that were complete before the
+  // call (the peers, the residual) for this thread's first kU chunks.  A
+  // send task loads only after its wait.
+  auto begin = [&](int task, auto& p) {
+    const TaskRef k = task_ref(r, task);
+    if (k.d != r.rank) return;  // a send task loads after its wait
+    p.s = slab_of(r, k.t, k.slab);
+    place<std::remove_reference_t<decltype(p)>::kChunks, kThreads>(p.s, tid, p.c);
+    if (r.prefetch) load_inputs(r, p.c);
+  };
+
+  // Workgroup w < x (the budget) owns tasks w, w + x, ... of the
+  // production-ordered list (Sec. 3.1).  A static deal needs no per-task
+  // atomic: one ticket counter shared by all workers serialized them.
+  int task = (int)blockIdx.x < f.workers ? (int)blockIdx.x : r.ntasks;
+  const int xcd = xcd_id();
+  while (true) {
+    // GEMM blocks until every list is exhausted.  The block's descriptors
+    // and output addresses stay in scalar registers.
+    int pick = 0;
+    if (tid < 64) pick = next_block(ctl, f.nb, xcd, tid);
+    const int b = share(pick);
     if (b < 0) break;
     gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b],
                                              smem);
   }
 
-  // Reduction tasks: workgroup w < x (the budget) takes tasks w, w + x, ...
-  // of the production-ordered list (Sec. 3.1), once it has left the GEMM
-  // loop, i.e. once every block has been taken.  A static deal needs no
-  // per-task atomic: one ticket counter shared by all workers serialized them.
-  if ((int)blockIdx.x < f.workers) {
-    for (int task = blockIdx.x; task < f.r.ntasks; task += f.workers, parity ^= 1) {
-      const TaskRef k = task_ref(f.r, task);
-      if (tid < 64) {
-        const bool ok = wait_tile(f.r, epoch, k.d, k.t, tid);
-        if (tid == 0) s_abort[parity] = ok ? 0 : 1;
+  // Every block has been taken: the remaining tasks, two at a time.  A task
+  // waits only for blocks that running workgroups have taken.  Both tasks'
+  // prefetches are issued, wave 0 polls both tasks' flags at once (lanes
+  // 0-31 and 32-63), and both tasks' own-partial loads are in flight before
+  // either is summed: each memory round trip serves two tasks.
+  while (task < r.ntasks) {
+    const int t0 = task, t1 = task + f.workers;
+    const bool has1 = t1 < r.ntasks;  // uniform
+    Pending<kU, PEER_F32, OUT_F32> p0, p1;
+    begin(t0, p0);
+    if (has1) begin(t1, p1);
+    int ok = 1;
+    if (tid < 64) {
+      const int tw = tid < 32 ? t0 : t1;
+      const uint32_t* fl = nullptr;
+      if (tw < r.ntasks) {
+        const TaskRef k = task_ref(r, tw);
+        fl = wait_flag(r, k.d, k.t, tid & 31);
       }
-      // The flag wait is ordered before every wave's reads of the tile.
-      __syncthreads();
-      if (s_abort[parity]) break;  // uniform
-      if (k.d == f.r.rank)
-        reduce_slab<kThreads, PEER_F32, OUT_F32>(f.r, k.t, k.slab, tid);
-      else
-        push_slab<kThreads, PEER_F32>(f.r, k.d, k.t, k.slab, tid);
+      ok = wait_flags(r, epoch, fl, tid);
     }
+    // The flag waits are ordered before every wave's reads of the tiles.
+    if (!share(ok)) break;  // the watchdog or the sticky error ended the wait
+    const bool own0 = task_ref(r, t0).d == r.rank;
+    const bool own1 = has1 && task_ref(r, t1).d == r.rank;
+    Raw8<true> o0[kU], o1[kU];
+    if (own0) {
+      if (!r.prefetch) load_inputs(r, p0.c);
+      load_own<kU, PEER_F32, OUT_F32, true>(r, p0.c, p0.s.e0, o0);
+    }
+    if (own1) {
+      if (!r.prefetch) load_inputs(r, p1.c);
+      load_own<kU, PEER_F32, OUT_F32, true>(r, p1.c, p1.s.e0, o1);
+    }
+    auto rest = [&](int t, bool own, auto& p, const Raw8<true> (&o)[kU]) {
+      if (own) {
+        sum_store(r, p.c, o);
+        reduce_slab<kThreads, kU, PEER_F32, OUT_F32>(r, p.s, tid, kU * kThreads);
+      } else {
+        const TaskRef k = task_ref(r, t);
+        push_slab<kThreads, PEER_F32>(r, k.d, k.t, k.slab, tid);
+      }
+    };
+    rest(t0, own0, p0, o0);
+    if (has1) rest(t1, own1, p1, o1);
+    task += 2 * f.workers;
   }
   if (tid == 0) fused_check_out(ctl, epoch);
 }

@@ -64,6 +64,10 @@ struct ReduceArgs {
   int32_t withhold_tile;            // -1, or a tile whose local wait watches `never_flag`
   int32_t never_flag;               // a flag slot that no GEMM of this call writes
   int32_t nowait;                   // 1: every flag counts as ready, no epoch check-out
+  // 1: the peers' contributions (and the residual) were complete before the
+  // call, so a task may load them before its wait; 0: they are loaded after
+  // the wait, as a real peer's data would be (symmetric readiness).
+  int32_t prefetch;
 };
 
 // Epochs.  A flag is ready when it equals the call's epoch, which both

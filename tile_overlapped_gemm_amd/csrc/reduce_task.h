@@ -116,43 +116,74 @@ __device__ __forceinline__ void store8<true>(void* base, int64_t e, const F8& ac
   *reinterpret_cast<f32x4*>(p + 4) = hi;
 }
 
-// Reduce U chunks at element offsets e[0..U): all loads first, then the
-// fixed-order fp32 sums (own, peers ascending, then the residual if any),
-// then the stores.  ok[u] masks chunks past the end.  COH: the own partial is
-// read with device-coherent loads relative to element e0 (wave-uniform).
-template <int U, bool PEER_F32, bool OUT_F32, bool COH>
-__device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t (&e)[U],
-                                              const bool (&ok)[U], int64_t e0) {
-  Raw8<true> own[U];
+// U chunks of one thread: their element offsets, which of them lie inside
+// the slab, and the inputs that were ready before the call (the peers'
+// contributions and the residual), loaded before the own partial.
+template <int U, bool PEER_F32, bool OUT_F32>
+struct Chunks {
+  int64_t e[U];
+  bool ok[U];
   Raw8<PEER_F32> pv[U][kMaxRanks];
   Raw8<OUT_F32> res[U];
+};
+
+// Issue the loads of the peers and the residual (all U chunks, nothing waits).
+template <int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void load_inputs(const ReduceArgs& a, Chunks<U, PEER_F32, OUT_F32>& c) {
   const bool with_res = a.residual != nullptr;  // uniform
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!c.ok[u]) continue;
+#pragma unroll
+    for (int q = 0; q < kMaxRanks; ++q)
+      if (q < a.P && q != a.rank) c.pv[u][q] = load_raw8<PEER_F32>(a.peers[q], c.e[u]);
+    if (with_res) c.res[u] = load_raw8<OUT_F32>(a.residual, c.e[u]);
+  }
+}
+
+// The own partial of U chunks.  COH: device-coherent loads relative to
+// element e0 (wave-uniform).
+template <int U, bool PEER_F32, bool OUT_F32, bool COH>
+__device__ __forceinline__ void load_own(const ReduceArgs& a, const Chunks<U, PEER_F32, OUT_F32>& c,
+                                         int64_t e0, Raw8<true> (&own)[U]) {
   const __amdgpu_buffer_rsrc_t own_r = coherent_rsrc(a.own + e0);
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (!ok[u]) continue;
+    if (!c.ok[u]) continue;
     if constexpr (COH) {
-      const int off = (int)((e[u] - e0) * 4);
+      const int off = (int)((c.e[u] - e0) * 4);
       own[u].a = __builtin_bit_cast(f32x4, load_coherent16(own_r, off));
       own[u].b = __builtin_bit_cast(f32x4, load_coherent16(own_r, off + 16));
     } else {
-      own[u] = load_raw8<true>(a.own, e[u]);
+      own[u] = load_raw8<true>(a.own, c.e[u]);
     }
-#pragma unroll
-    for (int q = 0; q < kMaxRanks; ++q)
-      if (q < a.P && q != a.rank) pv[u][q] = load_raw8<PEER_F32>(a.peers[q], e[u]);
-    if (with_res) res[u] = load_raw8<OUT_F32>(a.residual, e[u]);
   }
+}
+
+// The fixed-order fp32 sums (own, peers ascending, then the residual if
+// any), one rounding, the stores.
+template <int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void sum_store(const ReduceArgs& a, const Chunks<U, PEER_F32, OUT_F32>& c,
+                                          const Raw8<true> (&own)[U]) {
+  const bool with_res = a.residual != nullptr;  // uniform
 #pragma unroll
   for (int u = 0; u < U; ++u) {
-    if (!ok[u]) continue;
+    if (!c.ok[u]) continue;
     F8 acc = widen(own[u]);
 #pragma unroll
     for (int q = 0; q < kMaxRanks; ++q)
-      if (q < a.P && q != a.rank) add8(acc, pv[u][q]);
-    if (with_res) add8(acc, res[u]);
-    store8<OUT_F32>(a.out, e[u], acc);
+      if (q < a.P && q != a.rank) add8(acc, c.pv[u][q]);
+    if (with_res) add8(acc, c.res[u]);
+    store8<OUT_F32>(a.out, c.e[u], acc);
   }
+}
+
+template <int U, bool PEER_F32, bool OUT_F32, bool COH>
+__device__ __forceinline__ void finish(const ReduceArgs& a, Chunks<U, PEER_F32, OUT_F32>& c,
+                                       int64_t e0) {
+  Raw8<true> own[U];
+  load_own<U, PEER_F32, OUT_F32, COH>(a, c, e0, own);
+  sum_store(a, c, own);
 }
 
 // Wave 0 waits until every flag that tile t of partition d depends on equals
@@ -161,7 +192,7 @@ __device__ __forceinline__ void reduce_chunks(const ReduceArgs& a, const int64_t
 // wave) if the watchdog expired, or if the sticky error word is set: once one
 // workgroup has timed out, the others stop waiting too, so a failed call ends
 // within one timeout whatever its task count.
-__device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int d, int t, int lane) {
+__device__ __forceinline__ const uint32_t* wait_flag(const ReduceArgs& a, int d, int t, int lane) {
   int32_t idx = -1;
   if (d != a.rank) {
     idx = lane == 0 ? d * a.Q + t : -1;  // a send task: the tile's own flag
@@ -169,15 +200,19 @@ __device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int d, int t, int
     if (lane < a.wait_slots) idx = a.waits[t * a.wait_slots + lane];
     if (t == a.withhold_tile && lane == a.rank) idx = a.never_flag;
   }
-  const uint32_t* f = idx >= 0 ? a.flags + idx : nullptr;
+  return idx >= 0 ? a.flags + idx : nullptr;
+}
+
+// Wave 0 waits until the flag each lane watches (f; nullptr: none) equals
+// `epoch`.  The flag and the sticky error word are loaded together, so one
+// poll costs one memory round trip.
+__device__ bool wait_flags(const ReduceArgs& a, uint32_t epoch, const uint32_t* f, int lane) {
   const uint64_t start = wall_clock64();
   while (true) {
-    bool ready = true;
-    if (f) ready = __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == epoch;
-    if (__all(ready)) break;
-    if (__builtin_amdgcn_readfirstlane(
-            __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
-      return false;
+    const uint32_t v = f ? __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : epoch;
+    const int32_t err = __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (__all(v == epoch)) break;
+    if (__builtin_amdgcn_readfirstlane(err) != 0) return false;
     if (wall_clock64() - start > a.timeout_ticks) {
       if (lane == 0)
         __hip_atomic_store(a.error, (int32_t)5 /* ENTWINE_ERR_TIMEOUT */, __ATOMIC_RELAXED,
@@ -191,31 +226,60 @@ __device__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int d, int t, int
   return true;
 }
 
+__device__ __forceinline__ bool wait_tile(const ReduceArgs& a, uint32_t epoch, int d, int t,
+                                          int lane) {
+  return wait_flags(a, epoch, wait_flag(a, d, t, lane), lane);
+}
+
 constexpr int kUnroll = 2;
 
-// Reduce row slab `slab` of task tile t: thread tid of THREADS takes chunks
-// tid, tid + THREADS, ... of the slab (8 elements each).
-template <int THREADS, bool PEER_F32, bool OUT_F32>
-__device__ __forceinline__ void reduce_slab(const ReduceArgs& a, int t, int slab, int tid) {
-  const int chunks_per_row = a.tn >> 3;
+// Row slab `slab` of own tile t: 8-element chunks numbered row-major, chunk c
+// at row c / cpr, columns 8 (c % cpr) onward; masked past the partition's
+// last row and past N.
+struct Slab {
+  int64_t e0;    // element offset of the slab's first element
+  int cpr;       // chunks per tile row
+  int cols;      // valid columns of the tile
+  int n_chunks;  // chunks in the slab's valid rows
+  int N;
+};
+__device__ __forceinline__ Slab slab_of(const ReduceArgs& a, int t, int slab) {
   const int slab_rows = a.tm / a.slabs;
   const int row0 = a.tiles[2 * t] * a.tm + slab * slab_rows;
   const int col0 = a.tiles[2 * t + 1] * a.tn;
   const int rows = min(slab_rows, a.R - row0);
-  const int cols = min(a.tn, a.N - col0);
-  const int n_chunks = rows > 0 ? rows * chunks_per_row : 0;
-  for (int c0 = tid; c0 < n_chunks; c0 += kUnroll * THREADS) {
-    int64_t e[kUnroll];
-    bool ok[kUnroll];
+  Slab s;
+  s.e0 = (int64_t)row0 * a.N + col0;
+  s.cpr = a.tn >> 3;
+  s.cols = min(a.tn, a.N - col0);
+  s.n_chunks = rows > 0 ? rows * s.cpr : 0;
+  s.N = a.N;
+  return s;
+}
+
+// Chunks c0, c0 + STEP, ..., c0 + (U - 1) STEP of slab s.
+template <int U, int STEP, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void place(const Slab& s, int c0, Chunks<U, PEER_F32, OUT_F32>& c) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const int c = c0 + u * THREADS;
-      const int r = c / chunks_per_row;
-      const int col = (c - r * chunks_per_row) << 3;
-      ok[u] = c < n_chunks && col < cols;
-      e[u] = (int64_t)(row0 + r) * a.N + col0 + col;
-    }
-    reduce_chunks<kUnroll, PEER_F32, OUT_F32, true>(a, e, ok, (int64_t)row0 * a.N + col0);
+  for (int u = 0; u < U; ++u) {
+    const int k = c0 + u * STEP;
+    const int r = k / s.cpr;
+    const int col = (k - r * s.cpr) << 3;
+    c.ok[u] = k < s.n_chunks && col < s.cols;
+    c.e[u] = s.e0 + (int64_t)r * s.N + col;
+  }
+}
+
+// Reduce row slab `slab` of task tile t: thread tid of THREADS takes chunks
+// tid, tid + THREADS, ... of the slab, U at a time.
+template <int THREADS, int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void reduce_slab(const ReduceArgs& a, const Slab& s, int tid,
+                                            int first = 0) {
+  for (int c0 = tid + first; c0 < s.n_chunks; c0 += U * THREADS) {
+    Chunks<U, PEER_F32, OUT_F32> c;
+    place<U, THREADS>(s, c0, c);
+    load_inputs(a, c);
+    finish<U, PEER_F32, OUT_F32, true>(a, c, s.e0);
   }
 }
 

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
     if (s_abort[parity]) break;  // uniform: every thread read the same value
 
     if (k.d == a.rank)
-      reduce_slab<THREADS, PEER_F32, OUT_F32>(a, k.t, k.slab, tid);
+      reduce_slab<THREADS, kUnroll, PEER_F32, OUT_F32>(a, slab_of(a, k.t, k.slab), tid);
     else
       push_slab<THREADS, PEER_F32>(a, k.d, k.t, k.slab, tid);
   }
@@ -71,15 +71,15 @@ __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
   const int64_t stride = (int64_t)gridDim.x * THREADS * kUnroll;
   for (int64_t c0 = (int64_t)blockIdx.x * THREADS * kUnroll + threadIdx.x; c0 < n_chunks;
        c0 += stride) {
-    int64_t e[kUnroll];
-    bool ok[kUnroll];
+    Chunks<kUnroll, PEER_F32, OUT_F32> c;
 #pragma unroll
     for (int u = 0; u < kUnroll; ++u) {
-      const int64_t c = c0 + u * THREADS;
-      ok[u] = c < n_chunks;
-      e[u] = c * 8;
+      const int64_t k = c0 + u * THREADS;
+      c.ok[u] = k < n_chunks;
+      c.e[u] = k * 8;
     }
-    reduce_chunks<kUnroll, PEER_F32, OUT_F32, false>(a, e, ok, 0);
+    load_inputs(a, c);
+    finish<kUnroll, PEER_F32, OUT_F32, false>(a, c, 0);
   }
 }
 
