@@ -201,8 +201,11 @@ def main() -> int:
     slabs = args.slabs or tuned.get("slabs", 1)
     schedule = ({"streams": tog.SCHEDULE_STREAMS, "fused": tog.SCHEDULE_FUSED}[args.schedule]
                 if args.schedule != "auto" else (tuned.get("schedule") or tog.SCHEDULE_STREAMS))
-    # The overlapped schedules are also timed when the tuned step is sequential.
-    ov_budget = budget if budget > 0 else min(128, q, cus - 1)
+    # The overlapped schedules are also timed when the tuned step is sequential:
+    # then at the largest budget below the CU count with four row slabs per
+    # tile, where the fused schedule measured best (every CU reduces a share).
+    ov_budget = budget if budget > 0 else min(q * 4, cus - 1)
+    ov_slabs = slabs if budget > 0 else (4 if w.tile % 4 == 0 else 1)
     kind = "sequential" if budget == 0 else ("fused" if schedule == tog.SCHEDULE_FUSED
                                              else "streams")
     # The pipeline the step's GEMM runs (tuning-table numbering, 0 = base).
@@ -218,8 +221,8 @@ def main() -> int:
     cfg = tog.config(**cfg_kw)
     cfg_gemm = tog.config(**cfg_kw, stages=tog.STAGES_GEMM)
     cfg_red = tog.config(**cfg_kw, stages=tog.STAGES_REDUCE)
-    cfg_streams = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS))
-    cfg_fused = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED))
+    cfg_streams = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, task_slabs=ov_slabs))
+    cfg_fused = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED, task_slabs=ov_slabs))
     stream = torch.cuda.Stream(dev)
 
     def call(b, c=cfg, rank=w.rank, peers=pd):
@@ -304,12 +307,15 @@ def main() -> int:
     st = timed_graph(lambda: call(budget), args.steps, args.warmup)
     log("sequential step (budget 0): same protocol")
     sq = timed_graph(lambda: call(0), args.steps, args.warmup)
-    log(f"overlapped steps at budget {ov_budget}, two streams and fused: same protocol")
+    log(f"overlapped steps at budget {ov_budget}, {ov_slabs} slab(s) per tile, two streams and "
+        "fused: same protocol")
     ov_s = timed_graph(lambda: call(ov_budget, cfg_streams), args.steps, args.warmup)
     ov_f = timed_graph(lambda: call(ov_budget, cfg_fused), args.steps, args.warmup)
     log("the same with every peer-bound tile also pushed to the staging buffer")
-    cfg_push_s = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, push_outgoing=1))
-    cfg_push_f = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED, push_outgoing=1))
+    cfg_push_s = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, task_slabs=ov_slabs,
+                                   push_outgoing=1))
+    cfg_push_f = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED, task_slabs=ov_slabs,
+                                   push_outgoing=1))
     pu_s = timed_graph(lambda: call(ov_budget, cfg_push_s), args.steps, args.warmup)
     pu_f = timed_graph(lambda: call(ov_budget, cfg_push_f), args.steps, args.warmup)
 
@@ -407,7 +413,8 @@ def main() -> int:
         "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
         "sequential": lat(sq),
         "speedup_vs_sequential": sq["ms_per_step"] / st["ms_per_step"],
-        "overlapped": {"budget": ov_budget, "streams": lat(ov_s), "fused": lat(ov_f),
+        "overlapped": {"budget": ov_budget, "task_slabs": ov_slabs,
+                       "streams": lat(ov_s), "fused": lat(ov_f),
                        "best_speedup_vs_sequential":
                            sq["ms_per_step"] / min(ov_s["ms_per_step"], ov_f["ms_per_step"]),
                        # the sender's side of a push-based transfer: every
