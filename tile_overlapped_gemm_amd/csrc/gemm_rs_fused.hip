@@ -100,17 +100,19 @@ template <int U, bool PEER_F32, bool OUT_F32>
 struct Pending {
   static constexpr int kChunks = U;
   Slab s;
-  Chunks<U, PEER_F32, OUT_F32> c;
+  RelChunks<U, PEER_F32, OUT_F32> c;
 };
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedArgs f) {
   constexpr int kThreads = 64 * WGM * WGN;
-  // Chunks (8 elements) per thread prefetched for each of two tasks at once.
-  // One: with two, the 256 x 256 GEMM spills.  A task of 32 x 128 elements
-  // (a 128 x 128 tile in four slabs) is then one chunk per thread of a
-  // 512-thread workgroup.
-  constexpr int kU = 1;
+  // Tasks taken together after the GEMM phase, and the chunks (8 elements)
+  // per thread of each whose loads are issued at once.  A task of 32 x 128
+  // elements (a 128 x 128 tile in four slabs) is one chunk per thread of a
+  // 512-thread workgroup.  Four tasks need about 240 registers per lane: the
+  // 4-wave 128 x 128 instance takes two, so that two of its workgroups still
+  // fit on a CU.
+  constexpr int kB = kThreads >= 512 ? 4 : 2, kU = 1;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // Thread 0's broadcast word.  Slots alternate: the next write to a slot
   // comes after a barrier that every wave passes only once it has read it.
@@ -137,8 +139,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     const TaskRef k = task_ref(r, task);
     if (k.d != r.rank) return;  // a send task loads after its wait
     p.s = slab_of(r, k.t, k.slab);
-    place<std::remove_reference_t<decltype(p)>::kChunks, kThreads>(p.s, tid, p.c);
-    if (r.prefetch) load_inputs(r, p.c);
+    place_rel<std::remove_reference_t<decltype(p)>::kChunks, kThreads>(p.s, tid, p.c);
+    if (r.prefetch) load_inputs_rel(r, slab_io<PEER_F32, OUT_F32>(r, p.s.e0), p.c);
   };
 
   // Workgroup w < x (the budget) owns tasks w, w + x, ... of the
@@ -157,52 +159,52 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
                                              smem);
   }
 
-  // Every block has been taken: the remaining tasks, two at a time.  A task
-  // waits only for blocks that running workgroups have taken.  Both tasks'
-  // prefetches are issued, wave 0 polls both tasks' flags at once (lanes
-  // 0-31 and 32-63), and both tasks' own-partial loads are in flight before
-  // either is summed: each memory round trip serves two tasks.
+  // Every block has been taken: the remaining tasks, kB at a time.  A task
+  // waits only for blocks that running workgroups have taken.  The tasks'
+  // prefetches are issued, wave 0 polls all their flags at once (16 lanes
+  // per task), and all their own-partial loads are in flight before any is
+  // summed: each memory round trip serves kB tasks.
+  static_assert(kB * 16 <= 64, "16 wait lanes per task");
   while (task < r.ntasks) {
-    const int t0 = task, t1 = task + f.workers;
-    const bool has1 = t1 < r.ntasks;  // uniform
-    Pending<kU, PEER_F32, OUT_F32> p0, p1;
-    begin(t0, p0);
-    if (has1) begin(t1, p1);
+    Pending<kU, PEER_F32, OUT_F32> p[kB];
+#pragma unroll
+    for (int b = 0; b < kB; ++b)
+      if (task + b * f.workers < r.ntasks) begin(task + b * f.workers, p[b]);
     int ok = 1;
     if (tid < 64) {
-      const int tw = tid < 32 ? t0 : t1;
+      const int tw = task + (tid >> 4) * f.workers;
       const uint32_t* fl = nullptr;
       if (tw < r.ntasks) {
         const TaskRef k = task_ref(r, tw);
-        fl = wait_flag(r, k.d, k.t, tid & 31);
+        fl = wait_flag(r, k.d, k.t, tid & 15);
       }
       ok = wait_flags(r, epoch, fl, tid);
     }
     // The flag waits are ordered before every wave's reads of the tiles.
     if (!share(ok)) break;  // the watchdog or the sticky error ended the wait
-    const bool own0 = task_ref(r, t0).d == r.rank;
-    const bool own1 = has1 && task_ref(r, t1).d == r.rank;
-    Raw8<true> o0[kU], o1[kU];
-    if (own0) {
-      if (!r.prefetch) load_inputs(r, p0.c);
-      load_own<kU, PEER_F32, OUT_F32, true>(r, p0.c, p0.s.e0, o0);
+    Raw8<true> own[kB][kU];
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int t = task + b * f.workers;
+      if (t < r.ntasks && task_ref(r, t).d == r.rank) {
+        const SlabIO io = slab_io<PEER_F32, OUT_F32>(r, p[b].s.e0);
+        if (!r.prefetch) load_inputs_rel(r, io, p[b].c);
+        load_own_rel(io, p[b].c, own[b]);
+      }
     }
-    if (own1) {
-      if (!r.prefetch) load_inputs(r, p1.c);
-      load_own<kU, PEER_F32, OUT_F32, true>(r, p1.c, p1.s.e0, o1);
-    }
-    auto rest = [&](int t, bool own, auto& p, const Raw8<true> (&o)[kU]) {
-      if (own) {
-        sum_store(r, p.c, o);
-        reduce_slab<kThreads, kU, PEER_F32, OUT_F32>(r, p.s, tid, kU * kThreads);
+#pragma unroll
+    for (int b = 0; b < kB; ++b) {
+      const int t = task + b * f.workers;
+      if (t >= r.ntasks) break;
+      const TaskRef k = task_ref(r, t);
+      if (k.d == r.rank) {
+        sum_store_rel(r, slab_io<PEER_F32, OUT_F32>(r, p[b].s.e0), p[b].c, own[b]);
+        reduce_slab<kThreads, kU, PEER_F32, OUT_F32>(r, p[b].s, tid, kU * kThreads);
       } else {
-        const TaskRef k = task_ref(r, t);
         push_slab<kThreads, PEER_F32>(r, k.d, k.t, k.slab, tid);
       }
-    };
-    rest(t0, own0, p0, o0);
-    if (has1) rest(t1, own1, p1, o1);
-    task += 2 * f.workers;
+    }
+    task += kB * f.workers;
   }
   if (tid == 0) fused_check_out(ctl, epoch);
 }

@@ -283,6 +283,129 @@ __device__ __forceinline__ void reduce_slab(const ReduceArgs& a, const Slab& s, 
   }
 }
 
+// Slab-relative form (the fused kernel's tasks).  Every operand of a slab is
+// reached through a wave-uniform buffer descriptor based at the slab's first
+// element, so a chunk needs one 32-bit element offset rather than a 64-bit
+// address per operand, and the peers are numbered compactly (ranks ascending,
+// the own rank skipped), so no register holds the unused slot.  Same loads,
+// same order of the sums, same rounding as above.
+constexpr int kNT = 2;  // buffer cache policy NT: streaming
+
+struct SlabIO {
+  __amdgpu_buffer_rsrc_t peer[kMaxRanks - 1];  // j -> rank j + (j >= rank)
+  __amdgpu_buffer_rsrc_t own, res, out;
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rel_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, 0x7fffffff,
+                                           0x00020000);
+}
+
+template <bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ SlabIO slab_io(const ReduceArgs& a, int64_t e0) {
+  constexpr int ps = PEER_F32 ? 4 : 2, os = OUT_F32 ? 4 : 2;
+  SlabIO io;
+#pragma unroll
+  for (int j = 0; j < kMaxRanks - 1; ++j) {
+    const int q = j + (j >= a.rank ? 1 : 0);
+    io.peer[j] = rel_rsrc(j < a.P - 1 ? static_cast<const char*>(a.peers[q]) + e0 * ps : nullptr);
+  }
+  io.own = rel_rsrc(a.own + e0);
+  io.res = rel_rsrc(a.residual ? static_cast<const char*>(a.residual) + e0 * os : nullptr);
+  io.out = rel_rsrc(static_cast<char*>(a.out) + e0 * os);
+  return io;
+}
+
+template <bool F32, int AUX>
+__device__ __forceinline__ Raw8<F32> load_rel(__amdgpu_buffer_rsrc_t r, int off) {
+  if constexpr (F32) {
+    return Raw8<true>{
+        __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4, 0, AUX)),
+        __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 4 + 16, 0, AUX))};
+  } else {
+    return Raw8<false>{
+        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off * 2, 0, AUX))};
+  }
+}
+
+template <int U, bool PEER_F32, bool OUT_F32>
+struct RelChunks {
+  int off[U];  // element offset from the slab's first element
+  bool ok[U];
+  Raw8<PEER_F32> pv[U][kMaxRanks - 1];
+  Raw8<OUT_F32> res[U];
+};
+
+// Chunks c0, c0 + STEP, ..., c0 + (U - 1) STEP of slab s.
+template <int U, int STEP, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void place_rel(const Slab& s, int c0,
+                                          RelChunks<U, PEER_F32, OUT_F32>& c) {
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int k = c0 + u * STEP;
+    const int r = k / s.cpr;
+    const int col = (k - r * s.cpr) << 3;
+    c.ok[u] = k < s.n_chunks && col < s.cols;
+    c.off[u] = r * s.N + col;
+  }
+}
+
+// The peers' and the residual's loads (complete before the call).
+template <int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void load_inputs_rel(const ReduceArgs& a, const SlabIO& io,
+                                                RelChunks<U, PEER_F32, OUT_F32>& c) {
+  const bool with_res = a.residual != nullptr;  // uniform
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!c.ok[u]) continue;
+#pragma unroll
+    for (int j = 0; j < kMaxRanks - 1; ++j)
+      if (j < a.P - 1) c.pv[u][j] = load_rel<PEER_F32, kNT>(io.peer[j], c.off[u]);
+    if (with_res) c.res[u] = load_rel<OUT_F32, kNT>(io.res, c.off[u]);
+  }
+}
+
+// The own partial, device-coherent.
+template <int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void load_own_rel(const SlabIO& io,
+                                             const RelChunks<U, PEER_F32, OUT_F32>& c,
+                                             Raw8<true> (&own)[U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+    if (c.ok[u]) own[u] = load_rel<true, kSC1>(io.own, c.off[u]);
+}
+
+// own + peers (ranks ascending) + residual in fp32, one rounding, the store.
+template <int U, bool PEER_F32, bool OUT_F32>
+__device__ __forceinline__ void sum_store_rel(const ReduceArgs& a, const SlabIO& io,
+                                              const RelChunks<U, PEER_F32, OUT_F32>& c,
+                                              const Raw8<true> (&own)[U]) {
+  const bool with_res = a.residual != nullptr;  // uniform
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    if (!c.ok[u]) continue;
+    F8 acc = widen(own[u]);
+#pragma unroll
+    for (int j = 0; j < kMaxRanks - 1; ++j)
+      if (j < a.P - 1) add8(acc, c.pv[u][j]);
+    if (with_res) add8(acc, c.res[u]);
+    if constexpr (OUT_F32) {
+      f32x4 lo, hi;
+      lo[0] = acc.v[0]; lo[1] = acc.v[1]; lo[2] = acc.v[2]; lo[3] = acc.v[3];
+      hi[0] = acc.v[4]; hi[1] = acc.v[5]; hi[2] = acc.v[6]; hi[3] = acc.v[7];
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), io.out, c.off[u] * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), io.out, c.off[u] * 4 + 16, 0, 0);
+    } else {
+      u32x4 o;
+      o[0] = pack_bf16x2(acc.v[0], acc.v[1]);
+      o[1] = pack_bf16x2(acc.v[2], acc.v[3]);
+      o[2] = pack_bf16x2(acc.v[4], acc.v[5]);
+      o[3] = pack_bf16x2(acc.v[6], acc.v[7]);
+      __builtin_amdgcn_raw_buffer_store_b128(o, io.out, c.off[u] * 2, 0, 0);
+    }
+  }
+}
+
 // Global task id -> (partition, tile, slab).
 struct TaskRef {
   int d, t, slab;
