@@ -1,7 +1,7 @@
-"""Every workload at full size, in the launch configuration the benchmark
-times (the tuning table's AUTO choices): sampled rows against the CPU
-oracle, and bit-identity with the sequential (non-overlapped) schedule over
-the whole output."""
+"""Every workload at full size, in the launch configurations the benchmark
+times (the tuning table's AUTO choices, and its overlapped legs): sampled rows
+against the CPU oracle, and bit-identity with the sequential (non-overlapped)
+schedule over the whole output."""
 import os
 
 import numpy as np
@@ -37,10 +37,18 @@ def test_full_size_sampled_parity(w):
     seq = case.run(tog.ORDER_AUTO, tog.BUDGET_SEQUENTIAL)
     bits = lambda t: t.view(torch.int16) if t.dtype == torch.bfloat16 else t  # noqa: E731
     assert torch.equal(bits(out), bits(seq))
-    # both overlapped schedules at a budget of 128 (the tuned step may be sequential)
+    # Both overlapped schedules as the benchmark's overlapped legs run them when
+    # the tuned step is sequential (the largest budget below the CU count, four
+    # slabs per tile), and at a budget of 128 with one task per tile.
+    _, _, q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
+    x_max = min(q * 4, tog.entwine_device_cus() - 1)
+    slabs = 4 if w.tile % 4 == 0 else 1
     for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
-        print(f"workload {w.name}: overlapped run, budget 128, schedule {sched}", flush=True)
-        assert torch.equal(bits(case.run(tog.ORDER_AUTO, 128, schedule=sched)), bits(seq))
+        for budget, sl in ((x_max, slabs), (128, 1)):
+            print(f"workload {w.name}: overlapped run, budget {budget}, {sl} slab(s), "
+                  f"schedule {sched}", flush=True)
+            got = case.run(tog.ORDER_AUTO, budget, schedule=sched, task_slabs=sl)
+            assert torch.equal(bits(got), bits(seq))
     got = down(out)
     worst = 0.0
     for r in sample_rows(w.rows):

@@ -140,6 +140,20 @@ def test_fused_schedule_variants_bit_identical(dev, w):
     for publish_all in (0, 1):
         out = down(case.run(tog.ORDER_ROW_MAJOR, 3, publish_all=publish_all, **fused))
         np.testing.assert_array_equal(out, base)
+    # 8-wave instances take four tasks per poll round (the 4-wave 128 x 128
+    # instance above takes two): 256 x 256 blocks, both readiness modes,
+    # batches cut short by the task count.
+    wide = dict(block_m=256, block_n=256)
+    ref256 = down(case.run(tog.ORDER_INTERLEAVED, 0, **wide))
+    for mode in (tog.PEERS_PRESEEDED, tog.PEERS_SYMMETRIC):
+        for slabs in (1, 4):
+            for budget in (1, 3, 255):
+                budget = min(budget, tog.entwine_device_cus() - 1)
+                print(f"case {w.name} fused 256x256 mode={mode} slabs={slabs} x={budget}",
+                      flush=True)
+                out = down(case.run(tog.ORDER_INTERLEAVED, budget, peer_ready=mode,
+                                    task_slabs=slabs, schedule=tog.SCHEDULE_FUSED, **wide))
+                np.testing.assert_array_equal(out, ref256)
     # the two schedules alternating on one workspace
     for sched in SCHEDULES * 2:
         out = down(case.run(tog.ORDER_INTERLEAVED, 6, schedule=sched, **blk))
