@@ -378,6 +378,34 @@ def main() -> int:
     check_status("in the kernel timing loop")
     k_gemm, k_red = gm / n, rm / n
 
+    # The communication tail (Sec. 3.2, 5.3) from the device trace: the last
+    # reduction's end past the last GEMM block's end, and the reduction's span
+    # (first task loop entered to last store issued, waits included), median
+    # over replays of a graph of the tuned step and of both overlapped legs,
+    # captured with tracing on (each replay resets and records the stamps).
+    def traced(body, n=21):
+        tog.entwine_trace(True)
+        try:
+            g = graph_of(body)
+            rows = []
+            for _ in range(n):
+                with torch.cuda.stream(stream):
+                    g.replay()
+                rows.append(tog.entwine_trace_read())
+            del g
+        finally:
+            tog.entwine_trace(False)
+        check_status("in the traced calls")
+        med = lambda i: statistics.median(r[i] for r in rows)  # noqa: E731
+        return {"gemm_end_us": med(0), "reduce_start_us": med(1), "reduce_end_us": med(2),
+                "tail_us": med(3),
+                "reduce_span_us": statistics.median(r[2] - r[1] for r in rows)}
+
+    log("device trace of the communication tail: tuned step and both overlapped legs")
+    tr_step = traced(lambda: call(budget))
+    tr_streams = traced(lambda: call(ov_budget, cfg_streams))
+    tr_fused = traced(lambda: call(ov_budget, cfg_fused))
+
     flops = float(w.flops)
     red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
                                        else (4 + 2 * (w.P - 1) + 2))
@@ -433,8 +461,9 @@ def main() -> int:
         "step_kernels_us": ({"fused": k_gemm * 1e3} if kind == "fused"
                             else {"gemm": k_gemm * 1e3, "reduction": k_red * 1e3}),
         "overlap_efficiency": g_alone / st["ms_per_step"],
-        # after the GEMM alone would have ended: the reduction's exposed part
-        "tail_us": (st["ms_per_step"] - g_alone) * 1e3,
+        # the reduction's end past the GEMM's last block, from the device trace
+        "tail_us": tr_step["tail_us"],
+        "trace": {"step": tr_step, "overlapped_streams": tr_streams, "overlapped_fused": tr_fused},
         "reducer": {
             "bytes": red_bytes,
             "flat_warm_us": r_flat * 1e3,
@@ -445,6 +474,9 @@ def main() -> int:
             "tiled_at_budget_us": r_tile * 1e3,
             "tiled_at_budget_gbps": gbps(r_tile),
             "required_gbps_eq4": gbps(g_alone),
+            # bytes over the reduction's traced span, waits included (Sec. 5.4)
+            "measured_gbps_step": gbps(max(tr_step["reduce_span_us"], 1e-3) * 1e-3),
+            "measured_gbps_overlapped_streams": gbps(max(tr_streams["reduce_span_us"], 1e-3) * 1e-3),
         },
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,

@@ -340,6 +340,28 @@ int entwine_staging(const void** staging, int64_t* bytes);
 int entwine_timing(int enable);
 int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls);
 
+/* Device-side trace of the communication tail (Sec. 3.2 and 5.3: the time the
+ * reduction runs past the GEMM).  entwine_trace(1) makes every following
+ * eager call record four wall-clock stamps (s_memrealtime, 100 MHz on
+ * MI355X) in library-owned device memory, reset by a small kernel the call
+ * launches on its stream before its own: the first GEMM block's start, the
+ * first reduction work's start (a workgroup entering its task loop, waits
+ * included), the last GEMM block's end (its stores and flags issued) and the
+ * last reduction's end (its stores issued).  entwine_trace(0) stops
+ * recording.  A call captured into a graph while tracing is on records on
+ * every replay (the trace memory must exist: one traced call outside the
+ * capture first, else ENTWINE_ERR_INVALID_ARGUMENT).
+ *
+ * entwine_trace_read synchronizes the device and returns the last traced
+ * call's stamps in µs from the first GEMM block's start: the GEMM's end, the
+ * reduction's start and end, and the tail = reduction end - GEMM end (0 for
+ * the reduction figures when the call ran no reduction).  Any pointer may be
+ * NULL.  ENTWINE_ERR_INVALID_ARGUMENT if no call on the current device was
+ * traced or the last one ran no GEMM. */
+int entwine_trace(int enable);
+int entwine_trace_read(double* gemm_us, double* reduce_start_us, double* reduce_end_us,
+                       double* tail_us);
+
 /* Load an offline tuning table (text; one entry per line:
  * "M N K_local P tile_order comm_budget block_m block_n reducer_threads
  * [task_slabs [schedule [gemm_variant]]]", '#' starts a comment line; the

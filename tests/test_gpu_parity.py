@@ -404,3 +404,53 @@ def test_degenerate_shapes(dev, M, N, K, P, rank):
             if first is None:
                 first = out
             np.testing.assert_array_equal(out, first)
+
+
+@pytest.mark.parametrize("sched", ["sequential"] + SCHEDULES)
+def test_trace_stamps(dev, sched):
+    """The device trace: the output is unchanged with tracing on, the stamps
+    are ordered (the GEMM ends after it starts, the reduction ends after it
+    starts), the tail is the reduction's end past the GEMM's, and the
+    sequential reduction starts only after the GEMM kernel has ended."""
+    w = SMALL[0]
+    case, ref = case_for(w, dev)
+    kw = dict(block_m=256, block_n=256)
+    budget = 0 if sched == "sequential" else 8
+    if sched != "sequential":
+        kw.update(schedule=sched, task_slabs=2)
+    plain = down(case.run(tog.ORDER_INTERLEAVED, budget, **kw))
+    tog.entwine_trace(True)
+    try:
+        for _ in range(3):
+            out = down(case.run(tog.ORDER_INTERLEAVED, budget, **kw))
+            np.testing.assert_array_equal(out, plain)
+            gemm, r0, r1, tail = tog.entwine_trace_read()
+            print(f"trace {sched}: gemm {gemm:.2f} red {r0:.2f}..{r1:.2f} tail {tail:.2f} us",
+                  flush=True)
+            assert 0.0 < gemm < 1e6
+            assert r0 <= r1 and r1 > 0.0
+            assert tail == pytest.approx(r1 - gemm, abs=1e-6)
+            if sched == "sequential":
+                assert r0 >= gemm
+        # captured with tracing on: every replay resets and records the stamps
+        stream = torch.cuda.Stream()
+        out_d = torch.empty((w.rows, w.N), dtype=case.out_dtype, device=dev)
+        cfg = case.base_cfg(**kw)
+
+        def body():
+            tog.gemm_rs(case.Xd, case.Wd, case.pd, out_d, w.P, w.rank, tog.ORDER_INTERLEAVED,
+                        budget, cfg=cfg, stream=stream)
+
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph, stream=stream):
+            body()
+        for _ in range(2):
+            with torch.cuda.stream(stream):
+                out_d.fill_(float("nan"))
+                graph.replay()
+            gemm, r0, r1, tail = tog.entwine_trace_read()
+            assert 0.0 < gemm < 1e6 and r0 <= r1 and r1 > 0.0
+            np.testing.assert_array_equal(down(out_d), plain)
+    finally:
+        tog.entwine_trace(False)
+    np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, budget, **kw)), plain)

@@ -41,7 +41,8 @@ EXPORTS = [
     "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
     "entwine_plan_task_order", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
-    "entwine_workspace", "entwine_staging", "entwine_timing", "entwine_timing_read", "entwine_load_tuning",
+    "entwine_workspace", "entwine_staging", "entwine_timing", "entwine_timing_read",
+    "entwine_trace", "entwine_trace_read", "entwine_load_tuning",
     "entwine_release", "entwine_device_cus",
 ]
 
@@ -121,6 +122,8 @@ def load(path: str = LIB):
         "entwine_timing": ([i32], i32),
         "entwine_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), pi64],
                                 i32),
+        "entwine_trace": ([i32], i32),
+        "entwine_trace_read": ([ctypes.POINTER(ctypes.c_double)] * 4, i32),
         "entwine_load_tuning": ([ctypes.c_char_p], i32),
         "entwine_release": ([], i32),
         "entwine_device_cus": ([], i32),
@@ -185,6 +188,18 @@ def entwine_timing_read():
     g, r, n = ctypes.c_double(), ctypes.c_double(), ctypes.c_int64()
     _check(load().entwine_timing_read(ctypes.byref(g), ctypes.byref(r), ctypes.byref(n)))
     return g.value, r.value, n.value
+
+
+def entwine_trace(enable: bool) -> None:
+    _check(load().entwine_trace(int(enable)))
+
+
+def entwine_trace_read():
+    """The last traced call's stamps in µs from its first GEMM block's start:
+    (GEMM end, reduction start, reduction end, tail = reduction end - GEMM end)."""
+    v = [ctypes.c_double() for _ in range(4)]
+    _check(load().entwine_trace_read(*(ctypes.byref(x) for x in v)))
+    return tuple(x.value for x in v)
 
 
 def entwine_workspace():

@@ -98,6 +98,8 @@ struct Workspace {
   std::map<PlanKey, std::unique_ptr<DevicePlan>> plans;
   std::vector<TimingPair> timing_live;
   std::vector<TimingPair> timing_free;
+  uint64_t* trace = nullptr;  // kTraceWords stamps of the last traced call
+  bool trace_valid = false;
 };
 
 struct TuneEntry {
@@ -108,6 +110,7 @@ std::mutex g_mu;
 std::map<int, std::unique_ptr<Workspace>> g_ws;
 std::map<std::tuple<int64_t, int64_t, int64_t, int>, TuneEntry> g_tuning;
 bool g_timing = false;
+bool g_trace = false;
 
 void free_plan(DevicePlan* p) {
   if (p->d_blocks) (void)hipFree(p->d_blocks);
@@ -142,6 +145,7 @@ void destroy_workspace(Workspace* w) {
   if (w->flags) (void)hipFree(w->flags);
   if (w->error) (void)hipFree(w->error);
   if (w->ctl) (void)hipFree(w->ctl);
+  if (w->trace) (void)hipFree(w->trace);
   for (hipEvent_t e : {w->cap_fork, w->cap_red})
     if (e) (void)hipEventDestroy(e);
   if (w->ev_fork) (void)hipEventDestroy(w->ev_fork);
@@ -437,6 +441,9 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                   "no workspace on this device: make the same call once outside the capture");
     if (g_timing)
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "entwine_timing cannot record inside a capture");
+    if (g_trace && !g_ws[dev]->trace)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT,
+                  "tracing is on: make the same call once outside the capture first");
   }
   Workspace* w = nullptr;
   if ((rc = get_workspace(&w))) return rc;
@@ -528,6 +535,23 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   size_t flag_bytes = w->flag_count * 4;
   if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, flag_need, true))) return rc;
   w->flag_count = flag_bytes / 4;
+  if (g_trace && !w->trace) {
+    if (hipMalloc((void**)&w->trace, kTraceWords * sizeof(uint64_t)) != hipSuccess) {
+      w->trace = nullptr;
+      return fail(ENTWINE_ERR_OUT_OF_MEMORY, "trace words: allocation failed");
+    }
+  }
+  uint64_t* const trace = g_trace ? w->trace : nullptr;
+  // Before the call's kernels (after its waits on the previous call): the
+  // two "first" words to the largest value, the two "last" words to zero, by
+  // a kernel, so that a captured call resets them on every replay.
+  auto reset_trace = [&](hipStream_t s) -> int {
+    if (!trace) return ENTWINE_OK;
+    const hipError_t e = launch_trace_reset(trace, s);
+    if (e != hipSuccess) return fail(ENTWINE_ERR_HIP, "trace reset: %s", hipGetErrorString(e));
+    w->trace_valid = true;
+    return ENTWINE_OK;
+  };
 
   DevicePlan* dp = nullptr;
   if ((rc = get_plan(w, g, rank, rs.order, rs.peer_ready, rs.release_group, window, &dp)))
@@ -570,6 +594,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ga.outgoing_f32 = rs.peer_f32;
   ga.variant = rs.variant;
   ga.ctl = w->ctl;
+  ga.trace = trace;
 
   ReduceArgs ra{};
   ra.own = w->own;
@@ -599,6 +624,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   // them before its wait.  Under symmetric readiness they count as produced
   // with the tiles, so they are read only after the wait.
   ra.prefetch = rs.peer_ready == ENTWINE_PEERS_PRESEEDED;
+  ra.trace = trace;
 
   if (fused) {
     // One kernel on the caller's stream, after this workspace's previous
@@ -620,6 +646,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
       HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
     }
+    if ((rc = reset_trace(stream))) return rc;
     if (g_timing) {
       HIP_TRY(hipEventRecord(tp.g0, stream));
       HIP_TRY(hipEventRecord(tp.r0, stream));
@@ -693,6 +720,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
     HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
   }
+  if ((rc = reset_trace(stream))) return rc;
   if (forked) {
     HIP_TRY(hipEventRecord(ev_fork, stream));
     HIP_TRY(hipStreamWaitEvent(s_red, ev_fork, 0));
@@ -984,6 +1012,36 @@ int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls) {
   if (gemm_ms) *gemm_ms = gs;
   if (reduce_ms) *reduce_ms = rsum;
   if (calls) *calls = n;
+  return ENTWINE_OK;
+}
+
+int entwine_trace(int enable) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_trace = enable != 0;
+  return ENTWINE_OK;
+}
+
+int entwine_trace_read(double* gemm_us, double* reduce_start_us, double* reduce_end_us,
+                       double* tail_us) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end() || !it->second->trace || !it->second->trace_valid)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no traced call on this device");
+  Workspace* w = it->second.get();
+  HIP_TRY(hipDeviceSynchronize());
+  uint64_t t[kTraceWords];
+  HIP_TRY(hipMemcpy(t, w->trace, sizeof t, hipMemcpyDeviceToHost));
+  if (t[kTraceGemmStart] == UINT64_MAX || t[kTraceGemmEnd] == 0)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "the last traced call ran no GEMM");
+  const double us_per_tick = 1000.0 / (double)w->wall_khz;
+  auto at = [&](uint64_t v) { return ((double)v - (double)t[kTraceGemmStart]) * us_per_tick; };
+  const bool red = t[kTraceRedEnd] != 0;
+  if (gemm_us) *gemm_us = at(t[kTraceGemmEnd]);
+  if (reduce_start_us) *reduce_start_us = red ? at(t[kTraceRedStart]) : 0.0;
+  if (reduce_end_us) *reduce_end_us = red ? at(t[kTraceRedEnd]) : 0.0;
+  if (tail_us) *tail_us = red ? at(t[kTraceRedEnd]) - at(t[kTraceGemmEnd]) : 0.0;
   return ENTWINE_OK;
 }
 

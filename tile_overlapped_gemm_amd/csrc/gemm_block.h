@@ -244,6 +244,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
+  if (a.trace && tid == 0) trace_first(a.trace, kTraceGemmStart);
 
   const int d = blk.x, br = blk.y, bc = blk.z, t_first = blk.w;
   const int row0 = br * BM;  // within the partition
@@ -451,6 +452,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
       for (int t = 0; t < vm * vn; ++t)
         __hip_atomic_store(f + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+  }
+  if (a.trace) {  // uniform: every wave's stores issued
+    __syncthreads();
+    if (tid == 0) trace_last(a.trace, kTraceGemmEnd);
   }
 }
 

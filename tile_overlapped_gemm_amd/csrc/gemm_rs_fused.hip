@@ -109,10 +109,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   // Tasks taken together after the GEMM phase, and the chunks (8 elements)
   // per thread of each whose loads are issued at once.  A task of 32 x 128
   // elements (a 128 x 128 tile in four slabs) is one chunk per thread of a
-  // 512-thread workgroup.  Four tasks need about 240 registers per lane: the
-  // 4-wave 128 x 128 instance takes two, so that two of its workgroups still
-  // fit on a CU.
-  constexpr int kB = kThreads >= 512 ? 4 : 2, kU = 1;
+  // 512-thread workgroup.  Four tasks with bf16 data need about 240
+  // registers per lane.  The 4-wave 128 x 128 instance takes two, so that two
+  // of its workgroups still fit on a CU, and so does an fp32 output; fp32
+  // peers take twice the registers per chunk, and one task.
+  constexpr int kB = PEER_F32 ? 1 : (kThreads >= 512 && !OUT_F32 ? 4 : 2), kU = 1;
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // Thread 0's broadcast word.  Slots alternate: the next write to a slot
   // comes after a barrier that every wave passes only once it has read it.
@@ -165,6 +166,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   // per task), and all their own-partial loads are in flight before any is
   // summed: each memory round trip serves kB tasks.
   static_assert(kB * 16 <= 64, "16 wait lanes per task");
+  const bool worker = task < r.ntasks;  // uniform
+  if (r.trace && worker && tid == 0) trace_first(r.trace, kTraceRedStart);
   while (task < r.ntasks) {
     Pending<kU, PEER_F32, OUT_F32> p[kB];
 #pragma unroll
@@ -205,6 +208,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
       }
     }
     task += kB * f.workers;
+  }
+  if (r.trace && worker) {  // uniform: every wave's stores issued
+    __syncthreads();
+    if (tid == 0) trace_last(r.trace, kTraceRedEnd);
   }
   if (tid == 0) fused_check_out(ctl, epoch);
 }

@@ -42,6 +42,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   const int tid = threadIdx.x;
   const uint32_t epoch = a.ctl[kEpoch];
   int parity = 0;
+  if (a.trace && tid == 0) trace_first(a.trace, kTraceRedStart);
   for (int task = blockIdx.x; task < a.ntasks; task += gridDim.x, parity ^= 1) {
     const TaskRef k = task_ref(a, task);
     if (tid < 64) {
@@ -59,6 +60,10 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
     else
       push_slab<THREADS, PEER_F32>(a, k.d, k.t, k.slab, tid);
   }
+  if (a.trace) {  // uniform: every wave's stores issued
+    __syncthreads();
+    if (tid == 0) trace_last(a.trace, kTraceRedEnd);
+  }
   // Every workgroup, finished or timed out, checks out.
   if (tid == 0 && !a.nowait) check_out(a.ctl, epoch);
 }
@@ -67,6 +72,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
 // array of R * N / 8 chunks walked with a grid-stride loop.
 template <int THREADS, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
+  if (a.trace && threadIdx.x == 0) trace_first(a.trace, kTraceRedStart);
   const int64_t n_chunks = (int64_t)a.R * a.N / 8;
   const int64_t stride = (int64_t)gridDim.x * THREADS * kUnroll;
   for (int64_t c0 = (int64_t)blockIdx.x * THREADS * kUnroll + threadIdx.x; c0 < n_chunks;
@@ -80,6 +86,10 @@ __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
     }
     load_inputs(a, c);
     finish<kUnroll, PEER_F32, OUT_F32, false>(a, c, 0);
+  }
+  if (a.trace) {  // uniform: every wave's stores issued
+    __syncthreads();
+    if (threadIdx.x == 0) trace_last(a.trace, kTraceRedEnd);
   }
 }
 
@@ -131,6 +141,18 @@ int reduce_registers(int threads, int peer_f32, int out_f32) {
     case 512: return regs_threads<512>(peer_f32, out_f32);
     default: return 0;
   }
+}
+
+// The trace words' reset before a traced call: a kernel rather than a memset,
+// so that a captured graph resets them on every replay.
+__global__ void trace_reset_kernel(uint64_t* t) {
+  const int i = threadIdx.x;
+  if (i < kTraceWords) t[i] = (i == kTraceGemmStart || i == kTraceRedStart) ? ~0ull : 0ull;
+}
+
+hipError_t launch_trace_reset(uint64_t* trace, hipStream_t stream) {
+  trace_reset_kernel<<<1, 64, 0, stream>>>(trace);
+  return hipGetLastError();
 }
 
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
