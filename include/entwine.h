@@ -342,22 +342,22 @@ int entwine_timing_read(double* gemm_ms, double* reduce_ms, int64_t* calls);
 
 /* Device-side trace of the communication tail (Sec. 3.2 and 5.3: the time the
  * reduction runs past the GEMM).  entwine_trace(1) makes every following
- * eager call record four wall-clock stamps (s_memrealtime, 100 MHz on
- * MI355X) in library-owned device memory, reset by a small kernel the call
- * launches on its stream before its own: the first GEMM block's start, the
- * first reduction work's start (a workgroup entering its task loop, waits
- * included), the last GEMM block's end (its stores and flags issued) and the
- * last reduction's end (its stores issued).  entwine_trace(0) stops
- * recording.  A call captured into a graph while tracing is on records on
- * every replay (the trace memory must exist: one traced call outside the
- * capture first, else ENTWINE_ERR_INVALID_ARGUMENT).
+ * call record wall-clock stamps (s_memrealtime, 100 MHz on MI355X) in
+ * library-owned device memory: every GEMM block its start and its end (its
+ * stores and flags issued), every reduction workgroup the start of its task
+ * loop (waits included) and its end (its stores issued), each in slots of its
+ * own, written with plain stores.  A small kernel the call launches first
+ * zeroes the slots.  entwine_trace(0) stops recording.  A call captured into a
+ * graph while tracing is on records on every replay; its slots must exist,
+ * i.e. the same call once outside the capture first (else
+ * ENTWINE_ERR_INVALID_ARGUMENT).
  *
- * entwine_trace_read synchronizes the device and returns the last traced
- * call's stamps in µs from the first GEMM block's start: the GEMM's end, the
- * reduction's start and end, and the tail = reduction end - GEMM end (0 for
- * the reduction figures when the call ran no reduction).  Any pointer may be
- * NULL.  ENTWINE_ERR_INVALID_ARGUMENT if no call on the current device was
- * traced or the last one ran no GEMM. */
+ * entwine_trace_read synchronizes the device and reduces the last traced
+ * call's slots to µs from its first GEMM block's start: the last GEMM block's
+ * end, the reduction's first start and last end, and the tail = reduction end
+ * - GEMM end (0 for the reduction figures when the call ran no reduction).
+ * Any pointer may be NULL.  ENTWINE_ERR_INVALID_ARGUMENT if no call on the
+ * current device was traced or the last one ran no GEMM. */
 int entwine_trace(int enable);
 int entwine_trace_read(double* gemm_us, double* reduce_start_us, double* reduce_end_us,
                        double* tail_us);

@@ -98,7 +98,11 @@ struct Workspace {
   std::map<PlanKey, std::unique_ptr<DevicePlan>> plans;
   std::vector<TimingPair> timing_live;
   std::vector<TimingPair> timing_free;
-  uint64_t* trace = nullptr;  // kTraceWords stamps of the last traced call
+  // Trace slots of the last traced call: [2][trace_nb] GEMM block stamps, then
+  // [2][trace_g] reduction workgroup stamps (see trace_at in kernels.h).
+  uint64_t* trace = nullptr;
+  size_t trace_bytes = 0;
+  int64_t trace_nb = 0, trace_g = 0;
   bool trace_valid = false;
 };
 
@@ -441,9 +445,6 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                   "no workspace on this device: make the same call once outside the capture");
     if (g_timing)
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "entwine_timing cannot record inside a capture");
-    if (g_trace && !g_ws[dev]->trace)
-      return fail(ENTWINE_ERR_INVALID_ARGUMENT,
-                  "tracing is on: make the same call once outside the capture first");
   }
   Workspace* w = nullptr;
   if ((rc = get_workspace(&w))) return rc;
@@ -535,21 +536,31 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   size_t flag_bytes = w->flag_count * 4;
   if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, flag_need, true))) return rc;
   w->flag_count = flag_bytes / 4;
-  if (g_trace && !w->trace) {
-    if (hipMalloc((void**)&w->trace, kTraceWords * sizeof(uint64_t)) != hipSuccess) {
+  // Tracing: the call's slots are sized once its grids are known (arm_trace).
+  uint64_t* trace = nullptr;
+  auto arm_trace = [&](int64_t nb, int64_t grid_red, hipStream_t s) -> int {
+    if (!g_trace) return ENTWINE_OK;
+    const size_t need = (size_t)2 * (nb + grid_red) * sizeof(uint64_t);
+    if (w->trace_bytes < need) {
+      if (capturing)
+        return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tracing is on: make the same call once "
+                    "outside the capture first");
+      if (w->trace) (void)hipFree(w->trace);
       w->trace = nullptr;
-      return fail(ENTWINE_ERR_OUT_OF_MEMORY, "trace words: allocation failed");
+      w->trace_bytes = 0;
+      if (hipMalloc((void**)&w->trace, need) != hipSuccess) {
+        w->trace = nullptr;
+        return fail(ENTWINE_ERR_OUT_OF_MEMORY, "trace slots: allocation failed");
+      }
+      w->trace_bytes = need;
     }
-  }
-  uint64_t* const trace = g_trace ? w->trace : nullptr;
-  // Before the call's kernels (after its waits on the previous call): the
-  // two "first" words to the largest value, the two "last" words to zero, by
-  // a kernel, so that a captured call resets them on every replay.
-  auto reset_trace = [&](hipStream_t s) -> int {
-    if (!trace) return ENTWINE_OK;
-    const hipError_t e = launch_trace_reset(trace, s);
-    if (e != hipSuccess) return fail(ENTWINE_ERR_HIP, "trace reset: %s", hipGetErrorString(e));
+    trace = w->trace;
+    w->trace_nb = nb;
+    w->trace_g = grid_red;
     w->trace_valid = true;
+    // Zeroed by a kernel, so that a captured call zeroes them on every replay.
+    const hipError_t e = launch_trace_reset(trace, (int64_t)(need / sizeof(uint64_t)), s);
+    if (e != hipSuccess) return fail(ENTWINE_ERR_HIP, "trace reset: %s", hipGetErrorString(e));
     return ENTWINE_OK;
   };
 
@@ -594,7 +605,6 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ga.outgoing_f32 = rs.peer_f32;
   ga.variant = rs.variant;
   ga.ctl = w->ctl;
-  ga.trace = trace;
 
   ReduceArgs ra{};
   ra.own = w->own;
@@ -624,7 +634,6 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   // them before its wait.  Under symmetric readiness they count as produced
   // with the tiles, so they are read only after the wait.
   ra.prefetch = rs.peer_ready == ENTWINE_PEERS_PRESEEDED;
-  ra.trace = trace;
 
   if (fused) {
     // One kernel on the caller's stream, after this workspace's previous
@@ -646,7 +655,12 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
       HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
     }
-    if ((rc = reset_trace(stream))) return rc;
+    if ((rc = arm_trace(g.NB, grid, stream))) return rc;
+    if (trace) {
+      fa.g.trace = trace;
+      fa.g.trace_nb = (int32_t)g.NB;
+      fa.r.trace = trace + 2 * g.NB;
+    }
     if (g_timing) {
       HIP_TRY(hipEventRecord(tp.g0, stream));
       HIP_TRY(hipEventRecord(tp.r0, stream));
@@ -720,7 +734,12 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
     HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
   }
-  if ((rc = reset_trace(stream))) return rc;
+  if ((rc = arm_trace(run_gemm ? g.NB : 0, run_red ? grid : 0, stream))) return rc;
+  if (trace) {
+    ga.trace = run_gemm ? trace : nullptr;
+    ga.trace_nb = (int32_t)g.NB;
+    ra.trace = run_red ? trace + 2 * (run_gemm ? g.NB : 0) : nullptr;
+  }
   if (forked) {
     HIP_TRY(hipEventRecord(ev_fork, stream));
     HIP_TRY(hipStreamWaitEvent(s_red, ev_fork, 0));
@@ -1031,17 +1050,29 @@ int entwine_trace_read(double* gemm_us, double* reduce_start_us, double* reduce_
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no traced call on this device");
   Workspace* w = it->second.get();
   HIP_TRY(hipDeviceSynchronize());
-  uint64_t t[kTraceWords];
-  HIP_TRY(hipMemcpy(t, w->trace, sizeof t, hipMemcpyDeviceToHost));
-  if (t[kTraceGemmStart] == UINT64_MAX || t[kTraceGemmEnd] == 0)
+  const int64_t nb = w->trace_nb, gr = w->trace_g;
+  std::vector<uint64_t> t((size_t)2 * (nb + gr));
+  HIP_TRY(hipMemcpy(t.data(), w->trace, t.size() * sizeof(uint64_t), hipMemcpyDeviceToHost));
+  // First start and last end of each part; unwritten slots hold 0.
+  auto span = [&](int64_t base, int64_t n, uint64_t* first, uint64_t* last) {
+    *first = UINT64_MAX;
+    *last = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      if (t[base + i]) *first = std::min(*first, t[base + i]);
+      *last = std::max(*last, t[base + n + i]);
+    }
+    return *first != UINT64_MAX && *last != 0;
+  };
+  uint64_t g0, g1, r0, r1;
+  if (!span(0, nb, &g0, &g1))
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "the last traced call ran no GEMM");
+  const bool red = span(2 * nb, gr, &r0, &r1);
   const double us_per_tick = 1000.0 / (double)w->wall_khz;
-  auto at = [&](uint64_t v) { return ((double)v - (double)t[kTraceGemmStart]) * us_per_tick; };
-  const bool red = t[kTraceRedEnd] != 0;
-  if (gemm_us) *gemm_us = at(t[kTraceGemmEnd]);
-  if (reduce_start_us) *reduce_start_us = red ? at(t[kTraceRedStart]) : 0.0;
-  if (reduce_end_us) *reduce_end_us = red ? at(t[kTraceRedEnd]) : 0.0;
-  if (tail_us) *tail_us = red ? at(t[kTraceRedEnd]) - at(t[kTraceGemmEnd]) : 0.0;
+  auto at = [&](uint64_t v) { return ((double)v - (double)g0) * us_per_tick; };
+  if (gemm_us) *gemm_us = at(g1);
+  if (reduce_start_us) *reduce_start_us = red ? at(r0) : 0.0;
+  if (reduce_end_us) *reduce_end_us = red ? at(r1) : 0.0;
+  if (tail_us) *tail_us = red ? at(r1) - at(g1) : 0.0;
   return ENTWINE_OK;
 }
 

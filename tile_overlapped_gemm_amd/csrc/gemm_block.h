@@ -234,17 +234,18 @@ __device__ __forceinline__ void pingpong_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_
 
 // One BM x BN block of C_r = X_r W_r: main loop, epilogue stores and the
 // block's flags.  `blk` = (partition d, block row, block column, first tile);
-// `smem` is the workgroup's S::kLds bytes of LDS.  Every thread of the
+// `bidx` is its dispatch index; `smem` is the workgroup's S::kLds bytes of LDS.  Every thread of the
 // workgroup calls it; it contains workgroup barriers.
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP = false>
-__device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, char* smem) {
+__device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, int bidx,
+                                           char* smem) {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;
-  if (a.trace && tid == 0) trace_first(a.trace, kTraceGemmStart);
+  if (a.trace && tid == 0) trace_at(a.trace, bidx);
 
   const int d = blk.x, br = blk.y, bc = blk.z, t_first = blk.w;
   const int row0 = br * BM;  // within the partition
@@ -455,7 +456,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, ch
   }
   if (a.trace) {  // uniform: every wave's stores issued
     __syncthreads();
-    if (tid == 0) trace_last(a.trace, kTraceGemmEnd);
+    if (tid == 0) trace_at(a.trace, (int64_t)a.trace_nb + bidx);
   }
 }
 

@@ -52,7 +52,7 @@ template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(
-      a, reinterpret_cast<const int4*>(a.blocks)[blockIdx.x], smem);
+      a, reinterpret_cast<const int4*>(a.blocks)[blockIdx.x], (int)blockIdx.x, smem);
 }
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>

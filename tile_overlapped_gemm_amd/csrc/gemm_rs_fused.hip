@@ -156,7 +156,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     if (tid < 64) pick = next_block(ctl, f.nb, xcd, tid);
     const int b = share(pick);
     if (b < 0) break;
-    gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b],
+    gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b], b,
                                              smem);
   }
 
@@ -167,7 +167,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   // summed: each memory round trip serves kB tasks.
   static_assert(kB * 16 <= 64, "16 wait lanes per task");
   const bool worker = task < r.ntasks;  // uniform
-  if (r.trace && worker && tid == 0) trace_first(r.trace, kTraceRedStart);
+  if (r.trace && worker && tid == 0) trace_at(r.trace, blockIdx.x);
   while (task < r.ntasks) {
     Pending<kU, PEER_F32, OUT_F32> p[kB];
 #pragma unroll
@@ -211,7 +211,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   }
   if (r.trace && worker) {  // uniform: every wave's stores issued
     __syncthreads();
-    if (tid == 0) trace_last(r.trace, kTraceRedEnd);
+    if (tid == 0) trace_at(r.trace, (int64_t)gridDim.x + blockIdx.x);
   }
   if (tid == 0) fused_check_out(ctl, epoch);
 }

@@ -32,7 +32,8 @@ struct GemmArgs {
   int32_t publish;          // 0: no flags; 1: release local tiles, mark the rest; 2: release all
   int32_t flag_all;         // 1: every block stores its flags (else only the local ones)
   uint32_t* ctl;            // device control words (see check_out)
-  uint64_t* trace;          // measurement stamps (see kTrace*), nullptr: off
+  uint64_t* trace;          // measurement stamps [2][NB] (see trace_at), nullptr: off
+  int32_t trace_nb;         // NB: blocks of the call
 };
 
 struct ReduceArgs {
@@ -69,7 +70,7 @@ struct ReduceArgs {
   // call, so a task may load them before its wait; 0: they are loaded after
   // the wait, as a real peer's data would be (symmetric readiness).
   int32_t prefetch;
-  uint64_t* trace;                  // measurement stamps (see kTrace*), nullptr: off
+  uint64_t* trace;                  // measurement stamps [2][grid] (see trace_at), nullptr: off
 };
 
 // Epochs.  A flag is ready when it equals the call's epoch, which both
@@ -99,20 +100,17 @@ enum {
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
 
-// Measurement trace of one call: four wall-clock stamps (s_memrealtime),
-// taken by thread 0 of a workgroup.  The first GEMM block's start and the
-// first reduction work's start are minima, the last GEMM block's end (its
-// stores and flags issued) and the last reduction's end are maxima; the host
-// resets the words before the call.  The paper's communication tail is the
-// last reduction's end minus the last GEMM block's end.
-enum { kTraceGemmStart = 0, kTraceRedStart = 1, kTraceGemmEnd = 2, kTraceRedEnd = 3, kTraceWords = 4 };
-__device__ __forceinline__ void trace_first(uint64_t* t, int word) {
-  if (t) __hip_atomic_fetch_min(t + word, (uint64_t)wall_clock64(), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void trace_last(uint64_t* t, int word) {
-  if (t) __hip_atomic_fetch_max(t + word, (uint64_t)wall_clock64(), __ATOMIC_RELAXED,
-                                __HIP_MEMORY_SCOPE_AGENT);
+// Measurement trace of one call: wall-clock stamps (s_memrealtime), each
+// workgroup writing its own slots with plain stores, so tracing adds no
+// contended atomics to the kernels it measures.  GEMM: block b (dispatch
+// index) of nb stores its start at trace[b] and its end (stores and flags
+// issued) at trace[nb + b].  Reduction: workgroup w of a grid of g stores the
+// start of its task loop at trace[w] and its end (stores issued) at
+// trace[g + w].  The host zeroes the slots before the call and reduces them
+// (first start, last end) after it; the paper's communication tail is the
+// last reduction end minus the last GEMM block end.
+__device__ __forceinline__ void trace_at(uint64_t* t, int64_t slot) {
+  if (t) t[slot] = (uint64_t)wall_clock64();
 }
 
 // Counts this workgroup out of a grid of gridDim.x; the last one resets the
@@ -154,9 +152,9 @@ int gemm_blocks_per_cu(int bm, int bn, int variant);
 int gemm_waves(int bm, int bn, int variant);
 int reduce_registers(int threads, int peer_f32, int out_f32);
 
-// Sets the trace words to their reset values (minima to the largest value,
-// maxima to zero) on `stream`.
-hipError_t launch_trace_reset(uint64_t* trace, hipStream_t stream);
+// Zeroes `words` trace slots on `stream` (a kernel, so that a captured graph
+// zeroes them on every replay).
+hipError_t launch_trace_reset(uint64_t* trace, int64_t words, hipStream_t stream);
 
 // RMSNorm of each of `rows` rows of h (out dtype [rows][N], N % 8 == 0):
 // y = gamma * h / sqrt(mean(h^2) + eps), one 256-thread workgroup per row.

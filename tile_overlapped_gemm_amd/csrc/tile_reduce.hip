@@ -42,7 +42,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   const int tid = threadIdx.x;
   const uint32_t epoch = a.ctl[kEpoch];
   int parity = 0;
-  if (a.trace && tid == 0) trace_first(a.trace, kTraceRedStart);
+  if (a.trace && tid == 0) trace_at(a.trace, blockIdx.x);
   for (int task = blockIdx.x; task < a.ntasks; task += gridDim.x, parity ^= 1) {
     const TaskRef k = task_ref(a, task);
     if (tid < 64) {
@@ -62,7 +62,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   }
   if (a.trace) {  // uniform: every wave's stores issued
     __syncthreads();
-    if (tid == 0) trace_last(a.trace, kTraceRedEnd);
+    if (tid == 0) trace_at(a.trace, (int64_t)gridDim.x + blockIdx.x);
   }
   // Every workgroup, finished or timed out, checks out.
   if (tid == 0 && !a.nowait) check_out(a.ctl, epoch);
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
 // array of R * N / 8 chunks walked with a grid-stride loop.
 template <int THREADS, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
-  if (a.trace && threadIdx.x == 0) trace_first(a.trace, kTraceRedStart);
+  if (a.trace && threadIdx.x == 0) trace_at(a.trace, blockIdx.x);
   const int64_t n_chunks = (int64_t)a.R * a.N / 8;
   const int64_t stride = (int64_t)gridDim.x * THREADS * kUnroll;
   for (int64_t c0 = (int64_t)blockIdx.x * THREADS * kUnroll + threadIdx.x; c0 < n_chunks;
@@ -89,7 +89,7 @@ __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
   }
   if (a.trace) {  // uniform: every wave's stores issued
     __syncthreads();
-    if (threadIdx.x == 0) trace_last(a.trace, kTraceRedEnd);
+    if (threadIdx.x == 0) trace_at(a.trace, (int64_t)gridDim.x + blockIdx.x);
   }
 }
 
@@ -143,15 +143,19 @@ int reduce_registers(int threads, int peer_f32, int out_f32) {
   }
 }
 
-// The trace words' reset before a traced call: a kernel rather than a memset,
-// so that a captured graph resets them on every replay.
-__global__ void trace_reset_kernel(uint64_t* t) {
-  const int i = threadIdx.x;
-  if (i < kTraceWords) t[i] = (i == kTraceGemmStart || i == kTraceRedStart) ? ~0ull : 0ull;
+// The trace slots' reset before a traced call: a kernel rather than a
+// memset, so that a captured graph resets them on every replay.
+__global__ void trace_reset_kernel(uint64_t* t, int64_t words) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < words;
+       i += (int64_t)gridDim.x * blockDim.x)
+    t[i] = 0;
 }
 
-hipError_t launch_trace_reset(uint64_t* trace, hipStream_t stream) {
-  trace_reset_kernel<<<1, 64, 0, stream>>>(trace);
+hipError_t launch_trace_reset(uint64_t* trace, int64_t words, hipStream_t stream) {
+  int64_t blocks = (words + 255) / 256;
+  if (blocks > 256) blocks = 256;
+  if (blocks < 1) blocks = 1;
+  trace_reset_kernel<<<(int)blocks, 256, 0, stream>>>(trace, words);
   return hipGetLastError();
 }
 
