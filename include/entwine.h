@@ -33,6 +33,14 @@
  *   - Calls are serialized on the library's workspace: each call's kernels
  *     start after the previous call's kernels on the same device finished.
  *     Host threads may call concurrently; a mutex guards the workspace.
+ *   - Graph capture: a call may be captured into a HIP graph once the same
+ *     call (same shape and schedule) has run outside the capture, so that its
+ *     workspace and schedule exist (else ENTWINE_ERR_INVALID_ARGUMENT).  The
+ *     graph holds workspace addresses: after a capture, workspace buffers
+ *     that a later, larger call outgrows stay allocated until
+ *     entwine_release(), which the caller makes only after destroying the
+ *     graphs.  Replays of one graph, and eager calls between them, are
+ *     serialized like calls.
  *   - Element types: bf16 is IEEE binary32 truncated to its upper 16 bits
  *     (stored as uint16), rounding is to nearest even.
  */
@@ -370,7 +378,9 @@ int entwine_trace_read(double* gemm_us, double* reduce_start_us, double* reduce_
  * fields). */
 int entwine_load_tuning(const char* path);
 
-/* Frees the current device's workspace; the next call re-creates it. */
+/* Frees the current device's workspace (including buffers retired after a
+ * graph capture); the next call re-creates it.  Graphs that captured calls
+ * must be destroyed first. */
 int entwine_release(void);
 
 /* Number of compute units of the current device (0 when no device). */

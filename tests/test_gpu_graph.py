@@ -83,3 +83,50 @@ def test_capture_requires_prepared_workspace():
     assert err is not None and err.status == tog.ENTWINE_ERR_INVALID_ARGUMENT
     torch.cuda.synchronize()
 
+
+
+@pytest.mark.parametrize("sched", [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED])
+def test_graph_survives_workspace_growth(sched):
+    """A graph captured at one shape keeps working after a larger eager call
+    has grown the workspace: the outgrown buffers the graph refers to are
+    retired, not freed, until entwine_release()."""
+    dev = device()
+    tog.entwine_release()
+    small = wl.custom("grow_small", 512, 512, 256, 4, rank=1, index=323)
+    big = wl.custom("grow_big", 2048, 1024, 256, 4, rank=1, index=324)
+
+    def inputs(w):
+        X, W = wl.operands(w)
+        peers = wl.peer_partials(w)
+        return up(X, dev), up(W, dev), [None if p is None else up(p, dev) for p in peers]
+
+    Xs, Ws, ps = inputs(small)
+    Xb, Wb, pb = inputs(big)
+    cfg = tog.config(block_m=128, block_n=128, schedule=sched)
+    out = torch.empty((small.rows, small.N), dtype=torch.bfloat16, device=dev)
+    tog.gemm_rs(Xs, Ws, ps, out, small.P, small.rank, tog.ORDER_INTERLEAVED, 4, cfg=cfg)
+    torch.cuda.synchronize()
+    ref = down(out)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        tog.gemm_rs(Xs, Ws, ps, out, small.P, small.rank, tog.ORDER_INTERLEAVED, 4, cfg=cfg)
+    # a larger eager call outgrows the own and outgoing partials and the flags
+    out_b = torch.empty((big.rows, big.N), dtype=torch.bfloat16, device=dev)
+    tog.gemm_rs(Xb, Wb, pb, out_b, big.P, big.rank, tog.ORDER_INTERLEAVED, 4, cfg=cfg)
+    torch.cuda.synchronize()
+    ref_b = down(out_b)
+    for rep in range(3):
+        print(f"replay {rep} after growth, schedule {sched}", flush=True)
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert tog.entwine_device_status(torch.cuda.current_stream().cuda_stream) == tog.ENTWINE_OK
+        np.testing.assert_array_equal(down(out), ref)
+        # eager calls at the larger shape between replays
+        out_b.fill_(float("nan"))
+        tog.gemm_rs(Xb, Wb, pb, out_b, big.P, big.rank, tog.ORDER_INTERLEAVED, 4, cfg=cfg)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(down(out_b), ref_b)
+    del g
+    torch.cuda.synchronize()
+    tog.entwine_release()

@@ -104,6 +104,11 @@ struct Workspace {
   size_t trace_bytes = 0;
   int64_t trace_nb = 0, trace_g = 0;
   bool trace_valid = false;
+  // Once a call has been captured into a graph, the graph holds this
+  // workspace's addresses: a buffer outgrown after that is retired (kept
+  // allocated until entwine_release) instead of freed.
+  bool captured = false;
+  std::vector<void*> retired;
 };
 
 struct TuneEntry {
@@ -150,6 +155,8 @@ void destroy_workspace(Workspace* w) {
   if (w->error) (void)hipFree(w->error);
   if (w->ctl) (void)hipFree(w->ctl);
   if (w->trace) (void)hipFree(w->trace);
+  for (void* p : w->retired) (void)hipFree(p);
+  w->retired.clear();
   for (hipEvent_t e : {w->cap_fork, w->cap_red})
     if (e) (void)hipEventDestroy(e);
   if (w->ev_fork) (void)hipEventDestroy(w->ev_fork);
@@ -201,7 +208,10 @@ int ensure(Workspace* w, void** buf, size_t* have, size_t need, bool zero) {
     HIP_TRY(hipEventSynchronize(w->ev_red));
   }
   if (*buf) {
-    HIP_TRY(hipFree(*buf));
+    if (w->captured)
+      w->retired.push_back(*buf);  // a captured graph may still use it
+    else
+      HIP_TRY(hipFree(*buf));
     *buf = nullptr;
     *have = 0;
   }
@@ -448,6 +458,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   }
   Workspace* w = nullptr;
   if ((rc = get_workspace(&w))) return rc;
+  if (capturing) w->captured = true;
   if (rs.budget >= w->cus)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT,
                 "comm_budget %d must stay below the device's %d compute units", rs.budget, w->cus);
@@ -545,7 +556,12 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       if (capturing)
         return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tracing is on: make the same call once "
                     "outside the capture first");
-      if (w->trace) (void)hipFree(w->trace);
+      if (w->trace) {
+        if (w->captured)
+          w->retired.push_back(w->trace);  // a captured graph may still use it
+        else
+          (void)hipFree(w->trace);
+      }
       w->trace = nullptr;
       w->trace_bytes = 0;
       if (hipMalloc((void**)&w->trace, need) != hipSuccess) {
