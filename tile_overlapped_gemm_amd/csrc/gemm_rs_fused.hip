@@ -30,6 +30,14 @@
 // register and takes that XCD's next block; when its list is exhausted it
 // takes blocks from the other lists.
 //
+// Reduction phase.  A task's time is set by memory latency rather than by
+// its bytes, so tasks are small (row slabs of a tile, one chunk per thread)
+// and a worker takes four at a time: the inputs that existed before the call
+// (preseeded peers, the residual) are loaded before the wait, wave 0 polls
+// the four tasks' flags at once, and the four own-partial loads are in flight
+// together.  Operands go through buffer descriptors based at each slab, which
+// keeps four tasks within the GEMM's register budget.
+//
 // Check-out.  Every workgroup counts itself out; the last one clears the
 // tickets and advances the epoch, so the next call (or graph replay) starts
 // from zeroed tickets with a fresh epoch.
