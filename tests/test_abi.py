@@ -167,3 +167,15 @@ def chain_call(residual=FAKE * 8, gamma=FAKE * 9, eps=1e-5, h_out=FAKE * 3, y_ou
 def test_chain_validation_before_any_device_call(lib, kw):
     assert chain_call(**kw) == tog.ENTWINE_ERR_INVALID_ARGUMENT
     assert lib.entwine_last_error_message().decode()
+
+
+def test_trace_switch_and_read_without_a_traced_call(lib):
+    """entwine_trace only sets a switch (no device call); reading with no traced
+    call on the current device is an error, never a crash."""
+    assert lib.entwine_trace(1) == tog.ENTWINE_OK
+    assert lib.entwine_trace(0) == tog.ENTWINE_OK
+    out = [ctypes.c_double(-1.0) for _ in range(4)]
+    rc = lib.entwine_trace_read(*(ctypes.byref(x) for x in out))
+    assert rc in (tog.ENTWINE_ERR_INVALID_ARGUMENT, tog.ENTWINE_ERR_HIP)
+    assert lib.entwine_trace_read(None, None, None, None) in (tog.ENTWINE_ERR_INVALID_ARGUMENT,
+                                                              tog.ENTWINE_ERR_HIP)
