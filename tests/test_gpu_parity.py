@@ -300,34 +300,43 @@ def test_exact_integer_inputs_bit_exact(dev, w):
     ref = orc.gemm_rs(X, W, peers, w.P, w.rank)
     assert (np.abs(ref) < 256).all() and (ref == np.round(ref)).all()
     for order in ORDERS:
-        for budget in (0, 2):
-            out = down(case.run(order, budget))
+        for budget, sched in ((0, tog.SCHEDULE_STREAMS), (2, tog.SCHEDULE_STREAMS),
+                              (2, tog.SCHEDULE_FUSED), (255, tog.SCHEDULE_FUSED)):
+            budget = min(budget, tog.entwine_device_cus() - 1)
+            out = down(case.run(order, budget, schedule=sched, task_slabs=2))
             np.testing.assert_array_equal(as_f64(out), ref)
 
 
-def test_special_cases(dev):
-    """P = 1 is a plain GEMM; W = 0 leaves the sum of the peers; X = I passes W's rows."""
+@pytest.mark.parametrize("sched", SCHEDULES)
+def test_special_cases(dev, sched):
+    """P = 1 is a plain GEMM; W = 0 leaves the sum of the peers; X = I passes
+    W's rows; under both overlapped schedules (and the fused kernel's batches
+    with 256 x 256 blocks)."""
+    kw = dict(schedule=sched)
     w = wl.custom("p1", 256, 512, 128, 1, index=303)
     X, W = wl.operands(w)
     case = Case(w, X, W, [None], dev)
-    out = down(case.run(tog.ORDER_INTERLEAVED, 2))
-    assert err_ratio(out, orc.partial_gemm(X, W)) <= 1.0
+    for blk in ((128, 128), (256, 256)):
+        out = down(case.run(tog.ORDER_INTERLEAVED, 2, block_m=blk[0], block_n=blk[1], **kw))
+        assert err_ratio(out, orc.partial_gemm(X, W)) <= 1.0
     w = wl.custom("w0", 512, 256, 128, 4, rank=3, index=304)
     X, W = wl.operands(w)
     W[:] = 0
     peers = wl.peer_partials(w)
     case = Case(w, X, W, peers, dev)
-    out = down(case.run(tog.ORDER_ROW_MAJOR, 3))
     zero = np.zeros((w.rows, w.N), dtype=np.float32)
-    np.testing.assert_array_equal(out, orc.reduce_f32(zero, peers, w.P, w.rank))
+    for blk in ((128, 128), (256, 256)):
+        out = down(case.run(tog.ORDER_ROW_MAJOR, 3, block_m=blk[0], block_n=blk[1], **kw))
+        np.testing.assert_array_equal(out, orc.reduce_f32(zero, peers, w.P, w.rank))
     w = wl.custom("eye", 256, 384, 256, 2, rank=1, index=305)
     X = wl.bf16_bits(np.eye(256, dtype=np.float32))
     _, W = wl.operands(w)
     peers = wl.peer_partials(w)
     case = Case(w, X, W, peers, dev)
-    out = down(case.run(tog.ORDER_COL_MAJOR, 1))
     own = wl.bf16_to_f32(W.T[128:256]).copy()  # rows of W (as K x N) of partition 1
-    np.testing.assert_array_equal(out, orc.reduce_f32(own, peers, w.P, w.rank))
+    for blk in ((128, 128), (256, 256)):
+        out = down(case.run(tog.ORDER_COL_MAJOR, 1, block_m=blk[0], block_n=blk[1], **kw))
+        np.testing.assert_array_equal(out, orc.reduce_f32(own, peers, w.P, w.rank))
 
 
 def test_repeated_calls_and_release(dev):
