@@ -498,7 +498,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     const int rr = reduce_registers(rs.threads, rs.peer_f32, rs.out_f32);
     auto up8 = [](int v) { return (v + 7) / 8 * 8; };
     auto fits = [&](int variant, int* gr) {
-      *gr = gemm_registers(g.bm, g.bn, variant);
+      *gr = gemm_registers(g.bm, g.bn, variant, /*tickets=*/true);
       const int gemm_waves_per_simd = (gemm_waves(g.bm, g.bn, variant) + 3) / 4;
       return gemm_waves_per_simd * up8(*gr) + red_waves_per_simd * up8(rr) <= 512;
     };
@@ -621,6 +621,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   ga.outgoing_f32 = rs.peer_f32;
   ga.variant = rs.variant;
   ga.ctl = w->ctl;
+  ga.nb = (int32_t)g.NB;
 
   ReduceArgs ra{};
   ra.own = w->own;
@@ -763,7 +764,19 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
 
   if (g_timing) HIP_TRY(hipEventRecord(tp.g0, stream));
   if (run_gemm) {
-    hipError_t e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, stream);
+    // Beside the two-stream reduction the GEMM's workgroups take blocks from
+    // tickets: a CU that also runs a reduction workgroup is slower and takes
+    // fewer blocks.  With a fixed deal, a budget of 16 to 64 workgroups
+    // delayed the whole large_mlp GEMM by 10-25 % (the CUs that hosted busy
+    // reducers finished their blocks last).
+    hipError_t e;
+    if (forked) {
+      const int per_cu = std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1);
+      const int64_t gemm_grid = std::min<int64_t>((int64_t)per_cu * w->cus, g.NB);
+      e = launch_gemm_tickets(ga, g.bm, g.bn, (int)gemm_grid, stream);
+    } else {
+      e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, stream);
+    }
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
   }

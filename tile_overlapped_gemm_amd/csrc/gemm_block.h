@@ -232,16 +232,62 @@ __device__ __forceinline__ void pingpong_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_
   }
 }
 
+// Block tickets (the fused kernel and the persistent GEMM): block b of the
+// XCD-aware dispatch order belongs to XCD b % 8, whose ticket hands out its
+// blocks in order.
+// XCC_ID hardware register (id 20), bits [3:0]: the XCD this wave runs on.
+__device__ __forceinline__ int xcd_id() {
+  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;
+}
+
+__device__ __forceinline__ uint32_t take(uint32_t* w) {
+  return __hip_atomic_fetch_add(w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t peek(const uint32_t* w) {
+  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Wave 0 (lane = 0..63): the dispatch index of the next GEMM block for a
+// workgroup on XCD x, or -1 once every list is exhausted (uniform).  List y
+// holds blocks y, y + 8, ...; tickets only grow, so a list seen exhausted
+// stays exhausted.  The own list is taken from directly; once it is empty,
+// lanes 0-7 look at all eight tickets at once, so finding that every list is
+// empty costs one load latency, not eight.
+__device__ int next_block(uint32_t* ctl, int nb, int x, int lane) {
+  auto len = [nb](int y) { return nb > y ? (uint32_t)((nb - y + 7) >> 3) : 0u; };
+  int got = -1;
+  if (lane == 0) {
+    const uint32_t i = take(ctl + kBlockTicket + x * kLine);
+    if (i < len(x)) got = x + 8 * (int)i;
+  }
+  got = __builtin_amdgcn_readfirstlane(got);
+  while (got < 0) {
+    const bool open = lane < 8 && lane != x && peek(ctl + kBlockTicket + lane * kLine) < len(lane);
+    const uint64_t m = __ballot(open);
+    if (m == 0) return -1;
+    // The first open list after x, cyclically.
+    const uint32_t rot = (uint32_t)(((m >> (x + 1)) | (m << (7 - x))) & 0xffu);
+    const int y = (x + 1 + __builtin_ctz(rot)) & 7;
+    if (lane == 0) {
+      const uint32_t i = take(ctl + kBlockTicket + y * kLine);
+      if (i < len(y)) got = y + 8 * (int)i;
+    }
+    got = __builtin_amdgcn_readfirstlane(got);
+  }
+  return got;
+}
+
 // One BM x BN block of C_r = X_r W_r: main loop, epilogue stores and the
 // block's flags.  `blk` = (partition d, block row, block column, first tile);
-// `bidx` is its dispatch index; `smem` is the workgroup's S::kLds bytes of LDS.  Every thread of the
+// `bidx` is its dispatch index; `smem` is the workgroup's S::kLds bytes of LDS;
+// `tid` is threadIdx.x (a persistent caller passes it laundered, so that the
+// lane's offsets are recomputed per block rather than held across blocks).  Every thread of the
 // workgroup calls it; it contains workgroup barriers.
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP = false>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, int bidx,
-                                           char* smem) {
+                                           char* smem, int tid = threadIdx.x) {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
 
-  const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / WGN, wn = wave % WGN;

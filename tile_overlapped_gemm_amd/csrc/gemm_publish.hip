@@ -55,6 +55,51 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
       a, reinterpret_cast<const int4*>(a.blocks)[blockIdx.x], (int)blockIdx.x, smem);
 }
 
+// Persistent form: each workgroup takes blocks from its XCD's ticket (then
+// from the others) until every block is taken.  Used beside the two-stream
+// schedule's reduction workgroups: a CU shared with one runs its blocks more
+// slowly and simply takes fewer of them, where a fixed block-to-workgroup
+// deal would make the whole GEMM wait for the slowest such CU.
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+__global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs a) {
+  extern __shared__ __attribute__((aligned(1024))) char smem[];
+  // Thread 0's pick; slots alternate, and the next write to a slot comes
+  // after a barrier that every wave passes once it has read it.
+  __shared__ int s_pick[2];
+  const int tid = threadIdx.x;
+  const int xcd = xcd_id();
+  int parity = 0;
+  while (true) {
+    int pick = 0;
+    if (tid < 64) pick = next_block(a.ctl, a.nb, xcd, tid);
+    if (tid == 0) s_pick[parity] = pick;
+    __syncthreads();
+    const int b = __builtin_amdgcn_readfirstlane(s_pick[parity]);
+    parity ^= 1;
+    if (b < 0) break;
+    // Laundered thread index: the block's lane offsets are recomputed per
+    // block instead of living in registers across blocks, which keeps this
+    // kernel at the stand-alone GEMM's register count, and so beside a
+    // reduction workgroup on a CU.
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(a, reinterpret_cast<const int4*>(a.blocks)[b], b,
+                                             smem, ltid);
+  }
+  // Check-out: the last workgroup (every other one has taken its last
+  // ticket) resets the tickets for the next call.
+  if (tid == 0) {
+    const uint32_t n = __hip_atomic_fetch_add(a.ctl + kGemmDone, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+    if (n + 1 == gridDim.x) {
+      for (int y = 0; y < 8; ++y)
+        __hip_atomic_store(a.ctl + kBlockTicket + y * kLine, 0u, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.ctl + kGemmDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
@@ -66,6 +111,20 @@ hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
     attr_set = true;
   }
   gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<num_blocks, S::kThreads, S::kLds, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+hipError_t launch_tickets(const GemmArgs& a, int grid, hipStream_t s) {
+  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<grid, S::kThreads, S::kLds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -84,6 +143,15 @@ template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
 int regs_of() {
   hipFuncAttributes at{};
   if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>) !=
+      hipSuccess)
+    return 0;
+  return at.numRegs;
+}
+
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+int ticket_regs_of() {
+  hipFuncAttributes at{};
+  if (hipFuncGetAttributes(&at, (const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP>) !=
       hipSuccess)
     return 0;
   return at.numRegs;
@@ -127,6 +195,16 @@ struct Launch {
     else return launch_shape<BM, BN, BK, NS, WGM, WGN, PP>(a, num_blocks, s);
   }
 };
+struct LaunchTickets {
+  const GemmArgs& a;
+  int grid;
+  hipStream_t s;
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  hipError_t run() {
+    if constexpr (BM == 0) return hipErrorInvalidValue;
+    else return launch_tickets<BM, BN, BK, NS, WGM, WGN, PP>(a, grid, s);
+  }
+};
 struct Occupancy {
   template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   int run() {
@@ -135,16 +213,20 @@ struct Occupancy {
   }
 };
 struct Registers {
+  bool tickets;
   template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   int run() {
     if constexpr (BM == 0) return 0;
+    else if (tickets) return ticket_regs_of<BM, BN, BK, NS, WGM, WGN, PP>();
     else return regs_of<BM, BN, BK, NS, WGM, WGN, PP>();
   }
 };
 
 }  // namespace
 
-int gemm_registers(int bm, int bn, int variant) { return with_instance(bm, bn, variant, Registers{}); }
+int gemm_registers(int bm, int bn, int variant, bool tickets) {
+  return with_instance(bm, bn, variant, Registers{tickets});
+}
 
 int gemm_blocks_per_cu(int bm, int bn, int variant) {
   return with_instance(bm, bn, variant, Occupancy{});
@@ -160,6 +242,10 @@ int gemm_waves(int bm, int bn, int variant) { return with_instance(bm, bn, varia
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream) {
   return with_instance(bm, bn, a.variant, Launch{a, num_blocks, stream});
+}
+
+hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream) {
+  return with_instance(bm, bn, a.variant, LaunchTickets{a, grid, stream});
 }
 
 }  // namespace entwine

@@ -47,48 +47,6 @@
 namespace entwine {
 namespace {
 
-// XCC_ID hardware register (id 20), bits [3:0]: the XCD this wave runs on.
-__device__ __forceinline__ int xcd_id() {
-  return __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;
-}
-
-__device__ __forceinline__ uint32_t take(uint32_t* w) {
-  return __hip_atomic_fetch_add(w, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint32_t peek(const uint32_t* w) {
-  return __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wave 0 (lane = 0..63): the dispatch index of the next GEMM block for a
-// workgroup on XCD x, or -1 once every list is exhausted (uniform).  List y
-// holds blocks y, y + 8, ...; tickets only grow, so a list seen exhausted
-// stays exhausted.  The own list is taken from directly; once it is empty,
-// lanes 0-7 look at all eight tickets at once, so finding that every list is
-// empty costs one load latency, not eight.
-__device__ int next_block(uint32_t* ctl, int nb, int x, int lane) {
-  auto len = [nb](int y) { return nb > y ? (uint32_t)((nb - y + 7) >> 3) : 0u; };
-  int got = -1;
-  if (lane == 0) {
-    const uint32_t i = take(ctl + kBlockTicket + x * kLine);
-    if (i < len(x)) got = x + 8 * (int)i;
-  }
-  got = __builtin_amdgcn_readfirstlane(got);
-  while (got < 0) {
-    const bool open = lane < 8 && lane != x && peek(ctl + kBlockTicket + lane * kLine) < len(lane);
-    const uint64_t m = __ballot(open);
-    if (m == 0) return -1;
-    // The first open list after x, cyclically.
-    const uint32_t rot = (uint32_t)(((m >> (x + 1)) | (m << (7 - x))) & 0xffu);
-    const int y = (x + 1 + __builtin_ctz(rot)) & 7;
-    if (lane == 0) {
-      const uint32_t i = take(ctl + kBlockTicket + y * kLine);
-      if (i < len(y)) got = y + 8 * (int)i;
-    }
-    got = __builtin_amdgcn_readfirstlane(got);
-  }
-  return got;
-}
-
 __device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
   const uint32_t n = __hip_atomic_fetch_add(ctl + kFusedDone, 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);

@@ -34,6 +34,7 @@ struct GemmArgs {
   uint32_t* ctl;            // device control words (see check_out)
   uint64_t* trace;          // measurement stamps [2][NB] (see trace_at), nullptr: off
   int32_t trace_nb;         // NB: blocks of the call
+  int32_t nb;               // NB, for the persistent (ticket) GEMM
 };
 
 struct ReduceArgs {
@@ -95,7 +96,8 @@ enum {
   kReduceDone = 1 * kLine,
   kFusedDone = 2 * kLine,
   kBlockTicket = 3 * kLine,  // ticket of XCD y at kBlockTicket + y * kLine
-  kCtlWords = 11 * kLine
+  kGemmDone = 11 * kLine,    // check-out count of the persistent (ticket) GEMM
+  kCtlWords = 12 * kLine
 };
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
@@ -137,6 +139,11 @@ struct FusedArgs {
 // GEMM block shapes built: (bm, bn) in {128, 256}^2.
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream);
+// The same GEMM as `grid` persistent workgroups that take blocks from the
+// per-XCD tickets until all a.nb are taken (the two-stream schedule): a CU
+// that also hosts a reduction workgroup then takes fewer blocks.  The last
+// workgroup to finish resets the tickets.
+hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream);
 
 // peer / out dtype: 0 = bf16, 1 = fp32.  threads in {128, 256, 512}.  flat:
 // reduce the whole partition without flags (after the GEMM has finished).
@@ -145,7 +152,7 @@ hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, in
 
 // Registers per lane (VGPRs + AGPRs) of the kernels a launch would use, for
 // the co-residency check; 0 if unknown.
-int gemm_registers(int bm, int bn, int variant);
+int gemm_registers(int bm, int bn, int variant, bool tickets = false);
 // GEMM workgroups of a block shape resident per CU at once (0 if unknown).
 int gemm_blocks_per_cu(int bm, int bn, int variant);
 // Waves per GEMM workgroup (64 lanes each).
