@@ -43,6 +43,11 @@
 //  * Publication: tiles read on this device are written with device-coherent
 //    (SC1) stores; the workgroup synchronizes after its stores, then thread 0
 //    stores the call's epoch into the flag of every tile the block covers.
+//  * Two launch forms.  gemm_publish_kernel: one workgroup per block, block
+//    b of the dispatch order on workgroup b (sequential schedule, single
+//    stages).  gemm_ticket_kernel: persistent workgroups taking blocks from
+//    per-XCD tickets (beside the two-stream reduction, whose workgroups slow
+//    the CUs they share).
 #include "gemm_block.h"
 
 namespace entwine {
