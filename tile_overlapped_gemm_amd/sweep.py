@@ -18,7 +18,8 @@ The search is staged rather than exhaustive:
   A. every GEMM block shape and main-loop pipeline without overlap (x = 0,
      the order does not matter), and every block shape x production order
      with the two-stream schedule (base pipeline) and the fused schedule
-     (every pipeline) at budget min(128, Q);
+     (every pipeline) at budget min(128, Q); and both schedules per block
+     shape at the largest budget below the CU count with four slabs;
   B. for the best two overlapped (block, order, schedule) points of A: every
      budget of the list x task slabs;
   C. at the best two-stream point: reduction threads 128 / 256 / 512 (the
@@ -213,6 +214,12 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
                for bm, bn in blocks for order in orders
                for s in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED)
                for v in (pipelines_for(bm, bn) if s == tog.SCHEDULE_FUSED else [0])]
+    # The overlapped schedules also at the largest budget with four slabs per
+    # tile (every CU takes a share of the reduction), interleaved order.
+    x_max = min(q * 4, cus - 1)
+    if w.tile % 4 == 0:
+        stage_a += [run(Candidate(bm, bn, tog.ORDER_INTERLEAVED, x_max, slabs=4, schedule=s))
+                    for bm, bn in blocks for s in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED)]
     top = sorted((c for c in stage_a if c.us is not None), key=lambda c: c.us)[:2]
     log(f"stage A: no overlap {pick(seq)}; overlapped {top}")
     # B: budget x slabs at the two best overlapped points
