@@ -133,6 +133,8 @@ def main() -> int:
     ap.add_argument("--peers", default="preseeded", help="preseeded|symmetric")
     ap.add_argument("--schedule", default="auto", choices=["auto", "streams", "fused"],
                     help="overlapped schedule: two streams, one fused kernel, or the tuning table's")
+    ap.add_argument("--static-cus", type=int, default=32,
+                    help="CUs reserved for the reduction in the CU-policy leg (Sec. 5.3.3)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
@@ -223,6 +225,11 @@ def main() -> int:
     cfg_red = tog.config(**cfg_kw, stages=tog.STAGES_REDUCE)
     cfg_streams = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, task_slabs=ov_slabs))
     cfg_fused = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_FUSED, task_slabs=ov_slabs))
+    # CU policy (Sec. 5.3.3): n reduction workgroups in the shared pool against
+    # the same n on n CUs reserved for them.
+    n_static = max(1, min(args.static_cus, cus - 8))
+    cfg_static = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, task_slabs=ov_slabs,
+                                   reducer_cus=n_static))
     stream = torch.cuda.Stream(dev)
 
     def call(b, c=cfg, rank=w.rank, peers=pd):
@@ -318,6 +325,10 @@ def main() -> int:
                                    push_outgoing=1))
     pu_s = timed_graph(lambda: call(ov_budget, cfg_push_s), args.steps, args.warmup)
     pu_f = timed_graph(lambda: call(ov_budget, cfg_push_f), args.steps, args.warmup)
+    log(f"CU policy at {n_static} reduction workgroups, two streams: shared pool, then "
+        f"{n_static} CUs reserved for the reduction: same protocol")
+    cp_sh = timed_graph(lambda: call(n_static, cfg_streams), args.steps, args.warmup)
+    cp_st = timed_graph(lambda: call(n_static, cfg_static), args.steps, args.warmup)
 
     # Every rank's step under symmetric peer readiness (each peer's tile counts
     # as ready once this GPU has produced the block at the position where the
@@ -405,6 +416,8 @@ def main() -> int:
     tr_step = traced(lambda: call(budget))
     tr_streams = traced(lambda: call(ov_budget, cfg_streams))
     tr_fused = traced(lambda: call(ov_budget, cfg_fused))
+    tr_cp_sh = traced(lambda: call(n_static, cfg_streams))
+    tr_cp_st = traced(lambda: call(n_static, cfg_static))
 
     flops = float(w.flops)
     red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
@@ -448,6 +461,11 @@ def main() -> int:
                        # the sender's side of a push-based transfer: every
                        # peer-bound tile also copied, (M - M/P) * N * 2 * 2 bytes more
                        "push_outgoing": {"streams": lat(pu_s), "fused": lat(pu_f)}},
+        # Sec. 5.3.3: shared pool against static CU partitioning, same budget
+        "cu_policy": {"reduction_workgroups": n_static, "task_slabs": ov_slabs,
+                      "shared_pool": lat(cp_sh), "static": lat(cp_st),
+                      "shared_speedup_vs_static": cp_st["ms_per_step"] / cp_sh["ms_per_step"],
+                      "trace": {"shared_pool": tr_cp_sh, "static": tr_cp_st}},
         "layer_chain": {"step": lat(ch), "sequential": lat(ch_sq),
                         "speedup_vs_sequential": ch_sq["ms_per_step"] / ch["ms_per_step"],
                         # beyond the plain step: the residual read and the norm's

@@ -205,12 +205,19 @@ typedef struct entwine_config {
                               partials (reduction) as they were: for timing only. */
   int32_t schedule;        /* ENTWINE_SCHEDULE_*; FUSED is built for the variant-0 pipelines
                               of every block shape and variants 3 and 4 of 256x256 */
-  int32_t reducer_cus;     /* static CU partitioning (Sec. 5.3.3): 0 = shared pool, the only
-                              mode built (both kernels may use every CU).  n in [1, CUs) asks
-                              for the reduction on n CUs and the GEMM on the others through
-                              CU-masked streams, which the HIP runtime on MI355X did not
-                              support reliably: ENTWINE_ERR_UNSUPPORTED (n >= CUs:
-                              ENTWINE_ERR_INVALID_ARGUMENT) for overlapped calls */
+  int32_t reducer_cus;     /* static CU partitioning (Sec. 5.3.3).  0: shared pool (both
+                              kernels may use every CU).  n in [1, CUs): the reduction's n
+                              workgroups run on n CUs of their own and the GEMM's CUs - n
+                              persistent workgroups on the others, one workgroup per CU.
+                              The split is made by LDS reservations (each workgroup reserves
+                              more than half a CU's LDS, and a GEMM and a reduction
+                              workgroup more than all of it), not by CU masks; it is exact
+                              per XCD when n is a multiple of 8.  Overlapped calls only, and
+                              the two-stream schedule only: comm_budget must equal n (AUTO
+                              picks n and the two-stream schedule); FUSED ->
+                              ENTWINE_ERR_UNSUPPORTED; n >= CUs or comm_budget != n ->
+                              ENTWINE_ERR_INVALID_ARGUMENT.  The sequential schedule ignores
+                              it.  Output is bit-identical to the shared pool's. */
   int32_t push_outgoing;   /* 0: pull only (the method); 1: the reduction workgroups also push
                               every peer-bound tile, once its flag is set, from the outgoing
                               partials into a staging buffer (entwine_staging), in production

@@ -49,6 +49,13 @@ def test_full_size_sampled_parity(w):
                   f"schedule {sched}", flush=True)
             got = case.run(tog.ORDER_AUTO, budget, schedule=sched, task_slabs=sl)
             assert torch.equal(bits(got), bits(seq))
+    # Static CU partitioning as the benchmark's static leg runs it (32 reserved
+    # CUs, four slabs), and with a quarter of the CUs reserved.
+    for n in (32, 64):
+        print(f"workload {w.name}: static partition, {n} reduction CUs", flush=True)
+        got = case.run(tog.ORDER_AUTO, n, schedule=tog.SCHEDULE_STREAMS, task_slabs=slabs,
+                       reducer_cus=n)
+        assert torch.equal(bits(got), bits(seq))
     got = down(out)
     worst = 0.0
     for r in sample_rows(w.rows):

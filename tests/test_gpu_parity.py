@@ -223,20 +223,41 @@ def test_fused_many_rounds_bit_identical(dev):
         assert err_ratio(got[r:r + 1], ref) <= 1.0
 
 
-def test_static_cu_partitioning_is_reported_unsupported(dev):
-    """CU-masked streams with partial masks failed or crashed inside the HIP
-    runtime on MI355X, so an overlapped call asking for them is refused before
+def test_static_cu_partitioning(dev):
+    """Static CU partitioning (Sec. 5.3.3): the reduction on n CUs of its own,
+    the GEMM on the rest.  Same tasks and the same fp32 sum order as the shared
+    pool, so the output is bit-identical for any n, order, readiness mode and
+    slab count; the fused schedule and a budget other than n are refused before
     anything is enqueued, and the workspace stays usable."""
     w = SMALL[1]
     case, ref = case_for(w, dev)
     blk = dict(block_m=128, block_n=128)
-    base = down(case.run(tog.ORDER_INTERLEAVED, 4, **blk))
-    for sched in SCHEDULES:
-        with pytest.raises(tog.EntwineError) as e:
-            case.run(tog.ORDER_INTERLEAVED, 8, reducer_cus=16, schedule=sched, **blk)
-        assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+    base = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
+    assert err_ratio(base, ref) <= 1.0
+    cus = tog.entwine_device_cus()
+    for n, order, slabs, mode in ((8, tog.ORDER_INTERLEAVED, 1, tog.PEERS_PRESEEDED),
+                                  (16, tog.ORDER_PARTITION_MAJOR, 2, tog.PEERS_SYMMETRIC),
+                                  (3, tog.ORDER_ROW_MAJOR, 4, tog.PEERS_PRESEEDED),
+                                  (cus - 8, tog.ORDER_COL_MAJOR, 1, tog.PEERS_SYMMETRIC)):
+        print(f"static partition: {n} reduction CUs, order {order}, {slabs} slab(s), "
+              f"readiness {mode}", flush=True)
+        out = down(case.run(order, n, reducer_cus=n, task_slabs=slabs, peer_ready=mode, **blk))
+        np.testing.assert_array_equal(out, base)
+    # AUTO budget and schedule follow reducer_cus
+    np.testing.assert_array_equal(
+        down(case.run(tog.ORDER_INTERLEAVED, tog.BUDGET_AUTO, reducer_cus=24, **blk)), base)
+    # 256x256 blocks: the pipeline's own LDS already exceeds half of the CU's
+    big = dict(block_m=256, block_n=256)
+    np.testing.assert_array_equal(
+        down(case.run(tog.ORDER_INTERLEAVED, 32, reducer_cus=32, task_slabs=4, **big)), base)
     with pytest.raises(tog.EntwineError) as e:
-        case.run(tog.ORDER_INTERLEAVED, 8, reducer_cus=tog.entwine_device_cus(), **blk)
+        case.run(tog.ORDER_INTERLEAVED, 8, reducer_cus=8, schedule=tog.SCHEDULE_FUSED, **blk)
+    assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, 8, reducer_cus=16, **blk)
+    assert e.value.status == tog.ENTWINE_ERR_INVALID_ARGUMENT
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, 8, reducer_cus=cus, **blk)
     assert e.value.status == tog.ENTWINE_ERR_INVALID_ARGUMENT
     # the sequential schedule has no second kernel to place and ignores it
     np.testing.assert_array_equal(down(case.run(tog.ORDER_INTERLEAVED, 0, reducer_cus=16, **blk)),

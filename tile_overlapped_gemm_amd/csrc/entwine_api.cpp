@@ -77,6 +77,8 @@ struct TimingPair {
 struct Workspace {
   int device = -1;
   int cus = 0;
+  int lds_per_cu = 0;     // LDS bytes of one CU
+  int lds_per_block = 0;  // the most one workgroup may reserve
   int wall_khz = 100000;
   hipStream_t s_red = nullptr;  // the overlapped schedule's reducer
   // ev_gemm / ev_red: the last eager call's GEMM and last reduction kernel.
@@ -178,6 +180,9 @@ int get_workspace(Workspace** out) {
   auto w = std::make_unique<Workspace>();
   w->device = dev;
   HIP_TRY(hipDeviceGetAttribute(&w->cus, hipDeviceAttributeMultiprocessorCount, dev));
+  HIP_TRY(hipDeviceGetAttribute(&w->lds_per_cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor,
+                                dev));
+  HIP_TRY(hipDeviceGetAttribute(&w->lds_per_block, hipDeviceAttributeMaxSharedMemoryPerBlock, dev));
   int khz = 0;
   if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) == hipSuccess && khz > 0)
     w->wall_khz = khz;
@@ -341,15 +346,19 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->threads = c.reducer_threads ? c.reducer_threads : (te ? te->threads : 256);
   r->order = tile_order != ENTWINE_ORDER_AUTO ? tile_order
                                               : (te ? te->order : ENTWINE_ORDER_INTERLEAVED);
-  r->budget = comm_budget != ENTWINE_BUDGET_AUTO ? comm_budget : (te ? te->budget : 32);
+  // With reducer_cus set, AUTO means one reduction workgroup per reserved CU
+  // on two streams (static CU partitioning).
+  r->budget = comm_budget != ENTWINE_BUDGET_AUTO ? comm_budget
+              : c.reducer_cus > 0                ? c.reducer_cus
+                                                 : (te ? te->budget : 32);
   r->peer_f32 = c.peer_dtype == ENTWINE_F32;
   r->out_f32 = c.out_dtype == ENTWINE_F32;
   r->peer_ready = c.peer_ready;
   r->release_group = c.release_group;
   r->slabs = c.task_slabs ? c.task_slabs : (te ? te->slabs : 1);
-  r->schedule = c.schedule != ENTWINE_SCHEDULE_AUTO
-                    ? c.schedule
-                    : (te && te->schedule ? te->schedule : ENTWINE_SCHEDULE_STREAMS);
+  r->schedule = c.schedule != ENTWINE_SCHEDULE_AUTO ? c.schedule
+                : c.reducer_cus > 0 ? ENTWINE_SCHEDULE_STREAMS
+                                    : (te && te->schedule ? te->schedule : ENTWINE_SCHEDULE_STREAMS);
   r->publish_all = c.publish_all;
   r->stages = c.stages;
   r->linear_dispatch = c.linear_dispatch;
@@ -480,17 +489,38 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
                   "GEMM variant %d", g.bm, g.bn, rs.variant);
   }
-  if (rs.reducer_cus > 0 && !sequential && rs.stages == ENTWINE_STAGES_ALL) {
+  // Static CU partitioning (Sec. 5.3.3): the reduction's x workgroups on x
+  // CUs of their own, the GEMM's persistent workgroups on the other CUs.
+  // CU-masked streams would say this directly, but partial masks failed or
+  // crashed inside the HIP runtime on MI355X; LDS reservations say it instead.
+  // Every workgroup of either kernel reserves more than half of a CU's LDS,
+  // and a GEMM and a reduction workgroup together more than all of it, so no
+  // CU ever holds two of them: the CUs - x GEMM workgroups and the x reduction
+  // workgroups take CUs - x and x distinct CUs (exactly x per XCD group when
+  // x is a multiple of the 8 XCDs).  Nothing waits on a workgroup that is not
+  // resident: the GEMM's workgroups never wait for the reduction, and a
+  // workgroup left undispatched runs once one ahead of it ends.
+  const bool static_cus = rs.reducer_cus > 0 && !sequential && rs.stages == ENTWINE_STAGES_ALL;
+  int lds_gemm = 0, lds_red = 0;
+  if (static_cus) {
     if (rs.reducer_cus >= w->cus)
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "reducer_cus %d must stay below the device's "
                   "%d compute units", rs.reducer_cus, w->cus);
-    // Static partitioning needs streams whose CU masks enable part of the
-    // device; creating such streams failed or crashed inside the HIP runtime
-    // on MI355X, so this build does not attempt it.
-    return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning (reducer_cus > 0) is not "
-                "available in this build: partial CU masks are not supported by the runtime");
+    if (fused)
+      return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning (reducer_cus > 0) is built "
+                  "for the two-stream schedule; the fused kernel's workgroups do both tasks");
+    if (rs.budget != rs.reducer_cus)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "comm_budget %d must equal reducer_cus %d: one "
+                  "reduction workgroup per reserved CU", rs.budget, rs.reducer_cus);
+    const int half = w->lds_per_cu / 2 + 1024;
+    lds_gemm = std::max(gemm_lds_bytes(g.bm, g.bn, rs.variant), half);
+    lds_red = std::max(half, w->lds_per_cu - lds_gemm + 1024);
+    if (w->lds_per_cu <= 0 || lds_gemm > w->lds_per_block || lds_red > w->lds_per_block)
+      return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning needs LDS reservations of "
+                  "%d and %d bytes; a workgroup may reserve %d of the CU's %d", lds_gemm,
+                  lds_red, w->lds_per_block, w->lds_per_cu);
   }
-  if (!sequential && !fused && rs.stages == ENTWINE_STAGES_ALL) {
+  if (!sequential && !fused && !static_cus && rs.stages == ENTWINE_STAGES_ALL) {
     // The reduction workgroups wait for GEMM blocks, so a CU holding one
     // must still fit a GEMM block: otherwise reduction workgroups spread
     // over the device could starve the GEMM until the watchdog fires.
@@ -771,9 +801,12 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     // reducers finished their blocks last).
     hipError_t e;
     if (forked) {
-      const int per_cu = std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1);
-      const int64_t gemm_grid = std::min<int64_t>((int64_t)per_cu * w->cus, g.NB);
-      e = launch_gemm_tickets(ga, g.bm, g.bn, (int)gemm_grid, stream);
+      // Static partitioning: one workgroup on each CU not reserved for the
+      // reduction.
+      const int per_cu = static_cus ? 1 : std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1);
+      const int gemm_cus = static_cus ? w->cus - rs.reducer_cus : w->cus;
+      const int64_t gemm_grid = std::min<int64_t>((int64_t)per_cu * gemm_cus, g.NB);
+      e = launch_gemm_tickets(ga, g.bm, g.bn, (int)gemm_grid, stream, lds_gemm);
     } else {
       e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, stream);
     }
@@ -785,7 +818,8 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   if (g_timing) HIP_TRY(hipEventRecord(tp.r0, s_red));
   if (run_red) {
     hipError_t e =
-        launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, sequential, grid, s_red);
+        launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, sequential, grid, s_red,
+                           lds_red);
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
     // The chain's normalization needs whole rows: after the reduction.

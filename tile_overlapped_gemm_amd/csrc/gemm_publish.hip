@@ -119,17 +119,21 @@ hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
   return hipGetLastError();
 }
 
+// lds_min: LDS bytes each workgroup reserves at least (the pipeline uses the
+// first S::kLds of them); a reservation above half of a CU's LDS keeps every
+// workgroup alone on its CU.
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
-hipError_t launch_tickets(const GemmArgs& a, int grid, hipStream_t s) {
+hipError_t launch_tickets(const GemmArgs& a, int grid, int lds_min, hipStream_t s) {
   using S = Shape<BM, BN, BK, NS, WGM, WGN>;
-  static bool attr_set = false;
-  if (!attr_set) {
+  const int lds = lds_min > S::kLds ? lds_min : S::kLds;
+  static int attr_bytes = 0;
+  if (lds > attr_bytes) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds);
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    attr_set = true;
+    attr_bytes = lds;
   }
-  gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<grid, S::kThreads, S::kLds, s>>>(a);
+  gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<grid, S::kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
@@ -203,11 +207,19 @@ struct Launch {
 struct LaunchTickets {
   const GemmArgs& a;
   int grid;
+  int lds_min;
   hipStream_t s;
   template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
   hipError_t run() {
     if constexpr (BM == 0) return hipErrorInvalidValue;
-    else return launch_tickets<BM, BN, BK, NS, WGM, WGN, PP>(a, grid, s);
+    else return launch_tickets<BM, BN, BK, NS, WGM, WGN, PP>(a, grid, lds_min, s);
+  }
+};
+struct LdsBytes {
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  int run() {
+    if constexpr (BM == 0) return 0;
+    else return Shape<BM, BN, BK, NS, WGM, WGN>::kLds;
   }
 };
 struct Occupancy {
@@ -249,8 +261,13 @@ hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks
   return with_instance(bm, bn, a.variant, Launch{a, num_blocks, stream});
 }
 
-hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream) {
-  return with_instance(bm, bn, a.variant, LaunchTickets{a, grid, stream});
+int gemm_lds_bytes(int bm, int bn, int variant) {
+  return with_instance(bm, bn, variant, LdsBytes{});
+}
+
+hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream,
+                               int lds_min) {
+  return with_instance(bm, bn, a.variant, LaunchTickets{a, grid, lds_min, stream});
 }
 
 }  // namespace entwine

@@ -142,19 +142,26 @@ hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks
 // The same GEMM as `grid` persistent workgroups that take blocks from the
 // per-XCD tickets until all a.nb are taken (the two-stream schedule): a CU
 // that also hosts a reduction workgroup then takes fewer blocks.  The last
-// workgroup to finish resets the tickets.
-hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream);
+// workgroup to finish resets the tickets.  Each workgroup reserves at least
+// lds_min bytes of LDS (static CU partitioning: more than half of a CU's LDS
+// keeps it alone on its CU).
+hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream,
+                               int lds_min = 0);
 
 // peer / out dtype: 0 = bf16, 1 = fp32.  threads in {128, 256, 512}.  flat:
 // reduce the whole partition without flags (after the GEMM has finished).
+// lds_bytes: LDS each workgroup reserves without using it (static CU
+// partitioning keeps a reduction workgroup off the GEMM's CUs this way).
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
-                              bool flat, int grid, hipStream_t stream);
+                              bool flat, int grid, hipStream_t stream, int lds_bytes = 0);
 
 // Registers per lane (VGPRs + AGPRs) of the kernels a launch would use, for
 // the co-residency check; 0 if unknown.
 int gemm_registers(int bm, int bn, int variant, bool tickets = false);
 // GEMM workgroups of a block shape resident per CU at once (0 if unknown).
 int gemm_blocks_per_cu(int bm, int bn, int variant);
+// LDS bytes a GEMM workgroup's pipeline uses.
+int gemm_lds_bytes(int bm, int bn, int variant);
 // Waves per GEMM workgroup (64 lanes each).
 int gemm_waves(int bm, int bn, int variant);
 int reduce_registers(int threads, int peer_f32, int out_f32);

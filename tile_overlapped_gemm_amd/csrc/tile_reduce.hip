@@ -93,26 +93,32 @@ __global__ __launch_bounds__(THREADS) void flat_reduce_kernel(ReduceArgs a) {
   }
 }
 
+// lds: dynamic LDS each tile-reduction workgroup reserves and never touches
+// (0 unless the reduction is confined to CUs of its own).
 template <int THREADS, bool PEER_F32, bool OUT_F32>
-void launch_typed(const ReduceArgs& a, bool flat, int grid, hipStream_t s) {
-  if (flat)
+hipError_t launch_typed(const ReduceArgs& a, bool flat, int grid, int lds, hipStream_t s) {
+  if (flat) {
     flat_reduce_kernel<THREADS, PEER_F32, OUT_F32><<<grid, THREADS, 0, s>>>(a);
-  else
-    tile_reduce_kernel<THREADS, PEER_F32, OUT_F32><<<grid, THREADS, 0, s>>>(a);
+    return hipGetLastError();
+  }
+  static int attr_bytes = 0;
+  if (lds > attr_bytes) {
+    hipError_t e = hipFuncSetAttribute((const void*)tile_reduce_kernel<THREADS, PEER_F32, OUT_F32>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    attr_bytes = lds;
+  }
+  tile_reduce_kernel<THREADS, PEER_F32, OUT_F32><<<grid, THREADS, lds, s>>>(a);
+  return hipGetLastError();
 }
 
 template <int THREADS>
 hipError_t launch_threads(const ReduceArgs& a, int peer_f32, int out_f32, bool flat, int grid,
-                          hipStream_t s) {
-  if (!peer_f32 && !out_f32)
-    launch_typed<THREADS, false, false>(a, flat, grid, s);
-  else if (!peer_f32 && out_f32)
-    launch_typed<THREADS, false, true>(a, flat, grid, s);
-  else if (peer_f32 && !out_f32)
-    launch_typed<THREADS, true, false>(a, flat, grid, s);
-  else
-    launch_typed<THREADS, true, true>(a, flat, grid, s);
-  return hipGetLastError();
+                          int lds, hipStream_t s) {
+  if (!peer_f32 && !out_f32) return launch_typed<THREADS, false, false>(a, flat, grid, lds, s);
+  if (!peer_f32 && out_f32) return launch_typed<THREADS, false, true>(a, flat, grid, lds, s);
+  if (peer_f32 && !out_f32) return launch_typed<THREADS, true, false>(a, flat, grid, lds, s);
+  return launch_typed<THREADS, true, true>(a, flat, grid, lds, s);
 }
 
 template <int THREADS, bool PEER_F32, bool OUT_F32>
@@ -160,11 +166,11 @@ hipError_t launch_trace_reset(uint64_t* trace, int64_t words, hipStream_t stream
 }
 
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
-                              bool flat, int grid, hipStream_t stream) {
+                              bool flat, int grid, hipStream_t stream, int lds_bytes) {
   switch (threads) {
-    case 128: return launch_threads<128>(a, peer_f32, out_f32, flat, grid, stream);
-    case 256: return launch_threads<256>(a, peer_f32, out_f32, flat, grid, stream);
-    case 512: return launch_threads<512>(a, peer_f32, out_f32, flat, grid, stream);
+    case 128: return launch_threads<128>(a, peer_f32, out_f32, flat, grid, lds_bytes, stream);
+    case 256: return launch_threads<256>(a, peer_f32, out_f32, flat, grid, lds_bytes, stream);
+    case 512: return launch_threads<512>(a, peer_f32, out_f32, flat, grid, lds_bytes, stream);
     default: return hipErrorInvalidValue;
   }
 }
