@@ -135,6 +135,9 @@ def main() -> int:
                     help="overlapped schedule: two streams, one fused kernel, or the tuning table's")
     ap.add_argument("--static-cus", type=int, default=32,
                     help="CUs reserved for the reduction in the CU-policy leg (Sec. 5.3.3)")
+    ap.add_argument("--reducer-cus", type=int, default=0,
+                    help="with --profile: reserve this many CUs for the reduction (two streams; "
+                         "--budget must match)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--profile", action="store_true",
@@ -250,8 +253,10 @@ def main() -> int:
                             cfg=cfg, stream=stream)
 
     if args.profile:
+        pc = (tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS,
+                                reducer_cus=args.reducer_cus)) if args.reducer_cus else cfg)
         for _ in range(args.warmup + args.steps):
-            (chain if args.chain else call)(budget)
+            chain(budget) if args.chain else call(budget, pc)
         stream.synchronize()
         check_status("in the profiled calls")
         log(f"profiled {args.warmup + args.steps} calls: {kind}, block {bm}x{bn}, order {order}, "
