@@ -231,8 +231,10 @@ def main() -> int:
     # CU policy (Sec. 5.3.3): n reduction workgroups in the shared pool against
     # the same n on n CUs reserved for them.
     n_static = max(1, min(args.static_cus, cus - 8))
+    # Each policy with its own reduction workgroup size: the shared pool's must
+    # fit beside a GEMM block; a reserved CU takes the library's choice (512).
     cfg_static = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, task_slabs=ov_slabs,
-                                   reducer_cus=n_static))
+                                   reducer_cus=n_static, reducer_threads=0))
     stream = torch.cuda.Stream(dev)
 
     def call(b, c=cfg, rank=w.rank, peers=pd):
@@ -254,7 +256,8 @@ def main() -> int:
 
     if args.profile:
         pc = (tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS,
-                                reducer_cus=args.reducer_cus)) if args.reducer_cus else cfg)
+                                reducer_cus=args.reducer_cus,
+                                reducer_threads=args.threads)) if args.reducer_cus else cfg)
         for _ in range(args.warmup + args.steps):
             chain(budget) if args.chain else call(budget, pc)
         stream.synchronize()
@@ -468,6 +471,7 @@ def main() -> int:
                        "push_outgoing": {"streams": lat(pu_s), "fused": lat(pu_f)}},
         # Sec. 5.3.3: shared pool against static CU partitioning, same budget
         "cu_policy": {"reduction_workgroups": n_static, "task_slabs": ov_slabs,
+                      "threads": {"shared_pool": threads, "static": 512},
                       "shared_pool": lat(cp_sh), "static": lat(cp_st),
                       "shared_speedup_vs_static": cp_st["ms_per_step"] / cp_sh["ms_per_step"],
                       "trace": {"shared_pool": tr_cp_sh, "static": tr_cp_st}},

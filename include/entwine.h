@@ -214,7 +214,8 @@ typedef struct entwine_config {
                               workgroup more than all of it), not by CU masks; it is exact
                               per XCD when n is a multiple of 8.  Overlapped calls only, and
                               the two-stream schedule only: comm_budget must equal n (AUTO
-                              picks n and the two-stream schedule); FUSED ->
+                              picks n and the two-stream schedule, and reducer_threads 0
+                              picks 512, as a reserved CU holds nothing else); FUSED ->
                               ENTWINE_ERR_UNSUPPORTED; n >= CUs or comm_budget != n ->
                               ENTWINE_ERR_INVALID_ARGUMENT.  The sequential schedule ignores
                               it.  Output is bit-identical to the shared pool's. */

@@ -235,13 +235,15 @@ def test_static_cu_partitioning(dev):
     base = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
     assert err_ratio(base, ref) <= 1.0
     cus = tog.entwine_device_cus()
-    for n, order, slabs, mode in ((8, tog.ORDER_INTERLEAVED, 1, tog.PEERS_PRESEEDED),
-                                  (16, tog.ORDER_PARTITION_MAJOR, 2, tog.PEERS_SYMMETRIC),
-                                  (3, tog.ORDER_ROW_MAJOR, 4, tog.PEERS_PRESEEDED),
-                                  (cus - 8, tog.ORDER_COL_MAJOR, 1, tog.PEERS_SYMMETRIC)):
+    # reducer_threads 0 picks 512-thread workgroups for the static split
+    for n, order, slabs, mode, th in ((8, tog.ORDER_INTERLEAVED, 1, tog.PEERS_PRESEEDED, 0),
+                                      (16, tog.ORDER_PARTITION_MAJOR, 2, tog.PEERS_SYMMETRIC, 0),
+                                      (3, tog.ORDER_ROW_MAJOR, 4, tog.PEERS_PRESEEDED, 256),
+                                      (cus - 8, tog.ORDER_COL_MAJOR, 1, tog.PEERS_SYMMETRIC, 128)):
         print(f"static partition: {n} reduction CUs, order {order}, {slabs} slab(s), "
-              f"readiness {mode}", flush=True)
-        out = down(case.run(order, n, reducer_cus=n, task_slabs=slabs, peer_ready=mode, **blk))
+              f"readiness {mode}, threads {th}", flush=True)
+        out = down(case.run(order, n, reducer_cus=n, task_slabs=slabs, peer_ready=mode,
+                            reducer_threads=th, **blk))
         np.testing.assert_array_equal(out, base)
     # AUTO budget and schedule follow reducer_cus
     np.testing.assert_array_equal(

@@ -343,7 +343,11 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   r->bn = c.block_n ? c.block_n : (te ? te->bn : (N % 256 == 0 ? 256 : 128));
   r->tm = c.tile_m ? c.tile_m : 128;
   r->tn = c.tile_n ? c.tile_n : 128;
-  r->threads = c.reducer_threads ? c.reducer_threads : (te ? te->threads : 256);
+  // A reserved CU holds one reduction workgroup and nothing else, so the
+  // static split takes the largest one (more loads in flight per CU).
+  r->threads = c.reducer_threads ? c.reducer_threads
+               : c.reducer_cus > 0 ? 512
+                                   : (te ? te->threads : 256);
   r->order = tile_order != ENTWINE_ORDER_AUTO ? tile_order
                                               : (te ? te->order : ENTWINE_ORDER_INTERLEAVED);
   // With reducer_cus set, AUTO means one reduction workgroup per reserved CU
