@@ -248,6 +248,18 @@ def test_static_cu_partitioning(dev):
     # AUTO budget and schedule follow reducer_cus
     np.testing.assert_array_equal(
         down(case.run(tog.ORDER_INTERLEAVED, tog.BUDGET_AUTO, reducer_cus=24, **blk)), base)
+    # with the push of every peer-bound tile, and with a release group
+    np.testing.assert_array_equal(
+        down(case.run(tog.ORDER_INTERLEAVED, 16, reducer_cus=16, push_outgoing=1, **blk)), base)
+    np.testing.assert_array_equal(
+        down(case.run(tog.ORDER_INTERLEAVED, 16, reducer_cus=16, task_slabs=2,
+                      release_group=tog.RELEASE_PARTITION, **blk)), base)
+    # fp32 peers and output, 64 x 64 tiles
+    tiny, tiny_ref = case_for(SMALL[3], dev)
+    tiny_seq = down(tiny.run(tog.ORDER_INTERLEAVED, 0))
+    assert err_ratio(tiny_seq, tiny_ref) <= 1.0
+    np.testing.assert_array_equal(down(tiny.run(tog.ORDER_INTERLEAVED, 8, reducer_cus=8)),
+                                  tiny_seq)
     # 256x256 blocks: the pipeline's own LDS already exceeds half of the CU's
     big = dict(block_m=256, block_n=256)
     np.testing.assert_array_equal(
