@@ -401,8 +401,9 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   // sub-block is staged through the wave's own LDS area (rows padded by 16
   // bytes so the transposed writes spread over the banks) and read back
   // row-contiguous, so every global store instruction covers whole 128-byte
-  // lines: 16-byte fp32 stores for the local partition, 8-byte bf16 (or
-  // 16-byte fp32) stores for the outgoing contributions.
+  // lines: 16-byte fp32 stores for the local partition, 16-byte bf16 (8
+  // columns; 8-byte where a wave's 96 columns do not split so) or 16-byte
+  // fp32 stores for the outgoing contributions.
   //
   // Tiles that are released to a consumer are written with device-coherent
   // stores (cache policy SC1, the encoding of a relaxed agent-scope atomic
@@ -426,6 +427,15 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   const int csub = (lane % kLanesPerRow) * 4;
   const int col = col0 + wn * S::kWN + csub;
   const bool col_ok = col < a.N && lane < kRowsPerStore * kLanesPerRow;
+  // The 8-column form for bf16 rows, where whole rows split over the lanes
+  // (N is a multiple of 8, so a lane's 8 columns are all in or all out).
+  constexpr int kLanes16 = S::kWN / 8;
+  constexpr int kRows16 = 64 / kLanes16;
+  constexpr bool kWide16 = 64 % kLanes16 == 0 && 32 % kRows16 == 0;
+  const int rsub16 = lane / kLanes16;
+  const int csub16 = (lane % kLanes16) * 8;
+  const int col16 = col0 + wn * S::kWN + csub16;
+  const bool col16_ok = col16 < a.N;
   const bool coherent = local ? a.publish != 0 : a.publish == 2;
   const int strip_bytes = 32 * a.N * (local || a.outgoing_f32 ? 4 : 2);
 #pragma unroll
@@ -450,6 +460,37 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
     const int64_t og_row = (int64_t)d * a.R + srow;
     float* const og32_strip = static_cast<float*>(a.outgoing) + og_row * a.N;
     __bf16* const og16_strip = static_cast<__bf16*>(a.outgoing) + og_row * a.N;
+    bool stored = false;
+    if constexpr (kWide16) {
+      if (!local && !a.outgoing_f32) {
+        // bf16 contributions: 8 columns (one 16-byte store) per lane, half
+        // the store instructions of the 4-column form below.
+#pragma unroll
+        for (int q = 0; q < 32 / kRows16; ++q) {
+          const int r = q * kRows16 + rsub16;
+          const char* src = wbuf + r * kPitch + csub16 * 4;
+          const f32x4 v0 = *reinterpret_cast<const f32x4*>(src);
+          const f32x4 v1 = *reinterpret_cast<const f32x4*>(src + 16);
+          if (srow + r >= a.R || !col16_ok) continue;
+          const int e = r * a.N + col16;
+          bf16x8 h;
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            h[k] = static_cast<__bf16>(v0[k]);
+            h[4 + k] = static_cast<__bf16>(v1[k]);
+          }
+          if (coherent)
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, h),
+                                                   rsrc_of(og16_strip, strip_bytes), e * 2, 0,
+                                                   kCoherent);
+          else
+            __builtin_nontemporal_store(__builtin_bit_cast(u32x4, h),
+                                        reinterpret_cast<u32x4*>(og16_strip + e));
+        }
+        stored = true;
+      }
+    }
+    if (!stored) {
 #pragma unroll
     for (int q = 0; q < 32 / kRowsPerStore; ++q) {
       const int r = q * kRowsPerStore + rsub;
@@ -477,6 +518,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
           __builtin_nontemporal_store(__builtin_bit_cast(u32x2, h),
                                       reinterpret_cast<u32x2*>(og16_strip + e));
       }
+    }
     }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // strip read back before the next overwrites it
     __builtin_amdgcn_wave_barrier();
