@@ -179,7 +179,8 @@ typedef struct entwine_config {
                               block_m 128 (one round of blocks for short partitions) */
   int32_t tile_m;          /* reduction tile rows TM: 0 = 128, else 64 or 128; BM % TM == 0 */
   int32_t tile_n;          /* reduction tile cols TN: 0 = 128, else 64 or 128; BN % TN == 0 */
-  int32_t reducer_threads; /* b: 0 = 256, else 128, 256 or 512 (Sec. 4.3) */
+  int32_t reducer_threads; /* b: 128, 256 or 512 (Sec. 4.3); 0 = the tuning table's entry,
+                              else 256, and 512 under static CU partitioning (reducer_cus) */
   int32_t w_layout;        /* ENTWINE_W_NK */
   int32_t peer_dtype;      /* ENTWINE_BF16 or ENTWINE_F32: peers and outgoing contributions */
   int32_t out_dtype;       /* ENTWINE_BF16 or ENTWINE_F32 */
