@@ -276,27 +276,36 @@ def main() -> int:
         return g
 
     def timed_graph(body, steps, warmup, per_step=True):
-        """Per-replay and total device time of graph replays of `body`."""
+        """Device time of `steps` back-to-back graph replays of `body`, bracketed
+        by two events (ms_per_step), and, in a second pass with an event after
+        every replay, the per-replay spread.  An event between two replays
+        serializes them and added about 5 µs per mlp step, so the per-replay
+        figures run above ms_per_step."""
         g = graph_of(body)
         with torch.cuda.stream(stream):
             for _ in range(warmup):
                 g.replay()
         stream.synchronize()
         check_status("after warm-up")
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1 if per_step else 2)]
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
-            evs[0].record(stream)
-            for i in range(steps):
+            e0.record(stream)
+            for _ in range(steps):
                 g.replay()
-                if per_step:
-                    evs[i + 1].record(stream)
-            evs[-1].record(stream)
+            e1.record(stream)
         torch.cuda.synchronize()
         check_status("in the timed region")
-        total = evs[0].elapsed_time(evs[-1])
-        res = dict(ms_per_step=total / steps)
+        res = dict(ms_per_step=e0.elapsed_time(e1) / steps)
         if per_step:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            with torch.cuda.stream(stream):
+                evs[0].record(stream)
+                for i in range(steps):
+                    g.replay()
+                    evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            check_status("in the per-replay pass")
             per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
             res.update(median_ms=statistics.median(per), p10_ms=per[len(per) // 10],
                        p90_ms=per[(9 * len(per)) // 10])
