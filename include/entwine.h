@@ -343,6 +343,14 @@ const char* entwine_last_error_message(void);
  * (peer dtype) written by the last call.  Any pointer may be NULL. */
 int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* bytes);
 
+/* Allocated sizes in bytes of the current device's own-partial, outgoing and
+ * staging buffers (for tests that overwrite the workspace between calls, e.g.
+ * with a NaN pattern, to show that no call reads data a previous call left:
+ * writes must stay within these sizes).  Synchronizes like entwine_workspace.
+ * Any pointer may be NULL; ENTWINE_ERR_INVALID_ARGUMENT before any call on the
+ * device. */
+int entwine_workspace_sizes(int64_t* own_bytes, int64_t* outgoing_bytes, int64_t* staging_bytes);
+
 /* Device pointer of the current device's staging buffer (for tests and
  * measurements): peer dtype [M][N], whose rows of partition d != rank hold
  * the copies pushed by the last call with push_outgoing = 1 (the rank's own

@@ -45,6 +45,30 @@ def down(t: torch.Tensor) -> np.ndarray:
     return t.numpy().copy()
 
 
+def poison_workspace() -> bool:
+    """Overwrite the library's own-partial, outgoing and staging buffers with
+    0xFF bytes (a NaN in fp32 and in bf16), with the device idle before and
+    after.  A call that then read any of them before its own GEMM had stored
+    and released the data would return NaN or differ from the reference, where
+    without the poison it would read the identical values the previous call
+    left behind.  Writes stay within the allocated sizes.  Returns False when
+    the device has no workspace yet (the next call allocates it)."""
+    torch.cuda.synchronize()
+    try:
+        own_p, og_p, _ = tog.entwine_workspace()
+        own_b, og_b, st_b = tog.entwine_workspace_sizes()
+    except tog.EntwineError:
+        return False
+    for p, n in ((own_p, own_b), (og_p, og_b)):
+        if p and n:
+            assert hip().hipMemset(p, 0xFF, n) == 0
+    if st_b:
+        st_p, _ = tog.entwine_staging()
+        assert hip().hipMemset(st_p, 0xFF, st_b) == 0
+    torch.cuda.synchronize()
+    return True
+
+
 def as_f64(a: np.ndarray) -> np.ndarray:
     return (wl.bf16_to_f32(a) if a.dtype == np.uint16 else a).astype(np.float64)
 
@@ -67,8 +91,12 @@ class Case:
         d.update(kw)
         return tog.config(**d)
 
-    def run(self, order=tog.ORDER_INTERLEAVED, budget=4, check_status=True, **kw):
+    def run(self, order=tog.ORDER_INTERLEAVED, budget=4, check_status=True, poison=True, **kw):
+        """One call into a NaN-filled output, after poisoning the workspace
+        (poison_workspace) unless poison=False."""
         out = torch.full((self.w.rows, self.w.N), float("nan"), dtype=self.out_dtype, device=self.dev)
+        if poison:
+            poison_workspace()
         tog.gemm_rs(self.Xd, self.Wd, self.pd, out, self.w.P, self.w.rank, order, budget,
                     cfg=self.base_cfg(**kw))
         if check_status:

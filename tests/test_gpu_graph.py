@@ -8,7 +8,7 @@ import torch
 
 import tile_overlapped_gemm_amd as tog
 import workloads as wl
-from gpu_util import device, down, up
+from gpu_util import device, down, poison_workspace, up
 
 pytestmark = pytest.mark.gpu
 
@@ -53,6 +53,7 @@ def test_graph_replays_match_eager(sched, push):
         print(f"replay {rep} input {k}", flush=True)
         X.copy_(srcs[k])
         out.fill_(float("nan"))
+        poison_workspace()
         g.replay()
         torch.cuda.synchronize()
         assert tog.entwine_device_status(torch.cuda.current_stream().cuda_stream) == tog.ENTWINE_OK

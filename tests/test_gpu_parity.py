@@ -200,6 +200,39 @@ def test_push_outgoing_copies_every_peer_tile(dev, w):
     assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
 
 
+def test_late_flags_do_not_leak_into_the_next_call(dev):
+    """Regression test for the epoch hand-over of the two-stream schedule.  A
+    call that releases every tile (publish_all) with preseeded peers stores
+    flags of peer-bound tiles that none of its own waits read.  Row-major
+    order at rank 0 produces the local partition in the first of two rounds
+    of blocks, so the reduction ends while the GEMM still stores those flags.
+    The epoch advances only after both kernels' workgroups have checked out,
+    so the flags carry this call's epoch.  The next call pushes every
+    peer-bound tile, and its send tasks wait on exactly those flags.  With the
+    workspace poisoned in between, its staging rows must equal the outgoing
+    partials: a send task that took an old flag for its own would copy NaN
+    bytes."""
+    w = wl.custom("late_flags", 4096, 2048, 4096, 4, rank=0, index=307)
+    X, W = wl.operands(w)
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    blk = dict(block_m=128, block_n=128)
+    seq = down(case.run(tog.ORDER_ROW_MAJOR, 0, **blk))
+    rows = np.ones(w.M, dtype=bool)
+    rows[w.rank * w.rows:(w.rank + 1) * w.rows] = False
+    for it in range(3):
+        print(f"case late_flags iteration {it}: publish_all, then push", flush=True)
+        out = down(case.run(tog.ORDER_ROW_MAJOR, 128, publish_all=1,
+                            schedule=tog.SCHEDULE_STREAMS, **blk))
+        np.testing.assert_array_equal(out, seq)
+        out = down(case.run(tog.ORDER_ROW_MAJOR, 128, push_outgoing=1,
+                            schedule=tog.SCHEDULE_STREAMS, **blk))
+        np.testing.assert_array_equal(out, seq)
+        _, outgoing = read_workspace(w.rows, w.N, w.M, w.fp32_io)
+        staging = read_staging(w.M, w.N, w.fp32_io)
+        np.testing.assert_array_equal(staging[rows], outgoing[rows])
+
+
 def test_fused_many_rounds_bit_identical(dev):
     """More GEMM blocks than resident workgroups: workgroups take several
     blocks each (and take blocks from other XCDs' lists) before reducing."""

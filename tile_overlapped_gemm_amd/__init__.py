@@ -41,7 +41,8 @@ EXPORTS = [
     "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
     "entwine_plan_task_order", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
-    "entwine_workspace", "entwine_staging", "entwine_timing", "entwine_timing_read",
+    "entwine_workspace", "entwine_workspace_sizes", "entwine_staging", "entwine_timing",
+    "entwine_timing_read",
     "entwine_trace", "entwine_trace_read", "entwine_load_tuning",
     "entwine_release", "entwine_device_cus",
 ]
@@ -118,6 +119,7 @@ def load(path: str = LIB):
         "entwine_status_string": ([i32], ctypes.c_char_p),
         "entwine_last_error_message": ([], ctypes.c_char_p),
         "entwine_workspace": ([ctypes.POINTER(vp), ctypes.POINTER(vp), pi64], i32),
+        "entwine_workspace_sizes": ([pi64, pi64, pi64], i32),
         "entwine_staging": ([ctypes.POINTER(vp), pi64], i32),
         "entwine_timing": ([i32], i32),
         "entwine_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), pi64],
@@ -206,6 +208,13 @@ def entwine_workspace():
     own, outg, nb = ctypes.c_void_p(), ctypes.c_void_p(), ctypes.c_int64()
     _check(load().entwine_workspace(ctypes.byref(own), ctypes.byref(outg), ctypes.byref(nb)))
     return own.value, outg.value, nb.value
+
+
+def entwine_workspace_sizes():
+    """(own partial, outgoing, staging) bytes allocated on the current device."""
+    a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
+    _check(load().entwine_workspace_sizes(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
+    return a.value, b.value, c.value
 
 
 def entwine_staging():

@@ -810,6 +810,9 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       const int per_cu = static_cus ? 1 : std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1);
       const int gemm_cus = static_cus ? w->cus - rs.reducer_cus : w->cus;
       const int64_t gemm_grid = std::min<int64_t>((int64_t)per_cu * gemm_cus, g.NB);
+      // Both kernels' workgroups check out on one count; the last advances
+      // the epoch, once no workgroup of the call can still store a flag.
+      ga.checkout_total = ra.checkout_total = (int32_t)(gemm_grid + grid);
       e = launch_gemm_tickets(ga, g.bm, g.bn, (int)gemm_grid, stream, lds_gemm);
     } else {
       e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, stream);
@@ -1050,6 +1053,24 @@ int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* 
   if (outgoing) *outgoing = w->outgoing;
   if (bytes)
     *bytes = (int64_t)(w->own_bytes + w->outgoing_bytes + w->staging_bytes + w->flag_count * 4);
+  return ENTWINE_OK;
+}
+
+int entwine_workspace_sizes(int64_t* own_bytes, int64_t* outgoing_bytes, int64_t* staging_bytes) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end()) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no workspace on this device yet");
+  Workspace* w = it->second.get();
+  HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (w->have_prev) {
+    HIP_TRY(hipEventSynchronize(w->ev_gemm));
+    HIP_TRY(hipEventSynchronize(w->ev_red));
+  }
+  if (own_bytes) *own_bytes = (int64_t)w->own_bytes;
+  if (outgoing_bytes) *outgoing_bytes = (int64_t)w->outgoing_bytes;
+  if (staging_bytes) *staging_bytes = (int64_t)w->staging_bytes;
   return ENTWINE_OK;
 }
 

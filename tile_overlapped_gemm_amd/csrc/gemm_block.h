@@ -524,19 +524,28 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
     __builtin_amdgcn_wave_barrier();
   }
 
-  // Publish (Sec. 4.2): all stores of the block, then the tiles' flags.  The
-  // workgroup barrier waits until every wave's stores are acknowledged (its
-  // workgroup-scope fence waits for vmcnt 0), and the released tiles' stores
-  // were device-coherent, so their data is visible device-wide before thread
-  // 0 stores the covered tiles' flags.  Flags of tiles bound for peers only
-  // mark progress; they are stored when some wait reads them (flag_all).
+  // Publish (Sec. 4.2): all stores of the block, then the tiles' flags.
+  //  1. Every wave waits until each of its own stores has been acknowledged
+  //     (vmcnt 0).  The released tiles were stored device-coherent (SC1), so
+  //     an acknowledged store is visible to a device-coherent load from any
+  //     XCD.  The wait is explicit: the workgroup barrier's own fence has
+  //     workgroup scope and does not wait for outstanding stores.
+  //  2. The workgroup barrier: no wave passes it before every wave's stores
+  //     are acknowledged.
+  //  3. Thread 0 stores the covered tiles' flags (agent scope).
+  // The release is therefore a wait for acknowledgements, not a write-back of
+  // the XCD's whole L2 (which an agent-scope release fence would issue).
+  // Flags of tiles bound for peers only mark progress; they are stored when
+  // some wait reads them (flag_all).
   if (a.publish != 0 && (local || a.flag_all)) {
+    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
     if (tid == 0) {
       const int sub_m = BM / a.tm, sub_n = BN / a.tn;
       const int vm = min(sub_m, a.Rt - br * sub_m);
       const int vn = min(sub_n, a.Ct - bc * sub_n);
-      const uint32_t epoch = a.ctl[kEpoch];
+      const uint32_t epoch = peek(a.ctl + kEpoch);
       uint32_t* f = a.flags + (int64_t)d * a.Q + t_first;
       for (int t = 0; t < vm * vn; ++t)
         __hip_atomic_store(f + t, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

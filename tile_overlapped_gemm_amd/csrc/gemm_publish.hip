@@ -9,7 +9,8 @@
 //  * Sec. 3.1 / Equation (1): the workgroup at logical position p computes the
 //    block that the order table names for p (a custom block swizzle).
 //  * Sec. 4.2: after all of a block's output stores, the block publishes the
-//    flags of every reduction tile it covers with release semantics.
+//    flags of every reduction tile it covers (stores, a CTA barrier, then
+//    thread 0's release store of the flags).
 //
 // MI355X (gfx950) design.
 //  * 512 threads = 8 waves of 64 (two per SIMD, so one wave's waits are
@@ -41,8 +42,11 @@
 //  * Epilogue: accumulators leave through LDS in 32-row strips so that the
 //    global stores write whole cache lines.
 //  * Publication: tiles read on this device are written with device-coherent
-//    (SC1) stores; the workgroup synchronizes after its stores, then thread 0
-//    stores the call's epoch into the flag of every tile the block covers.
+//    (SC1) stores; every wave waits until its stores are acknowledged
+//    (s_waitcnt vmcnt(0)), the workgroup synchronizes, then thread 0 stores
+//    the call's epoch into the flag of every tile the block covers.  This
+//    orders the data before the flag without an agent-scope release fence,
+//    which would write back the XCD's whole L2.
 //  * Two launch forms.  gemm_publish_kernel: one workgroup per block, block
 //    b of the dispatch order on workgroup b (sequential schedule, single
 //    stages).  gemm_ticket_kernel: persistent workgroups taking blocks from
@@ -73,6 +77,8 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs
   __shared__ int s_pick[2];
   const int tid = threadIdx.x;
   const int xcd = xcd_id();
+  // The call's epoch: it cannot change before this workgroup has checked out.
+  const uint32_t epoch = tid == 0 ? peek(a.ctl + kEpoch) : 0u;
   int parity = 0;
   while (true) {
     int pick = 0;
@@ -91,8 +97,10 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs
     gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(a, reinterpret_cast<const int4*>(a.blocks)[b], b,
                                              smem, ltid);
   }
-  // Check-out: the last workgroup (every other one has taken its last
-  // ticket) resets the tickets for the next call.
+  // Check-out.  The last GEMM workgroup (every other one has taken its last
+  // ticket) resets the tickets for the next call.  Then the workgroup, whose
+  // flag stores are all issued, checks out of the call together with the
+  // reduction's workgroups: the last of either advances the epoch.
   if (tid == 0) {
     const uint32_t n = __hip_atomic_fetch_add(a.ctl + kGemmDone, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
@@ -102,6 +110,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs
                            __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.ctl + kGemmDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (a.checkout_total > 0) check_out(a.ctl, epoch, (uint32_t)a.checkout_total);
   }
 }
 

@@ -1,11 +1,13 @@
 // kernels.h -- argument blocks and launchers of the two device kernels.
 //
 // gemm_publish: the producer (Sec. 4.2, Producer): one workgroup per logical
-//   block position, bf16 MFMA main loop, stores, then one release flag per
-//   covered reduction tile.
+//   block position, bf16 MFMA main loop, stores, then one ready flag per
+//   covered reduction tile, stored once every wave's stores of the block are
+//   acknowledged (see the publication step in gemm_block.h).
 // tile_reduce: the consumer (Sec. 4.2, Consumer / ReduceTile): x persistent
-//   workgroups walking tasks j, j+x, ...; acquire-wait on the tile's flags,
-//   then local + peers (rank order) in fp32, one store per output element.
+//   workgroups walking tasks j, j+x, ...; wait for the tile's flags, then read
+//   the released data with device-coherent loads and sum local + peers (rank
+//   order) in fp32, one store per output element.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -35,6 +37,9 @@ struct GemmArgs {
   uint64_t* trace;          // measurement stamps [2][NB] (see trace_at), nullptr: off
   int32_t trace_nb;         // NB: blocks of the call
   int32_t nb;               // NB, for the persistent (ticket) GEMM
+  // Workgroups of the call that check out on ctl[kCallDone] (the ticket GEMM
+  // and the reduction it runs beside): the last one advances the epoch.
+  int32_t checkout_total;
 };
 
 struct ReduceArgs {
@@ -72,17 +77,18 @@ struct ReduceArgs {
   // the wait, as a real peer's data would be (symmetric readiness).
   int32_t prefetch;
   uint64_t* trace;                  // measurement stamps [2][grid] (see trace_at), nullptr: off
+  int32_t checkout_total;           // as GemmArgs::checkout_total
 };
 
-// Epochs.  A flag is ready when it equals the call's epoch, which both
-// kernels read from ctl[kEpoch] at run time (so a captured graph replays
-// correctly).  The last reduction workgroup to finish advances the epoch
-// (skipping 0, the value of flags never written).  Every tile the reduction
-// reads was published before it finished, so the data dependencies of the
-// call are complete; a GEMM block that publishes later (a tile bound for a
-// peer, whose flag only marks progress) may write the next epoch into its
-// flags, which the next call can only read as progress markers too: the
-// tile's own flag is always a wait slot of its own.
+// Epochs.  A flag is ready when it equals the call's epoch, which every
+// kernel reads from ctl[kEpoch] at run time (so a captured graph replays
+// correctly).  The epoch advances (skipping 0, the value of flags never
+// written) only once every workgroup of the call that may store or read a
+// flag has finished: in the two-stream schedule the GEMM's and the
+// reduction's workgroups check out on one shared count (check_out), in the
+// fused schedule the fused kernel's workgroups on its own.  So every flag a
+// call stores holds that call's epoch, and a later call, whose epoch differs,
+// can never take one of them for its own.
 //
 // The fused kernel (GEMM blocks and reduction tasks taken from tickets) keeps
 // its tickets and its own check-out count in further control words; its
@@ -93,7 +99,7 @@ struct ReduceArgs {
 enum {
   kLine = 32,  // control words per 128-byte line
   kEpoch = 0,
-  kReduceDone = 1 * kLine,
+  kCallDone = 1 * kLine,     // joint check-out count of the two-stream schedule
   kFusedDone = 2 * kLine,
   kBlockTicket = 3 * kLine,  // ticket of XCD y at kBlockTicket + y * kLine
   kGemmDone = 11 * kLine,    // check-out count of the persistent (ticket) GEMM
@@ -115,13 +121,15 @@ __device__ __forceinline__ void trace_at(uint64_t* t, int64_t slot) {
   if (t) t[slot] = (uint64_t)wall_clock64();
 }
 
-// Counts this workgroup out of a grid of gridDim.x; the last one resets the
-// count and advances the epoch.
-__device__ __forceinline__ void check_out(uint32_t* ctl, uint32_t epoch) {
-  const uint32_t n = __hip_atomic_fetch_add(ctl + kReduceDone, 1u, __ATOMIC_RELAXED,
+// Counts one workgroup out of `total` (the two-stream schedule's GEMM and
+// reduction workgroups together); the last one resets the count and advances
+// the epoch.  Called by thread 0 after the workgroup's last flag store or
+// flag read.
+__device__ __forceinline__ void check_out(uint32_t* ctl, uint32_t epoch, uint32_t total) {
+  const uint32_t n = __hip_atomic_fetch_add(ctl + kCallDone, 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
-  if (n + 1 != gridDim.x) return;
-  __hip_atomic_store(ctl + kReduceDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (n + 1 != total) return;
+  __hip_atomic_store(ctl + kCallDone, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 

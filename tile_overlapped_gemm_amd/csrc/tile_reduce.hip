@@ -5,11 +5,12 @@
 //  * Sec. 3.1 "Matching task order": consumer workgroup j takes tasks j, j+x,
 //    j+2x, ... in production order and waits for each tile before reducing it.
 //  * Sec. 3.2 "Communication budget": x = the grid size, fixed for the call.
-//  * Sec. 4.2: before a tile is read, its flags (the local one and the
-//    peers') are observed with acquire semantics and the workgroup then
-//    synchronizes; each thread reduces a disjoint part of the tile, starting
-//    from the local contribution and adding the peers in rank order; each
-//    output element has exactly one writer.
+//  * Sec. 4.2: before a tile is read, thread 0 acquires its flags (the local
+//    one and the peers') and the workgroup then synchronizes; each thread
+//    reduces a disjoint part of the tile, starting from the local
+//    contribution and adding the peers in rank order; each output element
+//    has exactly one writer.  Here the acquire is replaced by
+//    device-coherent loads of the released data (below).
 //
 // MI355X mapping.
 //  * A task is one row slab of a reduction tile (slabs = 1: the whole tile),
@@ -17,12 +18,14 @@
 //    workgroups.
 //  * Wave 0 polls the task's flags in parallel, one lane per flag, with
 //    relaxed agent-scope loads and an s_sleep back-off; the other waves wait
-//    at the workgroup barrier meanwhile.  The paper's acquire becomes
-//    device-coherent (SC1) loads of the released data: an agent-scope
-//    acquire fence on this GPU invalidates the XCD's whole L2, which a GEMM
-//    sharing the XCD is still reading its operands from.  The producers'
-//    SC1 stores were acknowledged before their flags were set, and SC1 loads
-//    issued after the wait cannot hit a stale line, so they see the stores.
+//    at the workgroup barrier meanwhile.  The polls are relaxed; in place of
+//    an acquire fence (which on this GPU invalidates the XCD's whole L2, where
+//    a GEMM sharing the XCD still reads its operands), the released data is
+//    read with device-coherent (SC1) loads.  Every producer wave's SC1 stores
+//    were acknowledged before the workgroup barrier that precedes the flag
+//    store (gemm_block.h), and these loads are issued only after the wait
+//    (the loop's exit depends on the flag value, then the barrier) and
+//    cannot hit a stale cache line, so they return the stored data.
 //  * The element loop moves 8 elements per thread step: two 16-byte fp32 loads
 //    of the local partial and one 16-byte load per bf16 peer.  Two steps are
 //    loaded before any add so that 2 * (P + 1) loads per thread are in flight.
@@ -40,7 +43,7 @@ template <int THREADS, bool PEER_F32, bool OUT_F32>
 __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   __shared__ int s_abort[2];
   const int tid = threadIdx.x;
-  const uint32_t epoch = a.ctl[kEpoch];
+  const uint32_t epoch = __hip_atomic_load(a.ctl + kEpoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   int parity = 0;
   if (a.trace && tid == 0) trace_at(a.trace, blockIdx.x);
   for (int task = blockIdx.x; task < a.ntasks; task += gridDim.x, parity ^= 1) {
@@ -65,7 +68,7 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
     if (tid == 0) trace_at(a.trace, (int64_t)gridDim.x + blockIdx.x);
   }
   // Every workgroup, finished or timed out, checks out.
-  if (tid == 0 && !a.nowait) check_out(a.ctl, epoch);
+  if (tid == 0 && !a.nowait) check_out(a.ctl, epoch, (uint32_t)a.checkout_total);
 }
 
 // The sequential schedule's reduction: no flags; the partition is one flat
