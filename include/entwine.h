@@ -237,6 +237,41 @@ int entwine_gemm_rs_ex(const void* X, const void* W, const void* const* peer_par
                        const entwine_config* cfg);
 
 /*
+ * entwine_gemm_rs_noalloc -- entwine_gemm_rs_ex for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  The call allocates nothing (no hipMalloc,
+ * hipFree or allocating library routine); its control words, tile flags,
+ * schedule tables, fp32 own partial, outgoing partials and (push_outgoing)
+ * staging copies live in a fixed 256 MiB device array of the library, one copy
+ * per GPU, held from the first call on that GPU until the process ends.
+ *
+ *   Arguments, layouts, numerics and results are those of entwine_gemm_rs_ex;
+ *   the output is bit-identical to entwine_gemm_rs_ex's with the same
+ *   arguments.  Schedules: the sequential one (comm_budget 0) and the fused
+ *   one (comm_budget >= 1; AUTO resolves to it), both on `stream` alone.
+ *   Errors, besides entwine_gemm_rs_ex's (nothing is enqueued on any of them):
+ *     ENTWINE_ERR_OUT_OF_MEMORY  the call's buffers exceed the 256 MiB array
+ *                                (own partial (M/P)*N*4 + outgoing M*N*2 or *4
+ *                                + staging with push + tables), or its P*Q + 1
+ *                                tile flags exceed 131072;
+ *     ENTWINE_ERR_UNSUPPORTED    schedule STREAMS, reducer_cus > 0, a
+ *                                measurement stage, or entwine_timing /
+ *                                entwine_trace switched on.
+ *   Sharing: every call on a GPU uses that GPU's one array, which keeps the
+ *   last call's contents.  Calls on one stream are ordered; calls that
+ *   overlap on one GPU (other streams, other host threads' streams) race on
+ *   the array and give undefined results.  A call whose shape or schedule
+ *   differs from the previous no-alloc call's on the GPU copies the new
+ *   schedule tables into the array and synchronizes `stream`, so it cannot be
+ *   captured into a graph; a repeat of the previous call's shape can.
+ *   A timeout of its reduction is reported by entwine_device_status(stream).
+ */
+int entwine_gemm_rs_noalloc(const void* X, const void* W, const void* const* peer_partials,
+                            void* out, int64_t M, int64_t N, int64_t K_local, int P, int rank,
+                            int tile_order, int comm_budget, void* stream,
+                            const entwine_config* cfg);
+
+/*
  * entwine_gemm_rs_rmsnorm -- the layer chain of Sec. 5.2.2 (Layer-Level
  * Performance): the GEMM-ReduceScatter above, then a residual addition and an
  * RMSNorm over the rank's rows, in one call with the same schedules.

@@ -36,7 +36,8 @@ GEMM_AUTO, GEMM_PINGPONG, GEMM_BASE = 0, 4, 5
 
 # Names exported by the library (one per declaration in include/entwine.h).
 EXPORTS = [
-    "entwine_gemm_rs", "entwine_config_init", "entwine_gemm_rs_ex", "entwine_gemm_rs_rmsnorm",
+    "entwine_gemm_rs", "entwine_config_init", "entwine_gemm_rs_ex", "entwine_gemm_rs_noalloc",
+    "entwine_gemm_rs_rmsnorm",
     "entwine_plan_shape",
     "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
     "entwine_plan_task_order", "entwine_plan_tasks",
@@ -104,6 +105,8 @@ def load(path: str = LIB):
         "entwine_gemm_rs": ([vp, vp, ctypes.POINTER(vp), vp, i64, i64, i64, i32, i32, i32, i32, vp], i32),
         "entwine_gemm_rs_ex": ([vp, vp, ctypes.POINTER(vp), vp, i64, i64, i64, i32, i32, i32, i32, vp,
                                 pcfg], i32),
+        "entwine_gemm_rs_noalloc": ([vp, vp, ctypes.POINTER(vp), vp, i64, i64, i64, i32, i32, i32,
+                                     i32, vp, pcfg], i32),
         "entwine_config_init": ([pcfg], None),
         "entwine_gemm_rs_rmsnorm": ([vp, vp, ctypes.POINTER(vp), vp, vp, ctypes.c_float, vp, vp,
                                      i64, i64, i64, i32, i32, i32, i32, vp, pcfg], i32),
@@ -175,6 +178,18 @@ def entwine_gemm_rs(X: int, W: int, peer_partials: list, out: int, M: int, N: in
 
 
 entwine_gemm_rs_ex = entwine_gemm_rs
+
+
+def entwine_gemm_rs_noalloc(X: int, W: int, peer_partials: list, out: int, M: int, N: int,
+                            K_local: int, P: int, rank: int, tile_order: int, comm_budget: int,
+                            stream: int, cfg: entwine_config | None = None) -> int:
+    """Raw pointers in, status out (raises EntwineError on failure): the
+    operation on the library's fixed device scratch, allocating nothing."""
+    lib = load()
+    arr = (ctypes.c_void_p * max(P, 1))(*[p or None for p in peer_partials])
+    rc = lib.entwine_gemm_rs_noalloc(X, W, arr, out, M, N, K_local, P, rank, tile_order,
+                                     comm_budget, stream, ctypes.byref(cfg) if cfg else None)
+    return _check(rc)
 
 
 def entwine_device_status(stream: int = 0) -> int:
@@ -369,6 +384,19 @@ def gemm_rs(X, W, peers, out, P: int, rank: int, tile_order: int = ORDER_AUTO,
         stream = torch.cuda.current_stream(X.device)
     return entwine_gemm_rs(X.data_ptr(), W.data_ptr(), ptrs, out.data_ptr(), M, N, K, P, rank,
                            tile_order, comm_budget, stream.cuda_stream, cfg)
+
+
+def gemm_rs_noalloc(X, W, peers, out, P: int, rank: int, tile_order: int = ORDER_AUTO,
+                    comm_budget: int = BUDGET_AUTO, cfg: entwine_config | None = None,
+                    stream=None):
+    """torch front end of entwine_gemm_rs_noalloc (same checks as gemm_rs)."""
+    import torch
+
+    M, N, K, ptrs = _check_operands(X, W, peers, out, P, rank, cfg)
+    if stream is None:
+        stream = torch.cuda.current_stream(X.device)
+    return entwine_gemm_rs_noalloc(X.data_ptr(), W.data_ptr(), ptrs, out.data_ptr(), M, N, K, P,
+                                   rank, tile_order, comm_budget, stream.cuda_stream, cfg)
 
 
 def gemm_rs_rmsnorm(X, W, peers, residual, gamma, eps: float, h_out, y_out, P: int, rank: int,

@@ -31,6 +31,7 @@
 #include <tuple>
 #include <vector>
 
+#include "api_internal.h"
 #include "entwine.h"
 #include "kernels.h"
 #include "plan.h"
@@ -403,9 +404,12 @@ struct Chain {
   float eps = 0.0f;
 };
 
-int run(const void* X, const void* W, const void* const* peers, void* out, int64_t M, int64_t N,
-        int64_t K, int P, int rank, int tile_order, int comm_budget, void* stream_,
-        const entwine_config* cfg, const Chain* chain = nullptr) {
+// Validation shared by every entry point that runs the operation: shapes,
+// configuration, pointers (presence, alignment, no aliasing of the outputs).
+// Nothing is enqueued.
+int prepare(const void* X, const void* W, const void* const* peers, void* out, int64_t M,
+            int64_t N, int64_t K, int P, int rank, int tile_order, int comm_budget,
+            const entwine_config* cfg, const Chain* chain, Resolved* rs_out, Geometry* g_out) {
   int rc = check_shape(M, N, K, P, rank);
   if (rc) return rc;
   Resolved rs;
@@ -454,6 +458,114 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "gamma overlaps h_out");
   }
 
+  *rs_out = rs;
+  *g_out = g;
+  return ENTWINE_OK;
+}
+
+// The device buffers a call runs on: the library workspace's, or the
+// caller-free scratch of entwine_gemm_rs_noalloc.
+struct Buffers {
+  float* own = nullptr;
+  void* outgoing = nullptr;
+  void* staging = nullptr;
+  uint32_t* flags = nullptr;
+  int32_t* error = nullptr;
+  uint32_t* ctl = nullptr;
+  const int32_t* blocks = nullptr;
+  const int32_t* tiles = nullptr;
+  const int32_t* waits = nullptr;
+  const int32_t* task_list = nullptr;
+  int wait_slots = 0;
+};
+
+// Kernel arguments common to every schedule (the schedule-specific fields --
+// publication, grids, task counts -- are set by the caller).
+void fill_args(const Resolved& rs, const Geometry& g, const void* X, const void* W,
+               const void* const* peers, void* out, int64_t M, int64_t N, int64_t K, int P,
+               int rank, const Chain* chain, const Buffers& b, uint64_t timeout_ticks,
+               GemmArgs* ga_out, ReduceArgs* ra_out) {
+  GemmArgs ga{};
+  ga.X = static_cast<const uint16_t*>(X);
+  ga.W = static_cast<const uint16_t*>(W);
+  ga.own = b.own;
+  ga.outgoing = b.outgoing;
+  ga.flags = b.flags;
+  ga.blocks = b.blocks;
+  ga.M = (int32_t)M;
+  ga.N = (int32_t)N;
+  ga.K = (int32_t)K;
+  ga.R = (int32_t)g.R;
+  ga.rank = rank;
+  ga.Q = (int32_t)g.Q;
+  ga.Rt = (int32_t)g.Rt;
+  ga.Ct = (int32_t)g.Ct;
+  ga.tm = g.tm;
+  ga.tn = g.tn;
+  ga.outgoing_f32 = rs.peer_f32;
+  ga.variant = rs.variant;
+  ga.ctl = b.ctl;
+  ga.nb = (int32_t)g.NB;
+
+  ReduceArgs ra{};
+  ra.own = b.own;
+  for (int r = 0; r < P; ++r) ra.peers[r] = r == rank ? nullptr : peers[r];
+  ra.out = out;
+  ra.flags = b.flags;
+  ra.waits = b.waits;
+  ra.tiles = b.tiles;
+  ra.error = b.error;
+  ra.R = (int32_t)g.R;
+  ra.N = (int32_t)N;
+  ra.P = P;
+  ra.rank = rank;
+  ra.Q = (int32_t)g.Q;
+  ra.wait_slots = b.wait_slots;
+  ra.tm = g.tm;
+  ra.tn = g.tn;
+  ra.ctl = b.ctl;
+  ra.timeout_ticks = timeout_ticks;
+  ra.withhold_tile = rs.withhold_tile;
+  ra.never_flag = (int32_t)(g.P * g.Q);
+  ra.outgoing = b.outgoing;
+  ra.staging = rs.push ? b.staging : nullptr;
+  ra.residual = chain ? chain->residual : nullptr;
+  ra.task_list = b.task_list;
+  // Preseeded peers (and the residual) exist before the call: a task may load
+  // them before its wait.  Under symmetric readiness they count as produced
+  // with the tiles, so they are read only after the wait.
+  ra.prefetch = rs.peer_ready == ENTWINE_PEERS_PRESEEDED;
+  *ga_out = ga;
+  *ra_out = ra;
+}
+
+// Flags a call's GEMM publishes: tiles a kernel on this device reads are
+// released (publish 1: the rank's own tiles; 2: every tile, when peer-bound
+// tiles are pushed or published too); flags of peer-bound tiles are stored
+// when some wait reads them (send tasks, symmetric peers, release groups).
+void set_publication(const Resolved& rs, GemmArgs* ga) {
+  ga->publish = rs.publish_all || rs.push ? 2 : 1;
+  ga->flag_all = rs.publish_all || rs.push || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
+                 rs.release_group != ENTWINE_RELEASE_TILE;
+}
+
+// The sequential schedule's reduction grid: up to 8 workgroups per CU over
+// the partition's 8-element chunks, two chunks per thread.
+int flat_grid(const Geometry& g, int64_t N, int threads, int cus) {
+  const int64_t chunks = g.R * N / 8;
+  const int64_t per_wg = (int64_t)threads * 2;
+  return (int)std::max<int64_t>(1, std::min<int64_t>((chunks + per_wg - 1) / per_wg,
+                                                      (int64_t)8 * cus));
+}
+
+int run(const void* X, const void* W, const void* const* peers, void* out, int64_t M, int64_t N,
+        int64_t K, int P, int rank, int tile_order, int comm_budget, void* stream_,
+        const entwine_config* cfg, const Chain* chain = nullptr) {
+  Resolved rs;
+  Geometry g;
+  int rc = prepare(X, W, peers, out, M, N, K, P, rank, tile_order, comm_budget, cfg, chain, &rs,
+                   &g);
+  if (rc) return rc;
   hipStream_t stream = static_cast<hipStream_t>(stream_);
   hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
   HIP_TRY(hipStreamIsCapturing(stream, &cap));
@@ -560,6 +672,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     window = (int64_t)std::max(per_cu, 1) * w->cus;
   }
 
+  const size_t peer_sz = rs.peer_f32 ? 4 : 2;
   const size_t own_need = (size_t)g.R * N * 4, og_need = (size_t)M * N * peer_sz;
   // One slot past the P x Q flags is never written by any GEMM (failure injection).
   const size_t flag_need = ((size_t)g.P * g.Q + 1) * 4;
@@ -635,63 +748,27 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   TimingPair tp{};
   if (g_timing && (rc = take_timing_pair(w, &tp))) return rc;
 
-  GemmArgs ga{};
-  ga.X = static_cast<const uint16_t*>(X);
-  ga.W = static_cast<const uint16_t*>(W);
-  ga.own = w->own;
-  ga.outgoing = w->outgoing;
-  ga.flags = w->flags;
-  ga.blocks = dp->d_blocks;
-  ga.M = (int32_t)M;
-  ga.N = (int32_t)N;
-  ga.K = (int32_t)K;
-  ga.R = (int32_t)g.R;
-  ga.rank = rank;
-  ga.Q = (int32_t)g.Q;
-  ga.Rt = (int32_t)g.Rt;
-  ga.Ct = (int32_t)g.Ct;
-  ga.tm = g.tm;
-  ga.tn = g.tn;
-  ga.outgoing_f32 = rs.peer_f32;
-  ga.variant = rs.variant;
-  ga.ctl = w->ctl;
-  ga.nb = (int32_t)g.NB;
-
-  ReduceArgs ra{};
-  ra.own = w->own;
-  for (int r = 0; r < P; ++r) ra.peers[r] = r == rank ? nullptr : peers[r];
-  ra.out = out;
-  ra.flags = w->flags;
-  ra.waits = dp->d_waits;
-  ra.tiles = dp->d_tiles;
-  ra.error = w->error;
-  ra.R = (int32_t)g.R;
-  ra.N = (int32_t)N;
-  ra.P = P;
-  ra.rank = rank;
-  ra.Q = (int32_t)g.Q;
-  ra.wait_slots = dp->plan.wait_slots;
-  ra.tm = g.tm;
-  ra.tn = g.tn;
-  ra.ctl = w->ctl;
-  ra.timeout_ticks = (uint64_t)rs.timeout_ms * (uint64_t)w->wall_khz;
-  ra.withhold_tile = rs.withhold_tile;
-  ra.never_flag = (int32_t)(g.P * g.Q);
-  ra.outgoing = w->outgoing;
-  ra.staging = rs.push ? w->staging : nullptr;
-  ra.residual = chain ? chain->residual : nullptr;
-  ra.task_list = d_task_list;
-  // Preseeded peers (and the residual) exist before the call: a task may load
-  // them before its wait.  Under symmetric readiness they count as produced
-  // with the tiles, so they are read only after the wait.
-  ra.prefetch = rs.peer_ready == ENTWINE_PEERS_PRESEEDED;
+  Buffers bufs;
+  bufs.own = w->own;
+  bufs.outgoing = w->outgoing;
+  bufs.staging = w->staging;
+  bufs.flags = w->flags;
+  bufs.error = w->error;
+  bufs.ctl = w->ctl;
+  bufs.blocks = dp->d_blocks;
+  bufs.tiles = dp->d_tiles;
+  bufs.waits = dp->d_waits;
+  bufs.task_list = d_task_list;
+  bufs.wait_slots = dp->plan.wait_slots;
+  GemmArgs ga;
+  ReduceArgs ra;
+  fill_args(rs, g, X, W, peers, out, M, N, K, P, rank, chain, bufs,
+            (uint64_t)rs.timeout_ms * (uint64_t)w->wall_khz, &ga, &ra);
 
   if (fused) {
     // One kernel on the caller's stream, after this workspace's previous
     // eager call (which may have run on other streams).
-    ga.publish = rs.publish_all || rs.push ? 2 : 1;
-    ga.flag_all = rs.publish_all || rs.push || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
-                  rs.release_group != ENTWINE_RELEASE_TILE;
+    set_publication(rs, &ga);
     ra.slabs = slabs_eff;
     ra.ntasks = (int32_t)(g.Q * ra.slabs * (rs.push ? g.P : 1));
     FusedArgs fa{};
@@ -745,18 +822,9 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     ga.publish = 0;
     ra.slabs = 1;
     ra.ntasks = 0;
-    const int64_t chunks = g.R * N / 8;
-    const int64_t per_wg = (int64_t)rs.threads * 2;
-    grid = (int)std::max<int64_t>(1, std::min<int64_t>((chunks + per_wg - 1) / per_wg,
-                                                        (int64_t)8 * w->cus));
+    grid = flat_grid(g, N, rs.threads, w->cus);
   } else {
-    // Pushing reads the peer-bound tiles on this device: they are released
-    // like the own ones.
-    ga.publish = rs.publish_all || rs.push ? 2 : 1;
-    // Flags of peer-bound tiles are read by send tasks, symmetric-peer and
-    // release-group waits only.
-    ga.flag_all = rs.publish_all || rs.push || rs.peer_ready == ENTWINE_PEERS_SYMMETRIC ||
-                  rs.release_group != ENTWINE_RELEASE_TILE;
+    set_publication(rs, &ga);
     ra.slabs = slabs_eff;
     ra.ntasks = (int32_t)(g.Q * ra.slabs * (rs.push ? g.P : 1));
     grid = (int)std::min<int64_t>(rs.budget, ra.ntasks);  // x, capped by the task count
@@ -843,7 +911,181 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   return ENTWINE_OK;
 }
 
+// Host-side state of the no-alloc path on one device: the schedule tables
+// its scratch holds (their key), and their host copy, the source of the last
+// upload.
+struct NoAllocTables {
+  bool valid = false;
+  std::tuple<PlanKey, int, int> key;
+  std::vector<int32_t> host;
+  size_t bytes = 0;
+};
+std::map<int, NoAllocTables> g_noalloc;
+
+size_t up256(size_t v) { return (v + 255) & ~size_t(255); }
+
 }  // namespace
+
+namespace entwine {
+
+int report(int status, const char* message) { return fail(status, "%s", message); }
+
+int run_noalloc(void* scratch, size_t scratch_bytes, const void* X, const void* W,
+                const void* const* peers, void* out, int64_t M, int64_t N, int64_t K, int P,
+                int rank, int tile_order, int comm_budget, hipStream_t stream,
+                const entwine_config* cfg) {
+  Resolved rs;
+  Geometry g;
+  int rc = prepare(X, W, peers, out, M, N, K, P, rank, tile_order, comm_budget, cfg, nullptr,
+                   &rs, &g);
+  if (rc) return rc;
+  int dev = 0, cus = 0, khz = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  HIP_TRY(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev));
+  if (hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, dev) != hipSuccess || khz <= 0)
+    khz = 100000;
+  if (rs.budget >= cus)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT,
+                "comm_budget %d must stay below the device's %d compute units", rs.budget, cus);
+  const bool sequential = rs.budget == ENTWINE_BUDGET_SEQUENTIAL;
+  // Only schedules that run on the caller's stream alone: a second stream and
+  // its events would be allocations.
+  if (cfg && cfg->struct_size >= (int32_t)(offsetof(entwine_config, schedule) + sizeof(int32_t)) &&
+      cfg->schedule == ENTWINE_SCHEDULE_STREAMS && !sequential)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "the no-alloc entry point runs the sequential and the "
+                "fused schedules only (the two-stream schedule needs a stream and events)");
+  if (rs.reducer_cus > 0 && !sequential)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning (reducer_cus) runs on two "
+                "streams: not available without allocation");
+  if (rs.stages != ENTWINE_STAGES_ALL)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "measurement stages are not available without allocation");
+  if (rs.push && sequential)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "push_outgoing applies to the overlapped schedules "
+                "(comm_budget >= 1)");
+  std::lock_guard<std::mutex> lock(g_mu);
+  if (g_timing || g_trace)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "entwine_timing and entwine_trace record into allocated "
+                "memory: turn them off for the no-alloc entry point");
+
+  int fused_per_cu = 0;
+  if (!sequential) {
+    fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32);
+    if (fused_per_cu <= 0 && rs.variant_auto && rs.variant != 0) {
+      rs.variant = 0;  // same accumulation order, same result
+      fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, 0, rs.peer_f32, rs.out_f32);
+    }
+    if (fused_per_cu <= 0)
+      return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
+                  "GEMM variant %d", g.bm, g.bn, rs.variant);
+  }
+  const int slabs = rs.slabs ? rs.slabs : 1;
+  int64_t window = 0;
+  if (!rs.linear_dispatch)
+    window = (int64_t)std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1) * cus;
+
+  // Schedule tables (host-built, cached by key; uploaded into the scratch
+  // when the key changes).
+  const size_t flag_words = (size_t)g.P * (size_t)g.Q + 1;
+  if (flag_words > kScratchFlagWords)
+    return fail(ENTWINE_ERR_OUT_OF_MEMORY, "%zu tile flags exceed the no-alloc scratch's %zu",
+                flag_words, kScratchFlagWords);
+  NoAllocTables& nt = g_noalloc[dev];
+  const auto key = std::make_tuple(PlanKey{g.M, g.N, g.P, g.bm, g.bn, g.tm, g.tn, rank, rs.order,
+                                           rs.peer_ready, rs.release_group, window},
+                                   sequential ? 0 : slabs, sequential ? 0 : rs.push + 1);
+  size_t n_blocks = 0, n_tiles = 0, n_waits = 0, n_tasks = 0;
+  int wait_slots = 0;
+  std::vector<int32_t> host;
+  if (!(nt.valid && nt.key == key)) {
+    Plan plan;
+    if ((rc = build_plan(g, rank, rs.order, rs.peer_ready, rs.release_group, &plan)))
+      return fail(rc, "schedule construction failed");
+    assign_dispatch(&plan, window);
+    std::vector<int32_t> tasks;
+    if (!sequential) tasks = task_list(plan, slabs, rs.push != 0);
+    host.reserve(plan.launch.size() + plan.tiles.size() + plan.waits.size() + tasks.size() + 1);
+    host.push_back(plan.wait_slots);  // header: the table sizes follow from the key
+    host.insert(host.end(), plan.launch.begin(), plan.launch.end());
+    host.insert(host.end(), plan.tiles.begin(), plan.tiles.end());
+    host.insert(host.end(), plan.waits.begin(), plan.waits.end());
+    host.insert(host.end(), tasks.begin(), tasks.end());
+  }
+  const std::vector<int32_t>& tab = host.empty() ? nt.host : host;
+  wait_slots = tab[0];
+  n_blocks = (size_t)g.NB * 4;
+  n_tiles = (size_t)g.Q * 2;
+  n_waits = (size_t)g.Q * wait_slots;
+  n_tasks = tab.size() - 1 - n_blocks - n_tiles - n_waits;
+
+  // Scratch layout: the fixed part, then tables, own partial, outgoing
+  // partials and (push) staging, each 256-byte aligned.
+  const size_t peer_sz = rs.peer_f32 ? 4 : 2;
+  const size_t off_tab = kScratchFixed;
+  const size_t off_own = up256(off_tab + tab.size() * 4);
+  const size_t off_og = up256(off_own + (size_t)g.R * N * 4);
+  const size_t off_st = up256(off_og + (size_t)M * N * peer_sz);
+  const size_t need = rs.push ? up256(off_st + (size_t)M * N * peer_sz) : off_st;
+  if (need > scratch_bytes)
+    return fail(ENTWINE_ERR_OUT_OF_MEMORY, "the call needs %zu bytes of scratch; the no-alloc "
+                "entry point's maximum is %zu", need, scratch_bytes);
+
+  char* base = static_cast<char*>(scratch);
+  if (!host.empty()) {
+    // The previous call's kernels may still read the old tables: the copy is
+    // ordered after them on `stream`, and waited for, so that the host source
+    // stays valid until the device has it.
+    HIP_TRY(hipMemcpyAsync(base + off_tab, host.data(), host.size() * 4, hipMemcpyHostToDevice,
+                           stream));
+    HIP_TRY(hipStreamSynchronize(stream));
+    nt.host.swap(host);
+    nt.key = key;
+    nt.valid = true;
+  }
+  const int32_t* d_tab = reinterpret_cast<const int32_t*>(base + off_tab) + 1;
+  Buffers b;
+  b.ctl = reinterpret_cast<uint32_t*>(base + kScratchCtl);
+  b.error = reinterpret_cast<int32_t*>(base + kScratchError);
+  b.flags = reinterpret_cast<uint32_t*>(base + kScratchFlags);
+  b.blocks = d_tab;
+  b.tiles = d_tab + n_blocks;
+  b.waits = d_tab + n_blocks + n_tiles;
+  b.task_list = n_tasks ? d_tab + n_blocks + n_tiles + n_waits : nullptr;
+  b.wait_slots = wait_slots;
+  b.own = reinterpret_cast<float*>(base + off_own);
+  b.outgoing = base + off_og;
+  b.staging = rs.push ? base + off_st : nullptr;
+  GemmArgs ga;
+  ReduceArgs ra;
+  fill_args(rs, g, X, W, peers, out, M, N, K, P, rank, nullptr, b,
+            (uint64_t)rs.timeout_ms * (uint64_t)khz, &ga, &ra);
+  hipError_t e;
+  if (sequential) {
+    ga.publish = 0;
+    ra.slabs = 1;
+    ra.ntasks = 0;
+    if ((e = launch_gemm_publish(ga, g.bm, g.bn, (int)g.NB, stream)) != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "GEMM launch failed: %s", hipGetErrorString(e));
+    if ((e = launch_tile_reduce(ra, rs.peer_f32, rs.out_f32, rs.threads, true,
+                                flat_grid(g, N, rs.threads, cus), stream)) != hipSuccess)
+      return fail(ENTWINE_ERR_HIP, "reduction launch failed: %s", hipGetErrorString(e));
+    return ENTWINE_OK;
+  }
+  set_publication(rs, &ga);
+  ra.slabs = slabs;
+  ra.ntasks = (int32_t)(g.Q * slabs * (rs.push ? g.P : 1));
+  FusedArgs fa{};
+  fa.g = ga;
+  fa.r = ra;
+  fa.nb = (int32_t)g.NB;
+  fa.workers = (int32_t)std::min<int64_t>(rs.budget, ra.ntasks);
+  const int64_t grid = std::min<int64_t>((int64_t)fused_per_cu * cus, g.NB + (int64_t)fa.workers);
+  if ((e = launch_gemm_rs_fused(fa, g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32, (int)grid,
+                                stream)) != hipSuccess)
+    return fail(ENTWINE_ERR_HIP, "fused launch failed: %s", hipGetErrorString(e));
+  return ENTWINE_OK;
+}
+
+}  // namespace entwine
 
 extern "C" {
 
@@ -1000,26 +1242,43 @@ int entwine_plan_tasks(int64_t Q, int comm_budget, int consumer, int32_t* tasks,
 
 int entwine_device_status(void* stream) {
   std::lock_guard<std::mutex> lock(g_mu);
-  Workspace* w = nullptr;
-  int rc = get_workspace(&w);
-  if (rc) return rc;
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
   HIP_TRY(hipStreamSynchronize(static_cast<hipStream_t>(stream)));
-  HIP_TRY(hipStreamSynchronize(w->s_red));
-  if (w->have_prev) {
-    HIP_TRY(hipEventSynchronize(w->ev_gemm));
-    HIP_TRY(hipEventSynchronize(w->ev_red));
+  int status = ENTWINE_OK;
+  const uint32_t ctl_init[kCtlWords] = {1};  // epoch 1; counters and tickets 0
+  auto it = g_ws.find(dev);
+  if (it != g_ws.end()) {
+    Workspace* w = it->second.get();
+    HIP_TRY(hipStreamSynchronize(w->s_red));
+    if (w->have_prev) {
+      HIP_TRY(hipEventSynchronize(w->ev_gemm));
+      HIP_TRY(hipEventSynchronize(w->ev_red));
+    }
+    int32_t err = 0;
+    HIP_TRY(hipMemcpy(&err, w->error, sizeof err, hipMemcpyDeviceToHost));
+    if (err != 0) {
+      // An aborted reduction advanced the epoch while GEMM blocks may still
+      // have been publishing; with every stream idle, start the flags afresh.
+      HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
+      if (w->flags) HIP_TRY(hipMemset(w->flags, 0, w->flag_count * sizeof(uint32_t)));
+      HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
+      status = err;
+    }
   }
-  int32_t err = 0;
-  HIP_TRY(hipMemcpy(&err, w->error, sizeof err, hipMemcpyDeviceToHost));
-  if (err != 0) {
-    // An aborted reduction advanced the epoch while GEMM blocks may still
-    // have been publishing; with every stream idle, start the flags afresh.
-    const uint32_t ctl_init[kCtlWords] = {1};
-    HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
-    if (w->flags) HIP_TRY(hipMemset(w->flags, 0, w->flag_count * sizeof(uint32_t)));
-    HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
-    return fail(err, "a reduction workgroup timed out waiting for a tile flag");
+  // The no-alloc entry point's scratch (its calls ran on `stream`).
+  if (char* sc = static_cast<char*>(noalloc_scratch(dev))) {
+    int32_t err = 0;
+    HIP_TRY(hipMemcpy(&err, sc + kScratchError, sizeof err, hipMemcpyDeviceToHost));
+    if (err != 0) {
+      HIP_TRY(hipMemset(sc + kScratchError, 0, sizeof(int32_t)));
+      HIP_TRY(hipMemset(sc + kScratchFlags, 0, kScratchFlagWords * sizeof(uint32_t)));
+      HIP_TRY(hipMemcpy(sc + kScratchCtl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
+      status = err;
+    }
   }
+  if (status != ENTWINE_OK)
+    return fail(status, "a reduction workgroup timed out waiting for a tile flag");
   return ENTWINE_OK;
 }
 
