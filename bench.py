@@ -8,28 +8,30 @@ Steps are replayed from a captured HIP graph, as the pages' prototype does with
 CUDA Graphs, so the timed loop measures device time rather than host launch
 overhead.
 
-Default workload: the MLP down-projection slice, M = N = 4096, K_local =
-1792, P = 8 simulated ranks, rank 0, bf16 inputs, fp32 accumulation, bf16
-output, in the configuration the offline tuning table picks for the shape
-(block shape, order, budget -- 0 when no overlapped schedule beat the
-sequential one --, schedule).  Timing follows the pages' protocol (Sec. 5.1):
-warm-up iterations, then timed iterations bracketed by HIP events, median
+Default workload: the large MLP slice, M = N = 8192, K_local = 3584, P = 8
+simulated ranks, rank 0, bf16 inputs, fp32 accumulation, bf16 output, in the
+configuration the offline tuning table picks for the shape (block shape,
+order, budget -- 0 when no overlapped schedule beat the sequential one --,
+schedule).  Timing follows the pages' protocol (Sec. 5.1): warm-up
+iterations, then timed iterations each bracketed by HIP events, the median
 reported.
 
 One JSON line on stdout:
-  value, ms_per_step   TFLOP/s (2*M*N*K_local / step time) and step time of
-                       the tuned step
+  value, ms_per_step   TFLOP/s (2*M*N*K_local / step time) and the median
+                       per-replay step time of the tuned step
   sequential           the non-overlapped schedule (GEMM, then reduction)
-  overlapped           both overlapped schedules (two streams, fused) at the
-                       tuned budget (or 128 if the tuned step is sequential)
+  overlapped           both overlapped schedules (two streams, fused)
+  ablations            Sec. 5.3.1 production order, Sec. 5.3.2 release
+                       granularity and the communication budget's response
+                       (Sec. 2.2, 5.4.2): end-to-end median and the device
+                       trace's GEMM end and communication tail
   symmetric_all_ranks  the tuned step for every rank under symmetric peer
                        readiness; the slowest rank bounds a P-GPU step
   roofline             the step's dominant kernel against the bf16 MFMA
                        dense peak; its duration comes from HIP events
                        recorded on the stream the kernel runs on
-  reducer              the reduction kernel alone: algorithmic bytes /
-                       duration against HBM peak, with the peers' buffers
-                       warm and scrubbed from the caches
+  reducer              the reduction kernel alone against HBM peak, warm and
+                       with the caches scrubbed, and the Eq. (4) comparison
   cpu_baseline         the CPU oracle on a bounded row sample of the workload
 """
 from __future__ import annotations
@@ -54,10 +56,19 @@ def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def kernel_sources_digest() -> str:
+# The source files each measured kernel is built from: its counters stay valid
+# while these are unchanged.
+KERNEL_SOURCES = {
+    "gemm_publish": ["kernels.h", "gemm_block.h", "gemm_publish.hip"],
+    "gemm_rs_fused": ["kernels.h", "gemm_block.h", "reduce_task.h", "gemm_rs_fused.hip"],
+    "flat_reduce": ["kernels.h", "reduce_task.h", "tile_reduce.hip"],
+}
+
+
+def kernel_sources_digest(kernel: str) -> str:
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "tile_overlapped_gemm_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in KERNEL_SOURCES[kernel]:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + f.read())
     return h.hexdigest()[:16]
@@ -65,14 +76,14 @@ def kernel_sources_digest() -> str:
 
 def traffic_for(workload: str, kernel: str):
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
-    was taken on the current kernel sources (else None)."""
+    was taken on the kernel's current sources (else None)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         tab = json.load(f)
     e = tab.get(f"{kernel}/{workload}")
-    if not e or e.get("sources") != kernel_sources_digest():
+    if not e or e.get("sources") != kernel_sources_digest(kernel):
         return None
     return e.get("bytes_per_launch")
 
@@ -93,27 +104,28 @@ def tuned_entry(w):
 
 def cpu_baseline(w, X, W, target_s: float):
     """The CPU oracle's fp64 partial GEMM on the first S rows of the M-row
-    product (S sized so the run takes about target_s seconds), as TFLOP/s."""
+    product (S sized so that three runs take about target_s seconds), median
+    of the three, as TFLOP/s."""
     from oracle import oracle as orc
 
     threads = orc.num_threads(0)
-    probe = max(1, min(w.M, 64))
+    probe = max(1, min(w.M, 32))
     t0 = time.perf_counter()
     orc.partial_gemm(X, W, row_begin=0, row_end=probe, threads=threads)
     per_row = max((time.perf_counter() - t0) / probe, 1e-6)
-    rows = int(max(1, min(w.M, target_s / per_row)))
-    # Whole passes over the sampled rows until about target_s of CPU work.
-    runs, dt = 0, 0.0
-    while runs == 0 or (dt < 0.8 * target_s and runs < 64):
+    rows = int(max(1, min(w.M, target_s / 3.0 / per_row)))
+    times = []
+    for _ in range(3):
         t0 = time.perf_counter()
         orc.partial_gemm(X, W, row_begin=0, row_end=rows, threads=threads)
-        dt += time.perf_counter() - t0
-        runs += 1
-    flops = 2.0 * rows * w.N * w.K * runs
+        times.append(time.perf_counter() - t0)
+    dt = statistics.median(times)
+    flops = 2.0 * rows * w.N * w.K
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{runs} pass(es) over rows 0..{rows - 1} of the {w.M}-row partial product "
-                      f"X*W (N={w.N}, K_local={w.K}) in fp64 plain loops on {threads} threads, "
-                      f"{dt:.1f} s wall; the reduction's adds are negligible next to it"}
+            "sample": f"rows 0..{rows - 1} of the {w.M}-row partial product X*W (N={w.N}, "
+                      f"K_local={w.K}) in fp64 plain loops on {threads} threads, median of 3 runs "
+                      f"({', '.join(f'{t:.2f}' for t in times)} s); the reduction's adds are "
+                      f"negligible next to it"}
 
 
 def main() -> int:
@@ -121,7 +133,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=120)
-    ap.add_argument("--workload", default="mlp")
+    ap.add_argument("--workload", default="large_mlp")
     ap.add_argument("--order", default="auto", help="auto|row|partition|interleaved|col")
     ap.add_argument("--budget", type=int, default=-1, help="comm budget x (-1: tuning table)")
     ap.add_argument("--block", default="", help="BMxBN, e.g. 256x256 (default: tuning table)")
@@ -138,8 +150,10 @@ def main() -> int:
     ap.add_argument("--reducer-cus", type=int, default=0,
                     help="with --profile: reserve this many CUs for the reduction (two streams; "
                          "--budget must match)")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--cpu-seconds", type=float, default=30.0)
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-ablations", action="store_true",
+                    help="skip the order / release-granularity / budget sweeps")
     ap.add_argument("--profile", action="store_true",
                     help="only run --warmup + --steps eager calls (for rocprofv3), print nothing")
     ap.add_argument("--chain", action="store_true",
@@ -276,17 +290,33 @@ def main() -> int:
         return g
 
     def timed_graph(body, steps, warmup, per_step=True):
-        """Device time of `steps` back-to-back graph replays of `body`, bracketed
-        by two events (ms_per_step), and, in a second pass with an event after
-        every replay, the per-replay spread.  An event between two replays
-        serializes them and added about 5 µs per mlp step, so the per-replay
-        figures run above ms_per_step."""
+        """Graph replays of `body` after `warmup` untimed ones.  per_step: the
+        pages' protocol (Sec. 5.1), `steps` replays each bracketed by HIP
+        events, the median (ms_per_step) and the 10th / 90th percentiles;
+        then, as a second figure, the mean over `steps` back-to-back replays
+        between two events (an event between replays serializes them, which
+        the back-to-back figure leaves out).  Without per_step only the
+        back-to-back mean (kernel timings of many launches per replay)."""
         g = graph_of(body)
         with torch.cuda.stream(stream):
             for _ in range(warmup):
                 g.replay()
         stream.synchronize()
         check_status("after warm-up")
+        res = {}
+        if per_step:
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+            torch.cuda.synchronize()
+            with torch.cuda.stream(stream):
+                evs[0].record(stream)
+                for i in range(steps):
+                    g.replay()
+                    evs[i + 1].record(stream)
+            torch.cuda.synchronize()
+            check_status("in the per-replay pass")
+            per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+            res.update(ms_per_step=statistics.median(per), p10_ms=per[len(per) // 10],
+                       p90_ms=per[(9 * len(per)) // 10])
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         torch.cuda.synchronize()
         with torch.cuda.stream(stream):
@@ -296,23 +326,14 @@ def main() -> int:
             e1.record(stream)
         torch.cuda.synchronize()
         check_status("in the timed region")
-        res = dict(ms_per_step=e0.elapsed_time(e1) / steps)
-        if per_step:
-            evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-            with torch.cuda.stream(stream):
-                evs[0].record(stream)
-                for i in range(steps):
-                    g.replay()
-                    evs[i + 1].record(stream)
-            torch.cuda.synchronize()
-            check_status("in the per-replay pass")
-            per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
-            res.update(median_ms=statistics.median(per), p10_ms=per[len(per) // 10],
-                       p90_ms=per[(9 * len(per)) // 10])
+        res["back_to_back_ms"] = e0.elapsed_time(e1) / steps
+        if not per_step:
+            res["ms_per_step"] = res["back_to_back_ms"]
         return res
 
     def lat(r):
-        return {"latency_us": r["ms_per_step"] * 1e3, "latency_us_median": r["median_ms"] * 1e3}
+        return {"latency_us": r["ms_per_step"] * 1e3,
+                "latency_us_back_to_back": r["back_to_back_ms"] * 1e3}
 
     # The GPU's clocks ramp over the first fraction of a second of work: about
     # one second of untimed replays of the step settles them before any of
@@ -358,7 +379,7 @@ def main() -> int:
         it = iter(seeded)
         pr = [None if k == r else next(it) for k in range(w.P)]
         body = (lambda r=r, pr=pr: call(budget, sym_cfg, r, pr))
-        per_rank.append(timed_graph(body, args.steps, args.warmup)["median_ms"] * 1e3)
+        per_rank.append(timed_graph(body, args.steps, args.warmup)["ms_per_step"] * 1e3)
 
     # The layer chain (Sec. 5.2.2): the same step followed by the residual
     # addition (in the reduction's store) and an RMSNorm of the rank's rows.
@@ -436,9 +457,68 @@ def main() -> int:
     tr_cp_sh = traced(lambda: call(n_static, cfg_streams))
     tr_cp_st = traced(lambda: call(n_static, cfg_static))
 
+    # Ablations on the paper's two-stream schedule, each leg with the pages'
+    # timing protocol (end-to-end median) and the device trace (GEMM end and
+    # the communication tail, median of 21 replays).
+    #  * order (Sec. 5.3.1, Fig. 7(a)): the four production orders under
+    #    symmetric peer readiness, at rank 0 and rank P-1 (a rank-dependent
+    #    order ranks its partitions differently; the slower of the two bounds
+    #    the step);
+    #  * release granularity (Sec. 5.3.2, Fig. 7(c)): tiles released alone, in
+    #    groups of 4, per partition and once for the whole output;
+    #  * budget response (Sec. 2.2, Fig. 2; Sec. 5.4.2): the reduction's
+    #    workgroup count x, 0 being the sequential schedule.
+    ablations = None
+    if not args.no_ablations:
+        def ablation_leg(b, o, rank=w.rank, peers=pd, **extra):
+            c = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS, task_slabs=ov_slabs,
+                                  **extra))
+
+            def body():
+                tog.gemm_rs(Xd, Wd, peers, out, w.P, rank, o, b, cfg=c, stream=stream)
+            t = timed_graph(body, args.steps, args.warmup)
+            tr = traced(body)
+            return {"latency_us": t["ms_per_step"] * 1e3, "gemm_end_us": tr["gemm_end_us"],
+                    "reduce_end_us": tr["reduce_end_us"], "tail_us": tr["tail_us"]}
+
+        last = w.P - 1
+        it = iter(seeded)
+        peers_last = [None if k == last else next(it) for k in range(w.P)]
+        log(f"ablation: production order, symmetric readiness, ranks 0 and {last}, budget "
+            f"{ov_budget}")
+        by_order = {}
+        for name in ("interleaved", "col", "partition", "row"):
+            o = tog.ORDERS[name]
+            r0 = ablation_leg(ov_budget, o, peer_ready=tog.PEERS_SYMMETRIC)
+            rl = ablation_leg(ov_budget, o, rank=last, peers=peers_last,
+                              peer_ready=tog.PEERS_SYMMETRIC)
+            by_order[name] = {f"rank{w.rank}": r0, f"rank{last}": rl,
+                              "latency_us_max": max(r0["latency_us"], rl["latency_us"]),
+                              "tail_us_max": max(r0["tail_us"], rl["tail_us"])}
+        log("ablation: release granularity (interleaved order, preseeded peers)")
+        by_group = {}
+        for name, grp in (("tile", tog.RELEASE_TILE), ("4_tiles", 4),
+                          ("partition", tog.RELEASE_PARTITION), ("output", tog.RELEASE_OUTPUT)):
+            by_group[name] = ablation_leg(ov_budget, tog.ORDER_INTERLEAVED, release_group=grp)
+        budgets = (list(range(0, 33)) if w.name == "ragged"
+                   else [0, 1, 2, 4, 8, 16, 32, 64, 128, 192, cus - 1])
+        log(f"ablation: budget response over x in {budgets}")
+        by_budget = {}
+        for b in budgets:
+            if b >= cus:
+                continue
+            by_budget[str(b)] = ablation_leg(b, tog.ORDER_INTERLEAVED)
+        ablations = {"schedule": "streams", "budget": ov_budget, "task_slabs": ov_slabs,
+                     "order_symmetric": by_order, "release_group": by_group,
+                     "budget_response": by_budget}
+
     flops = float(w.flops)
     red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
                                        else (4 + 2 * (w.P - 1) + 2))
+    # Eq. (4) (Sec. 3.3, 5.4.1): the bandwidth the reduction must sustain to
+    # keep up with the GEMM is the remote volume, the P-1 peers'
+    # contributions to the rank's partition, over the GEMM's time.
+    remote_bytes = float(w.P - 1) * w.rows * w.N * (4 if w.fp32_io else 2)
     tflops = flops / (st["ms_per_step"] * 1e-3) / 1e12
     achieved = flops / (k_gemm * 1e-3) / 1e12
     gbps = lambda ms: red_bytes / (ms * 1e-3) / 1e9
@@ -466,8 +546,8 @@ def main() -> int:
                    "source": "tuning table" if tuned and args.budget < 0 else "flags",
                    "launch": "HIP graph replay"},
         "latency_us": st["ms_per_step"] * 1e3,
-        "latency_us_median": st["median_ms"] * 1e3,
         "latency_us_p10_p90": [st["p10_ms"] * 1e3, st["p90_ms"] * 1e3],
+        "latency_us_back_to_back": st["back_to_back_ms"] * 1e3,
         "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
         "sequential": lat(sq),
         "speedup_vs_sequential": sq["ms_per_step"] / st["ms_per_step"],
@@ -489,9 +569,9 @@ def main() -> int:
                         # beyond the plain step: the residual read and the norm's
                         # h read + y write, (M/P)*N*3*2 bytes
                         "extra_over_step_us": (ch["ms_per_step"] - st["ms_per_step"]) * 1e3},
-        "symmetric_all_ranks": {"latency_us_median_max": max(per_rank),
-                                "latency_us_median_per_rank": per_rank,
-                                "speedup_vs_sequential": sq["median_ms"] * 1e3 / max(per_rank)},
+        "symmetric_all_ranks": {"latency_us_max": max(per_rank),
+                                "latency_us_per_rank": per_rank,
+                                "speedup_vs_sequential": sq["ms_per_step"] * 1e3 / max(per_rank)},
         "gemm_alone_us": g_alone * 1e3,
         "gemm_alone_tflops": flops / (g_alone * 1e-3) / 1e12,
         "step_kernels_us": ({"fused": k_gemm * 1e3} if kind == "fused"
@@ -509,11 +589,18 @@ def main() -> int:
             "pct_hbm_peak_cold": 100.0 * gbps(r_cold) / HBM_PEAK_GBPS,
             "tiled_at_budget_us": r_tile * 1e3,
             "tiled_at_budget_gbps": gbps(r_tile),
-            "required_gbps_eq4": gbps(g_alone),
-            # bytes over the reduction's traced span, waits included (Sec. 5.4)
-            "measured_gbps_step": gbps(max(tr_step["reduce_span_us"], 1e-3) * 1e-3),
-            "measured_gbps_overlapped_streams": gbps(max(tr_streams["reduce_span_us"], 1e-3) * 1e-3),
+            # the reduction's HBM bytes over its traced span, waits included
+            "hbm_gbps_step": gbps(max(tr_step["reduce_span_us"], 1e-3) * 1e-3),
+            "hbm_gbps_overlapped_streams": gbps(max(tr_streams["reduce_span_us"], 1e-3) * 1e-3),
         },
+        # Sec. 3.3 Eq. (4) and Sec. 5.4.1: required = remote volume / GEMM time
+        # alone; measured = remote volume / the reduction's traced span
+        "eq4": {"remote_bytes": remote_bytes,
+                "required_gbps": remote_bytes / (g_alone * 1e-3) / 1e9,
+                "measured_gbps_step": remote_bytes / (max(tr_step["reduce_span_us"], 1e-3) * 1e-6) / 1e9,
+                "measured_gbps_overlapped_streams":
+                    remote_bytes / (max(tr_streams["reduce_span_us"], 1e-3) * 1e-6) / 1e9},
+        "ablations": ablations,
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": achieved / BF16_PEAK_TFLOPS,
                      "traffic": traffic_for(w.name, traffic_key),
