@@ -143,6 +143,8 @@ def main() -> int:
                     help="GEMM pipeline (0: the tuning table's for its block shape, else 5 = "
                          "base, 4 = ping-pong, ...)")
     ap.add_argument("--peers", default="preseeded", help="preseeded|symmetric")
+    ap.add_argument("--w-layout", default="kn", choices=["kn", "nk"],
+                    help="W handed over [K_local][N] (the library's default) or [N][K_local]")
     ap.add_argument("--schedule", default="auto", choices=["auto", "streams", "fused"],
                     help="overlapped schedule: two streams, one fused kernel, or the tuning table's")
     ap.add_argument("--static-cus", type=int, default=32,
@@ -200,7 +202,9 @@ def main() -> int:
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    Xd, Wd = up(X), up(W)
+    wkn = args.w_layout == "kn"
+    W_kn = wl.w_as_kn(W)
+    Xd, Wd = up(X), up(W_kn if wkn else W)
     pd = [None if p is None else up(p) for p in peers]
     out = torch.empty((w.rows, w.N), dtype=torch.float32 if w.fp32_io else torch.bfloat16,
                       device=dev)
@@ -213,6 +217,8 @@ def main() -> int:
         bm, bn = (int(v) for v in args.block.lower().split("x"))
     else:
         bm, bn = tuned.get("bm", 256), tuned.get("bn", 256)
+        if wkn and bn == 384:
+            bn = 256  # W [K][N] is built for 128- and 256-wide blocks (as the library's AUTO)
     order = (tog.ORDERS[args.order] if args.order != "auto"
              else tuned.get("order", tog.ORDER_INTERLEAVED))
     budget = args.budget if args.budget >= 0 else tuned.get("budget", 32)
@@ -232,7 +238,10 @@ def main() -> int:
         pipeline = 0 if args.gemm_variant == tog.GEMM_BASE else args.gemm_variant
     else:
         pipeline = tuned.get("variant", 0) if (tuned.get("bm"), tuned.get("bn")) == (bm, bn) else 0
-    cfg_kw = dict(tile_m=w.tile, tile_n=w.tile, block_m=bm, block_n=bn, reducer_threads=threads,
+        if wkn:
+            pipeline = 0  # the base pipeline is the one built for W [K][N]
+    cfg_kw = dict(w_layout=tog.W_KN if wkn else tog.W_NK,
+                  tile_m=w.tile, tile_n=w.tile, block_m=bm, block_n=bn, reducer_threads=threads,
                   task_slabs=slabs, schedule=schedule, gemm_variant=args.gemm_variant,
                   peer_ready=tog.PEERS_SYMMETRIC if args.peers == "symmetric" else tog.PEERS_PRESEEDED)
     if w.fp32_io:
@@ -402,6 +411,20 @@ def main() -> int:
 
     log("kernels alone")
     g_alone = timed_graph(rep(lambda: call(0, cfg_gemm)), ksteps, 3, False)["ms_per_step"] / reps
+    # The same GEMM with W in the other layout (base pipeline, the other
+    # layout's allowed block shape), for the layout comparison.
+    other = not wkn
+    Wd_other = up(W_kn if other else W)
+    bn_other = 256 if (other and bn == 384) else bn
+    cfg_gemm_other = tog.config(**dict(cfg_kw, stages=tog.STAGES_GEMM, block_n=bn_other,
+                                       w_layout=tog.W_KN if other else tog.W_NK,
+                                       gemm_variant=tog.GEMM_BASE if other else args.gemm_variant))
+
+    def call_other():
+        tog.gemm_rs(Xd, Wd_other, pd, out, w.P, w.rank, order, 0, cfg=cfg_gemm_other,
+                    stream=stream)
+    g_alone_other = timed_graph(rep(call_other), ksteps, 3, False)["ms_per_step"] / reps
+    del Wd_other
     r_flat = timed_graph(rep(lambda: call(0, cfg_red)), ksteps, 3, False)["ms_per_step"] / reps
     r_tile = timed_graph(rep(lambda: call(ov_budget, cfg_red)), ksteps, 3,
                          False)["ms_per_step"] / reps
@@ -543,6 +566,7 @@ def main() -> int:
                    "rank": w.rank, "schedule": kind, "block": f"{bm}x{bn}", "tile": w.tile,
                    "tile_order": order, "comm_budget": budget, "reducer_threads": threads,
                    "task_slabs": slabs, "gemm_pipeline": pipeline, "peer_ready": args.peers,
+                   "w_layout": "[K_local][N]" if wkn else "[N][K_local]",
                    "source": "tuning table" if tuned and args.budget < 0 else "flags",
                    "launch": "HIP graph replay"},
         "latency_us": st["ms_per_step"] * 1e3,
@@ -573,6 +597,9 @@ def main() -> int:
                                 "latency_us_per_rank": per_rank,
                                 "speedup_vs_sequential": sq["ms_per_step"] * 1e3 / max(per_rank)},
         "gemm_alone_us": g_alone * 1e3,
+        "gemm_alone_us_by_w_layout": {("[K_local][N]" if wkn else "[N][K_local]"): g_alone * 1e3,
+                                      ("[N][K_local]" if wkn else "[K_local][N]"):
+                                          g_alone_other * 1e3},
         "gemm_alone_tflops": flops / (g_alone * 1e-3) / 1e12,
         "step_kernels_us": ({"fused": k_gemm * 1e3} if kind == "fused"
                             else {"gemm": k_gemm * 1e3, "reduction": k_red * 1e3}),

@@ -93,10 +93,10 @@ enum { ENTWINE_BF16 = 0, ENTWINE_F32 = 1 };
  * alike (Sec. 3.1: every rank runs the same traversal). */
 enum { ENTWINE_PEERS_PRESEEDED = 0, ENTWINE_PEERS_SYMMETRIC = 1 };
 
-/* Layout of W (K_local x N). */
+/* Layout of W (the K_local x N operand). */
 enum {
-  ENTWINE_W_NK = 0, /* [N][K_local] row-major: K contiguous (a linear layer's weight) */
-  ENTWINE_W_KN = 1  /* [K_local][N] row-major: N contiguous (reserved; not built yet) */
+  ENTWINE_W_KN = 0, /* [K_local][N] row-major: N contiguous (the default; entwine_gemm_rs) */
+  ENTWINE_W_NK = 1  /* [N][K_local] row-major: K contiguous (a linear layer's weight, W^T) */
 };
 
 enum { ENTWINE_STAGES_ALL = 0, ENTWINE_STAGES_GEMM = 1, ENTWINE_STAGES_REDUCE = 2 };
@@ -143,9 +143,10 @@ enum { ENTWINE_GEMM_AUTO = 0, ENTWINE_GEMM_PINGPONG = 4, ENTWINE_GEMM_BASE = 5 }
  *
  *   X              device, bf16 [M][K_local] row-major: this rank's slice of
  *                  the activations.  16-byte aligned.
- *   W              device, bf16 [N][K_local] row-major (K contiguous): this
- *                  rank's slice of the weight, element (k, n) at W[n*K_local+k].
- *                  16-byte aligned.
+ *   W              device, bf16 [K_local][N] row-major (N contiguous): this
+ *                  rank's slice of the weight, element (k, n) at W[k*N + n].
+ *                  16-byte aligned.  (entwine_gemm_rs_ex also takes [N][K_local]:
+ *                  entwine_config.w_layout.)
  *   peer_partials  HOST array of P device pointers.  peer_partials[r] (r !=
  *                  rank) is bf16 [M/P][N] row-major: peer r's contribution to
  *                  partition `rank`.  peer_partials[rank] is ignored (may be
@@ -154,7 +155,8 @@ enum { ENTWINE_GEMM_AUTO = 0, ENTWINE_GEMM_PINGPONG = 4, ENTWINE_GEMM_BASE = 5 }
  *                  (rank+1)*M/P) of sum_r C_r.  Fully overwritten, never read;
  *                  must not overlap any input.  16-byte aligned.
  *   M, N, K_local  M % P == 0, N % 8 == 0, K_local % 64 == 0, all > 0;
- *                  M*K_local, N*K_local and M*N below 2^31.
+ *                  M*K_local, N*K_local and M*N below 2^31 (W [K_local][N]:
+ *                  N*K_local below 2^30).
  *   P, rank        1 <= P <= 8, 0 <= rank < P.
  *   tile_order     ENTWINE_ORDER_* (AUTO = tuning table, else INTERLEAVED).
  *   comm_budget    x >= 1 overlapped (clamped to Q), 0 sequential, -1 AUTO.
@@ -181,7 +183,9 @@ typedef struct entwine_config {
   int32_t tile_n;          /* reduction tile cols TN: 0 = 128, else 64 or 128; BN % TN == 0 */
   int32_t reducer_threads; /* b: 128, 256 or 512 (Sec. 4.3); 0 = the tuning table's entry,
                               else 256, and 512 under static CU partitioning (reducer_cus) */
-  int32_t w_layout;        /* ENTWINE_W_NK */
+  int32_t w_layout;        /* ENTWINE_W_KN (default) or ENTWINE_W_NK.  Blocks for W [K][N]:
+                              128 or 256 wide (an automatic 384-wide choice becomes 256),
+                              base pipeline; same output bits as W [N][K] */
   int32_t peer_dtype;      /* ENTWINE_BF16 or ENTWINE_F32: peers and outgoing contributions */
   int32_t out_dtype;       /* ENTWINE_BF16 or ENTWINE_F32 */
   int32_t peer_ready;      /* ENTWINE_PEERS_PRESEEDED or ENTWINE_PEERS_SYMMETRIC */

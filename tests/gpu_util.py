@@ -74,18 +74,32 @@ def as_f64(a: np.ndarray) -> np.ndarray:
 
 
 class Case:
-    """Device copies of one workload's inputs plus an output buffer."""
+    """Device copies of one workload's inputs plus an output buffer.  W (drawn
+    [N][K] by workloads.operands) is handed over in the layout a call's
+    configuration names: [K][N] by default (the library's default), [N][K]
+    with w_layout=tog.W_NK."""
 
-    def __init__(self, w: wl.Workload, X, W, peers, dev):
+    def __init__(self, w: wl.Workload, X, W, peers, dev, w_layout=tog.W_KN):
         self.w = w
         self.X, self.W, self.peers = X, W, peers
-        self.Xd, self.Wd = up(X, dev), up(W, dev)
+        self.w_layout = w_layout
+        self.Xd = up(X, dev)
+        self._Wd = {}
         self.pd = [None if p is None else up(p, dev) for p in peers]
         self.out_dtype = torch.float32 if w.fp32_io else torch.bfloat16
         self.dev = dev
 
+    def W_dev(self, layout):
+        if layout not in self._Wd:
+            self._Wd[layout] = up(wl.w_as_kn(self.W) if layout == tog.W_KN else self.W, self.dev)
+        return self._Wd[layout]
+
+    @property
+    def Wd(self):
+        return self.W_dev(self.w_layout)
+
     def base_cfg(self, **kw):
-        d = dict(tile_m=self.w.tile, tile_n=self.w.tile)
+        d = dict(tile_m=self.w.tile, tile_n=self.w.tile, w_layout=self.w_layout)
         if self.w.fp32_io:
             d.update(peer_dtype=tog.F32, out_dtype=tog.F32)
         d.update(kw)
@@ -97,8 +111,9 @@ class Case:
         out = torch.full((self.w.rows, self.w.N), float("nan"), dtype=self.out_dtype, device=self.dev)
         if poison:
             poison_workspace()
-        tog.gemm_rs(self.Xd, self.Wd, self.pd, out, self.w.P, self.w.rank, order, budget,
-                    cfg=self.base_cfg(**kw))
+        cfg = self.base_cfg(**kw)
+        tog.gemm_rs(self.Xd, self.W_dev(cfg.w_layout), self.pd, out, self.w.P, self.w.rank, order,
+                    budget, cfg=cfg)
         if check_status:
             st = tog.entwine_device_status(torch.cuda.current_stream().cuda_stream)
             assert st == tog.ENTWINE_OK, f"device status {st}"

@@ -86,8 +86,8 @@ def test_validation_before_any_device_call(lib, kw, status):
 
 
 @pytest.mark.parametrize("field,value,status", [
-    ("w_layout", tog.W_KN, tog.ENTWINE_ERR_UNSUPPORTED),
     ("w_layout", 7, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("w_layout", -1, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("block_m", 64, tog.ENTWINE_ERR_UNSUPPORTED),
     ("tile_m", 32, tog.ENTWINE_ERR_UNSUPPORTED),
     ("reducer_threads", 384, tog.ENTWINE_ERR_INVALID_ARGUMENT),
@@ -105,6 +105,20 @@ def test_validation_before_any_device_call(lib, kw, status):
 def test_config_validation(lib, field, value, status):
     cfg = tog.config(**{field: value})
     assert call(cfg=cfg) == status
+
+
+def test_w_kn_builds(lib):
+    """W [K_local][N] (the default) is built for the base pipeline with 128- and
+    256-wide blocks; other explicit choices are refused before any device call."""
+    assert tog.config().w_layout == tog.W_KN
+    for kw in (dict(block_m=128, block_n=384), dict(block_m=256, block_n=256, gemm_variant=4),
+               dict(block_m=256, block_n=256, gemm_variant=3)):
+        assert call(cfg=tog.config(w_layout=tog.W_KN, **kw)) == tog.ENTWINE_ERR_UNSUPPORTED
+        assert lib.entwine_last_error_message().decode()
+    # the same choices with W [N][K_local] pass validation (and then fail at the
+    # first device call in a process without a GPU)
+    for kw in (dict(block_m=128, block_n=384), dict(block_m=256, block_n=256, gemm_variant=4)):
+        assert call(cfg=tog.config(w_layout=tog.W_NK, **kw)) != tog.ENTWINE_ERR_UNSUPPORTED
 
 
 def test_block_shapes(lib):

@@ -32,7 +32,8 @@ class Chain:
         self.X, self.W = wl.operands(w)
         self.peers = wl.peer_partials(w)
         self.res, self.gamma = wl.chain_inputs(w)
-        self.Xd, self.Wd = up(self.X, dev), up(self.W, dev)
+        # W handed over [K][N], the library's default layout
+        self.Xd, self.Wd = up(self.X, dev), up(wl.w_as_kn(self.W), dev)
         self.pd = [None if p is None else up(p, dev) for p in self.peers]
         self.resd, self.gd = up(self.res, dev), up(self.gamma, dev)
         self.dtype = torch.float32 if w.fp32_io else torch.bfloat16

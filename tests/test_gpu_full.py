@@ -40,9 +40,13 @@ def test_full_size_parity(w):
         assert worst[name] <= 1.0, name
         return got
 
+    # W handed over [K_local][N] (the default layout) in every leg, and once
+    # [N][K_local]: both layouts give the same bits.
     seq = leg("sequential", tog.ORDER_AUTO, tog.BUDGET_SEQUENTIAL)
     out = leg("tuned step (AUTO)", tog.ORDER_AUTO, tog.BUDGET_AUTO)
     assert torch.equal(bits(out), bits(seq))
+    got = leg("tuned step (AUTO), W [N][K]", tog.ORDER_AUTO, tog.BUDGET_AUTO, w_layout=tog.W_NK)
+    assert torch.equal(bits(got), bits(seq))
     # Both overlapped schedules as the benchmark's overlapped legs run them when
     # the tuned step is sequential (the largest budget below the CU count, four
     # slabs per tile), and at a budget of 128 with one task per tile.

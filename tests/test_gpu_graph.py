@@ -21,7 +21,7 @@ def test_graph_replays_match_eager(sched, push):
     Xa, W = wl.operands(w)
     Xb, _ = wl.operands(wl.custom("graph_b", 2048, 1536, 512, 4, rank=2, index=321))
     peers = wl.peer_partials(w)
-    Wd = up(W, dev)
+    Wd = up(wl.w_as_kn(W), dev)  # [K][N], the default layout
     pd = [None if p is None else up(p, dev) for p in peers]
     cfg = tog.config(block_m=256, block_n=128, schedule=sched, push_outgoing=push)
     srcs = [up(Xa, dev), up(Xb, dev)]
@@ -68,7 +68,7 @@ def test_capture_requires_prepared_workspace():
     w = wl.custom("graph_cold", 512, 256, 128, 2, rank=0, index=322)
     X, W = wl.operands(w)
     peers = wl.peer_partials(w)
-    Xd, Wd = up(X, dev), up(W, dev)
+    Xd, Wd = up(X, dev), up(wl.w_as_kn(W), dev)
     pd = [None if p is None else up(p, dev) for p in peers]
     out = torch.empty((w.rows, w.N), dtype=torch.bfloat16, device=dev)
     g = torch.cuda.CUDAGraph()
@@ -99,7 +99,8 @@ def test_graph_survives_workspace_growth(sched):
     def inputs(w):
         X, W = wl.operands(w)
         peers = wl.peer_partials(w)
-        return up(X, dev), up(W, dev), [None if p is None else up(p, dev) for p in peers]
+        return (up(X, dev), up(wl.w_as_kn(W), dev),
+                [None if p is None else up(p, dev) for p in peers])
 
     Xs, Ws, ps = inputs(small)
     Xb, Wb, pb = inputs(big)

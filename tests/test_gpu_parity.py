@@ -57,30 +57,34 @@ def test_parity_and_schedule_invariance(dev, w):
     _, _, q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
     first = {}
     runs = 0
-    for bm, bn in BLOCKS:
+    for (bm, bn), variant, layout in [(b, v, lay) for b in BLOCKS
+                                      for v in (tog.GEMM_BASE, 3, tog.GEMM_PINGPONG)
+                                      for lay in (tog.W_NK, tog.W_KN)]:
         if w.tile == 64 and bm == 256:
             continue
-        for variant in (tog.GEMM_BASE, 3, tog.GEMM_PINGPONG):
+        if True:
             if variant == tog.GEMM_PINGPONG and (bm, bn) != (256, 256):
                 continue  # the ping-pong pipeline is built for 256 x 256 blocks
             if variant != tog.GEMM_BASE and (bm, bn) == (128, 384):
                 continue  # one pipeline for 128 x 384
+            if layout == tog.W_KN and (variant != tog.GEMM_BASE or bn == 384):
+                continue  # W [K][N]: the base pipeline, 128- and 256-wide blocks
             for order in ORDERS:
                 for budget, sched in [(b, s) for b in (0, 1, 3, min(q, 64)) for s in SCHEDULES]:
                     if sched == tog.SCHEDULE_FUSED and (budget == 0 or not fused_built(bm, bn, variant)):
                         continue
-                    print(f"case {w.name} block {bm}x{bn} v{variant} order {order} budget {budget} "
-                          f"schedule {sched}", flush=True)
+                    print(f"case {w.name} block {bm}x{bn} v{variant} W {layout} order {order} "
+                          f"budget {budget} schedule {sched}", flush=True)
                     if variant == tog.GEMM_PINGPONG and sched == tog.SCHEDULE_STREAMS and budget > 0:
                         # 235 registers per lane leave no room for a reduction
                         # workgroup on the GEMM's CUs: refused, nothing runs
                         with pytest.raises(tog.EntwineError) as e:
                             case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant,
-                                     schedule=sched)
+                                     schedule=sched, w_layout=layout)
                         assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
                         continue
                     out = down(case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant,
-                                        schedule=sched))
+                                        schedule=sched, w_layout=layout))
                     runs += 1
                     r = err_ratio(out, ref)
                     assert r <= 1.0, f"max err/tol {r:.3f}"
@@ -92,6 +96,7 @@ def test_parity_and_schedule_invariance(dev, w):
                     else:
                         np.testing.assert_array_equal(out, first["out"])
     assert runs >= 2 * len(ORDERS) * (4 + 3 + 4)  # two shapes: v0 both schedules, v3 streams
+    # every W [K][N] run agreed with the [N][K] ones: one result per workload
 
 
 @pytest.mark.parametrize("w", SMALL[:2], ids=lambda w: w.name)
@@ -316,7 +321,7 @@ def test_fused_unbuilt_variant_rejected(dev):
     case, _ = case_for(SMALL[0], dev)
     with pytest.raises(tog.EntwineError) as e:
         case.run(tog.ORDER_INTERLEAVED, 4, schedule=tog.SCHEDULE_FUSED, block_m=256, block_n=256,
-                 gemm_variant=1)
+                 gemm_variant=1, w_layout=tog.W_NK)
     assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
 
 
@@ -326,7 +331,8 @@ def test_reducer_that_cannot_share_a_cu_is_rejected(dev):
     GEMM of CUs: the call is refused before anything is enqueued."""
     case, _ = case_for(SMALL[0], dev)
     with pytest.raises(tog.EntwineError) as e:
-        case.run(tog.ORDER_INTERLEAVED, 4, reducer_threads=512, block_m=256, block_n=256)
+        case.run(tog.ORDER_INTERLEAVED, 4, reducer_threads=512, block_m=256, block_n=256,
+                 w_layout=tog.W_NK)
     assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
     # the sequential schedule has no waiting reducers and stays available
     case.run(tog.ORDER_INTERLEAVED, 0, reducer_threads=512, block_m=256, block_n=256)

@@ -31,6 +31,7 @@ def test_pick_ties_go_to_smaller_budget_threads_order():
 def test_pipelines_per_block_shape():
     assert sweep.pipelines_for(256, 256) == [0, 4]
     assert sweep.pipelines_for(128, 384) == [0]
+    assert sweep.pipelines_for(256, 256, wkn=True) == [0]
 
 
 def test_budget_list():

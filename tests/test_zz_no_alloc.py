@@ -21,7 +21,7 @@ def inputs(w, dev):
     X, W = wl.operands(w)
     peers = wl.peer_partials(w)
     pd = [None if p is None else up(p, dev) for p in peers]
-    return up(X, dev), up(W, dev), pd
+    return up(X, dev), up(wl.w_as_kn(W), dev), pd  # W [K][N], the default layout
 
 
 def call(fn, w, Xd, Wd, pd, budget, cfg):
@@ -66,7 +66,7 @@ def test_noalloc_refusals():
     # 256 MiB scratch (rejected before any launch; the buffers are not read)
     M, N, K = 16384, 8192, 64
     X = torch.zeros((M, K), dtype=torch.bfloat16, device=dev)
-    W = torch.zeros((N, K), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((K, N), dtype=torch.bfloat16, device=dev)
     out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
     with pytest.raises(tog.EntwineError) as e:
         tog.entwine_gemm_rs_noalloc(X.data_ptr(), W.data_ptr(), [None], out.data_ptr(), M, N, K,

@@ -28,7 +28,7 @@ ORDERS = {"row": 0, "partition": 1, "interleaved": 2, "col": 3}
 BUDGET_AUTO, BUDGET_SEQUENTIAL = -1, 0
 BF16, F32 = 0, 1
 PEERS_PRESEEDED, PEERS_SYMMETRIC = 0, 1
-W_NK, W_KN = 0, 1
+W_KN, W_NK = 0, 1
 RELEASE_TILE, RELEASE_PARTITION, RELEASE_OUTPUT = 1, 0, -1
 STAGES_ALL, STAGES_GEMM, STAGES_REDUCE = 0, 1, 2
 SCHEDULE_AUTO, SCHEDULE_STREAMS, SCHEDULE_FUSED = 0, 1, 2
@@ -346,9 +346,14 @@ def _check_operands(X, W, peers, out, P, rank, cfg):
         if not t.is_contiguous():
             raise ValueError(f"{name} must be contiguous")
     M, K = X.shape
-    N = W.shape[0]
-    if W.shape[1] != K:
-        raise ValueError(f"W is {tuple(W.shape)}, expected ({N}, {K})")
+    if cfg is not None and cfg.w_layout == W_NK:
+        N = W.shape[0]
+        if W.shape[1] != K:
+            raise ValueError(f"W is {tuple(W.shape)}, expected [N][K_local] = ({N}, {K})")
+    else:
+        N = W.shape[1]
+        if W.shape[0] != K:
+            raise ValueError(f"W is {tuple(W.shape)}, expected [K_local][N] = ({K}, {N})")
     if out.shape != (M // P, N):
         raise ValueError(f"out is {tuple(out.shape)}, expected ({M // P}, {N})")
     want_out = torch.float32 if (cfg is not None and cfg.out_dtype == F32) else torch.bfloat16
@@ -374,7 +379,8 @@ def gemm_rs(X, W, peers, out, P: int, rank: int, tile_order: int = ORDER_AUTO,
     """torch front end: checks devices, dtypes, shapes and contiguity, then
     calls entwine_gemm_rs(_ex) on the current (or given) stream.
 
-    X [M][K] bf16, W [N][K] bf16, peers[r] [M/P][N] (None at `rank`),
+    X [M][K] bf16, W [K][N] bf16 ([N][K] with cfg.w_layout = W_NK), peers[r]
+    [M/P][N] (None at `rank`),
     out [M/P][N]; all CUDA tensors on one device.
     """
     import torch

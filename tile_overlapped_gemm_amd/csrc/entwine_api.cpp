@@ -305,7 +305,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
       slabs, withhold_tile, variant, variant_auto, publish_all, stages, linear_dispatch, schedule,
-      reducer_cus, push;
+      reducer_cus, push, wkn;
   uint32_t timeout_ms;
 };
 
@@ -322,9 +322,11 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tile_order %d out of range", tile_order);
   if (comm_budget < ENTWINE_BUDGET_AUTO)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "comm_budget %d out of range", comm_budget);
-  if (c.w_layout != ENTWINE_W_NK)
-    return fail(c.w_layout == ENTWINE_W_KN ? ENTWINE_ERR_UNSUPPORTED : ENTWINE_ERR_INVALID_ARGUMENT,
-                "w_layout %d is not built (only ENTWINE_W_NK)", c.w_layout);
+  if (c.w_layout != ENTWINE_W_KN && c.w_layout != ENTWINE_W_NK)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "w_layout %d out of range", c.w_layout);
+  r->wkn = c.w_layout == ENTWINE_W_KN;
+  if (r->wkn && N * K * 2 >= ((int64_t)1 << 31))
+    return fail(ENTWINE_ERR_UNSUPPORTED, "W [K_local][N] of 2^31 bytes or more is not built");
   if ((c.peer_dtype != ENTWINE_BF16 && c.peer_dtype != ENTWINE_F32) ||
       (c.out_dtype != ENTWINE_BF16 && c.out_dtype != ENTWINE_F32))
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "peer_dtype/out_dtype must be BF16 or F32");
@@ -342,6 +344,9 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   const int64_t R = M / P;
   r->bm = c.block_m ? c.block_m : (te ? te->bm : (R % 256 == 0 ? 256 : 128));
   r->bn = c.block_n ? c.block_n : (te ? te->bn : (N % 256 == 0 ? 256 : 128));
+  // W [K][N] is built for 128- and 256-wide blocks: an automatic 384-wide
+  // choice becomes 256.
+  if (r->wkn && !c.block_n && r->bn == 384) r->bn = 256;
   r->tm = c.tile_m ? c.tile_m : 128;
   r->tn = c.tile_n ? c.tile_n : 128;
   // A reserved CU holds one reduction workgroup and nothing else, so the
@@ -376,6 +381,8 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     r->variant = te && te->bm == r->bm && te->bn == r->bn ? te->variant : 0;
   else
     r->variant = c.gemm_variant == ENTWINE_GEMM_BASE ? 0 : c.gemm_variant;
+  // W [K][N] has the base pipeline only.
+  if (r->wkn && r->variant_auto) r->variant = 0;
   if (r->slabs < 0 || (r->slabs > 0 && r->tm % r->slabs != 0))
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "task_slabs must divide tile_m");
   if (c.publish_all != 0 && c.publish_all != 1)
@@ -418,6 +425,9 @@ int prepare(const void* X, const void* W, const void* const* peers, void* out, i
   if ((rc = make_geometry(M, N, P, rs.bm, rs.bn, rs.tm, rs.tn, &g)))
     return fail(rc, "unsupported tile geometry (block %dx%d, tile %dx%d)", rs.bm, rs.bn, rs.tm,
                 rs.tn);
+  if (!gemm_built(rs.bm, rs.bn, rs.variant, rs.wkn != 0))
+    return fail(ENTWINE_ERR_UNSUPPORTED, "the GEMM is not built for %dx%d blocks, pipeline %d, "
+                "W %s", rs.bm, rs.bn, rs.variant, rs.wkn ? "[K][N]" : "[N][K]");
 
   // Pointers: presence, alignment, no aliasing of the output.
   if (!X || !W || !out) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "X, W and out must be non-NULL");
@@ -504,6 +514,7 @@ void fill_args(const Resolved& rs, const Geometry& g, const void* X, const void*
   ga.tn = g.tn;
   ga.outgoing_f32 = rs.peer_f32;
   ga.variant = rs.variant;
+  ga.w_kn = rs.wkn;
   ga.ctl = b.ctl;
   ga.nb = (int32_t)g.NB;
 
@@ -600,7 +611,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   const int slabs_eff = rs.slabs ? rs.slabs : 1;
   int fused_per_cu = 0;
   if (fused) {
-    fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32);
+    fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32, rs.wkn);
     if (fused_per_cu <= 0)
       return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
                   "GEMM variant %d", g.bm, g.bn, rs.variant);
@@ -629,7 +640,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       return fail(ENTWINE_ERR_INVALID_ARGUMENT, "comm_budget %d must equal reducer_cus %d: one "
                   "reduction workgroup per reserved CU", rs.budget, rs.reducer_cus);
     const int half = w->lds_per_cu / 2 + 1024;
-    lds_gemm = std::max(gemm_lds_bytes(g.bm, g.bn, rs.variant), half);
+    lds_gemm = std::max(gemm_lds_bytes(g.bm, g.bn, rs.variant, rs.wkn), half);
     lds_red = std::max(half, w->lds_per_cu - lds_gemm + 1024);
     if (w->lds_per_cu <= 0 || lds_gemm > w->lds_per_block || lds_red > w->lds_per_block)
       return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning needs LDS reservations of "
@@ -644,8 +655,8 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     const int rr = reduce_registers(rs.threads, rs.peer_f32, rs.out_f32);
     auto up8 = [](int v) { return (v + 7) / 8 * 8; };
     auto fits = [&](int variant, int* gr) {
-      *gr = gemm_registers(g.bm, g.bn, variant, /*tickets=*/true);
-      const int gemm_waves_per_simd = (gemm_waves(g.bm, g.bn, variant) + 3) / 4;
+      *gr = gemm_registers(g.bm, g.bn, variant, rs.wkn, /*tickets=*/true);
+      const int gemm_waves_per_simd = (gemm_waves(g.bm, g.bn, variant, rs.wkn) + 3) / 4;
       return gemm_waves_per_simd * up8(*gr) + red_waves_per_simd * up8(rr) <= 512;
     };
     int gr = 0;
@@ -668,7 +679,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   // Blocks resident at once: the window inside which dispatch is XCD-aware.
   int64_t window = 0;
   if (!rs.linear_dispatch) {
-    const int per_cu = gemm_blocks_per_cu(g.bm, g.bn, rs.variant);
+    const int per_cu = gemm_blocks_per_cu(g.bm, g.bn, rs.variant, rs.wkn);
     window = (int64_t)std::max(per_cu, 1) * w->cus;
   }
 
@@ -875,7 +886,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     if (forked) {
       // Static partitioning: one workgroup on each CU not reserved for the
       // reduction.
-      const int per_cu = static_cus ? 1 : std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1);
+      const int per_cu = static_cus ? 1 : std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant, rs.wkn), 1);
       const int gemm_cus = static_cus ? w->cus - rs.reducer_cus : w->cus;
       const int64_t gemm_grid = std::min<int64_t>((int64_t)per_cu * gemm_cus, g.NB);
       // Both kernels' workgroups check out on one count; the last advances
@@ -969,10 +980,10 @@ int run_noalloc(void* scratch, size_t scratch_bytes, const void* X, const void* 
 
   int fused_per_cu = 0;
   if (!sequential) {
-    fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32);
+    fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32, rs.wkn);
     if (fused_per_cu <= 0 && rs.variant_auto && rs.variant != 0) {
       rs.variant = 0;  // same accumulation order, same result
-      fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, 0, rs.peer_f32, rs.out_f32);
+      fused_per_cu = fused_blocks_per_cu(g.bm, g.bn, 0, rs.peer_f32, rs.out_f32, rs.wkn);
     }
     if (fused_per_cu <= 0)
       return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
@@ -981,7 +992,7 @@ int run_noalloc(void* scratch, size_t scratch_bytes, const void* X, const void* 
   const int slabs = rs.slabs ? rs.slabs : 1;
   int64_t window = 0;
   if (!rs.linear_dispatch)
-    window = (int64_t)std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant), 1) * cus;
+    window = (int64_t)std::max(gemm_blocks_per_cu(g.bm, g.bn, rs.variant, rs.wkn), 1) * cus;
 
   // Schedule tables (host-built, cached by key; uploaded into the scratch
   // when the key changes).
@@ -1093,7 +1104,7 @@ void entwine_config_init(entwine_config* cfg) {
   if (!cfg) return;
   std::memset(cfg, 0, sizeof *cfg);
   cfg->struct_size = (int32_t)sizeof *cfg;
-  cfg->w_layout = ENTWINE_W_NK;
+  cfg->w_layout = ENTWINE_W_KN;
   cfg->peer_dtype = ENTWINE_BF16;
   cfg->out_dtype = ENTWINE_BF16;
   cfg->peer_ready = ENTWINE_PEERS_PRESEEDED;

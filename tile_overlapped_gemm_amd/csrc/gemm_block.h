@@ -20,25 +20,30 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
-// Block BM x BN, K stage BK (32 or 64), NS LDS stages, WGM x WGN waves.
-template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2>
+// Block BM x BN, K stage BK (32 or 64), NS LDS stages, WGM x WGN waves; W
+// held [N][K] (K contiguous) or, with WKN, [K][N] (N contiguous).
+template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2, bool WKN = false>
 struct Shape {
   static constexpr int kWaves = WGM * WGN;
   static constexpr int kThreads = 64 * kWaves;
   static constexpr int kWavesN = WGN;
-  static constexpr int kRow = BK * 2;                 // bytes per slab row
+  static constexpr bool kWKN = WKN;
+  static constexpr int kRow = BK * 2;                 // bytes per X slab row (and W's, [N][K])
+  static constexpr int kRowB = WKN ? BN * 2 : kRow;   // bytes per W slab row in LDS
   static constexpr int kRowsPerLoad = 1024 / kRow;    // rows per 1 KiB wave load
   static constexpr int kLanesPerRow = kRow / 16;
   static constexpr int kKS = BK / 16;                 // MFMA K steps per stage
   static constexpr int kWM = BM / WGM, kWN = BN / WGN;  // wave sub-block
   static constexpr int kMT = kWM / 32, kNT = kWN / 32;
-  static constexpr int kA = BM * kRow, kB = BN * kRow;  // stage slabs
+  static constexpr int kA = BM * kRow, kB = BN * BK * 2;  // stage slabs
   static constexpr int kStage = kA + kB;
   static constexpr int kLds = NS * kStage;
   static constexpr int kLoadsA = BM / (kWaves * kRowsPerLoad);  // per wave per stage
-  static constexpr int kLoadsB = BN / (kWaves * kRowsPerLoad);
-  static_assert(kLoadsA * kWaves * kRowsPerLoad == BM && kLoadsB * kWaves * kRowsPerLoad == BN,
+  static constexpr int kLoadsB = kB / (kWaves * 1024);
+  static_assert(kLoadsA * kWaves * kRowsPerLoad == BM && kLoadsB * kWaves * 1024 == kB,
                 "slab rows must split evenly over the waves");
+  static_assert(!WKN || (1024 % kRowB == 0 && kRowB >= 256 && BK == 64),
+                "[K][N] W slabs: whole rows per 1 KiB wave load, 16-chunk swizzle groups");
   static_assert(kWaves % 2 == 0, "load groups keep the row parity of the swizzle");
   static constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(kKS % 2 == 0, "fragment double buffer needs an even K-step count");
@@ -78,42 +83,66 @@ __device__ __forceinline__ bf16x8 lds_frag(const char* p) {
   return *reinterpret_cast<const bf16x8*>(p);
 }
 
-// One stage of global->LDS copies for this wave: load group o = wave + 4j of
-// X's slab, then of W's.  voff is the lane's byte offset (row and swizzled
-// chunk); soffset adds the group's rows and the stage's K offset.
+// Per-lane operand offsets of one block.  Loads: the lane's byte offset in
+// the X and W slabs of a K stage and the step between its load groups, and
+// the bytes W advances per K stage.  Fragments: LDS offsets of the lane's X
+// fragment per K step and of its W fragment (per K step with W [N][K]; per
+// 32-column fragment with W [K][N], whose K steps are fixed offsets).
 template <class S>
-__device__ __forceinline__ void issue_stage(__amdgpu_buffer_rsrc_t ra, __amdgpu_buffer_rsrc_t rb,
-                                            char* lds, int voff, int group_step, int kbyte,
-                                            int wave) {
-#pragma unroll
-  for (int j = 0; j < S::kLoadsA; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + S::kWaves * j) * 1024),
-                                             16, voff, j * group_step + kbyte, 0, 0);
-#pragma unroll
-  for (int j = 0; j < S::kLoadsB; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (lds_ptr_t)(lds + S::kA + (wave + S::kWaves * j) * 1024), 16, voff,
-        j * group_step + kbyte, 0, 0);
+struct Lanes {
+  int voff_a, step_a;
+  int voff_b, step_b, stage_b;
+  int a_off[S::kKS];
+  int b_off[S::kWKN ? S::kNT : S::kKS];
+};
+
+// One stage's global->LDS copies for this wave: X's slab (PART 1), W's
+// (PART 2) or both (3), load group wave + kWaves*j, 1 KiB each; voffset is the
+// lane's swizzled source, soffset the group and the stage.
+// One 16-byte-per-lane buffer load into LDS (lane l's bytes land at
+// lds + 16 l).  With W [K][N] the loads are issued through inline assembly:
+// the compiler then does not track them, which it otherwise does by waiting
+// for every outstanding vector memory operation before each transposing LDS
+// read (it cannot tell that the read and the loads touch different buffers),
+// stalling every K stage on its own prefetch.  The loads have no result
+// registers; the pipeline's stage barriers wait for them explicitly
+// (s_waitcnt vmcnt), as for the compiler-issued form.
+template <bool ASM>
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t r, char* lds, int voff,
+                                           int soff) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  if constexpr (ASM) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)(lds_ptr_t)lds;
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(m0), "v"(voff), "s"(r), "s"(soff)
+                 : "memory", "m0");
+  } else {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_ptr_t)lds, 16, voff, soff, 0, 0);
+  }
+#endif
 }
 
-// The X or the W half of issue_stage alone.
 template <class S>
-__device__ __forceinline__ void issue_x(__amdgpu_buffer_rsrc_t ra, char* lds, int voff,
-                                        int group_step, int kbyte, int wave) {
+struct Copy {
+  template <int PART = 3>
+  __device__ static __forceinline__ void stage(__amdgpu_buffer_rsrc_t ra,
+                                               __amdgpu_buffer_rsrc_t rb, char* lds,
+                                               const Lanes<S>& ln, int st, int wave) {
+  if constexpr ((PART & 1) != 0) {
 #pragma unroll
-  for (int j = 0; j < S::kLoadsA; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_ptr_t)(lds + (wave + S::kWaves * j) * 1024),
-                                             16, voff, j * group_step + kbyte, 0, 0);
-}
-template <class S>
-__device__ __forceinline__ void issue_w(__amdgpu_buffer_rsrc_t rb, char* lds, int voff,
-                                        int group_step, int kbyte, int wave) {
+    for (int j = 0; j < S::kLoadsA; ++j)
+      load_lds16<S::kWKN>(ra, lds + (wave + S::kWaves * j) * 1024, ln.voff_a,
+                          j * ln.step_a + st * S::kRow);
+  }
+  if constexpr ((PART & 2) != 0) {
 #pragma unroll
-  for (int j = 0; j < S::kLoadsB; ++j)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(
-        rb, (lds_ptr_t)(lds + S::kA + (wave + S::kWaves * j) * 1024), 16, voff,
-        j * group_step + kbyte, 0, 0);
-}
+    for (int j = 0; j < S::kLoadsB; ++j)
+      load_lds16<S::kWKN>(rb, lds + S::kA + (wave + S::kWaves * j) * 1024, ln.voff_b,
+                          j * ln.step_b + st * ln.stage_b);
+  }
+  }
+};
 
 template <class S>
 struct Frags {
@@ -121,12 +150,32 @@ struct Frags {
   bf16x8 a[S::kMT];  // X fragments (MFMA cols = output rows)
 };
 
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4* lds_i16x4_ptr;
+
+// K step ks of a stage: the lane's W fragments (8 consecutive k of one output
+// column) and X fragments (8 consecutive k of one output row).  With W [K][N]
+// each W fragment is two transposing LDS reads: lanes 4e..4e+3 of each
+// 16-lane group name row k0 + e (16 columns), and lane i receives column i of
+// the four rows, i.e. k0..k0+3 of its own column.
 template <class S>
-__device__ __forceinline__ void read_frags(Frags<S>& f, const char* stage, int a_off, int b_off) {
+__device__ __forceinline__ void read_frags(Frags<S>& f, const char* stage, const Lanes<S>& ln,
+                                           int ks) {
+  if constexpr (S::kWKN) {
 #pragma unroll
-  for (int j = 0; j < S::kNT; ++j) f.b[j] = lds_frag(stage + S::kA + b_off + j * 32 * S::kRow);
+    for (int j = 0; j < S::kNT; ++j) {
+      const char* p = stage + S::kA + ln.b_off[j] + ks * 16 * S::kRowB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 4 * S::kRowB));
+      f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    }
+  } else {
 #pragma unroll
-  for (int i = 0; i < S::kMT; ++i) f.a[i] = lds_frag(stage + a_off + i * 32 * S::kRow);
+    for (int j = 0; j < S::kNT; ++j)
+      f.b[j] = lds_frag(stage + S::kA + ln.b_off[ks] + j * 32 * S::kRow);
+  }
+#pragma unroll
+  for (int i = 0; i < S::kMT; ++i) f.a[i] = lds_frag(stage + ln.a_off[ks] + i * 32 * S::kRow);
 }
 
 template <class S>
@@ -187,15 +236,14 @@ __device__ __forceinline__ void phase_barrier_n(int n) {
 // copies of stage j before barrier 2j.
 template <class S>
 __device__ __forceinline__ void pingpong_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_t ra,
-                                              __amdgpu_buffer_rsrc_t rb, char* smem, int voff,
-                                              int group_step, const int (&a_off)[S::kKS],
-                                              const int (&b_off)[S::kKS], int nk, int wave) {
+                                              __amdgpu_buffer_rsrc_t rb, char* smem,
+                                              const Lanes<S>& ln, int nk, int wave) {
   constexpr int NS = S::kLds / S::kStage, L = NS - 1;
   static_assert(S::kWaves == 8 && NS >= 2 && NS <= 4, "ping-pong: 8 waves, 2 to 4 stages");
   constexpr int PER = S::kLoads;
   static_assert(PER * (L - 1) < 64, "vmcnt range");
   auto issue = [&](int st) {
-    issue_stage<S>(ra, rb, smem + (st % NS) * S::kStage, voff, group_step, st * S::kRow, wave);
+    Copy<S>::template stage<3>(ra, rb, smem + (st % NS) * S::kStage, ln, st, wave);
   };
   const bool g1 = wave >= 4;  // wave-uniform
   // Prologue: stages 0 .. L-1, then stage 0 landed for every wave.
@@ -214,7 +262,7 @@ __device__ __forceinline__ void pingpong_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_
     // Memory phase of stage i.
     if (!g1 && i + L < nk) issue(i + L);
 #pragma unroll
-    for (int ks = 0; ks < S::kKS; ++ks) read_frags<S>(fr[ks], cur, a_off[ks], b_off[ks]);
+    for (int ks = 0; ks < S::kKS; ++ks) read_frags<S>(fr[ks], cur, ln, ks);
     if (g1)
       phase_barrier_n<PER>(min(L - 1, nk - 2 - i));  // barrier 2(i+1): stage i+1 landed
     else
@@ -283,10 +331,10 @@ __device__ int next_block(uint32_t* ctl, int nb, int x, int lane) {
 // `tid` is threadIdx.x (a persistent caller passes it laundered, so that the
 // lane's offsets are recomputed per block rather than held across blocks).  Every thread of the
 // workgroup calls it; it contains workgroup barriers.
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP = false>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP = false, bool WKN = false>
 __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, int bidx,
                                            char* smem, int tid = threadIdx.x) {
-  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+  using S = Shape<BM, BN, BK, NS, WGM, WGN, WKN>;
 
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -300,31 +348,62 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   const int kbytes = K * 2;
 
   // Buffer descriptors bound the block's rows: X rows of partition d from
-  // row0, W rows (output columns) from col0.  Out-of-range rows read 0.
+  // row0 and, with W [N][K], W rows (output columns) from col0; out-of-range
+  // rows read 0.  With W [K][N] the descriptor starts at column col0 and runs
+  // to W's end: columns past N read the next row's values (or 0 past the
+  // end), which only reach output columns that are never stored.
   const int rows_a = min(BM, a.R - row0);
-  const int rows_b = min(BN, a.N - col0);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
       (void*)(a.X + ((int64_t)d * a.R + row0) * K), (short)0, rows_a * kbytes, kRsrcWord3);
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(a.W + (int64_t)col0 * K), (short)0, rows_b * kbytes, kRsrcWord3);
+  const __amdgpu_buffer_rsrc_t rb =
+      WKN ? __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + col0), (short)0,
+                                              (int)(((int64_t)K * a.N - col0) * 2), kRsrcWord3)
+          : __builtin_amdgcn_make_buffer_rsrc((void*)(a.W + (int64_t)col0 * K), (short)0,
+                                              min(BN, a.N - col0) * kbytes, kRsrcWord3);
 
-  // Global source of this lane: row wave*RPL + lane/LPR of each group of
-  // kWaves*RPL rows, logical chunk (lane % LPR) ^ swz(row).
+  Lanes<S> ln;
+  // X (and W [N][K]): row wave*RPL + lane/LPR of each group of kWaves*RPL
+  // rows, logical chunk (lane % LPR) ^ swz(row).
   const int lrow = wave * S::kRowsPerLoad + lane / S::kLanesPerRow;
   const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK>(lrow);
-  const int voff = lrow * kbytes + lchunk * 16;
-  const int group_step = S::kWaves * S::kRowsPerLoad * kbytes;
+  ln.voff_a = lrow * kbytes + lchunk * 16;
+  ln.step_a = S::kWaves * S::kRowsPerLoad * kbytes;
+  if constexpr (WKN) {
+    // W [K][N]: slab row k holds BN columns (CPR 16-byte chunks); the lane
+    // fills physical chunk lane % CPR of row wave*RPL + lane / CPR with the
+    // logical chunk XOR (k & 3) << 2 (k & 3 is the same in every load group).
+    constexpr int CPR = BN / 8, RPL = 64 / CPR;
+    const int krow = wave * RPL + lane / CPR;
+    const int nbytes = a.N * 2;
+    ln.voff_b = krow * nbytes + (((lane % CPR) ^ ((krow & 3) << 2)) << 4);
+    ln.step_b = S::kWaves * RPL * nbytes;
+    ln.stage_b = BK * nbytes;
+  } else {
+    ln.voff_b = ln.voff_a;
+    ln.step_b = ln.step_a;
+    ln.stage_b = S::kRow;
+  }
 
-  // LDS fragment offsets: MFMA lane l reads row (l & 31) of a 32-row group,
-  // logical chunk 2*ks + (l >> 5).
+  // LDS fragment offsets.  X (and W [N][K]): MFMA lane l reads row (l & 31)
+  // of a 32-row group, logical chunk 2*ks + (l >> 5).  W [K][N]: lane l of
+  // 16-lane group g names row 8*(g >> 1) + e (e = (l & 15) >> 2, plus
+  // 16*ks and 4 for the second read) at columns 16*(g & 1) + 4*(l & 3) of the
+  // fragment; the row's XOR is e << 2, as k & 3 == e.
   const int frow = lane & 31;
   const int khalf = lane >> 5;
-  int a_off[S::kKS], b_off[S::kKS];
 #pragma unroll
   for (int ks = 0; ks < S::kKS; ++ks) {
     const int c = ((2 * ks + khalf) ^ swz<BK>(frow)) << 4;
-    a_off[ks] = (wm * S::kWM + frow) * S::kRow + c;
-    b_off[ks] = (wn * S::kWN + frow) * S::kRow + c;
+    ln.a_off[ks] = (wm * S::kWM + frow) * S::kRow + c;
+    if constexpr (!WKN) ln.b_off[ks] = (wn * S::kWN + frow) * S::kRow + c;
+  }
+  if constexpr (WKN) {
+    const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+#pragma unroll
+    for (int j = 0; j < S::kNT; ++j) {
+      const int n = wn * S::kWN + 32 * j + 16 * (g & 1) + 4 * q;
+      ln.b_off[j] = (8 * (g >> 1) + e) * S::kRowB + (((n >> 3) ^ (e << 2)) << 4) + (q & 1) * 8;
+    }
   }
 
   Acc<S> acc;
@@ -337,22 +416,20 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
 
   const int nk = K / BK;
   if constexpr (PP) {
-    pingpong_loop<S>(acc, ra, rb, smem, voff, group_step, a_off, b_off, nk, wave);
+    pingpong_loop<S>(acc, ra, rb, smem, ln, nk, wave);
   } else {
   // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, then stage NS-1.
 #pragma unroll
   for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) issue_stage<S>(ra, rb, smem + s * S::kStage, voff, group_step, s * S::kRow, wave);
+    if (s < nk) Copy<S>::template stage<3>(ra, rb, smem + s * S::kStage, ln, s, wave);
   if (nk >= NS - 1)
     stage_barrier<S::kLoads * (NS - 2)>();
   else
     stage_barrier<0>();
-  if (NS - 1 < nk)
-    issue_stage<S>(ra, rb, smem + (NS - 1) * S::kStage, voff, group_step, (NS - 1) * S::kRow,
-                   wave);
+  if (NS - 1 < nk) Copy<S>::template stage<3>(ra, rb, smem + (NS - 1) * S::kStage, ln, NS - 1, wave);
 
   Frags<S> f0, f1;
-  read_frags<S>(f0, smem, a_off[0], b_off[0]);
+  read_frags<S>(f0, smem, ln, 0);
 
   // Stage kt + NS is loaded in two halves: X's slab right after the barrier
   // that frees its buffer, W's after the next stage's first MFMAs, so that
@@ -364,17 +441,16 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
     const char* cur = smem + buf * S::kStage;
 #pragma unroll
     for (int ks = 0; ks + 1 < S::kKS; ks += 2) {
-      read_frags<S>(f1, cur, a_off[ks + 1], b_off[ks + 1]);
+      read_frags<S>(f1, cur, ln, ks + 1);
       mfma_step<S>(acc, f0);
       if (ks == 0 && pending_w >= 0) {
         // The buffer of stage pending_w is not `cur`: it was freed by the
         // previous barrier.
-        issue_w<S>(rb, smem + (pending_w % NS) * S::kStage, voff, group_step,
-                   pending_w * S::kRow, wave);
+        Copy<S>::template stage<2>(ra, rb, smem + (pending_w % NS) * S::kStage, ln, pending_w, wave);
         pending_w = -1;
       }
       if (ks + 2 < S::kKS) {
-        read_frags<S>(f0, cur, a_off[ks + 2], b_off[ks + 2]);
+        read_frags<S>(f0, cur, ln, ks + 2);
         mfma_step<S>(acc, f1);
       }
     }
@@ -386,10 +462,10 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
       else
         stage_barrier<0>();
       if (kt + NS < nk) {
-        issue_x<S>(ra, smem + buf * S::kStage, voff, group_step, (kt + NS) * S::kRow, wave);
+        Copy<S>::template stage<1>(ra, rb, smem + buf * S::kStage, ln, kt + NS, wave);
         pending_w = kt + NS;
       }
-      read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, a_off[0], b_off[0]);
+      read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, ln, 0);
     }
     mfma_step<S>(acc, f1);
   }

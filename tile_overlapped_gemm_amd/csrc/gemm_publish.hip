@@ -57,10 +57,10 @@
 namespace entwine {
 namespace {
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
-  gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(
+  gemm_block<BM, BN, BK, NS, WGM, WGN, PP, WKN>(
       a, reinterpret_cast<const int4*>(a.blocks)[blockIdx.x], (int)blockIdx.x, smem);
 }
 
@@ -69,7 +69,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_publish_kernel(GemmArg
 // schedule's reduction workgroups: a CU shared with one runs its blocks more
 // slowly and simply takes fewer of them, where a fixed block-to-workgroup
 // deal would make the whole GEMM wait for the slowest such CU.
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs a) {
   extern __shared__ __attribute__((aligned(1024))) char smem[];
   // Thread 0's pick; slots alternate, and the next write to a slot comes
@@ -94,7 +94,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs
     // reduction workgroup on a CU.
     int ltid = tid;
     asm volatile("" : "+v"(ltid));
-    gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(a, reinterpret_cast<const int4*>(a.blocks)[b], b,
+    gemm_block<BM, BN, BK, NS, WGM, WGN, PP, WKN>(a, reinterpret_cast<const int4*>(a.blocks)[b], b,
                                              smem, ltid);
   }
   // Check-out.  The last GEMM workgroup (every other one has taken its last
@@ -114,103 +114,113 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_ticket_kernel(GemmArgs
   }
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 hipError_t launch_shape(const GemmArgs& a, int num_blocks, hipStream_t s) {
-  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+  using S = Shape<BM, BN, BK, NS, WGM, WGN, WKN>;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, S::kLds);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
-  gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<num_blocks, S::kThreads, S::kLds, s>>>(a);
+  gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN><<<num_blocks, S::kThreads, S::kLds, s>>>(a);
   return hipGetLastError();
 }
 
 // lds_min: LDS bytes each workgroup reserves at least (the pipeline uses the
 // first S::kLds of them); a reservation above half of a CU's LDS keeps every
 // workgroup alone on its CU.
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 hipError_t launch_tickets(const GemmArgs& a, int grid, int lds_min, hipStream_t s) {
-  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+  using S = Shape<BM, BN, BK, NS, WGM, WGN, WKN>;
   const int lds = lds_min > S::kLds ? lds_min : S::kLds;
   static int attr_bytes = 0;
   if (lds > attr_bytes) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
     attr_bytes = lds;
   }
-  gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP><<<grid, S::kThreads, lds, s>>>(a);
+  gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN><<<grid, S::kThreads, lds, s>>>(a);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 int occupancy_of() {
-  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
+  using S = Shape<BM, BN, BK, NS, WGM, WGN, WKN>;
   int n = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(
-          &n, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>, S::kThreads,
+          &n, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN>, S::kThreads,
           S::kLds) != hipSuccess)
     return 0;
   return n;
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 int regs_of() {
   hipFuncAttributes at{};
-  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP>) !=
+  if (hipFuncGetAttributes(&at, (const void*)gemm_publish_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN>) !=
       hipSuccess)
     return 0;
   return at.numRegs;
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
 int ticket_regs_of() {
   hipFuncAttributes at{};
-  if (hipFuncGetAttributes(&at, (const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP>) !=
+  if (hipFuncGetAttributes(&at, (const void*)gemm_ticket_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN>) !=
       hipSuccess)
     return 0;
   return at.numRegs;
 }
 
-// The kernel instance for a block shape and variant, handed to `f` as a
-// template functor call f.template run<BM, BN, BK, NS, WGM, WGN, PP>() (PP: the
-// ping-pong main loop).
+// The kernel instance for a block shape, variant and W layout, handed to `f`
+// as a template functor call f.template run<BM, BN, BK, NS, WGM, WGN, PP, WKN>()
+// (PP: the ping-pong main loop; WKN: W held [K][N]).  W [K][N] is built for
+// the base pipeline of the 128- and 256-wide shapes.
 template <class F>
-auto with_instance(int bm, int bn, int variant, F&& f) -> decltype(f.template run<128, 128, 64, 2, 2, 2, false>()) {
+auto with_instance(int bm, int bn, int variant, bool wkn,
+                   F&& f) -> decltype(f.template run<128, 128, 64, 2, 2, 2, false, false>()) {
+  if (wkn) {
+    if (variant != 0) return f.template run<0, 0, 0, 0, 0, 0, false, false>();
+    if (bm == 128 && bn == 128) return f.template run<128, 128, 64, 2, 2, 2, false, true>();
+    if (bm == 128 && bn == 256) return f.template run<128, 256, 64, 2, 2, 4, false, true>();
+    if (bm == 256 && bn == 128) return f.template run<256, 128, 64, 2, 4, 2, false, true>();
+    if (bm == 256 && bn == 256) return f.template run<256, 256, 64, 2, 2, 4, false, true>();
+    return f.template run<0, 0, 0, 0, 0, 0, false, false>();
+  }
   if (bm == 128 && bn == 128) {
-    if (variant == 3) return f.template run<128, 128, 64, 2, 2, 4, false>();
-    return f.template run<128, 128, 64, 2, 2, 2, false>();
+    if (variant == 3) return f.template run<128, 128, 64, 2, 2, 4, false, false>();
+    return f.template run<128, 128, 64, 2, 2, 2, false, false>();
   }
   if (bm == 128 && bn == 256) {
-    if (variant == 3) return f.template run<128, 256, 64, 2, 2, 2, false>();
-    return f.template run<128, 256, 64, 2, 2, 4, false>();
+    if (variant == 3) return f.template run<128, 256, 64, 2, 2, 2, false, false>();
+    return f.template run<128, 256, 64, 2, 2, 4, false, false>();
   }
-  if (bm == 128 && bn == 384) return f.template run<128, 384, 64, 2, 2, 4, false>();
+  if (bm == 128 && bn == 384) return f.template run<128, 384, 64, 2, 2, 4, false, false>();
   if (bm == 256 && bn == 128) {
-    if (variant == 3) return f.template run<256, 128, 64, 2, 2, 2, false>();
-    return f.template run<256, 128, 64, 2, 4, 2, false>();
+    if (variant == 3) return f.template run<256, 128, 64, 2, 2, 2, false, false>();
+    return f.template run<256, 128, 64, 2, 4, 2, false, false>();
   }
   if (bm == 256 && bn == 256) {
-    if (variant == 1) return f.template run<256, 256, 32, 4, 2, 2, false>();
-    if (variant == 2) return f.template run<256, 256, 32, 3, 2, 2, false>();
-    if (variant == 3) return f.template run<256, 256, 64, 2, 2, 2, false>();
-    if (variant == 4) return f.template run<256, 256, 64, 2, 2, 4, true>();
-    return f.template run<256, 256, 64, 2, 2, 4, false>();
+    if (variant == 1) return f.template run<256, 256, 32, 4, 2, 2, false, false>();
+    if (variant == 2) return f.template run<256, 256, 32, 3, 2, 2, false, false>();
+    if (variant == 3) return f.template run<256, 256, 64, 2, 2, 2, false, false>();
+    if (variant == 4) return f.template run<256, 256, 64, 2, 2, 4, true, false>();
+    return f.template run<256, 256, 64, 2, 2, 4, false, false>();
   }
-  return f.template run<0, 0, 0, 0, 0, 0, false>();
+  return f.template run<0, 0, 0, 0, 0, 0, false, false>();
 }
 
 struct Launch {
   const GemmArgs& a;
   int num_blocks;
   hipStream_t s;
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
   hipError_t run() {
     if constexpr (BM == 0) return hipErrorInvalidValue;
-    else return launch_shape<BM, BN, BK, NS, WGM, WGN, PP>(a, num_blocks, s);
+    else return launch_shape<BM, BN, BK, NS, WGM, WGN, PP, WKN>(a, num_blocks, s);
   }
 };
 struct LaunchTickets {
@@ -218,65 +228,71 @@ struct LaunchTickets {
   int grid;
   int lds_min;
   hipStream_t s;
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
   hipError_t run() {
     if constexpr (BM == 0) return hipErrorInvalidValue;
-    else return launch_tickets<BM, BN, BK, NS, WGM, WGN, PP>(a, grid, lds_min, s);
+    else return launch_tickets<BM, BN, BK, NS, WGM, WGN, PP, WKN>(a, grid, lds_min, s);
   }
 };
 struct LdsBytes {
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
   int run() {
     if constexpr (BM == 0) return 0;
-    else return Shape<BM, BN, BK, NS, WGM, WGN>::kLds;
+    else return Shape<BM, BN, BK, NS, WGM, WGN, WKN>::kLds;
   }
 };
 struct Occupancy {
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
   int run() {
     if constexpr (BM == 0) return 0;
-    else return occupancy_of<BM, BN, BK, NS, WGM, WGN, PP>();
+    else return occupancy_of<BM, BN, BK, NS, WGM, WGN, PP, WKN>();
   }
 };
 struct Registers {
   bool tickets;
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
   int run() {
     if constexpr (BM == 0) return 0;
-    else if (tickets) return ticket_regs_of<BM, BN, BK, NS, WGM, WGN, PP>();
-    else return regs_of<BM, BN, BK, NS, WGM, WGN, PP>();
+    else if (tickets) return ticket_regs_of<BM, BN, BK, NS, WGM, WGN, PP, WKN>();
+    else return regs_of<BM, BN, BK, NS, WGM, WGN, PP, WKN>();
   }
 };
 
 }  // namespace
 
-int gemm_registers(int bm, int bn, int variant, bool tickets) {
-  return with_instance(bm, bn, variant, Registers{tickets});
+int gemm_registers(int bm, int bn, int variant, bool wkn, bool tickets) {
+  return with_instance(bm, bn, variant, wkn, Registers{tickets});
 }
 
-int gemm_blocks_per_cu(int bm, int bn, int variant) {
-  return with_instance(bm, bn, variant, Occupancy{});
+int gemm_blocks_per_cu(int bm, int bn, int variant, bool wkn) {
+  return with_instance(bm, bn, variant, wkn, Occupancy{});
 }
 
 struct Waves {
-  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP>
+  template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN>
   int run() { return WGM * WGN; }
 };
 
-int gemm_waves(int bm, int bn, int variant) { return with_instance(bm, bn, variant, Waves{}); }
+int gemm_waves(int bm, int bn, int variant, bool wkn) {
+  return with_instance(bm, bn, variant, wkn, Waves{});
+}
+
+bool gemm_built(int bm, int bn, int variant, bool wkn) {
+  return with_instance(bm, bn, variant, wkn, LdsBytes{}) > 0;
+}
 
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,
                                hipStream_t stream) {
-  return with_instance(bm, bn, a.variant, Launch{a, num_blocks, stream});
+  return with_instance(bm, bn, a.variant, a.w_kn != 0, Launch{a, num_blocks, stream});
 }
 
-int gemm_lds_bytes(int bm, int bn, int variant) {
-  return with_instance(bm, bn, variant, LdsBytes{});
+int gemm_lds_bytes(int bm, int bn, int variant, bool wkn) {
+  return with_instance(bm, bn, variant, wkn, LdsBytes{});
 }
 
 hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipStream_t stream,
                                int lds_min) {
-  return with_instance(bm, bn, a.variant, LaunchTickets{a, grid, lds_min, stream});
+  return with_instance(bm, bn, a.variant, a.w_kn != 0, LaunchTickets{a, grid, lds_min, stream});
 }
 
 }  // namespace entwine

@@ -69,7 +69,8 @@ struct Pending {
   RelChunks<U, PEER_F32, OUT_F32> c;
 };
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool PEER_F32, bool OUT_F32>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN, bool PEER_F32,
+          bool OUT_F32>
 __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedArgs f) {
   constexpr int kThreads = 64 * WGM * WGN;
   // Tasks taken together after the GEMM phase, and the chunks (8 elements)
@@ -122,7 +123,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     if (tid < 64) pick = next_block(ctl, f.nb, xcd, tid);
     const int b = share(pick);
     if (b < 0) break;
-    gemm_block<BM, BN, BK, NS, WGM, WGN, PP>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b], b,
+    gemm_block<BM, BN, BK, NS, WGM, WGN, PP, WKN>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b], b,
                                              smem);
   }
 
@@ -182,10 +183,12 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   if (tid == 0) fused_check_out(ctl, epoch);
 }
 
-template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool PF, bool OF>
+template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN, bool PF, bool OF>
 struct Inst {
-  using S = Shape<BM, BN, BK, NS, WGM, WGN>;
-  static const void* fn() { return (const void*)gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PP, PF, OF>; }
+  using S = Shape<BM, BN, BK, NS, WGM, WGN, WKN>;
+  static const void* fn() {
+    return (const void*)gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN, PF, OF>;
+  }
   static hipError_t launch(const FusedArgs& a, int grid, hipStream_t s) {
     static bool attr_set = false;
     if (!attr_set) {
@@ -193,7 +196,8 @@ struct Inst {
       if (e != hipSuccess) return e;
       attr_set = true;
     }
-    gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PP, PF, OF><<<grid, S::kThreads, S::kLds, s>>>(a);
+    gemm_rs_fused_kernel<BM, BN, BK, NS, WGM, WGN, PP, WKN, PF, OF>
+        <<<grid, S::kThreads, S::kLds, s>>>(a);
     return hipGetLastError();
   }
   static int per_cu() {
@@ -204,26 +208,36 @@ struct Inst {
   }
 };
 
-// f.template run<Inst<...>>() for the instance of a shape, variant and the
-// peer / output dtypes; f.none() if it is not built.
+// f.template run<Inst<...>>() for the instance of a shape, variant, W layout
+// and the peer / output dtypes; f.none() if it is not built.
 template <bool PF, bool OF, class F>
-auto with_shape(int bm, int bn, int variant, F&& f) {
-  if (bm == 128 && bn == 128 && variant == 0) return f.template run<Inst<128, 128, 64, 2, 2, 2, false, PF, OF>>();
-  if (bm == 128 && bn == 256 && variant == 0) return f.template run<Inst<128, 256, 64, 2, 2, 4, false, PF, OF>>();
-  if (bm == 128 && bn == 384 && variant == 0) return f.template run<Inst<128, 384, 64, 2, 2, 4, false, PF, OF>>();
-  if (bm == 256 && bn == 128 && variant == 0) return f.template run<Inst<256, 128, 64, 2, 4, 2, false, PF, OF>>();
-  if (bm == 256 && bn == 256 && variant == 0) return f.template run<Inst<256, 256, 64, 2, 2, 4, false, PF, OF>>();
-  if (bm == 256 && bn == 256 && variant == 3) return f.template run<Inst<256, 256, 64, 2, 2, 2, false, PF, OF>>();
-  if (bm == 256 && bn == 256 && variant == 4) return f.template run<Inst<256, 256, 64, 2, 2, 4, true, PF, OF>>();
+auto with_shape(int bm, int bn, int variant, bool wkn, F&& f) {
+  if (wkn) {
+    if constexpr (PF == OF) {
+      if (variant != 0) return f.none();
+      if (bm == 128 && bn == 128) return f.template run<Inst<128, 128, 64, 2, 2, 2, false, true, PF, OF>>();
+      if (bm == 128 && bn == 256) return f.template run<Inst<128, 256, 64, 2, 2, 4, false, true, PF, OF>>();
+      if (bm == 256 && bn == 128) return f.template run<Inst<256, 128, 64, 2, 4, 2, false, true, PF, OF>>();
+      if (bm == 256 && bn == 256) return f.template run<Inst<256, 256, 64, 2, 2, 4, false, true, PF, OF>>();
+    }
+    return f.none();
+  }
+  if (bm == 128 && bn == 128 && variant == 0) return f.template run<Inst<128, 128, 64, 2, 2, 2, false, false, PF, OF>>();
+  if (bm == 128 && bn == 256 && variant == 0) return f.template run<Inst<128, 256, 64, 2, 2, 4, false, false, PF, OF>>();
+  if (bm == 128 && bn == 384 && variant == 0) return f.template run<Inst<128, 384, 64, 2, 2, 4, false, false, PF, OF>>();
+  if (bm == 256 && bn == 128 && variant == 0) return f.template run<Inst<256, 128, 64, 2, 4, 2, false, false, PF, OF>>();
+  if (bm == 256 && bn == 256 && variant == 0) return f.template run<Inst<256, 256, 64, 2, 2, 4, false, false, PF, OF>>();
+  if (bm == 256 && bn == 256 && variant == 3) return f.template run<Inst<256, 256, 64, 2, 2, 2, false, false, PF, OF>>();
+  if (bm == 256 && bn == 256 && variant == 4) return f.template run<Inst<256, 256, 64, 2, 2, 4, true, false, PF, OF>>();
   return f.none();
 }
 
 template <class F>
-auto with_fused(int bm, int bn, int variant, int peer_f32, int out_f32, F&& f) {
-  if (!peer_f32 && !out_f32) return with_shape<false, false>(bm, bn, variant, f);
-  if (!peer_f32 && out_f32) return with_shape<false, true>(bm, bn, variant, f);
-  if (peer_f32 && !out_f32) return with_shape<true, false>(bm, bn, variant, f);
-  return with_shape<true, true>(bm, bn, variant, f);
+auto with_fused(int bm, int bn, int variant, int peer_f32, int out_f32, bool wkn, F&& f) {
+  if (!peer_f32 && !out_f32) return with_shape<false, false>(bm, bn, variant, wkn, f);
+  if (!peer_f32 && out_f32) return with_shape<false, true>(bm, bn, variant, wkn, f);
+  if (peer_f32 && !out_f32) return with_shape<true, false>(bm, bn, variant, wkn, f);
+  return with_shape<true, true>(bm, bn, variant, wkn, f);
 }
 
 struct FusedLaunch {
@@ -244,11 +258,12 @@ struct FusedOccupancy {
 
 hipError_t launch_gemm_rs_fused(const FusedArgs& a, int bm, int bn, int variant, int peer_f32,
                                 int out_f32, int grid, hipStream_t stream) {
-  return with_fused(bm, bn, variant, peer_f32, out_f32, FusedLaunch{a, grid, stream});
+  return with_fused(bm, bn, variant, peer_f32, out_f32, a.g.w_kn != 0,
+                    FusedLaunch{a, grid, stream});
 }
 
-int fused_blocks_per_cu(int bm, int bn, int variant, int peer_f32, int out_f32) {
-  return with_fused(bm, bn, variant, peer_f32, out_f32, FusedOccupancy{});
+int fused_blocks_per_cu(int bm, int bn, int variant, int peer_f32, int out_f32, bool wkn) {
+  return with_fused(bm, bn, variant, peer_f32, out_f32, wkn, FusedOccupancy{});
 }
 
 }  // namespace entwine

@@ -20,7 +20,7 @@ constexpr int kMaxRanks = 8;
 
 struct GemmArgs {
   const uint16_t* X;        // bf16 [M][K]
-  const uint16_t* W;        // bf16 [N][K]
+  const uint16_t* W;        // bf16 [N][K], or [K][N] when w_kn is set
   float* own;               // fp32 [R][N]: partial of partition `rank`
   void* outgoing;           // peer dtype [M][N]: partials for other partitions
   uint32_t* flags;          // [P][Q] tile flags
@@ -31,6 +31,7 @@ struct GemmArgs {
   int32_t tm, tn;           // reduction tile
   int32_t outgoing_f32;     // outgoing partials in fp32 (else bf16)
   int32_t variant;          // GEMM pipeline variant (0 = default for the shape)
+  int32_t w_kn;             // 1: W is [K][N] (N contiguous); 0: [N][K]
   int32_t publish;          // 0: no flags; 1: release local tiles, mark the rest; 2: release all
   int32_t flag_all;         // 1: every block stores its flags (else only the local ones)
   uint32_t* ctl;            // device control words (see check_out)
@@ -163,15 +164,18 @@ hipError_t launch_gemm_tickets(const GemmArgs& a, int bm, int bn, int grid, hipS
 hipError_t launch_tile_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
                               bool flat, int grid, hipStream_t stream, int lds_bytes = 0);
 
-// Registers per lane (VGPRs + AGPRs) of the kernels a launch would use, for
-// the co-residency check; 0 if unknown.
-int gemm_registers(int bm, int bn, int variant, bool tickets = false);
+// Queries of the GEMM instance for a block shape, pipeline variant and W
+// layout (wkn: W [K][N]).  Registers per lane (VGPRs + AGPRs) of the kernel a
+// launch would use, for the co-residency check (0 if unknown or not built).
+int gemm_registers(int bm, int bn, int variant, bool wkn, bool tickets = false);
 // GEMM workgroups of a block shape resident per CU at once (0 if unknown).
-int gemm_blocks_per_cu(int bm, int bn, int variant);
-// LDS bytes a GEMM workgroup's pipeline uses.
-int gemm_lds_bytes(int bm, int bn, int variant);
+int gemm_blocks_per_cu(int bm, int bn, int variant, bool wkn);
+// LDS bytes a GEMM workgroup's pipeline uses (0 if not built).
+int gemm_lds_bytes(int bm, int bn, int variant, bool wkn);
 // Waves per GEMM workgroup (64 lanes each).
-int gemm_waves(int bm, int bn, int variant);
+int gemm_waves(int bm, int bn, int variant, bool wkn);
+// Whether the instance is built.
+bool gemm_built(int bm, int bn, int variant, bool wkn);
 int reduce_registers(int threads, int peer_f32, int out_f32);
 
 // Zeroes `words` trace slots on `stream` (a kernel, so that a captured graph
@@ -183,11 +187,13 @@ hipError_t launch_trace_reset(uint64_t* trace, int64_t words, hipStream_t stream
 hipError_t launch_rmsnorm(const void* h, const void* gamma, void* y, int rows, int N, float eps,
                           int out_f32, hipStream_t stream);
 
-// Fused kernel instances: the variant-0 pipelines of every block shape and
-// variant 3 of 256 x 256.  Returns hipErrorInvalidValue for other shapes.
+// Fused kernel instances (the layout of W from a.g.w_kn): with W [N][K] the
+// variant-0 pipelines of every block shape and variants 3 and 4 of
+// 256 x 256; with W [K][N] the variant-0 pipelines of the 128- and 256-wide
+// shapes, bf16 or fp32 I/O.  Returns hipErrorInvalidValue for others.
 hipError_t launch_gemm_rs_fused(const FusedArgs& a, int bm, int bn, int variant, int peer_f32,
                                 int out_f32, int grid, hipStream_t stream);
 // Fused workgroups resident per CU (0 if the instance is not built).
-int fused_blocks_per_cu(int bm, int bn, int variant, int peer_f32, int out_f32);
+int fused_blocks_per_cu(int bm, int bn, int variant, int peer_f32, int out_f32, bool wkn);
 
 }  // namespace entwine

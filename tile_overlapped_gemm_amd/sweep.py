@@ -91,9 +91,10 @@ def table_line(w, c: Candidate) -> str:
             f"{c.slabs} {c.schedule} {c.variant}")
 
 
-def pipelines_for(bm: int, bn: int) -> list[int]:
-    """GEMM pipelines worth timing for a block shape (tuning-table numbering)."""
-    return [0, 4] if (bm, bn) == (256, 256) else [0]
+def pipelines_for(bm: int, bn: int, wkn: bool = False) -> list[int]:
+    """GEMM pipelines worth timing for a block shape (tuning-table numbering);
+    with W [K][N] the base pipeline only."""
+    return [0, 4] if (bm, bn) == (256, 256) and not wkn else [0]
 
 
 def budgets_for(q: int, cus: int) -> list[int]:
@@ -109,8 +110,11 @@ def budgets_for(q: int, cus: int) -> list[int]:
     return out
 
 
-def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log=print):
-    """Run stages A-C for one workload on cuda:0; returns the chosen Candidate."""
+def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log=print,
+                     w_layout: str = "kn"):
+    """Run stages A-C for one workload on cuda:0, with W handed over [K][N]
+    ("kn", the library's default) or [N][K] ("nk"); returns the chosen
+    Candidate."""
     import numpy as np
 
     sys.path.insert(0, ROOT)
@@ -125,7 +129,8 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
             return torch.from_numpy(a.view(np.int16)).to(dev).view(torch.bfloat16)
         return torch.from_numpy(a).to(dev)
 
-    Xd, Wd = up(X), up(W)
+    wkn = w_layout == "kn"
+    Xd, Wd = up(X), up(wl.w_as_kn(W) if wkn else W)
     # Peer buffers for every rank's view: the values do not change the timing,
     # so the same P - 1 seeded partials serve whichever rank is local.
     seeded = [up(p) for p in peers if p is not None]
@@ -142,7 +147,8 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     def time_rank(c: Candidate, rank: int):
         kw = dict(block_m=c.bm, block_n=c.bn, tile_m=w.tile, tile_n=w.tile,
                   reducer_threads=c.threads, task_slabs=c.slabs, schedule=c.schedule,
-                  peer_ready=mode, gemm_variant=c.variant or tog.GEMM_BASE)
+                  peer_ready=mode, gemm_variant=c.variant or tog.GEMM_BASE,
+                  w_layout=tog.W_KN if wkn else tog.W_NK)
         if w.fp32_io:
             kw.update(peer_dtype=tog.F32, out_dtype=tog.F32)
         cfg = tog.config(**kw)
@@ -195,13 +201,14 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     t_warm = time_rank(warm, ranks[0]) * 1e-6
     for _ in range(max(1, int(1.0 / max(t_warm * (steps + warmup), 1e-3)))):
         time_rank(warm, ranks[0])
-    blocks = [(bm, bn) for bm, bn in BLOCKS if bm % w.tile == 0 and bn % w.tile == 0]
+    blocks = [(bm, bn) for bm, bn in BLOCKS if bm % w.tile == 0 and bn % w.tile == 0
+              and not (wkn and bn == 384)]
     orders = (tog.ORDER_ROW_MAJOR, tog.ORDER_PARTITION_MAJOR, tog.ORDER_INTERLEAVED,
               tog.ORDER_COL_MAJOR)
     # A: no overlap (every rank takes the same time), and the overlapped
     # schedules per block shape and order
     seq = [run(Candidate(bm, bn, tog.ORDER_INTERLEAVED, 0, variant=v), all_ranks=False)
-           for bm, bn in blocks for v in pipelines_for(bm, bn)]
+           for bm, bn in blocks for v in pipelines_for(bm, bn, wkn)]
     # Candidates timed later in a run measure slightly faster: a second pass
     # in reverse order, keeping each candidate's better time, evens that out
     # between the block shapes and pipelines without overlap.
@@ -213,7 +220,7 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     stage_a = [run(Candidate(bm, bn, order, x0, schedule=s, variant=v))
                for bm, bn in blocks for order in orders
                for s in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED)
-               for v in (pipelines_for(bm, bn) if s == tog.SCHEDULE_FUSED else [0])]
+               for v in (pipelines_for(bm, bn, wkn) if s == tog.SCHEDULE_FUSED else [0])]
     # The overlapped schedules also at the largest budget with four slabs per
     # tile (every CU takes a share of the reduction), interleaved order.
     x_max = min(q * 4, cus - 1)
@@ -251,6 +258,8 @@ def main(argv=None) -> int:
     ap.add_argument("--out", default=os.path.join(PKG, "tuning.txt"))
     ap.add_argument("--steps", type=int, default=60)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--w-layout", default="kn", choices=["kn", "nk"],
+                    help="W handed over [K_local][N] (the default) or [N][K_local]")
     ap.add_argument("--objective", default="symmetric", choices=["symmetric", "preseeded"],
                     help="max over ranks under symmetric peer readiness, or one rank with "
                          "preseeded peers")
@@ -271,12 +280,13 @@ def main(argv=None) -> int:
         w = wl.BY_NAME[name]
         print(f"workload {w.name}: M={w.M} N={w.N} K={w.K} P={w.P}", flush=True)
         best = measure_workload(w, tog, torch, args.steps, args.warmup, args.objective,
-                                log=lambda s: print(s, flush=True))
+                                log=lambda s: print(s, flush=True), w_layout=args.w_layout)
         lines.append(f"# {w.name}: median {best.us:.1f} us per step\n{table_line(w, best)}")
     header = [
         "# Offline tuning table read by entwine_load_tuning(): the AUTO choices per shape,",
         "# written by tile_overlapped_gemm_amd/sweep.py from the median latency of",
-        f"# graph-replayed steps on one MI355X (objective: {args.objective}).",
+        f"# graph-replayed steps on one MI355X (objective: {args.objective}, W "
+        f"{'[K_local][N]' if args.w_layout == 'kn' else '[N][K_local]'}).",
         "# M N K_local P tile_order comm_budget block_m block_n reducer_threads task_slabs schedule "
         "gemm_variant",
     ]
