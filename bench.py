@@ -217,8 +217,6 @@ def main() -> int:
         bm, bn = (int(v) for v in args.block.lower().split("x"))
     else:
         bm, bn = tuned.get("bm", 256), tuned.get("bn", 256)
-        if wkn and bn == 384:
-            bn = 256  # W [K][N] is built for 128- and 256-wide blocks (as the library's AUTO)
     order = (tog.ORDERS[args.order] if args.order != "auto"
              else tuned.get("order", tog.ORDER_INTERLEAVED))
     budget = args.budget if args.budget >= 0 else tuned.get("budget", 32)
@@ -411,12 +409,11 @@ def main() -> int:
 
     log("kernels alone")
     g_alone = timed_graph(rep(lambda: call(0, cfg_gemm)), ksteps, 3, False)["ms_per_step"] / reps
-    # The same GEMM with W in the other layout (base pipeline, the other
-    # layout's allowed block shape), for the layout comparison.
+    # The same GEMM with W in the other layout (base pipeline), for the layout
+    # comparison.
     other = not wkn
     Wd_other = up(W_kn if other else W)
-    bn_other = 256 if (other and bn == 384) else bn
-    cfg_gemm_other = tog.config(**dict(cfg_kw, stages=tog.STAGES_GEMM, block_n=bn_other,
+    cfg_gemm_other = tog.config(**dict(cfg_kw, stages=tog.STAGES_GEMM,
                                        w_layout=tog.W_KN if other else tog.W_NK,
                                        gemm_variant=tog.GEMM_BASE if other else args.gemm_variant))
 

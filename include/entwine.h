@@ -183,9 +183,9 @@ typedef struct entwine_config {
   int32_t tile_n;          /* reduction tile cols TN: 0 = 128, else 64 or 128; BN % TN == 0 */
   int32_t reducer_threads; /* b: 128, 256 or 512 (Sec. 4.3); 0 = the tuning table's entry,
                               else 256, and 512 under static CU partitioning (reducer_cus) */
-  int32_t w_layout;        /* ENTWINE_W_KN (default) or ENTWINE_W_NK.  Blocks for W [K][N]:
-                              128 or 256 wide (an automatic 384-wide choice becomes 256),
-                              base pipeline; same output bits as W [N][K] */
+  int32_t w_layout;        /* ENTWINE_W_KN (default) or ENTWINE_W_NK.  W [K][N] is built for
+                              the base pipeline of every block shape; same output bits as
+                              W [N][K] */
   int32_t peer_dtype;      /* ENTWINE_BF16 or ENTWINE_F32: peers and outgoing contributions */
   int32_t out_dtype;       /* ENTWINE_BF16 or ENTWINE_F32 */
   int32_t peer_ready;      /* ENTWINE_PEERS_PRESEEDED or ENTWINE_PEERS_SYMMETRIC */
@@ -230,6 +230,11 @@ typedef struct entwine_config {
                               order with the reductions: the sender's side of a push-based
                               transfer, on one GPU.  Overlapped schedules only (comm_budget 0:
                               ENTWINE_ERR_UNSUPPORTED); releases every tile like publish_all */
+  int32_t poll_backoff;    /* a waiting reduction workgroup polls its flags with pauses that
+                              start at 128 clock cycles and double up to poll_backoff x 128
+                              (0 = the default, 16; 1 = a fixed 128-cycle pause; at most 4096).
+                              Longer pauses load the memory system less while the GEMM runs
+                              and notice a released tile later */
 } entwine_config;
 
 void entwine_config_init(entwine_config* cfg);

@@ -108,10 +108,10 @@ def test_config_validation(lib, field, value, status):
 
 
 def test_w_kn_builds(lib):
-    """W [K_local][N] (the default) is built for the base pipeline with 128- and
-    256-wide blocks; other explicit choices are refused before any device call."""
+    """W [K_local][N] (the default) is built for the base pipeline of every
+    block shape; the other pipelines are refused before any device call."""
     assert tog.config().w_layout == tog.W_KN
-    for kw in (dict(block_m=128, block_n=384), dict(block_m=256, block_n=256, gemm_variant=4),
+    for kw in (dict(block_m=256, block_n=256, gemm_variant=4),
                dict(block_m=256, block_n=256, gemm_variant=3)):
         assert call(cfg=tog.config(w_layout=tog.W_KN, **kw)) == tog.ENTWINE_ERR_UNSUPPORTED
         assert lib.entwine_last_error_message().decode()
@@ -119,6 +119,8 @@ def test_w_kn_builds(lib):
     # first device call in a process without a GPU)
     for kw in (dict(block_m=128, block_n=384), dict(block_m=256, block_n=256, gemm_variant=4)):
         assert call(cfg=tog.config(w_layout=tog.W_NK, **kw)) != tog.ENTWINE_ERR_UNSUPPORTED
+    assert call(cfg=tog.config(w_layout=tog.W_KN, block_m=128, block_n=384)) != \
+        tog.ENTWINE_ERR_UNSUPPORTED
 
 
 def test_block_shapes(lib):

@@ -78,6 +78,7 @@ class entwine_config(ctypes.Structure):
         ("schedule", ctypes.c_int32),
         ("reducer_cus", ctypes.c_int32),
         ("push_outgoing", ctypes.c_int32),
+        ("poll_backoff", ctypes.c_int32),
     ]
 
 

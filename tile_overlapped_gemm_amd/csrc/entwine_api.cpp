@@ -305,7 +305,7 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
 struct Resolved {
   int bm, bn, tm, tn, threads, order, budget, peer_f32, out_f32, peer_ready, release_group,
       slabs, withhold_tile, variant, variant_auto, publish_all, stages, linear_dispatch, schedule,
-      reducer_cus, push, wkn;
+      reducer_cus, push, wkn, poll_backoff;
   uint32_t timeout_ms;
 };
 
@@ -344,9 +344,6 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
   const int64_t R = M / P;
   r->bm = c.block_m ? c.block_m : (te ? te->bm : (R % 256 == 0 ? 256 : 128));
   r->bn = c.block_n ? c.block_n : (te ? te->bn : (N % 256 == 0 ? 256 : 128));
-  // W [K][N] is built for 128- and 256-wide blocks: an automatic 384-wide
-  // choice becomes 256.
-  if (r->wkn && !c.block_n && r->bn == 384) r->bn = 256;
   r->tm = c.tile_m ? c.tile_m : 128;
   r->tn = c.tile_n ? c.tile_n : 128;
   // A reserved CU holds one reduction workgroup and nothing else, so the
@@ -395,6 +392,9 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "schedule %d out of range", r->schedule);
   r->reducer_cus = c.reducer_cus;
   r->push = c.push_outgoing;
+  if (c.poll_backoff < 0 || c.poll_backoff > 4096)
+    return fail(ENTWINE_ERR_INVALID_ARGUMENT, "poll_backoff %d outside [0, 4096]", c.poll_backoff);
+  r->poll_backoff = c.poll_backoff ? c.poll_backoff : 16;
   if (c.push_outgoing != 0 && c.push_outgoing != 1)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "push_outgoing must be 0 or 1");
   if (c.reducer_cus < 0)
@@ -542,6 +542,7 @@ void fill_args(const Resolved& rs, const Geometry& g, const void* X, const void*
   ra.staging = rs.push ? b.staging : nullptr;
   ra.residual = chain ? chain->residual : nullptr;
   ra.task_list = b.task_list;
+  ra.nap_max = rs.poll_backoff;
   // Preseeded peers (and the residual) exist before the call: a task may load
   // them before its wait.  Under symmetric readiness they count as produced
   // with the tiles, so they are read only after the wait.

@@ -42,8 +42,11 @@ struct Shape {
   static constexpr int kLoadsB = kB / (kWaves * 1024);
   static_assert(kLoadsA * kWaves * kRowsPerLoad == BM && kLoadsB * kWaves * 1024 == kB,
                 "slab rows must split evenly over the waves");
-  static_assert(!WKN || (1024 % kRowB == 0 && kRowB >= 256 && BK == 64),
-                "[K][N] W slabs: whole rows per 1 KiB wave load, 16-chunk swizzle groups");
+  static_assert(!WKN || (kRowB % 256 == 0 && BK == 64),
+                "[K][N] W slabs: rows of whole 16-chunk swizzle groups");
+  // W [K][N] rows that a 1 KiB wave load does not cover whole (384 wide):
+  // each load group of the lane has a source offset of its own.
+  static constexpr bool kPerLoadB = WKN && (1024 % kRowB != 0);
   static_assert(kWaves % 2 == 0, "load groups keep the row parity of the swizzle");
   static constexpr int kLoads = kLoadsA + kLoadsB;
   static_assert(kKS % 2 == 0, "fragment double buffer needs an even K-step count");
@@ -92,6 +95,7 @@ template <class S>
 struct Lanes {
   int voff_a, step_a;
   int voff_b, step_b, stage_b;
+  int voff_bj[S::kPerLoadB ? S::kLoadsB : 1];  // per load group (kPerLoadB)
   int a_off[S::kKS];
   int b_off[S::kWKN ? S::kNT : S::kKS];
 };
@@ -137,9 +141,14 @@ struct Copy {
   }
   if constexpr ((PART & 2) != 0) {
 #pragma unroll
-    for (int j = 0; j < S::kLoadsB; ++j)
-      load_lds16<S::kWKN>(rb, lds + S::kA + (wave + S::kWaves * j) * 1024, ln.voff_b,
-                          j * ln.step_b + st * ln.stage_b);
+    for (int j = 0; j < S::kLoadsB; ++j) {
+      if constexpr (S::kPerLoadB)
+        load_lds16<true>(rb, lds + S::kA + (wave + S::kWaves * j) * 1024, ln.voff_bj[j],
+                         st * ln.stage_b);
+      else
+        load_lds16<S::kWKN>(rb, lds + S::kA + (wave + S::kWaves * j) * 1024, ln.voff_b,
+                            j * ln.step_b + st * ln.stage_b);
+    }
   }
   }
 };
@@ -368,7 +377,23 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK>(lrow);
   ln.voff_a = lrow * kbytes + lchunk * 16;
   ln.step_a = S::kWaves * S::kRowsPerLoad * kbytes;
-  if constexpr (WKN) {
+  if constexpr (S::kPerLoadB) {
+    // W [K][N], rows not a divisor of 1 KiB: the lane's 16 bytes of load
+    // group wave + kWaves*j land at slab byte q = 1024*(wave + kWaves*j) +
+    // 16*lane, i.e. row q / kRowB, physical chunk (q % kRowB) / 16, which
+    // holds the logical chunk XOR (row & 3) << 2.
+    constexpr int CPR = BN / 8;
+    const int nbytes = a.N * 2;
+#pragma unroll
+    for (int j = 0; j < S::kLoadsB; ++j) {
+      const int q = (wave + S::kWaves * j) * 64 + lane;  // 16-byte chunk of the slab
+      const int krow = q / CPR, pc = q % CPR;
+      ln.voff_bj[j] = krow * nbytes + ((pc ^ ((krow & 3) << 2)) << 4);
+    }
+    ln.voff_b = 0;
+    ln.step_b = 0;
+    ln.stage_b = BK * nbytes;
+  } else if constexpr (WKN) {
     // W [K][N]: slab row k holds BN columns (CPR 16-byte chunks); the lane
     // fills physical chunk lane % CPR of row wave*RPL + lane / CPR with the
     // logical chunk XOR (k & 3) << 2 (k & 3 is the same in every load group).

@@ -178,7 +178,7 @@ int ticket_regs_of() {
 // The kernel instance for a block shape, variant and W layout, handed to `f`
 // as a template functor call f.template run<BM, BN, BK, NS, WGM, WGN, PP, WKN>()
 // (PP: the ping-pong main loop; WKN: W held [K][N]).  W [K][N] is built for
-// the base pipeline of the 128- and 256-wide shapes.
+// the base pipeline of every block shape.
 template <class F>
 auto with_instance(int bm, int bn, int variant, bool wkn,
                    F&& f) -> decltype(f.template run<128, 128, 64, 2, 2, 2, false, false>()) {
@@ -188,6 +188,7 @@ auto with_instance(int bm, int bn, int variant, bool wkn,
     if (bm == 128 && bn == 256) return f.template run<128, 256, 64, 2, 2, 4, false, true>();
     if (bm == 256 && bn == 128) return f.template run<256, 128, 64, 2, 4, 2, false, true>();
     if (bm == 256 && bn == 256) return f.template run<256, 256, 64, 2, 2, 4, false, true>();
+    if (bm == 128 && bn == 384) return f.template run<128, 384, 64, 2, 2, 4, false, true>();
     return f.template run<0, 0, 0, 0, 0, 0, false, false>();
   }
   if (bm == 128 && bn == 128) {

@@ -219,6 +219,7 @@ auto with_shape(int bm, int bn, int variant, bool wkn, F&& f) {
       if (bm == 128 && bn == 256) return f.template run<Inst<128, 256, 64, 2, 2, 4, false, true, PF, OF>>();
       if (bm == 256 && bn == 128) return f.template run<Inst<256, 128, 64, 2, 4, 2, false, true, PF, OF>>();
       if (bm == 256 && bn == 256) return f.template run<Inst<256, 256, 64, 2, 2, 4, false, true, PF, OF>>();
+      if (bm == 128 && bn == 384) return f.template run<Inst<128, 384, 64, 2, 2, 4, false, true, PF, OF>>();
     }
     return f.none();
   }

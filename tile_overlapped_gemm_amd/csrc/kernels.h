@@ -79,6 +79,9 @@ struct ReduceArgs {
   int32_t prefetch;
   uint64_t* trace;                  // measurement stamps [2][grid] (see trace_at), nullptr: off
   int32_t checkout_total;           // as GemmArgs::checkout_total
+  // A waiting workgroup's pause between two polls starts at 128 clock cycles
+  // and doubles up to nap_max x 128 cycles.
+  int32_t nap_max;
 };
 
 // Epochs.  A flag is ready when it equals the call's epoch, which every
@@ -189,8 +192,8 @@ hipError_t launch_rmsnorm(const void* h, const void* gamma, void* y, int rows, i
 
 // Fused kernel instances (the layout of W from a.g.w_kn): with W [N][K] the
 // variant-0 pipelines of every block shape and variants 3 and 4 of
-// 256 x 256; with W [K][N] the variant-0 pipelines of the 128- and 256-wide
-// shapes, bf16 or fp32 I/O.  Returns hipErrorInvalidValue for others.
+// 256 x 256; with W [K][N] the variant-0 pipelines of every shape, bf16 or
+// fp32 I/O.  Returns hipErrorInvalidValue for others.
 hipError_t launch_gemm_rs_fused(const FusedArgs& a, int bm, int bn, int variant, int peer_f32,
                                 int out_f32, int grid, hipStream_t stream);
 // Fused workgroups resident per CU (0 if the instance is not built).

@@ -205,9 +205,13 @@ __device__ __forceinline__ const uint32_t* wait_flag(const ReduceArgs& a, int d,
 
 // Wave 0 waits until the flag each lane watches (f; nullptr: none) equals
 // `epoch`.  The flag and the sticky error word are loaded together, so one
-// poll costs one memory round trip.
+// poll costs one memory round trip.  The pause between polls doubles from
+// 128 cycles up to a.nap_max x 128: workgroups that wait long (a tile the
+// GEMM produces late) then poll rarely, which keeps their device-coherent
+// loads out of the way of the GEMM sharing the memory system.
 __device__ bool wait_flags(const ReduceArgs& a, uint32_t epoch, const uint32_t* f, int lane) {
   const uint64_t start = wall_clock64();
+  int nap = 1;
   while (true) {
     const uint32_t v = f ? __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : epoch;
     const int32_t err = __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -219,7 +223,8 @@ __device__ bool wait_flags(const ReduceArgs& a, uint32_t epoch, const uint32_t* 
                            __HIP_MEMORY_SCOPE_AGENT);
       return false;
     }
-    __builtin_amdgcn_s_sleep(2);
+    for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(2);
+    nap = min(2 * nap, a.nap_max);
   }
   // No acquire: the tile's data is read with device-coherent loads, issued
   // after this wait (program order, then the workgroup barrier that follows).

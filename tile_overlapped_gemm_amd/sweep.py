@@ -201,8 +201,7 @@ def measure_workload(w, tog, torch, steps: int, warmup: int, objective: str, log
     t_warm = time_rank(warm, ranks[0]) * 1e-6
     for _ in range(max(1, int(1.0 / max(t_warm * (steps + warmup), 1e-3)))):
         time_rank(warm, ranks[0])
-    blocks = [(bm, bn) for bm, bn in BLOCKS if bm % w.tile == 0 and bn % w.tile == 0
-              and not (wkn and bn == 384)]
+    blocks = [(bm, bn) for bm, bn in BLOCKS if bm % w.tile == 0 and bn % w.tile == 0]
     orders = (tog.ORDER_ROW_MAJOR, tog.ORDER_PARTITION_MAJOR, tog.ORDER_INTERLEAVED,
               tog.ORDER_COL_MAJOR)
     # A: no overlap (every rank takes the same time), and the overlapped
