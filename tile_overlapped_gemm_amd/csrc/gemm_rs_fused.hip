@@ -102,60 +102,48 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   // Start of a reduction task: the slab's chunk placement and, when
   // r.prefetch is set, the loads of the inputs that were complete before the
   // call (the peers, the residual) for this thread's first kU chunks.  A
-  // send task loads only after its wait.
-  auto begin = [&](int task, auto& p) {
+  // send task loads only after its wait.  `lt` is the thread index.
+  auto begin = [&](int task, auto& p, int lt) {
     const TaskRef k = task_ref(r, task);
     if (k.d != r.rank) return;  // a send task loads after its wait
     p.s = slab_of(r, k.t, k.slab);
-    place_rel<std::remove_reference_t<decltype(p)>::kChunks, kThreads>(p.s, tid, p.c);
+    place_rel<std::remove_reference_t<decltype(p)>::kChunks, kThreads>(p.s, lt, p.c);
     if (r.prefetch) load_inputs_rel(r, slab_io<PEER_F32, OUT_F32>(r, p.s.e0), p.c);
   };
 
-  // Workgroup w < x (the budget) owns tasks w, w + x, ... of the
-  // production-ordered list (Sec. 3.1).  A static deal needs no per-task
-  // atomic: one ticket counter shared by all workers serialized them.
-  int task = (int)blockIdx.x < f.workers ? (int)blockIdx.x : r.ntasks;
-  const int xcd = xcd_id();
-  while (true) {
-    // GEMM blocks until every list is exhausted.  The block's descriptors
-    // and output addresses stay in scalar registers.
-    int pick = 0;
-    if (tid < 64) pick = next_block(ctl, f.nb, xcd, tid);
-    const int b = share(pick);
-    if (b < 0) break;
-    gemm_block<BM, BN, BK, NS, WGM, WGN, PP, WKN>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b], b,
-                                             smem);
-  }
-
-  // Every block has been taken: the remaining tasks, kB at a time.  A task
-  // waits only for blocks that running workgroups have taken.  The tasks'
-  // prefetches are issued, wave 0 polls all their flags at once (16 lanes
-  // per task), and all their own-partial loads are in flight before any is
-  // summed: each memory round trip serves kB tasks.
+  // One batch: tasks t0, t0 + x, ..., t0 + (kB - 1) x of the
+  // production-ordered list (x = the workers).  The peers' loads are issued
+  // first (with preseeded peers), wave 0 then waits for all the tasks' flags
+  // at once (16 lanes per task), and all their own-partial loads are in
+  // flight before any is summed, so each memory round trip serves kB tasks.
+  // False when the watchdog or the sticky error ended the wait.
   static_assert(kB * 16 <= 64, "16 wait lanes per task");
-  const bool worker = task < r.ntasks;  // uniform
-  if (r.trace && worker && tid == 0) trace_at(r.trace, blockIdx.x);
-  while (task < r.ntasks) {
+  const int x = f.workers;
+  auto batch = [&](int t0) -> bool {
+    // The thread index, laundered so that the batch recomputes its offsets
+    // rather than keeping the GEMM's in registers (fewer registers in all).
+    int lt = tid;
+    asm volatile("" : "+v"(lt));
     Pending<kU, PEER_F32, OUT_F32> p[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b)
-      if (task + b * f.workers < r.ntasks) begin(task + b * f.workers, p[b]);
+      if (t0 + b * x < r.ntasks) begin(t0 + b * x, p[b], lt);
     int ok = 1;
-    if (tid < 64) {
-      const int tw = task + (tid >> 4) * f.workers;
+    if (lt < 64) {
+      const int tw = t0 + (lt >> 4) * x;
       const uint32_t* fl = nullptr;
       if (tw < r.ntasks) {
         const TaskRef k = task_ref(r, tw);
-        fl = wait_flag(r, k.d, k.t, tid & 15);
+        fl = wait_flag(r, k.d, k.t, lt & 15);
       }
-      ok = wait_flags(r, epoch, fl, tid);
+      ok = wait_flags(r, epoch, fl, lt);
     }
     // The flag waits are ordered before every wave's reads of the tiles.
-    if (!share(ok)) break;  // the watchdog or the sticky error ended the wait
+    if (!share(ok)) return false;
     Raw8<true> own[kB][kU];
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int t = task + b * f.workers;
+      const int t = t0 + b * x;
       if (t < r.ntasks && task_ref(r, t).d == r.rank) {
         const SlabIO io = slab_io<PEER_F32, OUT_F32>(r, p[b].s.e0);
         if (!r.prefetch) load_inputs_rel(r, io, p[b].c);
@@ -164,17 +152,47 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     }
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
-      const int t = task + b * f.workers;
+      const int t = t0 + b * x;
       if (t >= r.ntasks) break;
       const TaskRef k = task_ref(r, t);
       if (k.d == r.rank) {
         sum_store_rel(r, slab_io<PEER_F32, OUT_F32>(r, p[b].s.e0), p[b].c, own[b]);
-        reduce_slab<kThreads, kU, PEER_F32, OUT_F32>(r, p[b].s, tid, kU * kThreads);
+        reduce_slab<kThreads, kU, PEER_F32, OUT_F32>(r, p[b].s, lt, kU * kThreads);
       } else {
-        push_slab<kThreads, PEER_F32>(r, k.d, k.t, k.slab, tid);
+        push_slab<kThreads, PEER_F32>(r, k.d, k.t, k.slab, lt);
       }
     }
-    task += kB * f.workers;
+    return true;
+  };
+
+  // GEMM blocks until every list is exhausted (tickets of this XCD first).
+  // The thread index is laundered: the block's lane offsets are recomputed
+  // per block rather than held in registers into the reduction phase.
+  const int xcd = xcd_id();
+  while (true) {
+    int pick = 0;
+    if (tid < 64) pick = next_block(ctl, f.nb, xcd, tid);
+    const int b = share(pick);
+    if (b < 0) break;
+    int ltid = tid;
+    asm volatile("" : "+v"(ltid));
+    gemm_block<BM, BN, BK, NS, WGM, WGN, PP, WKN>(f.g, reinterpret_cast<const int4*>(f.g.blocks)[b],
+                                                  b, smem, ltid);
+  }
+
+  // Every block has been taken: workgroup w < x (the budget) owns tasks w,
+  // w + x, ... of the production-ordered list (Sec. 3.1), kB at a time.  A
+  // task waits only for blocks that running workgroups have taken.  A static
+  // deal needs no per-task atomic: one ticket counter shared by all workers
+  // serialized them.  (Reducing released tasks between GEMM blocks instead
+  // was measured: each batch holds its CU at memory latency, and the GEMM
+  // ended later by more than the whole reduction takes on its own.)
+  int task = (int)blockIdx.x < x ? (int)blockIdx.x : r.ntasks;
+  const bool worker = task < r.ntasks;  // uniform
+  if (r.trace && worker && tid == 0) trace_at(r.trace, blockIdx.x);
+  while (task < r.ntasks) {
+    if (!batch(task)) break;  // the watchdog or the sticky error ended the wait
+    task += kB * x;
   }
   if (r.trace && worker) {  // uniform: every wave's stores issued
     __syncthreads();
