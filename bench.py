@@ -275,7 +275,18 @@ def main() -> int:
         tog.gemm_rs_rmsnorm(Xd, Wd, pd, res_d, gamma_d, 1e-5, h_buf, y_buf, w.P, w.rank, order, b,
                             cfg=cfg, stream=stream)
 
+    def settle_clocks(seconds=1.0):
+        """About a second of a library bf16 GEMM (kernels of other names in a
+        trace), so that the GPU's clocks have ramped before what is measured."""
+        a = torch.randn((8192, 8192), dtype=torch.bfloat16, device=dev)
+        t_end = time.perf_counter() + seconds
+        while time.perf_counter() < t_end:
+            for _ in range(4):
+                torch.matmul(a, a)
+            torch.cuda.synchronize()
+
     if args.profile:
+        settle_clocks()
         pc = (tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS,
                                 reducer_cus=args.reducer_cus,
                                 reducer_threads=args.threads)) if args.reducer_cus else cfg)
@@ -430,6 +441,14 @@ def main() -> int:
                          False)["ms_per_step"]
     r_cold = max(t_both - t_scrub, 1e-6)
     del scrub
+    # For scale: a library GEMM of the same shape (hipBLASLt through
+    # torch.matmul; X [M][K] times W [K][N], bf16 out), which does only the
+    # GEMM part of the step.
+    Wt = Wd if wkn else Wd.t().contiguous()
+    lib_out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
+    lib_gemm = timed_graph(rep(lambda: torch.matmul(Xd, Wt, out=lib_out)), ksteps, 3,
+                           False)["ms_per_step"] / reps
+    del Wt, lib_out
 
     # The step's kernels, from HIP events recorded on each kernel's own stream
     # around eager calls: GEMM and reduction (sequential: one after the other;
@@ -594,6 +613,7 @@ def main() -> int:
                                 "latency_us_per_rank": per_rank,
                                 "speedup_vs_sequential": sq["ms_per_step"] * 1e3 / max(per_rank)},
         "gemm_alone_us": g_alone * 1e3,
+        "library_gemm_us": lib_gemm * 1e3,
         "gemm_alone_us_by_w_layout": {("[K_local][N]" if wkn else "[N][K_local]"): g_alone * 1e3,
                                       ("[N][K_local]" if wkn else "[K_local][N]"):
                                           g_alone_other * 1e3},
