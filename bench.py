@@ -62,6 +62,7 @@ KERNEL_SOURCES = {
     "gemm_publish": ["kernels.h", "gemm_block.h", "gemm_publish.hip"],
     "gemm_rs_fused": ["kernels.h", "gemm_block.h", "reduce_task.h", "gemm_rs_fused.hip"],
     "flat_reduce": ["kernels.h", "reduce_task.h", "tile_reduce.hip"],
+    "rmsnorm_rows": ["kernels.h", "rmsnorm.hip"],
 }
 
 
