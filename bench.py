@@ -161,6 +161,9 @@ def main() -> int:
                     help="only run --warmup + --steps eager calls (for rocprofv3), print nothing")
     ap.add_argument("--chain", action="store_true",
                     help="with --profile: the calls run the layer chain (residual + RMSNorm)")
+    ap.add_argument("--stage", default="all", choices=["all", "gemm", "reduce"],
+                    help="with --profile: run one kernel of the step alone (the reduction alone "
+                         "with --budget x runs x workgroups without waits)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -291,12 +294,15 @@ def main() -> int:
         pc = (tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS,
                                 reducer_cus=args.reducer_cus,
                                 reducer_threads=args.threads)) if args.reducer_cus else cfg)
+        if args.stage != "all":
+            pc = tog.config(**dict(cfg_kw, stages=tog.STAGES_GEMM if args.stage == "gemm"
+                                   else tog.STAGES_REDUCE))
         for _ in range(args.warmup + args.steps):
             chain(budget) if args.chain else call(budget, pc)
         stream.synchronize()
         check_status("in the profiled calls")
         log(f"profiled {args.warmup + args.steps} calls: {kind}, block {bm}x{bn}, order {order}, "
-            f"budget {budget}")
+            f"budget {budget}, stage {args.stage}")
         return 0
 
     def graph_of(body):
@@ -442,6 +448,16 @@ def main() -> int:
                          False)["ms_per_step"]
     r_cold = max(t_both - t_scrub, 1e-6)
     del scrub
+    # The Fig. 12 analogue (Sec. 5.4.2): the tiled reduction alone (no waits,
+    # warm caches) with x workgroups, x from 1 to the largest budget: how its
+    # bandwidth grows with the resources given to communication.
+    cfg_red_x = tog.config(**dict(cfg_kw, stages=tog.STAGES_REDUCE, task_slabs=ov_slabs))
+    red_by_x = {}
+    for x in (1, 2, 4, 8, 16, 32, 64, 128, 192, cus - 1):
+        n = 1 if x < 32 else reps
+        red_by_x[x] = timed_graph(lambda x=x, n=n: [call(x, cfg_red_x) for _ in range(n)],
+                                  4 if x < 32 else ksteps, 1, False)["ms_per_step"] / n
+    check_status("in the reduction-bandwidth legs")
     # For scale: a library GEMM of the same shape (hipBLASLt through
     # torch.matmul; X [M][K] times W [K][N], bf16 out), which does only the
     # GEMM part of the step.
@@ -634,6 +650,9 @@ def main() -> int:
             "pct_hbm_peak_cold": 100.0 * gbps(r_cold) / HBM_PEAK_GBPS,
             "tiled_at_budget_us": r_tile * 1e3,
             "tiled_at_budget_gbps": gbps(r_tile),
+            # Fig. 12 analogue: GB/s of the reduction alone against its
+            # workgroup count x (task_slabs as in the overlapped legs)
+            "gbps_by_workgroups": {str(x): gbps(t) for x, t in red_by_x.items()},
             # the reduction's HBM bytes over its traced span, waits included
             "hbm_gbps_step": gbps(max(tr_step["reduce_span_us"], 1e-3) * 1e-3),
             "hbm_gbps_overlapped_streams": gbps(max(tr_streams["reduce_span_us"], 1e-3) * 1e-3),
