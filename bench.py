@@ -457,6 +457,13 @@ def main() -> int:
         n = 1 if x < 32 else reps
         red_by_x[x] = timed_graph(lambda x=x, n=n: [call(x, cfg_red_x) for _ in range(n)],
                                   4 if x < 32 else ksteps, 1, False)["ms_per_step"] / n
+    # ... and at the largest x with each workgroup size b (Sec. 4.3).
+    red_by_b = {}
+    for b_thr in (128, 256, 512):
+        cb = tog.config(**dict(cfg_kw, stages=tog.STAGES_REDUCE, task_slabs=ov_slabs,
+                               reducer_threads=b_thr))
+        red_by_b[b_thr] = timed_graph(rep(lambda cb=cb: call(cus - 1, cb)), ksteps, 3,
+                                      False)["ms_per_step"] / reps
     check_status("in the reduction-bandwidth legs")
     # For scale: a library GEMM of the same shape (hipBLASLt through
     # torch.matmul; X [M][K] times W [K][N], bf16 out), which does only the
@@ -606,6 +613,9 @@ def main() -> int:
         "latency_us_p10_p90": [st["p10_ms"] * 1e3, st["p90_ms"] * 1e3],
         "latency_us_back_to_back": st["back_to_back_ms"] * 1e3,
         "pct_bf16_peak": 100.0 * tflops / BF16_PEAK_TFLOPS,
+        # the end-to-end roofline: every workload here is MFMA-bound, so the
+        # lower bound is the GEMM's FLOP at the bf16 peak
+        "fraction_of_roofline": (flops / (BF16_PEAK_TFLOPS * 1e12)) / (st["ms_per_step"] * 1e-3),
         "sequential": lat(sq),
         "speedup_vs_sequential": sq["ms_per_step"] / st["ms_per_step"],
         "overlapped": {"budget": ov_budget, "task_slabs": ov_slabs,
@@ -635,6 +645,9 @@ def main() -> int:
                                       ("[N][K_local]" if wkn else "[K_local][N]"):
                                           g_alone_other * 1e3},
         "gemm_alone_tflops": flops / (g_alone * 1e-3) / 1e12,
+        # the GEMM inside the two-stream overlapped step (device trace: first
+        # block's start to the last block's end)
+        "gemm_in_overlap_tflops": flops / (max(tr_streams["gemm_end_us"], 1e-3) * 1e-6) / 1e12,
         "step_kernels_us": ({"fused": k_gemm * 1e3} if kind == "fused"
                             else {"gemm": k_gemm * 1e3, "reduction": k_red * 1e3}),
         "overlap_efficiency": g_alone / st["ms_per_step"],
@@ -653,6 +666,8 @@ def main() -> int:
             # Fig. 12 analogue: GB/s of the reduction alone against its
             # workgroup count x (task_slabs as in the overlapped legs)
             "gbps_by_workgroups": {str(x): gbps(t) for x, t in red_by_x.items()},
+            f"gbps_by_threads_at_{cus - 1}_workgroups": {str(b): gbps(t)
+                                                         for b, t in red_by_b.items()},
             # the reduction's HBM bytes over its traced span, waits included
             "hbm_gbps_step": gbps(max(tr_step["reduce_span_us"], 1e-3) * 1e-3),
             "hbm_gbps_overlapped_streams": gbps(max(tr_streams["reduce_span_us"], 1e-3) * 1e-3),

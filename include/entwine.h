@@ -265,14 +265,18 @@ int entwine_gemm_rs_ex(const void* X, const void* W, const void* const* peer_par
  *                                tile flags exceed 131072;
  *     ENTWINE_ERR_UNSUPPORTED    schedule STREAMS, reducer_cus > 0, a
  *                                measurement stage, or entwine_timing /
- *                                entwine_trace switched on.
+ *                                entwine_trace switched on;
+ *     ENTWINE_ERR_INVALID_ARGUMENT  `stream` is being captured and the call
+ *                                is the first on the GPU (it initialises the
+ *                                array) or needs new schedule tables (below).
  *   Sharing: every call on a GPU uses that GPU's one array, which keeps the
  *   last call's contents.  Calls on one stream are ordered; calls that
  *   overlap on one GPU (other streams, other host threads' streams) race on
  *   the array and give undefined results.  A call whose shape or schedule
  *   differs from the previous no-alloc call's on the GPU copies the new
- *   schedule tables into the array and synchronizes `stream`, so it cannot be
- *   captured into a graph; a repeat of the previous call's shape can.
+ *   schedule tables into the array and synchronizes `stream`, so it is
+ *   refused under graph capture; a repeat of the previous call's shape and
+ *   schedule can be captured.
  *   A timeout of its reduction is reported by entwine_device_status(stream).
  */
 int entwine_gemm_rs_noalloc(const void* X, const void* W, const void* const* peer_partials,

@@ -2,7 +2,8 @@
 against entwine_gemm_rs_ex with the same arguments, through the C ABI: two
 calls in a row, the second on a smaller input, each bit-identical to the
 allocating entry point, for the sequential and the fused schedules; and the
-refusals (a call beyond the scratch's maximum, the two-stream schedule)."""
+refusals (a call beyond the scratch's maximum, the two-stream schedule); graph capture
+of a repeated call, and the refusal of one that needs new tables."""
 import numpy as np
 import pytest
 import torch
@@ -74,3 +75,44 @@ def test_noalloc_refusals():
                                     torch.cuda.current_stream().cuda_stream,
                                     tog.config(block_m=128, block_n=128))
     assert e.value.status == tog.ENTWINE_ERR_OUT_OF_MEMORY
+
+
+def test_noalloc_under_graph_capture():
+    """A repeat of the previous no-alloc call's shape and schedule can be
+    captured, and every replay equals the eager result; a call that would
+    upload new schedule tables is refused while capturing, before anything
+    is enqueued."""
+    dev = device()
+    cfg = tog.config(block_m=128, block_n=128, schedule=tog.SCHEDULE_FUSED)
+    Xs, Ws, ps = inputs(SMALL, dev)
+    Xb, Wb, pb = inputs(BIG, dev)
+    ref = call(tog.entwine_gemm_rs_noalloc, SMALL, Xs, Ws, ps, 5, cfg)  # tables of SMALL
+    stream = torch.cuda.Stream(dev)
+    out = torch.full((SMALL.rows, SMALL.N), float("nan"), dtype=torch.bfloat16, device=dev)
+
+    def enqueue(w, X, W, pd, o):
+        tog.entwine_gemm_rs_noalloc(X.data_ptr(), W.data_ptr(),
+                                    [None if p is None else p.data_ptr() for p in pd],
+                                    o.data_ptr(), w.M, w.N, w.K, w.P, w.rank,
+                                    tog.ORDER_INTERLEAVED, 5, stream.cuda_stream, cfg)
+
+    print("case noalloc capture: refused table upload", flush=True)
+    big_out = torch.empty((BIG.rows, BIG.N), dtype=torch.bfloat16, device=dev)
+    g_bad = torch.cuda.CUDAGraph()
+    with pytest.raises(tog.EntwineError) as e:
+        with torch.cuda.graph(g_bad, stream=stream):
+            enqueue(BIG, Xb, Wb, pb, big_out)
+    assert e.value.status == tog.ENTWINE_ERR_INVALID_ARGUMENT
+    del g_bad
+    print("case noalloc capture: repeat of the previous shape, three replays", flush=True)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        enqueue(SMALL, Xs, Ws, ps, out)
+    for it in range(3):
+        out.fill_(float("nan"))
+        torch.cuda.synchronize()
+        with torch.cuda.stream(stream):
+            g.replay()
+        stream.synchronize()
+        assert tog.entwine_device_status(stream.cuda_stream) == tog.ENTWINE_OK
+        np.testing.assert_array_equal(down(out), ref, err_msg=f"replay {it}")

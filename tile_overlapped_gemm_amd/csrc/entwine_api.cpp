@@ -1043,6 +1043,14 @@ int run_noalloc(void* scratch, size_t scratch_bytes, const void* X, const void* 
 
   char* base = static_cast<char*>(scratch);
   if (!host.empty()) {
+    // The upload is a copy from host memory followed by a synchronization,
+    // neither of which a graph capture may hold.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    HIP_TRY(hipStreamIsCapturing(stream, &cap));
+    if (cap != hipStreamCaptureStatusNone)
+      return fail(ENTWINE_ERR_INVALID_ARGUMENT, "the schedule tables of this shape and "
+                  "configuration are not in the no-alloc scratch: make the same call once "
+                  "outside the graph capture");
     // The previous call's kernels may still read the old tables: the copy is
     // ordered after them on `stream`, and waited for, so that the host source
     // stays valid until the device has it.

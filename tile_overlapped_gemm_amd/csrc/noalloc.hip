@@ -47,6 +47,15 @@ int setup(hipStream_t stream, char** out) {
     return report(ENTWINE_ERR_UNSUPPORTED, "device index beyond the no-alloc scratch table");
   std::lock_guard<std::mutex> lock(g_setup_mu);
   if (!g_ptr[dev]) {
+    // The initialisation is a kernel on `stream`: captured into a graph, it
+    // would reset the epoch at every replay, and flags of the previous replay
+    // would read as ready.  The first call on a device must not be captured.
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(stream, &cap) != hipSuccess)
+      return report(ENTWINE_ERR_HIP, "hipStreamIsCapturing failed");
+    if (cap != hipStreamCaptureStatusNone)
+      return report(ENTWINE_ERR_INVALID_ARGUMENT, "the first no-alloc call on a device sets up "
+                    "its scratch: make it outside a graph capture");
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
       return report(ENTWINE_ERR_HIP, "hipGetSymbolAddress of the no-alloc scratch failed");
