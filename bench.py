@@ -161,6 +161,9 @@ def main() -> int:
                     help="only run --warmup + --steps eager calls (for rocprofv3), print nothing")
     ap.add_argument("--chain", action="store_true",
                     help="with --profile: the calls run the layer chain (residual + RMSNorm)")
+    ap.add_argument("--scrub", type=int, default=0, metavar="MIB",
+                    help="with --profile: fill a MIB-sized buffer before each call, so that the "
+                         "call starts from cold caches (L2 and the 256 MB MALL)")
     ap.add_argument("--stage", default="all", choices=["all", "gemm", "reduce"],
                     help="with --profile: run one kernel of the step alone (the reduction alone "
                          "with --budget x runs x workgroups without waits)")
@@ -297,7 +300,12 @@ def main() -> int:
         if args.stage != "all":
             pc = tog.config(**dict(cfg_kw, stages=tog.STAGES_GEMM if args.stage == "gemm"
                                    else tog.STAGES_REDUCE))
+        scrub_buf = (torch.empty(args.scrub << 20, dtype=torch.uint8, device=dev)
+                     if args.scrub else None)
         for _ in range(args.warmup + args.steps):
+            if scrub_buf is not None:
+                with torch.cuda.stream(stream):
+                    scrub_buf.fill_(1)
             chain(budget) if args.chain else call(budget, pc)
         stream.synchronize()
         check_status("in the profiled calls")
