@@ -341,6 +341,8 @@ def _check_operands(X, W, peers, out, P, rank, cfg):
 
     if not (X.is_cuda and W.is_cuda and out.is_cuda):
         raise ValueError("X, W and out must be device tensors")
+    if W.device != X.device or out.device != X.device:
+        raise ValueError("X, W and out must be on one device")
     if X.dtype != torch.bfloat16 or W.dtype != torch.bfloat16:
         raise TypeError("X and W must be bfloat16")
     for name, t in (("X", X), ("W", W), ("out", out)):
@@ -369,6 +371,8 @@ def _check_operands(X, W, peers, out, P, rank, cfg):
             continue
         if not p.is_cuda or not p.is_contiguous() or p.shape != (M // P, N):
             raise ValueError(f"peer {r} must be a contiguous device tensor of shape {(M // P, N)}")
+        if p.device != X.device:
+            raise ValueError(f"peer {r} must be on X's device")
         if p.dtype != want_peer:
             raise TypeError(f"peer {r} must be {want_peer} for this configuration")
         ptrs.append(p.data_ptr())
