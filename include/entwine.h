@@ -391,6 +391,16 @@ const char* entwine_last_error_message(void);
  * (peer dtype) written by the last call.  Any pointer may be NULL. */
 int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* bytes);
 
+/* The current device's tile flags (for tests of the publication protocol):
+ * the device pointer of the u32 flag array -- flag of tile t of partition d
+ * at d * Q + t, Q the tiles per partition of the last call's tiling, plus one
+ * slot no GEMM ever writes -- its allocated length in words, and the epoch the
+ * next overlapped call will stamp into the flags it publishes (each such
+ * call advances it by one, skipping 0; the sequential schedule publishes no
+ * flags and leaves it).  Synchronizes like entwine_workspace.  Any pointer
+ * may be NULL; ENTWINE_ERR_INVALID_ARGUMENT before any call on the device. */
+int entwine_flags(const void** flags, int64_t* words, uint32_t* epoch);
+
 /* Allocated sizes in bytes of the current device's own-partial, outgoing and
  * staging buffers (for tests that overwrite the workspace between calls, e.g.
  * with a NaN pattern, to show that no call reads data a previous call left:

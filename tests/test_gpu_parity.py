@@ -205,6 +205,53 @@ def test_push_outgoing_copies_every_peer_tile(dev, w):
     assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
 
 
+def _flags(P, Q):
+    ptr, words, epoch = tog.entwine_flags()
+    assert words >= P * Q + 1
+    f = np.empty(P * Q, dtype=np.uint32)
+    assert hip().hipMemcpy(f.ctypes.data, ptr, f.nbytes, 2) == 0
+    return f.reshape(P, Q), epoch
+
+
+def _next_epoch(e):
+    return 1 if e == 0xFFFFFFFF else e + 1
+
+
+def test_flags_hold_the_call_epoch(dev):
+    """The publication protocol's end state (Sec. 4.2; epoch-valued flags):
+    after an overlapped call every flag it publishes holds that call's epoch
+    and the epoch has advanced by one; with publish_all every tile of every
+    partition is flagged; the sequential schedule publishes nothing and
+    leaves the epoch."""
+    w = wl.custom("flags", 1024, 768, 256, 4, rank=1, index=350)
+    X, W = wl.operands(w)
+    peers = wl.peer_partials(w)
+    case = Case(w, X, W, peers, dev)
+    blk = dict(block_m=128, block_n=128)
+    _, _, Q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
+    seq = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
+        print(f"case flags: schedule {sched}", flush=True)
+        _, e0 = _flags(w.P, Q)
+        out = down(case.run(tog.ORDER_INTERLEAVED, 5, schedule=sched, **blk))
+        np.testing.assert_array_equal(out, seq)
+        f, e1 = _flags(w.P, Q)
+        assert e1 == _next_epoch(e0)
+        assert (f[w.rank] == e0).all(), f[w.rank]
+        out = down(case.run(tog.ORDER_INTERLEAVED, 5, schedule=sched, publish_all=1, **blk))
+        np.testing.assert_array_equal(out, seq)
+        f, e2 = _flags(w.P, Q)
+        assert e2 == _next_epoch(e1)
+        assert (f == e1).all(), f
+    print("case flags: sequential", flush=True)
+    f0, e0 = _flags(w.P, Q)
+    out = down(case.run(tog.ORDER_INTERLEAVED, 0, **blk))
+    np.testing.assert_array_equal(out, seq)
+    f1, e1 = _flags(w.P, Q)
+    assert e1 == e0
+    np.testing.assert_array_equal(f1, f0)
+
+
 def test_late_flags_do_not_leak_into_the_next_call(dev):
     """Regression test for the epoch hand-over of the two-stream schedule.  A
     call that releases every tile (publish_all) with preseeded peers stores

@@ -42,7 +42,8 @@ EXPORTS = [
     "entwine_plan_blocks", "entwine_plan_dispatch", "entwine_plan_tiles", "entwine_plan_waits",
     "entwine_plan_task_order", "entwine_plan_tasks",
     "entwine_device_status", "entwine_status_string", "entwine_last_error_message",
-    "entwine_workspace", "entwine_workspace_sizes", "entwine_staging", "entwine_timing",
+    "entwine_workspace", "entwine_workspace_sizes", "entwine_flags", "entwine_staging",
+    "entwine_timing",
     "entwine_timing_read",
     "entwine_trace", "entwine_trace_read", "entwine_load_tuning",
     "entwine_release", "entwine_device_cus",
@@ -124,6 +125,7 @@ def load(path: str = LIB):
         "entwine_last_error_message": ([], ctypes.c_char_p),
         "entwine_workspace": ([ctypes.POINTER(vp), ctypes.POINTER(vp), pi64], i32),
         "entwine_workspace_sizes": ([pi64, pi64, pi64], i32),
+        "entwine_flags": ([ctypes.POINTER(vp), pi64, ctypes.POINTER(ctypes.c_uint32)], i32),
         "entwine_staging": ([ctypes.POINTER(vp), pi64], i32),
         "entwine_timing": ([i32], i32),
         "entwine_timing_read": ([ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double), pi64],
@@ -231,6 +233,13 @@ def entwine_workspace_sizes():
     a, b, c = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int64()
     _check(load().entwine_workspace_sizes(ctypes.byref(a), ctypes.byref(b), ctypes.byref(c)))
     return a.value, b.value, c.value
+
+
+def entwine_flags():
+    """(device pointer, words, next epoch) of the current device's tile flags."""
+    fl, n, ep = ctypes.c_void_p(), ctypes.c_int64(), ctypes.c_uint32()
+    _check(load().entwine_flags(ctypes.byref(fl), ctypes.byref(n), ctypes.byref(ep)))
+    return fl.value, n.value, ep.value
 
 
 def entwine_staging():

@@ -1335,6 +1335,24 @@ int entwine_workspace(const void** own_partial, const void** outgoing, int64_t* 
   return ENTWINE_OK;
 }
 
+int entwine_flags(const void** flags, int64_t* words, uint32_t* epoch) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  int dev = 0;
+  HIP_TRY(hipGetDevice(&dev));
+  auto it = g_ws.find(dev);
+  if (it == g_ws.end()) return fail(ENTWINE_ERR_INVALID_ARGUMENT, "no workspace on this device yet");
+  Workspace* w = it->second.get();
+  HIP_TRY(hipStreamSynchronize(w->s_red));
+  if (w->have_prev) {
+    HIP_TRY(hipEventSynchronize(w->ev_gemm));
+    HIP_TRY(hipEventSynchronize(w->ev_red));
+  }
+  if (flags) *flags = w->flags;
+  if (words) *words = (int64_t)w->flag_count;
+  if (epoch) HIP_TRY(hipMemcpy(epoch, w->ctl + kEpoch, sizeof *epoch, hipMemcpyDeviceToHost));
+  return ENTWINE_OK;
+}
+
 int entwine_workspace_sizes(int64_t* own_bytes, int64_t* outgoing_bytes, int64_t* staging_bytes) {
   std::lock_guard<std::mutex> lock(g_mu);
   int dev = 0;
