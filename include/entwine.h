@@ -128,8 +128,11 @@ enum { ENTWINE_SCHEDULE_AUTO = 0, ENTWINE_SCHEDULE_STREAMS = 1, ENTWINE_SCHEDULE
  *            CUs (ENTWINE_ERR_UNSUPPORTED when requested explicitly).
  *  AUTO (0)  the tuning table's pipeline when its entry names the block shape
  *            in use, else BASE; BASE also replaces a pipeline the two-stream
- *            reduction cannot share CUs with.
- * Other values select BASE. */
+ *            reduction cannot share CUs with.  With W [K_local][N] AUTO is
+ *            always BASE.
+ * Pipelines 1-4 are built for W [N][K_local] only; with W [K_local][N] (the
+ * default layout) BASE is the only one.  A pipeline that is not built for the
+ * block shape and layout in use is refused with ENTWINE_ERR_UNSUPPORTED. */
 enum { ENTWINE_GEMM_AUTO = 0, ENTWINE_GEMM_PINGPONG = 4, ENTWINE_GEMM_BASE = 5 };
 
 /* Release granularity (Sec. 5.3.2): tiles released together. */
