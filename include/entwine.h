@@ -159,7 +159,9 @@ enum { ENTWINE_GEMM_AUTO = 0, ENTWINE_GEMM_PINGPONG = 4, ENTWINE_GEMM_BASE = 5 }
  *                  must not overlap any input.  16-byte aligned.
  *   M, N, K_local  M % P == 0, N % 8 == 0, K_local % 64 == 0, all > 0;
  *                  M*K_local, N*K_local and M*N below 2^31 (W [K_local][N]:
- *                  N*K_local below 2^30).
+ *                  N*K_local below 2^30); K_local <= 2^21 and N <= 2^22 (the
+ *                  kernels' 32-bit buffer offsets).  Beyond any of these:
+ *                  ENTWINE_ERR_UNSUPPORTED.
  *   P, rank        1 <= P <= 8, 0 <= rank < P.
  *   tile_order     ENTWINE_ORDER_* (AUTO = tuning table, else INTERLEAVED).
  *   comm_budget    x >= 1 overlapped (clamped to Q), 0 sequential, -1 AUTO.

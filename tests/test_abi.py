@@ -79,6 +79,8 @@ def call(M=512, N=256, K=128, P=4, rank=0, order=tog.ORDER_INTERLEAVED, budget=4
     (dict(out=FAKE * 2), tog.ENTWINE_ERR_INVALID_ARGUMENT),    # out aliases W
     (dict(out=FAKE * 5), tog.ENTWINE_ERR_INVALID_ARGUMENT),    # out aliases a peer
     (dict(M=1 << 20, K=1 << 12), tog.ENTWINE_ERR_UNSUPPORTED),  # beyond 2^31 elements
+    (dict(M=8, K=(1 << 21) + 64), tog.ENTWINE_ERR_UNSUPPORTED),  # K_local above 2^21
+    (dict(M=8, N=(1 << 22) + 8), tog.ENTWINE_ERR_UNSUPPORTED),   # N above 2^22
 ])
 def test_validation_before_any_device_call(lib, kw, status):
     assert call(**kw) == status

@@ -299,6 +299,12 @@ int check_shape(int64_t M, int64_t N, int64_t K, int P, int rank) {
   const int64_t lim = (int64_t)1 << 31;
   if (M * K >= lim || N * K >= lim || M * N >= lim)
     return fail(ENTWINE_ERR_UNSUPPORTED, "operands beyond 2^31 elements are not built");
+  // The kernels address a block's operand rows, an output strip and a
+  // reduction task's rows through buffer descriptors with 32-bit byte offsets:
+  // 384 rows of K_local bf16 values and 128 rows of N fp32 values must stay
+  // below 2^31 bytes.
+  if (K > ((int64_t)1 << 21) || N > ((int64_t)1 << 22))
+    return fail(ENTWINE_ERR_UNSUPPORTED, "K_local above 2^21 or N above 2^22 is not built");
   return ENTWINE_OK;
 }
 
