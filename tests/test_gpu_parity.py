@@ -252,6 +252,53 @@ def test_flags_hold_the_call_epoch(dev):
     np.testing.assert_array_equal(f1, f0)
 
 
+def test_calls_from_two_host_threads(dev):
+    """Two host threads, each on a stream of its own, make calls of two
+    shapes (the workspace grows between them and both share it), one thread
+    with the two-stream schedule and one with the fused kernel.  The library
+    orders every call after the previous one on the workspace, so every
+    output equals its single-thread result."""
+    import threading
+
+    cases = []
+    for w in (wl.custom("thr_a", 1024, 768, 256, 4, rank=1, index=370),
+              wl.custom("thr_b", 2048, 1024, 512, 8, rank=6, index=371)):
+        X, W = wl.operands(w)
+        peers = wl.peer_partials(w)
+        case = Case(w, X, W, peers, dev)
+        ref = down(case.run(tog.ORDER_INTERLEAVED, 0, block_m=128, block_n=128))
+        cases.append((w, case, ref))
+    errors = []
+
+    def worker(w, case, ref, sched, budget):
+        try:
+            s = torch.cuda.Stream(dev)
+            cfg = case.base_cfg(block_m=128, block_n=128, schedule=sched)
+            outs = []
+            for _ in range(6):
+                out = torch.full((w.rows, w.N), float("nan"), dtype=torch.bfloat16, device=dev)
+                tog.gemm_rs(case.Xd, case.Wd, case.pd, out, w.P, w.rank, tog.ORDER_INTERLEAVED,
+                            budget, cfg=cfg, stream=s)
+                outs.append(out)
+            s.synchronize()
+            for o in outs:
+                np.testing.assert_array_equal(down(o), ref)
+        except Exception as e:  # reported by the main thread
+            errors.append(e)
+
+    print("case two host threads: streams and fused schedules", flush=True)
+    threads = [threading.Thread(target=worker, args=(*cases[0], tog.SCHEDULE_STREAMS, 5)),
+               threading.Thread(target=worker, args=(*cases[1], tog.SCHEDULE_FUSED, 7))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join(timeout=120)
+    assert not any(t.is_alive() for t in threads)
+    torch.cuda.synchronize()
+    assert tog.entwine_device_status(torch.cuda.current_stream().cuda_stream) == tog.ENTWINE_OK
+    assert not errors, errors
+
+
 def test_late_flags_do_not_leak_into_the_next_call(dev):
     """Regression test for the epoch hand-over of the two-stream schedule.  A
     call that releases every tile (publish_all) with preseeded peers stores
