@@ -164,9 +164,14 @@ def main() -> int:
     ap.add_argument("--scrub", type=int, default=0, metavar="MIB",
                     help="with --profile: fill a MIB-sized buffer before each call, so that the "
                          "call starts from cold caches (L2 and the 256 MB MALL)")
-    ap.add_argument("--stage", default="all", choices=["all", "gemm", "reduce"],
+    ap.add_argument("--scrub-mode", default="fill", choices=["fill", "read"],
+                    help="with --scrub: write the buffer (a fill) or only read it (a sum), so "
+                         "that the evicted lines are dirty or clean")
+    ap.add_argument("--stage", default="all", choices=["all", "gemm", "reduce", "copy"],
                     help="with --profile: run one kernel of the step alone (the reduction alone "
-                         "with --budget x runs x workgroups without waits)")
+                         "with --budget x runs x workgroups without waits), or, for scale, the "
+                         "runtime's device copy moving the reduction's bytes (half read, half "
+                         "written)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -297,16 +302,29 @@ def main() -> int:
         pc = (tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_STREAMS,
                                 reducer_cus=args.reducer_cus,
                                 reducer_threads=args.threads)) if args.reducer_cus else cfg)
-        if args.stage != "all":
+        if args.stage in ("gemm", "reduce"):
             pc = tog.config(**dict(cfg_kw, stages=tog.STAGES_GEMM if args.stage == "gemm"
                                    else tog.STAGES_REDUCE))
-        scrub_buf = (torch.empty(args.scrub << 20, dtype=torch.uint8, device=dev)
+        scrub_buf = (torch.empty(args.scrub << 20, dtype=torch.uint8, device=dev).fill_(1)
                      if args.scrub else None)
+        scrub_sum = torch.zeros((), dtype=torch.float32, device=dev)
+        if args.stage == "copy":
+            n_red = w.rows * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
+                                    else (4 + 2 * (w.P - 1) + 2))
+            cp_src = torch.ones(n_red // 2, dtype=torch.uint8, device=dev)
+            cp_dst = torch.empty_like(cp_src)
         for _ in range(args.warmup + args.steps):
             if scrub_buf is not None:
                 with torch.cuda.stream(stream):
-                    scrub_buf.fill_(1)
-            chain(budget) if args.chain else call(budget, pc)
+                    if args.scrub_mode == "fill":
+                        scrub_buf.fill_(1)
+                    else:
+                        torch.sum(scrub_buf.view(torch.float32), 0, out=scrub_sum)
+            if args.stage == "copy":
+                with torch.cuda.stream(stream):
+                    cp_dst.copy_(cp_src)
+            else:
+                chain(budget) if args.chain else call(budget, pc)
         stream.synchronize()
         check_status("in the profiled calls")
         log(f"profiled {args.warmup + args.steps} calls: {kind}, block {bm}x{bn}, order {order}, "
@@ -426,6 +444,10 @@ def main() -> int:
     # cold reduction subtracts a graph holding only the cache scrub.
     reps, ksteps = 10, max(10, min(args.steps, 50))
     scrub = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # The reduction's algorithmic bytes: the local fp32 partial and P-1 peer
+    # contributions read, the output written.
+    red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
+                                       else (4 + 2 * (w.P - 1) + 2))
 
     def rep(body):
         def f():
@@ -455,7 +477,17 @@ def main() -> int:
     t_both = timed_graph(lambda: (scrub.fill_(1), call(0, cfg_red)), ksteps, 3,
                          False)["ms_per_step"]
     r_cold = max(t_both - t_scrub, 1e-6)
-    del scrub
+    # For scale, the runtime's device-to-device copy moving the same bytes
+    # (half read, half written), warm and after the same scrub: what a plain
+    # streaming kernel reaches at this size.
+    cp_src = torch.ones(int(red_bytes) // 2, dtype=torch.uint8, device=dev)
+    cp_dst = torch.empty_like(cp_src)
+    c_warm = timed_graph(rep(lambda: cp_dst.copy_(cp_src)), ksteps, 3,
+                         False)["ms_per_step"] / reps
+    c_both = timed_graph(lambda: (scrub.fill_(1), cp_dst.copy_(cp_src)), ksteps, 3,
+                         False)["ms_per_step"]
+    c_cold = max(c_both - t_scrub, 1e-6)
+    del scrub, cp_src, cp_dst
     # The Fig. 12 analogue (Sec. 5.4.2): the tiled reduction alone (no waits,
     # warm caches) with x workgroups, x from 1 to the largest budget: how its
     # bandwidth grows with the resources given to communication.
@@ -584,8 +616,6 @@ def main() -> int:
                      "budget_response": by_budget}
 
     flops = float(w.flops)
-    red_bytes = float(w.rows) * w.N * ((4 + 4 * (w.P - 1) + 4) if w.fp32_io
-                                       else (4 + 2 * (w.P - 1) + 2))
     # Eq. (4) (Sec. 3.3, 5.4.1): the bandwidth the reduction must sustain to
     # keep up with the GEMM is the remote volume, the P-1 peers'
     # contributions to the rank's partition, over the GEMM's time.
@@ -669,6 +699,9 @@ def main() -> int:
             "flat_cold_us": r_cold * 1e3,
             "flat_cold_gbps": gbps(r_cold),
             "pct_hbm_peak_cold": 100.0 * gbps(r_cold) / HBM_PEAK_GBPS,
+            # the runtime's device copy of the same byte count, same protocol
+            "copy_same_bytes_warm_gbps": gbps(c_warm),
+            "copy_same_bytes_cold_gbps": gbps(c_cold),
             "tiled_at_budget_us": r_tile * 1e3,
             "tiled_at_budget_gbps": gbps(r_tile),
             # Fig. 12 analogue: GB/s of the reduction alone against its
