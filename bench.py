@@ -167,11 +167,12 @@ def main() -> int:
     ap.add_argument("--scrub-mode", default="fill", choices=["fill", "read"],
                     help="with --scrub: write the buffer (a fill) or only read it (a sum), so "
                          "that the evicted lines are dirty or clean")
-    ap.add_argument("--stage", default="all", choices=["all", "gemm", "reduce", "copy"],
+    ap.add_argument("--stage", default="all", choices=["all", "gemm", "reduce", "copy", "library"],
                     help="with --profile: run one kernel of the step alone (the reduction alone "
                          "with --budget x runs x workgroups without waits), or, for scale, the "
                          "runtime's device copy moving the reduction's bytes (half read, half "
-                         "written)")
+                         "written), or a library GEMM of the same shape (torch.matmul, X [M][K] "
+                         "times W [K][N])")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -313,6 +314,9 @@ def main() -> int:
                                     else (4 + 2 * (w.P - 1) + 2))
             cp_src = torch.ones(n_red // 2, dtype=torch.uint8, device=dev)
             cp_dst = torch.empty_like(cp_src)
+        if args.stage == "library":
+            W_lib = Wd if wkn else Wd.t().contiguous()
+            lib_out = torch.empty((w.M, w.N), dtype=torch.bfloat16, device=dev)
         for _ in range(args.warmup + args.steps):
             if scrub_buf is not None:
                 with torch.cuda.stream(stream):
@@ -323,6 +327,9 @@ def main() -> int:
             if args.stage == "copy":
                 with torch.cuda.stream(stream):
                     cp_dst.copy_(cp_src)
+            elif args.stage == "library":
+                with torch.cuda.stream(stream):
+                    torch.matmul(Xd, W_lib, out=lib_out)
             else:
                 chain(budget) if args.chain else call(budget, pc)
         stream.synchronize()

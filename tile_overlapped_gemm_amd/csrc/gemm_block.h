@@ -7,6 +7,8 @@
 // Sec. 3.1 and Sec. 4.2; the MI355X design is described in gemm_publish.hip.
 #pragma once
 
+#include <type_traits>
+
 #include "kernels.h"
 
 namespace entwine {
@@ -20,6 +22,14 @@ typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
 constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
 
+// MFMA tile edge: 16 (v_mfma_f32_16x16x32_bf16, the default) or 32
+// (v_mfma_f32_32x32x16_bf16, built with -DENTWINE_MFMA_EDGE=32 for
+// comparison).  Both have the same peak rate per cycle; the 16 x 16 form runs
+// the GEMM about 6 % faster here.
+#ifndef ENTWINE_MFMA_EDGE
+#define ENTWINE_MFMA_EDGE 16
+#endif
+
 // Block BM x BN, K stage BK (32 or 64), NS LDS stages, WGM x WGN waves; W
 // held [N][K] (K contiguous) or, with WKN, [K][N] (N contiguous).
 template <int BM, int BN, int BK, int NS, int WGM = 2, int WGN = 2, bool WKN = false>
@@ -32,9 +42,13 @@ struct Shape {
   static constexpr int kRowB = WKN ? BN * 2 : kRow;   // bytes per W slab row in LDS
   static constexpr int kRowsPerLoad = 1024 / kRow;    // rows per 1 KiB wave load
   static constexpr int kLanesPerRow = kRow / 16;
-  static constexpr int kKS = BK / 16;                 // MFMA K steps per stage
+  // MFMA tiles: 16 x 16 and 32 deep, or 32 x 32 and 16 deep.
+  static constexpr int kMF = ENTWINE_MFMA_EDGE;
+  static constexpr int kMK = kMF == 16 ? 32 : 16;     // MFMA depth
+  static constexpr int kKS = BK / kMK;                // MFMA K steps per stage
   static constexpr int kWM = BM / WGM, kWN = BN / WGN;  // wave sub-block
-  static constexpr int kMT = kWM / 32, kNT = kWN / 32;
+  static constexpr int kMT = kWM / kMF, kNT = kWN / kMF;
+  static_assert(kMT * kMF == kWM && kNT * kMF == kWN, "wave sub-block of whole MFMA tiles");
   static constexpr int kA = BM * kRow, kB = BN * BK * 2;  // stage slabs
   static constexpr int kStage = kA + kB;
   static constexpr int kLds = NS * kStage;
@@ -49,7 +63,10 @@ struct Shape {
   static constexpr bool kPerLoadB = WKN && (1024 % kRowB != 0);
   static_assert(kWaves % 2 == 0, "load groups keep the row parity of the swizzle");
   static constexpr int kLoads = kLoadsA + kLoadsB;
-  static_assert(kKS % 2 == 0, "fragment double buffer needs an even K-step count");
+  static_assert(kMT % 2 == 0 && kNT % 2 == 0, "tiles split into halves");
+  // W [K][N] with 16 x 16 tiles and a wave sub-block 64 wide: the LDS offsets
+  // of the lane's W fragments differ from fragment 0's by an XOR (see Lanes).
+  static constexpr bool kKnXor = WKN && kMF == 16 && kWN == 64;
   static_assert(kLoads * (NS - 2 > 0 ? NS - 2 : 0) < 64, "vmcnt range");
 };
 
@@ -97,8 +114,25 @@ struct Lanes {
   int voff_b, step_b, stage_b;
   int voff_bj[S::kPerLoadB ? S::kLoadsB : 1];  // per load group (kPerLoadB)
   int a_off[S::kKS];
-  int b_off[S::kWKN ? S::kNT : S::kKS];
+  int b_off[S::kKnXor ? 1 : (S::kWKN ? S::kNT : S::kKS)];
 };
+
+// LDS offset of the lane's W [K][N] fragment j (first read, K step 0).  With
+// kKnXor, fragment j covers 16-byte chunks 2j and 2j + 1 more than fragment
+// 0 within the wave's 64 columns, and the row swizzle touches other chunk
+// bits, so its offset is fragment 0's XOR 32*j.  Fragment 0's offset is
+// laundered where it is used, so that the compiler computes the XORs there
+// rather than holding one register per fragment through the main loop.
+template <class S>
+__device__ __forceinline__ int kn_b_off(const Lanes<S>& ln, int j) {
+  if constexpr (S::kKnXor) {
+    int o = ln.b_off[0];
+    asm volatile("" : "+v"(o));
+    return o ^ (32 * j);
+  } else {
+    return ln.b_off[j];
+  }
+}
 
 // One stage's global->LDS copies for this wave: X's slab (PART 1), W's
 // (PART 2) or both (3), load group wave + kWaves*j, 1 KiB each; voffset is the
@@ -173,7 +207,7 @@ __device__ __forceinline__ void read_frags(Frags<S>& f, const char* stage, const
   if constexpr (S::kWKN) {
 #pragma unroll
     for (int j = 0; j < S::kNT; ++j) {
-      const char* p = stage + S::kA + ln.b_off[j] + ks * 16 * S::kRowB;
+      const char* p = stage + S::kA + kn_b_off<S>(ln, j) + ks * S::kMK * S::kRowB;
       const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
       const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 4 * S::kRowB));
       f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -181,15 +215,18 @@ __device__ __forceinline__ void read_frags(Frags<S>& f, const char* stage, const
   } else {
 #pragma unroll
     for (int j = 0; j < S::kNT; ++j)
-      f.b[j] = lds_frag(stage + S::kA + ln.b_off[ks] + j * 32 * S::kRow);
+      f.b[j] = lds_frag(stage + S::kA + ln.b_off[ks] + j * S::kMF * S::kRow);
   }
 #pragma unroll
-  for (int i = 0; i < S::kMT; ++i) f.a[i] = lds_frag(stage + ln.a_off[ks] + i * 32 * S::kRow);
+  for (int i = 0; i < S::kMT; ++i)
+    f.a[i] = lds_frag(stage + ln.a_off[ks] + i * S::kMF * S::kRow);
 }
 
+// One MFMA tile's accumulators: 4 per lane (16 x 16) or 16 (32 x 32).
 template <class S>
 struct Acc {
-  f32x16 c[S::kMT][S::kNT];
+  typedef typename std::conditional<S::kMF == 16, f32x4, f32x16>::type Tile;
+  Tile c[S::kMT][S::kNT];
 };
 
 template <class S>
@@ -197,8 +234,12 @@ __device__ __forceinline__ void mfma_step(Acc<S>& acc, const Frags<S>& f) {
 #pragma unroll
   for (int i = 0; i < S::kMT; ++i)
 #pragma unroll
-    for (int j = 0; j < S::kNT; ++j)
-      acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
+    for (int j = 0; j < S::kNT; ++j) {
+      if constexpr (S::kMF == 16)
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
+      else
+        acc.c[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.b[j], f.a[i], acc.c[i][j], 0, 0, 0);
+    }
 }
 
 // Workgroup barrier that the compiler may not schedule any instruction across
@@ -286,6 +327,167 @@ __device__ __forceinline__ void pingpong_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_
       phase_barrier_n<PER>(min(L - 1, nk - 2 - i));  // barrier 2(i+1): stage i+1 landed
     else if (i + 1 < nk)
       phase_barrier_lds();
+  }
+}
+
+// Half of a K step's X fragments (MFMA row tiles h*kMT/2 ..) or of its W
+// fragments (column tiles h*kNT/2 ..), for the quarter-step pipeline.
+template <class S>
+struct HalfA {
+  bf16x8 a[S::kMT / 2];
+};
+template <class S>
+struct HalfB {
+  bf16x8 b[S::kNT / 2];
+};
+
+template <class S>
+__device__ __forceinline__ void read_half_a(HalfA<S>& f, const char* stage, const Lanes<S>& ln,
+                                            int ks, int h) {
+#pragma unroll
+  for (int i = 0; i < S::kMT / 2; ++i)
+    f.a[i] = lds_frag(stage + ln.a_off[ks] + (h * S::kMT / 2 + i) * S::kMF * S::kRow);
+}
+
+template <class S>
+__device__ __forceinline__ void read_half_b(HalfB<S>& f, const char* stage, const Lanes<S>& ln,
+                                            int ks, int h) {
+#pragma unroll
+  for (int j = 0; j < S::kNT / 2; ++j) {
+    const int jj = h * S::kNT / 2 + j;
+    if constexpr (S::kWKN) {
+      const char* p = stage + S::kA + kn_b_off<S>(ln, jj) + ks * S::kMK * S::kRowB;
+      const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)p);
+      const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4_ptr)(p + 4 * S::kRowB));
+      f.b[j] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+    } else {
+      f.b[j] = lds_frag(stage + S::kA + ln.b_off[ks] + jj * S::kMF * S::kRow);
+    }
+  }
+}
+
+// The MFMAs of one quarter of a K step: X half HA times W half HB.
+template <class S, int HA, int HB>
+__device__ __forceinline__ void mfma_quarter(Acc<S>& acc, const HalfA<S>& fa, const HalfB<S>& fb) {
+  static_assert(S::kMF == 16, "quarter steps are built for 16 x 16 tiles");
+#pragma unroll
+  for (int i = 0; i < S::kMT / 2; ++i)
+#pragma unroll
+    for (int j = 0; j < S::kNT / 2; ++j) {
+      auto& c = acc.c[HA * S::kMT / 2 + i][HB * S::kNT / 2 + j];
+      c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb.b[j], fa.a[i], c, 0, 0, 0);
+    }
+}
+
+// The base main loop.  Prologue: stages 0 .. NS-2 in flight, wait for stage
+// 0, then stage NS-1.  Stage kt + NS is loaded in two halves: X's slab right
+// after the barrier that frees its buffer, W's after the next stage's first
+// MFMAs, so that the eight waves' loads do not all reach the address units
+// and LDS at once (1.5-2 % on the 4-round shapes).
+//
+// 16 x 16 tiles: each K step runs in four quarters (X half 0 or 1 times W
+// half 0 or 1), and the fragments of a quarter are read while the previous
+// quarter's MFMAs run: W half 1 during quarter 0, X half 1 during quarter 1,
+// the next step's X and W halves 0 after quarter 2 (after the stage barrier
+// at a stage's last step), so four half sets (as many registers as one K
+// step's fragments) are live and each read batch stays within the LDS
+// counter's reach.  Every output tile still accumulates its K steps in order.
+// 32 x 32 tiles: whole K steps of fragments, double-buffered.
+template <class S>
+__device__ __forceinline__ void base_loop(Acc<S>& acc, __amdgpu_buffer_rsrc_t ra,
+                                          __amdgpu_buffer_rsrc_t rb, char* smem,
+                                          const Lanes<S>& ln, int nk, int wave) {
+  constexpr int NS = S::kLds / S::kStage;
+#pragma unroll
+  for (int s = 0; s < NS - 1; ++s)
+    if (s < nk) Copy<S>::template stage<3>(ra, rb, smem + s * S::kStage, ln, s, wave);
+  if (nk >= NS - 1)
+    stage_barrier<S::kLoads * (NS - 2)>();
+  else
+    stage_barrier<0>();
+  if (NS - 1 < nk) Copy<S>::template stage<3>(ra, rb, smem + (NS - 1) * S::kStage, ln, NS - 1, wave);
+
+  // The barrier that ends stage kt: stage kt+1 landed (stages up to kt+NS-1
+  // were issued) and every wave done reading stage kt's buffer, which then
+  // takes X's slab of stage kt+NS.
+  int pending_w = -1;  // stage whose W slab is still to be issued
+  auto hand_over = [&](int kt) {
+    if (kt + NS - 1 < nk)
+      stage_barrier<S::kLoads * (NS - 2)>();
+    else
+      stage_barrier<0>();
+    if (kt + NS < nk) {
+      Copy<S>::template stage<1>(ra, rb, smem + (kt % NS) * S::kStage, ln, kt + NS, wave);
+      pending_w = kt + NS;
+    }
+  };
+  // W's slab of stage pending_w, whose buffer (not the current one) the
+  // previous barrier freed.
+  auto issue_w = [&]() {
+    if (pending_w >= 0) {
+      Copy<S>::template stage<2>(ra, rb, smem + (pending_w % NS) * S::kStage, ln, pending_w, wave);
+      pending_w = -1;
+    }
+  };
+
+  if constexpr (S::kMF == 16) {
+    HalfA<S> alo, ahi;
+    HalfB<S> blo, bhi;
+    read_half_b<S>(blo, smem, ln, 0, 0);
+    read_half_a<S>(alo, smem, ln, 0, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = smem + (kt % NS) * S::kStage;
+#pragma unroll
+      for (int ks = 0; ks < S::kKS; ++ks) {
+        // The scheduling barriers keep each read batch between the quarters
+        // named above: hoisted further, the reads would need registers of
+        // their own and a wait for all of them before the first MFMA.
+        read_half_b<S>(bhi, cur, ln, ks, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_quarter<S, 0, 0>(acc, alo, blo);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks == 0) issue_w();
+        read_half_a<S>(ahi, cur, ln, ks, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_quarter<S, 0, 1>(acc, alo, bhi);
+        mfma_quarter<S, 1, 0>(acc, ahi, blo);
+        __builtin_amdgcn_sched_barrier(0);
+        if (ks + 1 < S::kKS) {
+          read_half_b<S>(blo, cur, ln, ks + 1, 0);
+          read_half_a<S>(alo, cur, ln, ks + 1, 0);
+        } else if (kt + 1 < nk) {
+          hand_over(kt);
+          const char* nxt = smem + ((kt + 1) % NS) * S::kStage;
+          read_half_b<S>(blo, nxt, ln, 0, 0);
+          read_half_a<S>(alo, nxt, ln, 0, 0);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+        mfma_quarter<S, 1, 1>(acc, ahi, bhi);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  } else {
+    static_assert(S::kKS % 2 == 0, "fragment double buffer needs an even K-step count");
+    Frags<S> f0, f1;
+    read_frags<S>(f0, smem, ln, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const char* cur = smem + (kt % NS) * S::kStage;
+#pragma unroll
+      for (int ks = 0; ks + 1 < S::kKS; ks += 2) {
+        read_frags<S>(f1, cur, ln, ks + 1);
+        mfma_step<S>(acc, f0);
+        if (ks == 0) issue_w();
+        if (ks + 2 < S::kKS) {
+          read_frags<S>(f0, cur, ln, ks + 2);
+          mfma_step<S>(acc, f1);
+        }
+      }
+      if (kt + 1 < nk) {
+        hand_over(kt);
+        read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, ln, 0);
+      }
+      mfma_step<S>(acc, f1);
+    }
   }
 }
 
@@ -409,25 +611,29 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
     ln.stage_b = S::kRow;
   }
 
-  // LDS fragment offsets.  X (and W [N][K]): MFMA lane l reads row (l & 31)
-  // of a 32-row group, logical chunk 2*ks + (l >> 5).  W [K][N]: lane l of
-  // 16-lane group g names row 8*(g >> 1) + e (e = (l & 15) >> 2, plus
-  // 16*ks and 4 for the second read) at columns 16*(g & 1) + 4*(l & 3) of the
-  // fragment; the row's XOR is e << 2, as k & 3 == e.
-  const int frow = lane & 31;
-  const int khalf = lane >> 5;
+  // LDS fragment offsets.  X (and W [N][K]): MFMA lane l reads row
+  // l % kMF of a kMF-row group at logical chunk (kMK/8)*ks + l / kMF, i.e. the
+  // 8 consecutive k that the lane's group takes in K step ks.  W [K][N]: lane
+  // l of 16-lane group g names row k0 + e (e = (l & 15) >> 2; 4 more for the
+  // second read; kMK*ks more per K step) at columns c0 + 4*(l & 3) of the
+  // fragment, with k0 = 8*g and c0 = 0 for 16 x 16 tiles, k0 = 8*(g >> 1)
+  // and c0 = 16*(g & 1) for 32 x 32; the row's XOR is e << 2, as k & 3 == e.
+  const int frow = lane % S::kMF;
+  const int kgrp = lane / S::kMF;
 #pragma unroll
   for (int ks = 0; ks < S::kKS; ++ks) {
-    const int c = ((2 * ks + khalf) ^ swz<BK>(frow)) << 4;
+    const int c = ((S::kMK / 8 * ks + kgrp) ^ swz<BK>(frow)) << 4;
     ln.a_off[ks] = (wm * S::kWM + frow) * S::kRow + c;
     if constexpr (!WKN) ln.b_off[ks] = (wn * S::kWN + frow) * S::kRow + c;
   }
   if constexpr (WKN) {
     const int g = lane >> 4, e = (lane & 15) >> 2, q = lane & 3;
+    const int k0 = S::kMF == 16 ? 8 * g : 8 * (g >> 1);
+    const int c0 = S::kMF == 16 ? 0 : 16 * (g & 1);
 #pragma unroll
-    for (int j = 0; j < S::kNT; ++j) {
-      const int n = wn * S::kWN + 32 * j + 16 * (g & 1) + 4 * q;
-      ln.b_off[j] = (8 * (g >> 1) + e) * S::kRowB + (((n >> 3) ^ (e << 2)) << 4) + (q & 1) * 8;
+    for (int j = 0; j < (S::kKnXor ? 1 : S::kNT); ++j) {
+      const int n = wn * S::kWN + S::kMF * j + c0 + 4 * q;
+      ln.b_off[j] = (k0 + e) * S::kRowB + (((n >> 3) ^ (e << 2)) << 4) + (q & 1) * 8;
     }
   }
 
@@ -437,68 +643,18 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
 #pragma unroll
     for (int j = 0; j < S::kNT; ++j)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc.c[i][j][v] = 0.0f;
+      for (int v = 0; v < (S::kMF == 16 ? 4 : 16); ++v) acc.c[i][j][v] = 0.0f;
 
   const int nk = K / BK;
-  if constexpr (PP) {
+  if constexpr (PP)
     pingpong_loop<S>(acc, ra, rb, smem, ln, nk, wave);
-  } else {
-  // Prologue: stages 0 .. NS-2 in flight, wait for stage 0, then stage NS-1.
-#pragma unroll
-  for (int s = 0; s < NS - 1; ++s)
-    if (s < nk) Copy<S>::template stage<3>(ra, rb, smem + s * S::kStage, ln, s, wave);
-  if (nk >= NS - 1)
-    stage_barrier<S::kLoads * (NS - 2)>();
   else
-    stage_barrier<0>();
-  if (NS - 1 < nk) Copy<S>::template stage<3>(ra, rb, smem + (NS - 1) * S::kStage, ln, NS - 1, wave);
-
-  Frags<S> f0, f1;
-  read_frags<S>(f0, smem, ln, 0);
-
-  // Stage kt + NS is loaded in two halves: X's slab right after the barrier
-  // that frees its buffer, W's after the next stage's first MFMAs, so that
-  // the eight waves' loads do not all reach the address units and LDS at once
-  // (1.5-2 % on the 4-round shapes).
-  int pending_w = -1;  // stage whose W slab is still to be issued
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt % NS;
-    const char* cur = smem + buf * S::kStage;
-#pragma unroll
-    for (int ks = 0; ks + 1 < S::kKS; ks += 2) {
-      read_frags<S>(f1, cur, ln, ks + 1);
-      mfma_step<S>(acc, f0);
-      if (ks == 0 && pending_w >= 0) {
-        // The buffer of stage pending_w is not `cur`: it was freed by the
-        // previous barrier.
-        Copy<S>::template stage<2>(ra, rb, smem + (pending_w % NS) * S::kStage, ln, pending_w, wave);
-        pending_w = -1;
-      }
-      if (ks + 2 < S::kKS) {
-        read_frags<S>(f0, cur, ln, ks + 2);
-        mfma_step<S>(acc, f1);
-      }
-    }
-    if (kt + 1 < nk) {
-      // Stage kt+1 must have landed (stages up to kt+NS-1 were issued), and
-      // every wave must be done reading `cur`, which then takes stage kt+NS.
-      if (kt + NS - 1 < nk)
-        stage_barrier<S::kLoads * (NS - 2)>();
-      else
-        stage_barrier<0>();
-      if (kt + NS < nk) {
-        Copy<S>::template stage<1>(ra, rb, smem + buf * S::kStage, ln, kt + NS, wave);
-        pending_w = kt + NS;
-      }
-      read_frags<S>(f0, smem + ((kt + 1) % NS) * S::kStage, ln, 0);
-    }
-    mfma_step<S>(acc, f1);
-  }
-  }
+    base_loop<S>(acc, ra, rb, smem, ln, nk, wave);
 
   // Epilogue.  With the W fragment as the MFMA's row operand, accumulator
-  // element v of lane l holds output row (l & 31) of its 32 x 32 tile and
-  // columns 8*(v/4) + 4*(l/32) + v%4.  Each 32-row strip of the wave's
+  // element v of lane l holds output row l % 16 of its 16 x 16 tile and column
+  // 4*(l/16) + v (32 x 32: row l % 32, columns 8*(v/4) + 4*(l/32) + v%4).
+  // Each 32-row strip of the wave's
   // sub-block is staged through the wave's own LDS area (rows padded by 16
   // bytes so the transposed writes spread over the banks) and read back
   // row-contiguous, so every global store instruction covers whole 128-byte
@@ -539,19 +695,29 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   const bool col16_ok = col16 < a.N;
   const bool coherent = local ? a.publish != 0 : a.publish == 2;
   const int strip_bytes = 32 * a.N * (local || a.outgoing_f32 ? 4 : 2);
+  static_assert(S::kWM % 32 == 0, "the wave sub-block splits into 32-row strips");
 #pragma unroll
-  for (int i = 0; i < S::kMT; ++i) {
+  for (int i = 0; i < S::kWM / 32; ++i) {
+    if constexpr (S::kMF == 16) {
 #pragma unroll
-    for (int j = 0; j < S::kNT; ++j)
+      for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        f32x4 v;
-        v[0] = acc.c[i][j][4 * g + 0];
-        v[1] = acc.c[i][j][4 * g + 1];
-        v[2] = acc.c[i][j][4 * g + 2];
-        v[3] = acc.c[i][j][4 * g + 3];
-        *reinterpret_cast<f32x4*>(wbuf + frow * kPitch + (32 * j + 8 * g + 4 * khalf) * 4) = v;
-      }
+        for (int j = 0; j < S::kNT; ++j)
+          *reinterpret_cast<f32x4*>(wbuf + (16 * h + frow) * kPitch + (16 * j + 4 * kgrp) * 4) =
+              acc.c[2 * i + h][j];
+    } else {
+#pragma unroll
+      for (int j = 0; j < S::kNT; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 v;
+          v[0] = acc.c[i][j][4 * g + 0];
+          v[1] = acc.c[i][j][4 * g + 1];
+          v[2] = acc.c[i][j][4 * g + 2];
+          v[3] = acc.c[i][j][4 * g + 3];
+          *reinterpret_cast<f32x4*>(wbuf + frow * kPitch + (32 * j + 8 * g + 4 * kgrp) * 4) = v;
+        }
+    }
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the strip is in LDS
     __builtin_amdgcn_wave_barrier();
     // The strip's first row (wave-uniform) in the partition, and the output
