@@ -70,16 +70,27 @@ struct Shape {
   static_assert(kLoads * (NS - 2 > 0 ? NS - 2 : 0) < 64, "vmcnt range");
 };
 
-// XOR swizzle of 16-byte chunks, a function of (row mod 16): every group of
-// 8 (or 16) consecutive fragment rows read at one logical chunk hits distinct
-// LDS banks.
-template <int BK>
+// XOR swizzle of the 16-byte chunks of an X (or W [N][K]) slab row r: the
+// physical chunk of logical chunk c is c ^ swz(r).  A fragment read names the
+// same logical chunk in 16 (16 x 16 tiles) or 32 (32 x 32) consecutive rows;
+// each form has its own swizzle, chosen by the LDS bank-conflict counter
+// (SQ_LDS_BANK_CONFLICT): 0 conflict cycles per read with the forms below,
+// about 4 with the other form's swizzle.
+template <int BK, int MF>
 __device__ __forceinline__ int swz(int r) {
-  if constexpr (BK == 64)
+  if constexpr (MF == 16)
+    return BK == 64 ? (r & 7) : ((r >> 1) & 3);
+  else if constexpr (BK == 64)
     return (r & 7) ^ ((r >> 3) & 1);
   else
     return ((r >> 1) ^ (r >> 3)) & 3;
 }
+
+// XOR swizzle of the 16-byte chunks of W [K][N] slab row k: (k & 3) << 2
+// spreads the four rows one 16-lane group of a transposing read names over
+// the banks, and bit 3 of k moves the next group's rows (8 further) to other
+// banks again, so that 32 lanes of a read are served without conflict.
+__device__ __forceinline__ int kn_swz(int k) { return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1); }
 
 // Wait until at most VM of this wave's vector-memory operations are pending
 // and all of its LDS reads returned, then synchronize the workgroup.  No
@@ -576,21 +587,21 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   // X (and W [N][K]): row wave*RPL + lane/LPR of each group of kWaves*RPL
   // rows, logical chunk (lane % LPR) ^ swz(row).
   const int lrow = wave * S::kRowsPerLoad + lane / S::kLanesPerRow;
-  const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK>(lrow);
+  const int lchunk = (lane % S::kLanesPerRow) ^ swz<BK, S::kMF>(lrow);
   ln.voff_a = lrow * kbytes + lchunk * 16;
   ln.step_a = S::kWaves * S::kRowsPerLoad * kbytes;
   if constexpr (S::kPerLoadB) {
     // W [K][N], rows not a divisor of 1 KiB: the lane's 16 bytes of load
     // group wave + kWaves*j land at slab byte q = 1024*(wave + kWaves*j) +
     // 16*lane, i.e. row q / kRowB, physical chunk (q % kRowB) / 16, which
-    // holds the logical chunk XOR (row & 3) << 2.
+    // holds the logical chunk XOR kn_swz(row).
     constexpr int CPR = BN / 8;
     const int nbytes = a.N * 2;
 #pragma unroll
     for (int j = 0; j < S::kLoadsB; ++j) {
       const int q = (wave + S::kWaves * j) * 64 + lane;  // 16-byte chunk of the slab
       const int krow = q / CPR, pc = q % CPR;
-      ln.voff_bj[j] = krow * nbytes + ((pc ^ ((krow & 3) << 2)) << 4);
+      ln.voff_bj[j] = krow * nbytes + ((pc ^ kn_swz(krow)) << 4);
     }
     ln.voff_b = 0;
     ln.step_b = 0;
@@ -598,11 +609,13 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   } else if constexpr (WKN) {
     // W [K][N]: slab row k holds BN columns (CPR 16-byte chunks); the lane
     // fills physical chunk lane % CPR of row wave*RPL + lane / CPR with the
-    // logical chunk XOR (k & 3) << 2 (k & 3 is the same in every load group).
+    // logical chunk XOR kn_swz(k) (the same in every load group, which are
+    // a multiple of 16 rows apart).
     constexpr int CPR = BN / 8, RPL = 64 / CPR;
     const int krow = wave * RPL + lane / CPR;
     const int nbytes = a.N * 2;
-    ln.voff_b = krow * nbytes + (((lane % CPR) ^ ((krow & 3) << 2)) << 4);
+    static_assert(S::kWaves * RPL % 16 == 0, "load groups keep kn_swz");
+    ln.voff_b = krow * nbytes + (((lane % CPR) ^ kn_swz(krow)) << 4);
     ln.step_b = S::kWaves * RPL * nbytes;
     ln.stage_b = BK * nbytes;
   } else {
@@ -617,12 +630,13 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   // l of 16-lane group g names row k0 + e (e = (l & 15) >> 2; 4 more for the
   // second read; kMK*ks more per K step) at columns c0 + 4*(l & 3) of the
   // fragment, with k0 = 8*g and c0 = 0 for 16 x 16 tiles, k0 = 8*(g >> 1)
-  // and c0 = 16*(g & 1) for 32 x 32; the row's XOR is e << 2, as k & 3 == e.
+  // and c0 = 16*(g & 1) for 32 x 32; the row's XOR is kn_swz(k0 + e), the
+  // same for both reads and every K step (k0 is a multiple of 8).
   const int frow = lane % S::kMF;
   const int kgrp = lane / S::kMF;
 #pragma unroll
   for (int ks = 0; ks < S::kKS; ++ks) {
-    const int c = ((S::kMK / 8 * ks + kgrp) ^ swz<BK>(frow)) << 4;
+    const int c = ((S::kMK / 8 * ks + kgrp) ^ swz<BK, S::kMF>(frow)) << 4;
     ln.a_off[ks] = (wm * S::kWM + frow) * S::kRow + c;
     if constexpr (!WKN) ln.b_off[ks] = (wn * S::kWN + frow) * S::kRow + c;
   }
@@ -633,7 +647,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
 #pragma unroll
     for (int j = 0; j < (S::kKnXor ? 1 : S::kNT); ++j) {
       const int n = wn * S::kWN + S::kMF * j + c0 + 4 * q;
-      ln.b_off[j] = (k0 + e) * S::kRowB + (((n >> 3) ^ (e << 2)) << 4) + (q & 1) * 8;
+      ln.b_off[j] = (k0 + e) * S::kRowB + (((n >> 3) ^ kn_swz(k0 + e)) << 4) + (q & 1) * 8;
     }
   }
 
