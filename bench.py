@@ -173,6 +173,11 @@ def main() -> int:
                          "runtime's device copy moving the reduction's bytes (half read, half "
                          "written), or a library GEMM of the same shape (torch.matmul, X [M][K] "
                          "times W [K][N])")
+    ap.add_argument("--lib", default="", metavar="PATH",
+                    help="load the HIP library from PATH instead of the in-tree build (to "
+                         "compare build options, e.g. one built by "
+                         "tile_overlapped_gemm_amd._build.build(out=PATH, "
+                         "extra=['-DENTWINE_MFMA_EDGE=32']))")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only copy a MIB-sized device buffer --steps times (the reference "
                          "kernel for scaling FETCH_SIZE / WRITE_SIZE)")
@@ -203,7 +208,10 @@ def main() -> int:
         torch.cuda.synchronize()
         log(f"copied {args.copy_calibration} MiB x {args.steps}")
         return 0
-    tog.load()
+    if args.lib:
+        tog.load(os.path.abspath(args.lib))
+    else:
+        tog.load()
     tog.entwine_load_tuning(os.path.join(ROOT, "tile_overlapped_gemm_amd", "tuning.txt"))
     w = wl.BY_NAME[args.workload]
     log(f"workload {w.name}: M={w.M} N={w.N} K={w.K} P={w.P} rank={w.rank}; generating inputs")

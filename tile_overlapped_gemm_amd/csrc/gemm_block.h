@@ -63,7 +63,7 @@ struct Shape {
   static constexpr bool kPerLoadB = WKN && (1024 % kRowB != 0);
   static_assert(kWaves % 2 == 0, "load groups keep the row parity of the swizzle");
   static constexpr int kLoads = kLoadsA + kLoadsB;
-  static_assert(kMT % 2 == 0 && kNT % 2 == 0, "tiles split into halves");
+  static_assert(kMF != 16 || (kMT % 2 == 0 && kNT % 2 == 0), "quarter steps: tiles split in halves");
   // W [K][N] with 16 x 16 tiles and a wave sub-block 64 wide: the LDS offsets
   // of the lane's W fragments differ from fragment 0's by an XOR (see Lanes).
   static constexpr bool kKnXor = WKN && kMF == 16 && kWN == 64;
