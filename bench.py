@@ -146,8 +146,9 @@ def main() -> int:
     ap.add_argument("--peers", default="preseeded", help="preseeded|symmetric")
     ap.add_argument("--w-layout", default="kn", choices=["kn", "nk"],
                     help="W handed over [K_local][N] (the library's default) or [N][K_local]")
-    ap.add_argument("--schedule", default="auto", choices=["auto", "streams", "fused"],
-                    help="overlapped schedule: two streams, one fused kernel, or the tuning table's")
+    ap.add_argument("--schedule", default="auto", choices=["auto", "streams", "fused", "assisted"],
+                    help="overlapped schedule: two streams, one fused kernel, the fused kernel "
+                         "with helper workgroups on a second stream, or the tuning table's")
     ap.add_argument("--static-cus", type=int, default=32,
                     help="CUs reserved for the reduction in the CU-policy leg (Sec. 5.3.3)")
     ap.add_argument("--reducer-cus", type=int, default=0,
@@ -243,7 +244,8 @@ def main() -> int:
     budget = args.budget if args.budget >= 0 else tuned.get("budget", 32)
     threads = args.threads or tuned.get("threads", 256)
     slabs = args.slabs or tuned.get("slabs", 1)
-    schedule = ({"streams": tog.SCHEDULE_STREAMS, "fused": tog.SCHEDULE_FUSED}[args.schedule]
+    schedule = ({"streams": tog.SCHEDULE_STREAMS, "fused": tog.SCHEDULE_FUSED,
+                 "assisted": tog.SCHEDULE_ASSISTED}[args.schedule]
                 if args.schedule != "auto" else (tuned.get("schedule") or tog.SCHEDULE_STREAMS))
     # The overlapped schedules are also timed when the tuned step is sequential:
     # then at the largest budget below the CU count with four row slabs per

@@ -110,10 +110,24 @@ enum { ENTWINE_STAGES_ALL = 0, ENTWINE_STAGES_GEMM = 1, ENTWINE_STAGES_REDUCE = 
  *           flags) until every block is taken; then workgroup w < x takes
  *           reduction tasks w, w + x, ... in production order.  No fork or
  *           join.
+ *  ASSISTED the FUSED kernel on the caller's stream plus x reduction
+ *           workgroups on the internal stream, forked from the caller's
+ *           stream but never joined back: they reduce tiles as the GEMM
+ *           releases them, each task going to whoever claims it first, and
+ *           the fused kernel ends only once every task is done.  The caller's
+ *           stream thus waits on nothing of the internal stream.  Eager calls
+ *           only: inside a graph capture the fused kernel runs alone (a
+ *           captured branch needs a join).  Not with push_outgoing, not from
+ *           the no-alloc entry point.
  *  AUTO     the tuning table's choice for the shape, else STREAMS.
- * Both give bit-identical output.  The sequential schedule (comm_budget 0)
+ * All give bit-identical output.  The sequential schedule (comm_budget 0)
  * and single stages ignore this field. */
-enum { ENTWINE_SCHEDULE_AUTO = 0, ENTWINE_SCHEDULE_STREAMS = 1, ENTWINE_SCHEDULE_FUSED = 2 };
+enum {
+  ENTWINE_SCHEDULE_AUTO = 0,
+  ENTWINE_SCHEDULE_STREAMS = 1,
+  ENTWINE_SCHEDULE_FUSED = 2,
+  ENTWINE_SCHEDULE_ASSISTED = 3
+};
 
 /* GEMM main-loop pipeline (entwine_config.gemm_variant).  Every pipeline
  * multiplies the K steps in the same order, so all give bit-identical output.

@@ -98,7 +98,7 @@ def test_validation_before_any_device_call(lib, kw, status):
     ("release_group", -2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("task_slabs", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("publish_all", 2, tog.ENTWINE_ERR_INVALID_ARGUMENT),
-    ("schedule", 3, tog.ENTWINE_ERR_INVALID_ARGUMENT),
+    ("schedule", 4, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("schedule", -1, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("reducer_cus", -4, tog.ENTWINE_ERR_INVALID_ARGUMENT),
     ("push_outgoing", 2, tog.ENTWINE_ERR_INVALID_ARGUMENT),

@@ -82,7 +82,7 @@ def test_chain_parity_and_invariance(dev, w):
     r = err_ratio(y0, ref_y)
     print(f"case {w.name}: y max err/tol {r:.3f}", flush=True)
     assert r <= 1.0
-    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED, tog.SCHEDULE_ASSISTED):
         for order, budget in ((tog.ORDER_INTERLEAVED, 4), (tog.ORDER_COL_MAJOR, 1),
                               (tog.ORDER_ROW_MAJOR, 64)):
             for in_place in (False, True):
@@ -106,7 +106,7 @@ def test_chain_full_size(dev):
     c = Chain(w, dev)
     print("chain mlp: AUTO and both overlapped schedules", flush=True)
     h0, y0 = c.run(tog.ORDER_AUTO, tog.BUDGET_AUTO)
-    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED, tog.SCHEDULE_ASSISTED):
         for budget, slabs in ((128, 1), (255, 4)):
             h, y = c.run(tog.ORDER_AUTO, budget, schedule=sched, task_slabs=slabs)
             np.testing.assert_array_equal(h, h0)

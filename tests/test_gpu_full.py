@@ -47,13 +47,13 @@ def test_full_size_parity(w):
     assert torch.equal(bits(out), bits(seq))
     got = leg("tuned step (AUTO), W [N][K]", tog.ORDER_AUTO, tog.BUDGET_AUTO, w_layout=tog.W_NK)
     assert torch.equal(bits(got), bits(seq))
-    # Both overlapped schedules as the benchmark's overlapped legs run them when
+    # The overlapped schedules as the benchmark's overlapped legs run them when
     # the tuned step is sequential (the largest budget below the CU count, four
     # slabs per tile), and at a budget of 128 with one task per tile.
     _, _, q = tog.entwine_plan_shape(w.M, w.N, w.P, 128, 128, w.tile, w.tile)
     x_max = min(q * 4, tog.entwine_device_cus() - 1)
     slabs = 4 if w.tile % 4 == 0 else 1
-    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED, tog.SCHEDULE_ASSISTED):
         for budget, sl in ((x_max, slabs), (128, 1)):
             got = leg(f"schedule {sched}, budget {budget}, {sl} slab(s)", tog.ORDER_AUTO, budget,
                       schedule=sched, task_slabs=sl)

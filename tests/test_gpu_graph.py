@@ -14,7 +14,7 @@ pytestmark = pytest.mark.gpu
 
 
 @pytest.mark.parametrize("sched,push", [(tog.SCHEDULE_STREAMS, 0), (tog.SCHEDULE_FUSED, 0),
-                                        (tog.SCHEDULE_FUSED, 1)])
+                                        (tog.SCHEDULE_FUSED, 1), (tog.SCHEDULE_ASSISTED, 0)])
 def test_graph_replays_match_eager(sched, push):
     dev = device()
     w = wl.custom("graph", 2048, 1536, 512, 4, rank=2, index=320)
@@ -86,7 +86,8 @@ def test_capture_requires_prepared_workspace():
 
 
 
-@pytest.mark.parametrize("sched", [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED])
+@pytest.mark.parametrize("sched", [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED,
+                                   tog.SCHEDULE_ASSISTED])
 def test_graph_survives_workspace_growth(sched):
     """A graph captured at one shape keeps working after a larger eager call
     has grown the workspace: the outgrown buffers the graph refers to are

@@ -2,7 +2,8 @@
 
 Bar: |out - ref| <= 1e-2 * max(1, |ref|) element by element against the fp64
 oracle; bit-identical output across production orders, budgets (sequential
-included), schedules (two streams or one fused kernel), reducer thread
+included), schedules (two streams, one fused kernel, or the fused kernel
+with helper workgroups on another stream), reducer thread
 counts, peer-readiness modes and release groups; bit-exact on integer
 inputs; bit-exact reduction given the device's own fp32 partial.
 """
@@ -25,7 +26,8 @@ SMALL = [
     wl.BY_NAME["tiny"],                                              # fp32 peers/out, 64x64 tiles
 ]
 BLOCKS = [(128, 128), (128, 256), (256, 128), (256, 256), (128, 384)]
-SCHEDULES = [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED]
+SCHEDULES = [tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED, tog.SCHEDULE_ASSISTED]
+FUSED_KERNEL = (tog.SCHEDULE_FUSED, tog.SCHEDULE_ASSISTED)
 
 
 def fused_built(bm, bn, variant):
@@ -71,16 +73,17 @@ def test_parity_and_schedule_invariance(dev, w):
                 continue  # W [K][N]: the base pipeline
             for order in ORDERS:
                 for budget, sched in [(b, s) for b in (0, 1, 3, min(q, 64)) for s in SCHEDULES]:
-                    if sched == tog.SCHEDULE_FUSED and (budget == 0 or not fused_built(bm, bn, variant)):
+                    if sched in FUSED_KERNEL and (budget == 0 or not fused_built(bm, bn, variant)):
                         continue
                     print(f"case {w.name} block {bm}x{bn} v{variant} W {layout} order {order} "
                           f"budget {budget} schedule {sched}", flush=True)
-                    if sched == tog.SCHEDULE_STREAMS and budget > 0 and (
+                    if sched != tog.SCHEDULE_FUSED and budget > 0 and (
                             variant == tog.GEMM_PINGPONG or (variant == 3 and (bm, bn) == (256, 256))):
                         # The ping-pong pipeline (235 registers per lane) and
                         # the four 128 x 128 waves (256 accumulator registers
                         # plus 214) leave no room for a reduction workgroup on
-                        # the GEMM's CUs: refused, nothing runs
+                        # the GEMM's CUs (two streams, or the assisted
+                        # schedule's helpers): refused, nothing runs
                         with pytest.raises(tog.EntwineError) as e:
                             case.run(order, budget, block_m=bm, block_n=bn, gemm_variant=variant,
                                      schedule=sched, w_layout=layout)
@@ -186,7 +189,10 @@ def test_push_outgoing_copies_every_peer_tile(dev, w):
     base = down(case.run(tog.ORDER_INTERLEAVED, 4, **blk))
     rows = np.ones(w.M, dtype=bool)
     rows[w.rank * w.rows:(w.rank + 1) * w.rows] = False
-    for sched in SCHEDULES:
+    with pytest.raises(tog.EntwineError) as e:
+        case.run(tog.ORDER_INTERLEAVED, 4, push_outgoing=1, schedule=tog.SCHEDULE_ASSISTED, **blk)
+    assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_FUSED):
         for order, budget, slabs, mode in ((tog.ORDER_INTERLEAVED, 4, 1, tog.PEERS_PRESEEDED),
                                            (tog.ORDER_PARTITION_MAJOR, 1, 2, tog.PEERS_SYMMETRIC),
                                            (tog.ORDER_COL_MAJOR, 64, 4, tog.PEERS_PRESEEDED)):

@@ -59,10 +59,11 @@ def test_noalloc_refusals():
     dev = device()
     w = SMALL
     Xd, Wd, pd = inputs(w, dev)
-    cfg = tog.config(block_m=128, block_n=128, schedule=tog.SCHEDULE_STREAMS)
-    with pytest.raises(tog.EntwineError) as e:
-        call(tog.entwine_gemm_rs_noalloc, w, Xd, Wd, pd, 4, cfg)
-    assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
+    for sched in (tog.SCHEDULE_STREAMS, tog.SCHEDULE_ASSISTED):
+        cfg = tog.config(block_m=128, block_n=128, schedule=sched)
+        with pytest.raises(tog.EntwineError) as e:
+            call(tog.entwine_gemm_rs_noalloc, w, Xd, Wd, pd, 4, cfg)
+        assert e.value.status == tog.ENTWINE_ERR_UNSUPPORTED
     # 16384 x 8192 outputs at P = 1: a 512 MiB fp32 partial, beyond the
     # 256 MiB scratch (rejected before any launch; the buffers are not read)
     M, N, K = 16384, 8192, 64

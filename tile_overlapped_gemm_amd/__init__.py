@@ -31,7 +31,7 @@ PEERS_PRESEEDED, PEERS_SYMMETRIC = 0, 1
 W_KN, W_NK = 0, 1
 RELEASE_TILE, RELEASE_PARTITION, RELEASE_OUTPUT = 1, 0, -1
 STAGES_ALL, STAGES_GEMM, STAGES_REDUCE = 0, 1, 2
-SCHEDULE_AUTO, SCHEDULE_STREAMS, SCHEDULE_FUSED = 0, 1, 2
+SCHEDULE_AUTO, SCHEDULE_STREAMS, SCHEDULE_FUSED, SCHEDULE_ASSISTED = 0, 1, 2, 3
 GEMM_AUTO, GEMM_PINGPONG, GEMM_BASE = 0, 4, 5
 
 # Names exported by the library (one per declaration in include/entwine.h).

@@ -88,6 +88,14 @@ struct Workspace {
   // captured into a graph, so that eager calls never wait on a captured record.
   hipEvent_t cap_fork = nullptr, cap_red = nullptr;
   bool have_prev = false;
+  // The last eager call was assisted: its helpers (ev_red) never touch what a
+  // later call uses, so later calls wait for its fused kernel (ev_gemm) only.
+  bool prev_assisted = false;
+  // The assisted schedule's sequence number (the last call's) and task claim
+  // words (one per task, see kAssistCall in kernels.h).
+  uint32_t assist_seq = 0;
+  uint32_t* claims = nullptr;
+  size_t claims_bytes = 0;
   float* own = nullptr;
   size_t own_bytes = 0;
   void* outgoing = nullptr;
@@ -117,6 +125,8 @@ struct Workspace {
 struct TuneEntry {
   int order, budget, bm, bn, threads, slabs, schedule, variant;
 };
+
+static_assert(kCtlWords * 4 <= kScratchError, "the control words fit before the error word");
 
 std::mutex g_mu;
 std::map<int, std::unique_ptr<Workspace>> g_ws;
@@ -155,6 +165,7 @@ void destroy_workspace(Workspace* w) {
   if (w->outgoing) (void)hipFree(w->outgoing);
   if (w->staging) (void)hipFree(w->staging);
   if (w->flags) (void)hipFree(w->flags);
+  if (w->claims) (void)hipFree(w->claims);
   if (w->error) (void)hipFree(w->error);
   if (w->ctl) (void)hipFree(w->ctl);
   if (w->trace) (void)hipFree(w->trace);
@@ -394,7 +405,7 @@ int resolve(const entwine_config* cfg, int64_t M, int64_t N, int64_t K, int P, i
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "linear_dispatch must be 0 or 1");
   if (c.stages < ENTWINE_STAGES_ALL || c.stages > ENTWINE_STAGES_REDUCE)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "stages %d out of range", c.stages);
-  if (r->schedule < ENTWINE_SCHEDULE_STREAMS || r->schedule > ENTWINE_SCHEDULE_FUSED)
+  if (r->schedule < ENTWINE_SCHEDULE_STREAMS || r->schedule > ENTWINE_SCHEDULE_ASSISTED)
     return fail(ENTWINE_ERR_INVALID_ARGUMENT, "schedule %d out of range", r->schedule);
   r->reducer_cus = c.reducer_cus;
   r->push = c.push_outgoing;
@@ -608,10 +619,17 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
 
   const bool sequential = (rs.budget == ENTWINE_BUDGET_SEQUENTIAL);
   const bool fused = !sequential && rs.stages == ENTWINE_STAGES_ALL &&
-                     rs.schedule == ENTWINE_SCHEDULE_FUSED;
+                     (rs.schedule == ENTWINE_SCHEDULE_FUSED ||
+                      rs.schedule == ENTWINE_SCHEDULE_ASSISTED);
+  // The assisted schedule's helpers run eagerly only: inside a capture the
+  // fused kernel does every task.
+  const bool assisted = fused && rs.schedule == ENTWINE_SCHEDULE_ASSISTED && !capturing;
   if (rs.push && sequential)
     return fail(ENTWINE_ERR_UNSUPPORTED, "push_outgoing applies to the overlapped schedules "
                 "(comm_budget >= 1)");
+  if (rs.push && fused && rs.schedule == ENTWINE_SCHEDULE_ASSISTED)
+    return fail(ENTWINE_ERR_UNSUPPORTED, "push_outgoing is built for the two-stream and fused "
+                "schedules, not the assisted one");
   // A list of tasks in production order: always for the fused kernel, and for
   // the two-stream reducer when it also pushes.
   const bool listed = !sequential && (fused || rs.push);
@@ -622,6 +640,21 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     if (fused_per_cu <= 0)
       return fail(ENTWINE_ERR_UNSUPPORTED, "the fused schedule is not built for %dx%d blocks, "
                   "GEMM variant %d", g.bm, g.bn, rs.variant);
+  }
+  if (assisted) {
+    // The helpers help only beside the fused kernel's workgroups: one helper
+    // workgroup must fit on a CU that holds a fused one.
+    const int hr = assist_registers(rs.threads, rs.peer_f32, rs.out_f32);
+    const int fr = fused_registers(g.bm, g.bn, rs.variant, rs.peer_f32, rs.out_f32, rs.wkn);
+    if (hr <= 0 || fr <= 0) return fail(ENTWINE_ERR_HIP, "kernel register counts unavailable");
+    auto up8 = [](int v) { return (v + 7) / 8 * 8; };
+    const int fw = (gemm_waves(g.bm, g.bn, rs.variant, rs.wkn) + 3) / 4;
+    const int hw = (rs.threads / 64 + 3) / 4;
+    if (fw * up8(fr) + hw * up8(hr) > 512)
+      return fail(ENTWINE_ERR_UNSUPPORTED,
+                  "a %d-thread helper workgroup (%d registers per lane) cannot share a CU with "
+                  "a %dx%d fused workgroup (%d registers per lane)",
+                  rs.threads, hr, g.bm, g.bn, fr);
   }
   // Static CU partitioning (Sec. 5.3.3): the reduction's x workgroups on x
   // CUs of their own, the GEMM's persistent workgroups on the other CUs.
@@ -712,6 +745,9 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   size_t flag_bytes = w->flag_count * 4;
   if ((rc = ensure(w, (void**)&w->flags, &flag_bytes, flag_need, true))) return rc;
   w->flag_count = flag_bytes / 4;
+  if (assisted &&
+      (rc = ensure(w, (void**)&w->claims, &w->claims_bytes, (size_t)g.Q * slabs_eff * 4, true)))
+    return rc;
   // Tracing: the call's slots are sized once its grids are known (arm_trace).
   uint64_t* trace = nullptr;
   auto arm_trace = [&](int64_t nb, int64_t grid_red, hipStream_t s) -> int {
@@ -799,13 +835,26 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
         std::min<int64_t>((int64_t)fused_per_cu * w->cus, g.NB + (int64_t)fa.workers);
     if (w->have_prev && !capturing) {
       HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
-      HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+      if (!w->prev_assisted) HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
     }
-    if ((rc = arm_trace(g.NB, grid, stream))) return rc;
+    // The assisted schedule's helpers: x workgroups on the internal stream.
+    const int hgrid = assisted ? (int)std::min<int64_t>(rs.budget, ra.ntasks) : 0;
+    if ((rc = arm_trace(g.NB, grid + hgrid, stream))) return rc;
     if (trace) {
       fa.g.trace = trace;
       fa.g.trace_nb = (int32_t)g.NB;
       fa.r.trace = trace + 2 * g.NB;
+      fa.r.trace_g = (int32_t)(grid + hgrid);
+    }
+    if (assisted) {
+      // A fresh sequence number (never 0), and the fork: the helpers start
+      // after the caller's earlier work, which wrote the inputs.  No join:
+      // the fused kernel ends only once every task is done.
+      if (++w->assist_seq == 0) ++w->assist_seq;
+      fa.r.assist_seq = w->assist_seq;
+      fa.r.claims = w->claims;
+      HIP_TRY(hipEventRecord(w->ev_fork, stream));
+      HIP_TRY(hipStreamWaitEvent(w->s_red, w->ev_fork, 0));
     }
     if (g_timing) {
       HIP_TRY(hipEventRecord(tp.g0, stream));
@@ -815,6 +864,14 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
                                         (int)grid, stream);
     if (e != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "fused launch failed: %s", hipGetErrorString(e));
+    if (assisted) {
+      ReduceArgs ha = fa.r;
+      ha.trace_slot0 = (int32_t)grid;
+      if ((e = launch_assist_reduce(ha, rs.peer_f32, rs.out_f32, rs.threads, hgrid, w->s_red)) !=
+          hipSuccess)
+        return fail(ENTWINE_ERR_HIP, "helper launch failed: %s", hipGetErrorString(e));
+      HIP_TRY(hipEventRecord(w->ev_red, w->s_red));
+    }
     if (chain && (e = launch_rmsnorm(out, chain->gamma, chain->y, (int)g.R, (int)N, chain->eps,
                                      rs.out_f32, stream)) != hipSuccess)
       return fail(ENTWINE_ERR_HIP, "RMSNorm launch failed: %s", hipGetErrorString(e));
@@ -825,8 +882,9 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
     }
     if (!capturing) {
       HIP_TRY(hipEventRecord(w->ev_gemm, stream));
-      HIP_TRY(hipEventRecord(w->ev_red, stream));
+      if (!assisted) HIP_TRY(hipEventRecord(w->ev_red, stream));
       w->have_prev = true;
+      w->prev_assisted = assisted;
     }
     return ENTWINE_OK;
   }
@@ -869,7 +927,7 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   hipEvent_t ev_red = capturing ? w->cap_red : w->ev_red;
   if (w->have_prev && !capturing) {
     HIP_TRY(hipStreamWaitEvent(stream, w->ev_gemm, 0));
-    HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
+    if (!w->prev_assisted) HIP_TRY(hipStreamWaitEvent(stream, w->ev_red, 0));
   }
   if ((rc = arm_trace(run_gemm ? g.NB : 0, run_red ? grid : 0, stream))) return rc;
   if (trace) {
@@ -922,7 +980,10 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
   }
   if (g_timing) HIP_TRY(hipEventRecord(tp.r1, s_red));
   if (forked || !capturing) HIP_TRY(hipEventRecord(ev_red, s_red));
-  if (!capturing) w->have_prev = true;
+  if (!capturing) {
+    w->have_prev = true;
+    w->prev_assisted = false;
+  }
   // Join: the caller's stream continues after the reducer too.
   if (forked) HIP_TRY(hipStreamWaitEvent(stream, ev_red, 0));
   if (g_timing) w->timing_live.push_back(tp);
@@ -969,9 +1030,11 @@ int run_noalloc(void* scratch, size_t scratch_bytes, const void* X, const void* 
   // Only schedules that run on the caller's stream alone: a second stream and
   // its events would be allocations.
   if (cfg && cfg->struct_size >= (int32_t)(offsetof(entwine_config, schedule) + sizeof(int32_t)) &&
-      cfg->schedule == ENTWINE_SCHEDULE_STREAMS && !sequential)
+      (cfg->schedule == ENTWINE_SCHEDULE_STREAMS || cfg->schedule == ENTWINE_SCHEDULE_ASSISTED) &&
+      !sequential)
     return fail(ENTWINE_ERR_UNSUPPORTED, "the no-alloc entry point runs the sequential and the "
-                "fused schedules only (the two-stream schedule needs a stream and events)");
+                "fused schedules only (the two-stream and assisted schedules need a stream and "
+                "events)");
   if (rs.reducer_cus > 0 && !sequential)
     return fail(ENTWINE_ERR_UNSUPPORTED, "static CU partitioning (reducer_cus) runs on two "
                 "streams: not available without allocation");
@@ -1288,6 +1351,7 @@ int entwine_device_status(void* stream) {
       // have been publishing; with every stream idle, start the flags afresh.
       HIP_TRY(hipMemset(w->error, 0, sizeof(int32_t)));
       if (w->flags) HIP_TRY(hipMemset(w->flags, 0, w->flag_count * sizeof(uint32_t)));
+      if (w->claims) HIP_TRY(hipMemset(w->claims, 0, w->claims_bytes));
       HIP_TRY(hipMemcpy(w->ctl, ctl_init, sizeof ctl_init, hipMemcpyHostToDevice));
       status = err;
     }
@@ -1481,11 +1545,11 @@ int entwine_load_tuning(const char* path) {
     int P, order, budget, bm, bn, threads, slabs = 1, schedule = ENTWINE_SCHEDULE_AUTO, variant = 0;
     const int n = std::sscanf(line, "%lld %lld %lld %d %d %d %d %d %d %d %d %d", &M, &N, &K, &P,
                               &order, &budget, &bm, &bn, &threads, &slabs, &schedule, &variant);
-    if (n < 9 || schedule < ENTWINE_SCHEDULE_AUTO || schedule > ENTWINE_SCHEDULE_FUSED ||
+    if (n < 9 || schedule < ENTWINE_SCHEDULE_AUTO || schedule > ENTWINE_SCHEDULE_ASSISTED ||
         variant < 0 || variant > 4) {
       std::fclose(f);
       return fail(ENTWINE_ERR_INVALID_ARGUMENT,
-                  "%s:%d: expected 9 to 12 integers (schedule 0, 1 or 2; GEMM variant 0 to 4)",
+                  "%s:%d: expected 9 to 12 integers (schedule 0 to 3; GEMM variant 0 to 4)",
                   path, lineno);
     }
     table[std::make_tuple((int64_t)M, (int64_t)N, (int64_t)K, P)] =

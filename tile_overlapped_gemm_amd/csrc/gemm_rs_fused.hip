@@ -47,7 +47,8 @@
 namespace entwine {
 namespace {
 
-__device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
+__device__ void fused_check_out(const ReduceArgs& r, uint32_t epoch) {
+  uint32_t* const ctl = r.ctl;
   const uint32_t n = __hip_atomic_fetch_add(ctl + kFusedDone, 1u, __ATOMIC_RELAXED,
                                             __HIP_MEMORY_SCOPE_AGENT);
   if (n + 1 != gridDim.x) return;
@@ -55,6 +56,26 @@ __device__ void fused_check_out(uint32_t* ctl, uint32_t epoch) {
   auto clear = [&](int i) {
     __hip_atomic_store(ctl + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   };
+  if (r.assist_seq) {
+    // The assisted schedule: every task of the call was claimed (this
+    // kernel's workers claimed all that were left), and a helper claims a
+    // task only once its flags are set, so the count reaches the task count
+    // within one task's time.  Then the call is over for the helpers too.
+    const uint64_t start = wall_clock64();
+    while (__hip_atomic_load(ctl + kTasksDone, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) !=
+           (uint32_t)r.ntasks) {
+      if (__hip_atomic_load(r.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) break;
+      if (wall_clock64() - start > r.timeout_ticks) {
+        __hip_atomic_store(r.error, (int32_t)5 /* ENTWINE_ERR_TIMEOUT */, __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    clear(kTasksDone);
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(ctl + kAssistCall), assist_pack(r.assist_seq, 0),
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   for (int y = 0; y < 8; ++y) clear(kBlockTicket + y * kLine);
   clear(kFusedDone);
   __hip_atomic_store(ctl + kEpoch, next_epoch(epoch), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -89,6 +110,11 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   uint32_t* const ctl = f.g.ctl;
   const ReduceArgs& r = f.r;
   const uint32_t epoch = peek(ctl + kEpoch);
+  // The assisted schedule: the call is live for its helpers from here on.
+  if (r.assist_seq && blockIdx.x == 0 && tid == 0)
+    __hip_atomic_store(reinterpret_cast<uint64_t*>(ctl + kAssistCall),
+                       assist_pack(r.assist_seq, epoch), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   int parity = 0;
   // Thread 0's v, for every thread, as a wave-uniform (scalar) value.
   auto share = [&](int v) {
@@ -124,15 +150,26 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     // rather than keeping the GEMM's in registers (fewer registers in all).
     int lt = tid;
     asm volatile("" : "+v"(lt));
+    // The batch's tasks this workgroup reduces: all of them, or in the
+    // assisted schedule those it claims (helpers have the others).
+    int mine = (1 << kB) - 1;
+    if (r.assist_seq) {
+      int m = 0;
+      if (tid == 0)
+        for (int b = 0; b < kB; ++b)
+          if (t0 + b * x < r.ntasks && claim_task(r.claims, t0 + b * x, epoch)) m |= 1 << b;
+      mine = share(m);
+      if (mine == 0) return true;
+    }
     Pending<kU, PEER_F32, OUT_F32> p[kB];
 #pragma unroll
     for (int b = 0; b < kB; ++b)
-      if (t0 + b * x < r.ntasks) begin(t0 + b * x, p[b], lt);
+      if (t0 + b * x < r.ntasks && ((mine >> b) & 1)) begin(t0 + b * x, p[b], lt);
     int ok = 1;
     if (lt < 64) {
       const int tw = t0 + (lt >> 4) * x;
       const uint32_t* fl = nullptr;
-      if (tw < r.ntasks) {
+      if (tw < r.ntasks && ((mine >> (lt >> 4)) & 1)) {
         const TaskRef k = task_ref(r, tw);
         fl = wait_flag(r, k.d, k.t, lt & 15);
       }
@@ -144,7 +181,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
 #pragma unroll
     for (int b = 0; b < kB; ++b) {
       const int t = t0 + b * x;
-      if (t < r.ntasks && task_ref(r, t).d == r.rank) {
+      if (t < r.ntasks && ((mine >> b) & 1) && task_ref(r, t).d == r.rank) {
         const SlabIO io = slab_io<PEER_F32, OUT_F32>(r, p[b].s.e0);
         if (!r.prefetch) load_inputs_rel(r, io, p[b].c);
         load_own_rel(io, p[b].c, own[b]);
@@ -154,6 +191,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
     for (int b = 0; b < kB; ++b) {
       const int t = t0 + b * x;
       if (t >= r.ntasks) break;
+      if (!((mine >> b) & 1)) continue;
       const TaskRef k = task_ref(r, t);
       if (k.d == r.rank) {
         sum_store_rel(r, slab_io<PEER_F32, OUT_F32>(r, p[b].s.e0), p[b].c, own[b]);
@@ -162,6 +200,9 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
         push_slab<kThreads, PEER_F32>(r, k.d, k.t, k.slab, lt);
       }
     }
+    if (r.assist_seq && tid == 0)
+      __hip_atomic_fetch_add(ctl + kTasksDone, (uint32_t)__builtin_popcount(mine), __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
     return true;
   };
 
@@ -189,16 +230,17 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
   // ended later by more than the whole reduction takes on its own.)
   int task = (int)blockIdx.x < x ? (int)blockIdx.x : r.ntasks;
   const bool worker = task < r.ntasks;  // uniform
-  if (r.trace && worker && tid == 0) trace_at(r.trace, blockIdx.x);
+  const int trace_g = r.trace_g ? r.trace_g : (int)gridDim.x;
+  if (r.trace && worker && tid == 0) trace_at(r.trace, r.trace_slot0 + blockIdx.x);
   while (task < r.ntasks) {
     if (!batch(task)) break;  // the watchdog or the sticky error ended the wait
     task += kB * x;
   }
   if (r.trace && worker) {  // uniform: every wave's stores issued
     __syncthreads();
-    if (tid == 0) trace_at(r.trace, (int64_t)gridDim.x + blockIdx.x);
+    if (tid == 0) trace_at(r.trace, (int64_t)trace_g + r.trace_slot0 + blockIdx.x);
   }
-  if (tid == 0) fused_check_out(ctl, epoch);
+  if (tid == 0) fused_check_out(r, epoch);
 }
 
 template <int BM, int BN, int BK, int NS, int WGM, int WGN, bool PP, bool WKN, bool PF, bool OF>
@@ -272,6 +314,14 @@ struct FusedOccupancy {
   int run() { return I::per_cu(); }
   int none() { return 0; }
 };
+struct FusedRegisters {
+  template <class I>
+  int run() {
+    hipFuncAttributes at{};
+    return hipFuncGetAttributes(&at, I::fn()) == hipSuccess ? at.numRegs : 0;
+  }
+  int none() { return 0; }
+};
 
 }  // namespace
 
@@ -283,6 +333,10 @@ hipError_t launch_gemm_rs_fused(const FusedArgs& a, int bm, int bn, int variant,
 
 int fused_blocks_per_cu(int bm, int bn, int variant, int peer_f32, int out_f32, bool wkn) {
   return with_fused(bm, bn, variant, peer_f32, out_f32, wkn, FusedOccupancy{});
+}
+
+int fused_registers(int bm, int bn, int variant, int peer_f32, int out_f32, bool wkn) {
+  return with_fused(bm, bn, variant, peer_f32, out_f32, wkn, FusedRegisters{});
 }
 
 }  // namespace entwine

@@ -78,7 +78,15 @@ struct ReduceArgs {
   // the wait, as a real peer's data would be (symmetric readiness).
   int32_t prefetch;
   uint64_t* trace;                  // measurement stamps [2][grid] (see trace_at), nullptr: off
+  // Trace slots: workgroup w stores its start at trace[trace_slot0 + w] and
+  // its end at trace[trace_g + trace_slot0 + w]; trace_g 0: the grid size.
+  int32_t trace_slot0, trace_g;
   int32_t checkout_total;           // as GemmArgs::checkout_total
+  // The assisted schedule (see kAssistCall): the call's sequence number
+  // (0: not assisted) and one claim word per task (the epoch of the call in
+  // which the task was claimed).
+  uint32_t assist_seq;
+  uint32_t* claims;
   // A waiting workgroup's pause between two polls starts at 128 clock cycles
   // and doubles up to nap_max x 128 cycles.
   int32_t nap_max;
@@ -100,6 +108,18 @@ struct ReduceArgs {
 // workgroups update has a 128-byte line of its own: atomics to one line are
 // serialized, and with the eight block tickets in one line a multi-round
 // 768-block GEMM ran 30 % slower.
+//
+// The assisted schedule: the fused kernel on the caller's stream and, on the
+// internal stream with no event between them, reduction workgroups that help
+// with the tasks while the GEMM runs.  kAssistCall holds (sequence number,
+// epoch) of the call whose fused kernel is running, (sequence number, 0)
+// once it has finished: the helpers of call s work only while it reads
+// (s, e), so a helper that starts late or outlives its call does nothing.
+// A task goes to whoever first moves its claim word to the call's epoch
+// (compare-and-swap); kTasksDone counts the completed tasks, and the fused
+// kernel's last workgroup waits for all of them before it finishes the call.
+// No wait ever depends on a helper being scheduled: a helper claims a task
+// only once the task's flags are set, so a claimed task always completes.
 enum {
   kLine = 32,  // control words per 128-byte line
   kEpoch = 0,
@@ -107,7 +127,9 @@ enum {
   kFusedDone = 2 * kLine,
   kBlockTicket = 3 * kLine,  // ticket of XCD y at kBlockTicket + y * kLine
   kGemmDone = 11 * kLine,    // check-out count of the persistent (ticket) GEMM
-  kCtlWords = 12 * kLine
+  kAssistCall = 12 * kLine,  // two words: sequence number, epoch (0: finished)
+  kTasksDone = 13 * kLine,   // tasks completed in the assisted call
+  kCtlWords = 14 * kLine
 };
 
 __device__ __forceinline__ uint32_t next_epoch(uint32_t e) { return e + 1 == 0 ? 1 : e + 1; }
@@ -147,6 +169,15 @@ struct FusedArgs {
   int32_t nb;                 // GEMM blocks
   int32_t workers;            // workgroups that may reduce (the comm budget)
 };
+
+// The assisted schedule's helpers: `grid` workgroups of `threads` take tasks
+// j, j + grid, ... of a.task_list once their flags are set (a.assist_seq,
+// a.claims as for the fused kernel of the same call).
+hipError_t launch_assist_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
+                                int grid, hipStream_t stream);
+int assist_registers(int threads, int peer_f32, int out_f32);
+// Registers per lane of a fused kernel instance (0 if not built).
+int fused_registers(int bm, int bn, int variant, int peer_f32, int out_f32, bool wkn);
 
 // GEMM block shapes built: (bm, bn) in {128, 256}^2.
 hipError_t launch_gemm_publish(const GemmArgs& a, int bm, int bn, int num_blocks,

@@ -380,8 +380,9 @@ __device__ __forceinline__ void load_own_rel(const SlabIO& io,
     if (c.ok[u]) own[u] = load_rel<true, kSC1>(io.own, c.off[u]);
 }
 
-// own + peers (ranks ascending) + residual in fp32, one rounding, the store.
-template <int U, bool PEER_F32, bool OUT_F32>
+// own + peers (ranks ascending) + residual in fp32, one rounding, the store
+// (cache policy OUT_AUX: kSC1 makes an acknowledged store visible device-wide).
+template <int U, bool PEER_F32, bool OUT_F32, int OUT_AUX = 0>
 __device__ __forceinline__ void sum_store_rel(const ReduceArgs& a, const SlabIO& io,
                                               const RelChunks<U, PEER_F32, OUT_F32>& c,
                                               const Raw8<true> (&own)[U]) {
@@ -398,17 +399,42 @@ __device__ __forceinline__ void sum_store_rel(const ReduceArgs& a, const SlabIO&
       f32x4 lo, hi;
       lo[0] = acc.v[0]; lo[1] = acc.v[1]; lo[2] = acc.v[2]; lo[3] = acc.v[3];
       hi[0] = acc.v[4]; hi[1] = acc.v[5]; hi[2] = acc.v[6]; hi[3] = acc.v[7];
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), io.out, c.off[u] * 4, 0, 0);
-      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), io.out, c.off[u] * 4 + 16, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, lo), io.out, c.off[u] * 4, 0,
+                                             OUT_AUX);
+      __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, hi), io.out,
+                                             c.off[u] * 4 + 16, 0, OUT_AUX);
     } else {
       u32x4 o;
       o[0] = pack_bf16x2(acc.v[0], acc.v[1]);
       o[1] = pack_bf16x2(acc.v[2], acc.v[3]);
       o[2] = pack_bf16x2(acc.v[4], acc.v[5]);
       o[3] = pack_bf16x2(acc.v[6], acc.v[7]);
-      __builtin_amdgcn_raw_buffer_store_b128(o, io.out, c.off[u] * 2, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b128(o, io.out, c.off[u] * 2, 0, OUT_AUX);
     }
   }
+}
+
+// The assisted schedule (kernels.h, kAssistCall).  The (sequence number,
+// epoch) word of the call whose fused kernel runs.
+__device__ __forceinline__ uint64_t assist_word(const uint32_t* ctl) {
+  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(ctl + kAssistCall), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t assist_pack(uint32_t seq, uint32_t epoch) {
+  return (uint64_t)seq | ((uint64_t)epoch << 32);
+}
+
+// Claims task j for the call of `epoch`: true if this caller moved its claim
+// word to the epoch, false if someone already had.  Only equality matters, so
+// the words may hold any earlier epoch.
+__device__ __forceinline__ bool claim_task(uint32_t* claims, int j, uint32_t epoch) {
+  uint32_t old = __hip_atomic_load(claims + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  while (old != epoch) {
+    if (__hip_atomic_compare_exchange_strong(claims + j, &old, epoch, __ATOMIC_RELAXED,
+                                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
+      return true;
+  }
+  return false;
 }
 
 // Global task id -> (partition, tile, slab).

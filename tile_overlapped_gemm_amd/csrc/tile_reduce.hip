@@ -71,6 +71,116 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
   if (tid == 0 && !a.nowait) check_out(a.ctl, epoch, (uint32_t)a.checkout_total);
 }
 
+// Wave 0 of an assisted helper, for task j whose flags lane `lane` watches
+// (f; nullptr: none): 1 if the task is or becomes claimed by someone else, 2
+// once its flags are set and this workgroup has claimed it, 0 to leave (the
+// call is over, the sticky error is set, or the watchdog expired; a helper
+// never raises the error itself: the fused kernel does what is left).
+// Uniform across the wave.
+__device__ uint32_t assist_take(const ReduceArgs& a, uint32_t epoch, uint64_t live, int j,
+                                const uint32_t* f, int lane) {
+  auto claimed = [&]() {
+    return __builtin_amdgcn_readfirstlane(
+               __hip_atomic_load(a.claims + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
+           epoch;
+  };
+  if (claimed()) return 1;
+  const uint64_t start = wall_clock64();
+  int nap = 1;
+  while (true) {
+    const uint32_t v = f ? __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) : epoch;
+    if (__all(v == epoch)) break;
+    if (__builtin_amdgcn_readfirstlane(
+            __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
+      return 0;
+    if (assist_word(a.ctl) != live || wall_clock64() - start > a.timeout_ticks) return 0;
+    if (claimed()) return 1;
+    for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(2);
+    nap = min(2 * nap, a.nap_max);
+  }
+  uint32_t won = 0;
+  if (lane == 0) won = claim_task(a.claims, j, epoch) ? 2u : 1u;
+  return __builtin_amdgcn_readfirstlane(won);
+}
+
+// The assisted schedule's helpers (kernels.h, kAssistCall).  They run on the
+// internal stream with no event after the fused kernel of their call, so they
+// may start before it, beside it or after it has finished.  A helper first
+// waits (bounded) until the call's (sequence number, epoch) word shows the
+// fused kernel running, and leaves at once if the call is over or a later
+// call runs.  Then it walks tasks j, j + grid, ... of the production-ordered
+// list: it skips claimed tasks, waits for a task's flags while the call
+// lasts, claims it, reduces it (the fused kernel's slab code, with
+// device-coherent output stores), and once every wave's stores are
+// acknowledged counts it done; the fused kernel's last workgroup waits for
+// that count, so the call's output is complete when the fused kernel ends.
+template <int THREADS, bool PEER_F32, bool OUT_F32>
+__global__ __launch_bounds__(THREADS) void assist_reduce_kernel(ReduceArgs a) {
+  constexpr int kU = 2;  // chunks per thread per pass
+  __shared__ uint32_t s_word[2];
+  const int tid = threadIdx.x;
+  int parity = 0;
+  // Thread 0's v, for every thread, as a wave-uniform value.
+  auto share = [&](uint32_t v) {
+    if (tid == 0) s_word[parity] = v;
+    __syncthreads();
+    const uint32_t out = __builtin_amdgcn_readfirstlane(s_word[parity]);
+    parity ^= 1;
+    return out;
+  };
+  uint32_t epoch = 0;
+  if (tid == 0) {
+    const uint64_t start = wall_clock64();
+    int nap = 1;
+    while (true) {
+      const uint64_t w = assist_word(a.ctl);
+      const uint32_t seq = (uint32_t)w;
+      if (seq == a.assist_seq) {
+        epoch = (uint32_t)(w >> 32);  // 0: the call is over
+        break;
+      }
+      if ((int32_t)(seq - a.assist_seq) > 0 || wall_clock64() - start > a.timeout_ticks) break;
+      for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(2);
+      nap = min(2 * nap, a.nap_max);
+    }
+  }
+  epoch = share(epoch);
+  if (epoch == 0) return;  // uniform
+  const uint64_t live = assist_pack(a.assist_seq, epoch);
+  const int trace_g = a.trace_g ? a.trace_g : (int)gridDim.x;
+  if (a.trace && tid == 0) trace_at(a.trace, a.trace_slot0 + blockIdx.x);
+  for (int j = blockIdx.x; j < a.ntasks; j += gridDim.x) {
+    const TaskRef k = task_ref(a, j);
+    if (k.d != a.rank) continue;  // send tasks are not built here (the host refuses them)
+    uint32_t go = 0;
+    if (tid < 64) go = assist_take(a, epoch, live, j, wait_flag(a, k.d, k.t, tid), tid);
+    // The flag wait and the claim are ordered before every wave's reads.
+    go = share(go);
+    if (go == 0) break;  // uniform
+    if (go == 1) continue;
+    const Slab sl = slab_of(a, k.t, k.slab);
+    const SlabIO io = slab_io<PEER_F32, OUT_F32>(a, sl.e0);
+    for (int c0 = tid; c0 < sl.n_chunks; c0 += kU * THREADS) {
+      RelChunks<kU, PEER_F32, OUT_F32> c;
+      place_rel<kU, THREADS>(sl, c0, c);
+      load_inputs_rel(a, io, c);
+      Raw8<true> own[kU];
+      load_own_rel(io, c, own);
+      sum_store_rel<kU, PEER_F32, OUT_F32, kSC1>(a, io, c, own);
+    }
+    // Every wave's stores acknowledged (device-coherent: visible to any XCD),
+    // then the count.
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_fetch_add(a.ctl + kTasksDone, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (a.trace) {  // uniform: every wave's stores issued
+    __syncthreads();
+    if (tid == 0) trace_at(a.trace, (int64_t)trace_g + a.trace_slot0 + blockIdx.x);
+  }
+}
+
 // The sequential schedule's reduction: no flags; the partition is one flat
 // array of R * N / 8 chunks walked with a grid-stride loop.
 template <int THREADS, bool PEER_F32, bool OUT_F32>
@@ -141,7 +251,57 @@ int regs_threads(int peer_f32, int out_f32) {
   return regs_typed<THREADS, true, true>();
 }
 
+template <int THREADS, bool PEER_F32, bool OUT_F32>
+int assist_regs_typed() {
+  hipFuncAttributes at{};
+  if (hipFuncGetAttributes(&at, (const void*)assist_reduce_kernel<THREADS, PEER_F32, OUT_F32>) !=
+      hipSuccess)
+    return 0;
+  return at.numRegs;
+}
+
+template <int THREADS>
+hipError_t assist_launch_threads(const ReduceArgs& a, int peer_f32, int out_f32, int grid,
+                                 hipStream_t s) {
+  if (!peer_f32 && !out_f32)
+    assist_reduce_kernel<THREADS, false, false><<<grid, THREADS, 0, s>>>(a);
+  else if (!peer_f32 && out_f32)
+    assist_reduce_kernel<THREADS, false, true><<<grid, THREADS, 0, s>>>(a);
+  else if (peer_f32 && !out_f32)
+    assist_reduce_kernel<THREADS, true, false><<<grid, THREADS, 0, s>>>(a);
+  else
+    assist_reduce_kernel<THREADS, true, true><<<grid, THREADS, 0, s>>>(a);
+  return hipGetLastError();
+}
+
+template <int THREADS>
+int assist_regs_threads(int peer_f32, int out_f32) {
+  if (!peer_f32 && !out_f32) return assist_regs_typed<THREADS, false, false>();
+  if (!peer_f32 && out_f32) return assist_regs_typed<THREADS, false, true>();
+  if (peer_f32 && !out_f32) return assist_regs_typed<THREADS, true, false>();
+  return assist_regs_typed<THREADS, true, true>();
+}
+
 }  // namespace
+
+hipError_t launch_assist_reduce(const ReduceArgs& a, int peer_f32, int out_f32, int threads,
+                                int grid, hipStream_t stream) {
+  switch (threads) {
+    case 128: return assist_launch_threads<128>(a, peer_f32, out_f32, grid, stream);
+    case 256: return assist_launch_threads<256>(a, peer_f32, out_f32, grid, stream);
+    case 512: return assist_launch_threads<512>(a, peer_f32, out_f32, grid, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+int assist_registers(int threads, int peer_f32, int out_f32) {
+  switch (threads) {
+    case 128: return assist_regs_threads<128>(peer_f32, out_f32);
+    case 256: return assist_regs_threads<256>(peer_f32, out_f32);
+    case 512: return assist_regs_threads<512>(peer_f32, out_f32);
+    default: return 0;
+  }
+}
 
 int reduce_registers(int threads, int peer_f32, int out_f32) {
   switch (threads) {
