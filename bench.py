@@ -399,6 +399,34 @@ def main() -> int:
             res["ms_per_step"] = res["back_to_back_ms"]
         return res
 
+    def timed_eager(body, steps, warmup):
+        """The same per-step protocol as timed_graph, with the calls issued
+        eagerly (the library's own launches, no graph): the median of `steps`
+        calls each bracketed by HIP events, and the back-to-back mean."""
+        with torch.cuda.stream(stream):
+            for _ in range(warmup):
+                body()
+        stream.synchronize()
+        check_status("after the eager warm-up")
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        with torch.cuda.stream(stream):
+            evs[0].record(stream)
+            for i in range(steps):
+                body()
+                evs[i + 1].record(stream)
+        stream.synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(stream):
+            e0.record(stream)
+            for _ in range(steps):
+                body()
+            e1.record(stream)
+        stream.synchronize()
+        check_status("in the eager timed region")
+        return {"ms_per_step": statistics.median(per), "p10_ms": per[len(per) // 10],
+                "p90_ms": per[(9 * len(per)) // 10], "back_to_back_ms": e0.elapsed_time(e1) / steps}
+
     def lat(r):
         return {"latency_us": r["ms_per_step"] * 1e3,
                 "latency_us_back_to_back": r["back_to_back_ms"] * 1e3}
@@ -435,6 +463,14 @@ def main() -> int:
         f"{n_static} CUs reserved for the reduction: same protocol")
     cp_sh = timed_graph(lambda: call(n_static, cfg_streams), args.steps, args.warmup)
     cp_st = timed_graph(lambda: call(n_static, cfg_static), args.steps, args.warmup)
+    # Eager calls (no graph), where the assisted schedule's helpers run: the
+    # sequential step and the three overlapped schedules at the same budget.
+    log(f"eager calls: sequential, two streams, fused and assisted at budget {ov_budget}")
+    cfg_assist = tog.config(**dict(cfg_kw, schedule=tog.SCHEDULE_ASSISTED, task_slabs=ov_slabs))
+    eg = {"sequential": timed_eager(lambda: call(0), args.steps, args.warmup),
+          "streams": timed_eager(lambda: call(ov_budget, cfg_streams), args.steps, args.warmup),
+          "fused": timed_eager(lambda: call(ov_budget, cfg_fused), args.steps, args.warmup),
+          "assisted": timed_eager(lambda: call(ov_budget, cfg_assist), args.steps, args.warmup)}
 
     # Every rank's step under symmetric peer readiness (each peer's tile counts
     # as ready once this GPU has produced the block at the position where the
@@ -577,6 +613,27 @@ def main() -> int:
     tr_cp_sh = traced(lambda: call(n_static, cfg_streams))
     tr_cp_st = traced(lambda: call(n_static, cfg_static))
 
+    def traced_eager(body, n=21):
+        """The device trace of eager calls (synchronized one by one)."""
+        tog.entwine_trace(True)
+        try:
+            rows = []
+            for _ in range(n):
+                with torch.cuda.stream(stream):
+                    body()
+                stream.synchronize()
+                rows.append(tog.entwine_trace_read())
+        finally:
+            tog.entwine_trace(False)
+        check_status("in the traced eager calls")
+        med = lambda i: statistics.median(r[i] for r in rows)  # noqa: E731
+        return {"gemm_end_us": med(0), "reduce_start_us": med(1), "reduce_end_us": med(2),
+                "tail_us": med(3),
+                "reduce_span_us": statistics.median(r[2] - r[1] for r in rows)}
+
+    tr_eager = {"sequential": traced_eager(lambda: call(0)),
+                "assisted": traced_eager(lambda: call(ov_budget, cfg_assist))}
+
     # Ablations on the paper's two-stream schedule, each leg with the pages'
     # timing protocol (end-to-end median) and the device trace (GEMM end and
     # the communication tail, median of 21 replays).
@@ -679,7 +736,13 @@ def main() -> int:
                            sq["ms_per_step"] / min(ov_s["ms_per_step"], ov_f["ms_per_step"]),
                        # the sender's side of a push-based transfer: every
                        # peer-bound tile also copied, (M - M/P) * N * 2 * 2 bytes more
-                       "push_outgoing": {"streams": lat(pu_s), "fused": lat(pu_f)}},
+                       "push_outgoing": {"streams": lat(pu_s), "fused": lat(pu_f)},
+                       # eager calls, with the assisted schedule (fused kernel
+                       # plus helpers, no join); same budget and slabs
+                       "eager": {**{k: lat(v) for k, v in eg.items()},
+                                 "assisted_speedup_vs_sequential":
+                                     eg["sequential"]["ms_per_step"] / eg["assisted"]["ms_per_step"],
+                                 "trace": tr_eager}},
         # Sec. 5.3.3: shared pool against static CU partitioning, same budget
         "cu_policy": {"reduction_workgroups": n_static, "task_slabs": ov_slabs,
                       "threads": {"shared_pool": threads, "static": 512},
