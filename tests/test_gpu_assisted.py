@@ -117,3 +117,30 @@ def test_assisted_reaches_the_oracle_on_ragged_tiles(dev):
             out = down(case.run(tog.ORDER_INTERLEAVED, budget, schedule=AS, task_slabs=slabs,
                                 block_m=128, block_n=128))
             np.testing.assert_array_equal(out, base)
+
+
+def test_assisted_late_helpers_never_touch_a_later_call(dev):
+    """Sixty calls queued back to back on the smallest shape, where the fused
+    kernel reaches its tasks a few µs after it starts: helpers of one call
+    may still be running when the next call's fused workgroups claim tasks
+    whose flags still hold the earlier epoch.  A claim moves only from an
+    older call's number, so every output must be its own input's."""
+    w = wl.custom("assist_late", 512, 512, 128, 4, rank=1, index=338)
+    Xa, W = wl.operands(w)
+    Xb, _ = wl.operands(wl.custom("assist_late_b", 512, 512, 128, 4, rank=1, index=339))
+    peers = wl.peer_partials(w)
+    cases = (Case(w, Xa, W, peers, dev), Case(w, Xb, W, peers, dev))
+    seq = [down(c.run(tog.ORDER_INTERLEAVED, 0, block_m=128, block_n=128)) for c in cases]
+    assert err_ratio(seq[0], orc.gemm_rs(Xa, W, peers, w.P, w.rank)) <= 1.0
+    assert not np.array_equal(seq[0], seq[1])
+    cfg = cases[0].base_cfg(schedule=AS, task_slabs=2, block_m=128, block_n=128)
+    outs = [torch.full((w.rows, w.N), float("nan"), dtype=torch.bfloat16, device=dev)
+            for _ in range(60)]
+    poison_workspace()
+    for k, o in enumerate(outs):
+        c = cases[k % 2]
+        tog.gemm_rs(c.Xd, c.W_dev(cfg.w_layout), c.pd, o, w.P, w.rank, tog.ORDER_INTERLEAVED,
+                    (1, 4, 16)[k % 3], cfg=cfg)
+    assert tog.entwine_device_status(torch.cuda.current_stream().cuda_stream) == tog.ENTWINE_OK
+    for k, o in enumerate(outs):
+        np.testing.assert_array_equal(down(o), seq[k % 2])

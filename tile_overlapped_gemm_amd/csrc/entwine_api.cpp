@@ -850,7 +850,16 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
       // A fresh sequence number (never 0), and the fork: the helpers start
       // after the caller's earlier work, which wrote the inputs.  No join:
       // the fused kernel ends only once every task is done.
-      if (++w->assist_seq == 0) ++w->assist_seq;
+      if (++w->assist_seq == 0x80000000u) {
+        // Claim words and the liveness word compare sequence numbers within
+        // half the 32-bit range: before leaving it, wait until no kernel of
+        // an earlier call runs, clear both and start again from 1.
+        HIP_TRY(hipStreamSynchronize(stream));
+        HIP_TRY(hipStreamSynchronize(w->s_red));
+        HIP_TRY(hipMemset(w->claims, 0, w->claims_bytes));
+        HIP_TRY(hipMemset(w->ctl + kAssistCall, 0, 2 * sizeof(uint32_t)));
+        w->assist_seq = 1;
+      }
       fa.r.assist_seq = w->assist_seq;
       fa.r.claims = w->claims;
       HIP_TRY(hipEventRecord(w->ev_fork, stream));

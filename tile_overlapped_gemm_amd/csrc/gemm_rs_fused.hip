@@ -157,7 +157,7 @@ __global__ __launch_bounds__(64 * WGM * WGN, 1) void gemm_rs_fused_kernel(FusedA
       int m = 0;
       if (tid == 0)
         for (int b = 0; b < kB; ++b)
-          if (t0 + b * x < r.ntasks && claim_task(r.claims, t0 + b * x, epoch)) m |= 1 << b;
+          if (t0 + b * x < r.ntasks && claim_task(r.claims, t0 + b * x, r.assist_seq)) m |= 1 << b;
       mine = share(m);
       if (mine == 0) return true;
     }

@@ -83,8 +83,8 @@ struct ReduceArgs {
   int32_t trace_slot0, trace_g;
   int32_t checkout_total;           // as GemmArgs::checkout_total
   // The assisted schedule (see kAssistCall): the call's sequence number
-  // (0: not assisted) and one claim word per task (the epoch of the call in
-  // which the task was claimed).
+  // (0: not assisted) and one claim word per task (the sequence number of
+  // the call in which the task was last claimed).
   uint32_t assist_seq;
   uint32_t* claims;
   // A waiting workgroup's pause between two polls starts at 128 clock cycles
@@ -115,9 +115,12 @@ struct ReduceArgs {
 // epoch) of the call whose fused kernel is running, (sequence number, 0)
 // once it has finished: the helpers of call s work only while it reads
 // (s, e), so a helper that starts late or outlives its call does nothing.
-// A task goes to whoever first moves its claim word to the call's epoch
-// (compare-and-swap); kTasksDone counts the completed tasks, and the fused
-// kernel's last workgroup waits for all of them before it finishes the call.
+// A task goes to whoever first moves its claim word to the call's sequence
+// number (compare-and-swap), which succeeds only from an older call's
+// number: a helper that outlives its call can never take a task from a later
+// one, even while that task's flag still holds the earlier call's epoch.
+// kTasksDone counts the completed tasks, and the fused kernel's last
+// workgroup waits for all of them before it finishes the call.
 // No wait ever depends on a helper being scheduled: a helper claims a task
 // only once the task's flags are set, so a claimed task always completes.
 enum {

@@ -424,13 +424,18 @@ __device__ __forceinline__ uint64_t assist_pack(uint32_t seq, uint32_t epoch) {
   return (uint64_t)seq | ((uint64_t)epoch << 32);
 }
 
-// Claims task j for the call of `epoch`: true if this caller moved its claim
-// word to the epoch, false if someone already had.  Only equality matters, so
-// the words may hold any earlier epoch.
-__device__ __forceinline__ bool claim_task(uint32_t* claims, int j, uint32_t epoch) {
+// Sequence numbers of assisted calls compare within half the 32-bit range
+// (the host clears the claim words before a call's number would leave it).
+__device__ __forceinline__ bool seq_newer(uint32_t a, uint32_t b) { return (int32_t)(a - b) > 0; }
+
+// Claims task j for the assisted call `seq`: true if this caller moved the
+// task's claim word from an older call's number to seq; false if the word
+// already holds seq (someone of this call has the task) or a later call's
+// number (this call is over).
+__device__ __forceinline__ bool claim_task(uint32_t* claims, int j, uint32_t seq) {
   uint32_t old = __hip_atomic_load(claims + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (old != epoch) {
-    if (__hip_atomic_compare_exchange_strong(claims + j, &old, epoch, __ATOMIC_RELAXED,
+  while (seq_newer(seq, old)) {
+    if (__hip_atomic_compare_exchange_strong(claims + j, &old, seq, __ATOMIC_RELAXED,
                                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT))
       return true;
   }

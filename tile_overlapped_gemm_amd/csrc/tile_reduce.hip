@@ -72,19 +72,24 @@ __global__ __launch_bounds__(THREADS) void tile_reduce_kernel(ReduceArgs a) {
 }
 
 // Wave 0 of an assisted helper, for task j whose flags lane `lane` watches
-// (f; nullptr: none): 1 if the task is or becomes claimed by someone else, 2
-// once its flags are set and this workgroup has claimed it, 0 to leave (the
-// call is over, the sticky error is set, or the watchdog expired; a helper
-// never raises the error itself: the fused kernel does what is left).
-// Uniform across the wave.
+// (f; nullptr: none): 1 if the task is or becomes claimed by someone else of
+// this call, 2 once its flags are set and this workgroup has claimed it, 0 to
+// leave (the call is over -- its liveness word has changed or a later call
+// holds the task --, the sticky error is set, or the watchdog expired; a
+// helper never raises the error itself: the fused kernel does what is left).
+// A helper that outlives its call cannot take a task of a later one: the
+// claim moves a word only from an older call's number (claim_task), so flags
+// that still hold this call's epoch do not matter.  Uniform across the wave.
 __device__ uint32_t assist_take(const ReduceArgs& a, uint32_t epoch, uint64_t live, int j,
                                 const uint32_t* f, int lane) {
-  auto claimed = [&]() {
-    return __builtin_amdgcn_readfirstlane(
-               __hip_atomic_load(a.claims + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) ==
-           epoch;
+  // 1: claimed in this call; 0: a later call has claimed it; 2: free.
+  auto state = [&]() -> uint32_t {
+    const uint32_t c = __builtin_amdgcn_readfirstlane(
+        __hip_atomic_load(a.claims + j, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+    return c == a.assist_seq ? 1u : seq_newer(c, a.assist_seq) ? 0u : 2u;
   };
-  if (claimed()) return 1;
+  uint32_t st = state();
+  if (st != 2) return st;
   const uint64_t start = wall_clock64();
   int nap = 1;
   while (true) {
@@ -94,12 +99,12 @@ __device__ uint32_t assist_take(const ReduceArgs& a, uint32_t epoch, uint64_t li
             __hip_atomic_load(a.error, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) != 0)
       return 0;
     if (assist_word(a.ctl) != live || wall_clock64() - start > a.timeout_ticks) return 0;
-    if (claimed()) return 1;
+    if ((st = state()) != 2) return st;
     for (int i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(2);
     nap = min(2 * nap, a.nap_max);
   }
   uint32_t won = 0;
-  if (lane == 0) won = claim_task(a.claims, j, epoch) ? 2u : 1u;
+  if (lane == 0) won = claim_task(a.claims, j, a.assist_seq) ? 2u : 1u;
   return __builtin_amdgcn_readfirstlane(won);
 }
 
