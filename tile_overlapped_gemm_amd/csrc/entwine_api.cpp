@@ -758,10 +758,18 @@ int run(const void* X, const void* W, const void* const* peers, void* out, int64
         return fail(ENTWINE_ERR_INVALID_ARGUMENT, "tracing is on: make the same call once "
                     "outside the capture first");
       if (w->trace) {
-        if (w->captured)
+        if (w->captured) {
           w->retired.push_back(w->trace);  // a captured graph may still use it
-        else
+        } else {
+          // Kernels of earlier calls may still write their stamps: the
+          // internal stream's (an assisted call's helpers are never joined)
+          // and the previous eager call's.
+          if (hipStreamSynchronize(w->s_red) != hipSuccess ||
+              (w->have_prev && (hipEventSynchronize(w->ev_gemm) != hipSuccess ||
+                                hipEventSynchronize(w->ev_red) != hipSuccess)))
+            return fail(ENTWINE_ERR_HIP, "trace slots: synchronization failed");
           (void)hipFree(w->trace);
+        }
       }
       w->trace = nullptr;
       w->trace_bytes = 0;
