@@ -16,7 +16,9 @@
 //  * 512 threads = 8 waves of 64 (two per SIMD, so one wave's waits are
 //    covered by the other's MFMAs) in a 2 x 4 (or 4 x 2) arrangement; a wave
 //    owns a (BM/WGM) x (BN/WGN) sub-block computed with
-//    v_mfma_f32_32x32x16_bf16 into fp32 accumulators.  A 4-wave (2 x 2)
+//    v_mfma_f32_16x16x32_bf16 into fp32 accumulators (the 32 x 32 x 16 form
+//    builds with -DENTWINE_MFMA_EDGE=32: the same nominal rate, but the chip
+//    clocks lower under it).  A 4-wave (2 x 2)
 //    instance remains as variant 3, and variant 4 of 256 x 256 runs the
 //    ping-pong schedule of gemm_block.h (the dispatcher places waves i and
 //    i + 4 of a workgroup on the same SIMD).  128 x 384 blocks (64 x 96 per
@@ -24,21 +26,25 @@
 //    128 x 128, each with 1.5 times the MFMA work per byte loaded.  The MFMA's
 //    first operand is the W fragment and the second the X fragment, so each
 //    lane holds runs of 4 consecutive output columns.
-//  * K advances in stages of 64 (128 bytes per row).  X and W are both
-//    K-contiguous, so each stage is a BM x 128 B and a BN x 128 B slab.  Slabs
+//  * K advances in stages of 64 (128 bytes per row).  X is K-contiguous, so
+//    each stage's X slab is BM x 128 B; W's is BN x 128 B when W is held
+//    [N][K], and 64 rows of BN columns when it is held [K][N] (the default),
+//    transposed on its way into the MFMA by transposing LDS reads.  Slabs
 //    move from global memory straight into LDS with buffer_load_dwordx4 ...
 //    lds: one wave instruction fills 1 KiB = 8 rows.  The buffer descriptors
 //    bound the block's rows, so rows past the partition's (or N's) end read as
 //    zeros without any clamping.  Two LDS stages: the loads of stage k+1 are
 //    in flight while stage k is multiplied.
 //  * LDS rows are XOR-swizzled in 16-byte chunks (chunk c of row r is stored
-//    at c ^ swz(r)), so the 32 rows one fragment read touches spread over all
-//    banks.  The swizzle is realised through each lane's global source
-//    address, since the LDS destination of lane l is fixed at 16*l.
-//  * Fragments are double-buffered in registers across the four 16-deep K
-//    steps of a stage and across the stage boundary: the workgroup barrier
-//    that hands over the next stage sits before the last K step's MFMAs, which
-//    cover the barrier and the next stage's first fragment reads.
+//    at c ^ swz(r), a function chosen per MFMA form by the bank-conflict
+//    counter), so the rows one fragment read touches spread over all banks.
+//    The swizzle is realised through each lane's global source address,
+//    since the LDS destination of lane l is fixed at 16*l.
+//  * Each 32-deep K step runs in four quarters (X half times W half of the
+//    wave's tiles); a quarter's fragments are read from LDS while the
+//    previous quarter's MFMAs run.  The workgroup barrier that hands over the
+//    next stage sits before the last quarter of the stage, whose MFMAs cover
+//    the barrier and the next stage's first fragment reads.
 //  * Epilogue: accumulators leave through LDS in 32-row strips so that the
 //    global stores write whole cache lines.
 //  * Publication: tiles read on this device are written with device-coherent

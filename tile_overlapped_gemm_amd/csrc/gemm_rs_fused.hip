@@ -41,6 +41,12 @@
 // Check-out.  Every workgroup counts itself out; the last one clears the
 // tickets and advances the epoch, so the next call (or graph replay) starts
 // from zeroed tickets with a fresh epoch.
+//
+// The assisted schedule runs this kernel beside helper workgroups on another
+// stream (tile_reduce.hip, assist_reduce_kernel).  Then a worker reduces only
+// the tasks it claims (a claim word per task, moved to the call's sequence
+// number), every claimer counts its finished tasks, and the last workgroup
+// waits for the count to reach the task count before it finishes the call.
 #include "gemm_block.h"
 #include "reduce_task.h"
 
