@@ -659,6 +659,14 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
 #pragma unroll
       for (int v = 0; v < (S::kMF == 16 ? 4 : 16); ++v) acc.c[i][j][v] = 0.0f;
 
+  // The epilogue's publication arguments, loaded now into scalar registers:
+  // a scalar load still in flight when the main loop starts would make the
+  // compiler wait for every outstanding LDS read (lgkmcnt 0) at the top of
+  // each K stage, since scalar loads may return in any order.
+  int publish = __builtin_amdgcn_readfirstlane(a.publish);
+  int flag_all = __builtin_amdgcn_readfirstlane(a.flag_all);
+  asm volatile("" : "+s"(publish), "+s"(flag_all));
+
   const int nk = K / BK;
   if constexpr (PP)
     pingpong_loop<S>(acc, ra, rb, smem, ln, nk, wave);
@@ -707,7 +715,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   const int csub16 = (lane % kLanes16) * 8;
   const int col16 = col0 + wn * S::kWN + csub16;
   const bool col16_ok = col16 < a.N;
-  const bool coherent = local ? a.publish != 0 : a.publish == 2;
+  const bool coherent = local ? publish != 0 : publish == 2;
   const int strip_bytes = 32 * a.N * (local || a.outgoing_f32 ? 4 : 2);
   static_assert(S::kWM % 32 == 0, "the wave sub-block splits into 32-row strips");
 #pragma unroll
@@ -818,7 +826,7 @@ __device__ __forceinline__ void gemm_block(const GemmArgs& a, const int4 blk, in
   // the XCD's whole L2 (which an agent-scope release fence would issue).
   // Flags of tiles bound for peers only mark progress; they are stored when
   // some wait reads them (flag_all).
-  if (a.publish != 0 && (local || a.flag_all)) {
+  if (publish != 0 && (local || flag_all)) {
     __builtin_amdgcn_sched_barrier(0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
